@@ -1,0 +1,164 @@
+"""CPU oracle for the KDA forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product path (the HIP library and its Python binding)
+never imports, links or calls anything here, and this package imports nothing
+from the product path: the two share no code.
+
+Contents
+  * ``forward`` / ``forward_arrays``: the fp64 token-by-token recurrence in C
+    (kda_oracle.c, OpenMP over independent (sequence, head) chains).  It is
+    the plain definition of the method: decay, erase, write, then read
+    ("Kimi K3 の KDA ..." page, section 1.2.1; "GDN, KDA の整理", sections
+    "Kimi Delta Attention" and "Online learning").
+  * ``decode_steps``: the same recurrence, one token per call, carrying the
+    fp64 state between calls (the recurrent form that the chunkwise page
+    assigns to decode: "Kimi K3 模型结构（2）", Q&A on train/prefill/decode).
+  * ``product_form``: a second, independently written NumPy formulation that
+    builds each transition matrix (I - beta k k^T) Diag(alpha) explicitly
+    (page 1, section 2.3.5: the state map is the ordered product of per-token
+    transitions).  Used for tiny brute-force checks.
+
+Every function here is pinned by tests in tests/test_oracle_pins.py against
+identities the pages state and textbook linear algebra; see each test's
+docstring for the passage it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+EPS = 1e-6  # inside the square root of the L2 norm (the pages give no value)
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (host only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                               "-std=c99", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        f = lib.kda_oracle_forward
+        f.restype = ctypes.c_int
+        P = ctypes.c_void_p
+        f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int, P] + [P] * 5 + [P, ctypes.c_double,
+                                                                         ctypes.c_double, ctypes.c_int,
+                                                                         P, P, ctypes.c_int]
+        lib.kda_oracle_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return _load().kda_oracle_num_threads()
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def forward_arrays(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, scale=1.0, eps=EPS,
+                   normalize=True, want_o=True, threads=0):
+    """Run the recurrence.  q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]
+    (all converted to fp32, which is exact for bf16 values); init_state
+    [N,H,dk,dv] (converted to fp64).  Returns (o fp64 [B,T,H,dv] or None,
+    final_state fp64 [N,H,dk,dv])."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and g.shape == q.shape and v.shape == (B, T, H, dv)
+    assert beta.shape == (B, T, H)
+    cu = None
+    N = B
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        N = len(cu) - 1
+    s0 = None
+    if init_state is not None:
+        s0 = np.ascontiguousarray(init_state, dtype=np.float64)
+        assert s0.shape == (N, H, dk, dv)
+    o = np.empty((B, T, H, dv), dtype=np.float64) if want_o else None
+    sT = np.empty((N, H, dk, dv), dtype=np.float64)
+    rc = lib.kda_oracle_forward(B, T, H, dk, dv, N, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(s0), float(scale), float(eps), int(bool(normalize)),
+                                _ptr(o), _ptr(sT), int(threads))
+    if rc != 0:
+        raise ValueError("kda_oracle_forward rejected its arguments")
+    return o, sT
+
+
+def forward(inp, heads: Optional[slice] = None, *, scale=1.0, want_o=True, threads=0):
+    """Oracle on a kda_inputs.PrefillInputs, optionally on a subset of heads."""
+    s0 = inp.f32("init_state", heads) if inp.init_state is not None else None
+    return forward_arrays(inp.f32("q", heads), inp.f32("k", heads), inp.f32("v", heads),
+                          inp.g if heads is None else inp.g[:, :, heads],
+                          inp.beta if heads is None else inp.beta[:, :, heads],
+                          s0, inp.cu_seqlens, scale=scale, want_o=want_o, threads=threads)
+
+
+def decode_steps(state, q, k, v, g, beta, *, scale=1.0, threads=0):
+    """One recurrent step for every (n, h): q, k, g [N,H,dk]; v [N,H,dv];
+    beta [N,H]; state fp64 [N,H,dk,dv].  Returns (o [N,H,dv], new state)."""
+    N, H, dk = np.shape(q)
+    dv = np.shape(v)[-1]
+    o, sT = forward_arrays(np.reshape(q, (N, 1, H, dk)), np.reshape(k, (N, 1, H, dk)),
+                           np.reshape(v, (N, 1, H, dv)), np.reshape(g, (N, 1, H, dk)),
+                           np.reshape(beta, (N, 1, H)), state, scale=scale, threads=threads)
+    return o[:, 0], sT
+
+
+# ----------------------------------------------------------------------------
+# Second formulation: explicit transition matrices (tiny sizes only)
+# ----------------------------------------------------------------------------
+def transition(alpha, beta, k):
+    """(I - beta k k^T) Diag(alpha) for one token, general real alpha and beta
+    (the signed-gate / beta in [0, 2] range of the Complex KDA pages is
+    allowed here so the worked rotation example can pin this function)."""
+    alpha = np.asarray(alpha, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    d = k.shape[0]
+    return (np.eye(d) - beta * np.outer(k, k)) @ np.diag(alpha)
+
+
+def product_form(q, k, v, g, beta, S0=None, *, scale=1.0, eps=EPS):
+    """One chain, explicit matrices: S_t = M_t S_{t-1} + beta_t k^_t v_t^T with
+    M_t = (I - beta_t k^_t k^_t^T) Diag(exp g_t); o_t = scale * S_t^T q^_t.
+    q, k, g: [T, dk]; v: [T, dv]; beta: [T].  Returns (o [T, dv], S_T)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g = np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        qh = q[t] / np.sqrt(q[t] @ q[t] + eps)
+        kh = k[t] / np.sqrt(k[t] @ k[t] + eps)
+        M = transition(np.exp(g[t]), beta[t], kh)
+        S = M @ S + beta[t] * np.outer(kh, v[t])
+        o[t] = scale * (S.T @ qh)
+    return o, S

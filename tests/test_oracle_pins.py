@@ -1,0 +1,367 @@
+"""Pins for the CPU oracle: every check compares it with something other than
+itself -- a closed form, an identity the pages state, a worked example they
+print, or a second formulation written independently.  CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import kda_inputs
+import oracle
+from oracle import chunk_model
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng0 = np.random.default_rng(1234)
+
+
+def _rand_chain(rng, T, dk, dv, gate_lo=-5.0, beta_hi=1.0):
+    q = rng.standard_normal((T, dk)).astype(np.float32)
+    k = rng.standard_normal((T, dk)).astype(np.float32)
+    v = rng.standard_normal((T, dv)).astype(np.float32)
+    g = rng.uniform(gate_lo, 0.0, (T, dk)).astype(np.float32)
+    beta = rng.uniform(0.0, beta_hi, T).astype(np.float32)
+    return q, k, v, g, beta
+
+
+def _run(q, k, v, g, beta, S0=None, eps=oracle.EPS, scale=1.0):
+    """C oracle on one chain."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    o, sT = oracle.forward_arrays(q[None, :, None], k[None, :, None], v[None, :, None], g[None, :, None],
+                                  beta[None, :, None], None if S0 is None else S0[None, None],
+                                  eps=eps, scale=scale)
+    return o[0, :, 0], sT[0, 0]
+
+
+def _unit(x, eps=oracle.EPS):
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(x @ x + eps)
+
+
+# ---------------------------------------------------------------------------
+# P1 -- brute force: the general solution of the affine recurrence as an
+# ordered product of transitions ("Kimi K3 の KDA ..." section 2.3.5: the
+# state map is prod_t T_t, later factors on the left; section 2.3.4.1: the
+# composed write term of (A2,b2)o(A1,b1) is A2 b1 + b2).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [2, 3, 4, 8])
+@pytest.mark.parametrize("T", [1, 5, 12])
+def test_brute_force_transition_products(d, T):
+    rng = np.random.default_rng(100 * d + T)
+    q, k, v, g, beta = _rand_chain(rng, T, d, d + 1)
+    S0 = rng.standard_normal((d, d + 1))
+    o, sT = _run(q, k, v, g, beta, S0)
+    kh = [_unit(k[t]) for t in range(T)]
+    M = [oracle.transition(np.exp(g[t].astype(np.float64)), float(beta[t]), kh[t]) for t in range(T)]
+
+    def prod(lo, hi):  # M_{hi-1} ... M_lo  (empty product = I)
+        P = np.eye(d)
+        for t in range(lo, hi):
+            P = M[t] @ P
+        return P
+
+    for t in range(T):
+        St = prod(0, t + 1) @ S0
+        for s in range(t + 1):
+            St = St + prod(s + 1, t + 1) @ (float(beta[s]) * np.outer(kh[s], v[s]))
+        np.testing.assert_allclose(o[t], St.T @ _unit(q[t]), rtol=1e-12, atol=1e-12)
+        if t == T - 1:
+            np.testing.assert_allclose(sT, St, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P2 -- the worked example printed with Figure 1 of the Complex KDA review
+# ---------------------------------------------------------------------------
+def test_worked_example_rotation():
+    with open(os.path.join(GOLDEN, "rotation_90.json")) as f:
+        ex = json.load(f)
+    M = oracle.transition(ex["alpha"], ex["beta"], ex["k"])
+    np.testing.assert_allclose(M, np.array(ex["expected_transition"]), atol=1e-15)
+    assert abs(np.linalg.det(M) - 1.0) < 1e-14
+    np.testing.assert_allclose(M.T @ M, np.eye(2), atol=1e-15)
+    # rotates (1,0) by +90 degrees
+    angle = np.degrees(np.arctan2(*(M @ np.array([1.0, 0.0]))[::-1]))
+    assert abs(angle - ex["rotation_degrees"]) < 1e-12
+
+
+def test_printed_constants():
+    with open(os.path.join(GOLDEN, "printed_constants.json")) as f:
+        c = json.load(f)
+    assert abs(np.exp(-c["g_min"] * c["sub_tile"]) / c["exp80_approx"] - 1) < 0.01
+    bf16_max = float(kda_inputs.bf16_to_f32(np.array([0x7F7F], np.uint16))[0])
+    assert abs(bf16_max / c["bf16_max_approx"] - 1) < 0.01
+    assert np.exp(-c["g_min"] * c["sub_tile"]) < bf16_max
+    assert abs(np.exp(c["g_min"]) - c["exp_minus5_approx"]) < 5e-5
+    assert chunk_model.SUB == c["sub_tile"]
+
+
+# ---------------------------------------------------------------------------
+# P3 -- GDN reduction ("GDN, KDA の整理", section "Kimi Delta Attention":
+# D_t = alpha_t I gives Gated DeltaNet)
+# ---------------------------------------------------------------------------
+def test_gdn_reduction():
+    rng = np.random.default_rng(3)
+    T, dk, dv = 40, 16, 12
+    q, k, v, _, beta = _rand_chain(rng, T, dk, dv)
+    a = rng.uniform(-3.0, 0.0, T).astype(np.float32)
+    g = np.repeat(a[:, None], dk, axis=1)
+    o, sT = _run(q, k, v, g, beta)
+    # scalar-gated delta rule, written in its own (GDN) form
+    S = np.zeros((dk, dv))
+    for t in range(T):
+        kh = _unit(k[t])
+        alpha = np.exp(np.float64(a[t]))
+        S = alpha * (S - beta[t] * np.outer(kh, kh @ S)) + beta[t] * np.outer(kh, v[t])
+        np.testing.assert_allclose(o[t], S.T @ _unit(q[t]), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sT, S, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P4 -- beta = 0: pure decay, S_t = Diag(exp(sum_{u<=t} g_u)) S_0
+# ("Kimi K3 の KDA ..." section 2.3.5, pure-decay approximation)
+# ---------------------------------------------------------------------------
+def test_beta_zero_closed_form():
+    rng = np.random.default_rng(4)
+    T, dk, dv = 33, 8, 5
+    q, k, v, g, _ = _rand_chain(rng, T, dk, dv, gate_lo=-0.5)
+    beta = np.zeros(T, np.float32)
+    S0 = rng.standard_normal((dk, dv))
+    o, sT = _run(q, k, v, g, beta, S0)
+    cum = np.cumsum(g.astype(np.float64), axis=0)
+    for t in range(T):
+        St = np.exp(cum[t])[:, None] * S0
+        np.testing.assert_allclose(o[t], St.T @ _unit(q[t]), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(sT, np.exp(cum[-1])[:, None] * S0, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P5 -- non-expansiveness (page 1 section 1.2.1: L2-normalised k keeps the
+# erase operator's spectral norm <= 1; Complex KDA review, key terms)
+# ---------------------------------------------------------------------------
+def test_non_expansive():
+    rng = np.random.default_rng(5)
+    T, dk, dv = 50, 16, 8
+    q, k, _, g, beta = _rand_chain(rng, T, dk, dv, gate_lo=-0.05)
+    v = np.zeros((T, dv), np.float32)
+    S0 = rng.standard_normal((dk, dv))
+    norms = [np.linalg.norm(S0)]
+    for t in range(1, T + 1):
+        _, sT = _run(q[:t], k[:t], v[:t], g[:t], beta[:t], S0)
+        norms.append(np.linalg.norm(sT))
+    assert all(n2 <= n1 * (1 + 1e-13) for n1, n2 in zip(norms, norms[1:]))
+    assert norms[-1] < norms[0]
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.3, 1.0])
+def test_erase_operator_spectrum(beta):
+    k = _unit(rng0.standard_normal(7), eps=0.0)
+    E = np.eye(7) - beta * np.outer(k, k)
+    ev = np.sort(np.linalg.eigvalsh(E))
+    np.testing.assert_allclose(ev, np.sort([1.0 - beta] + [1.0] * 6), atol=1e-14)
+    assert np.linalg.norm(E, 2) <= 1 + 1e-14
+
+
+# ---------------------------------------------------------------------------
+# P6 -- local loss: after the update the residual on k is (1-beta) times the
+# pre-update one; beta = 1 recalls v exactly ("GDN, KDA の整理", 局所損失)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("b_last", [0.37, 1.0])
+def test_residual_contraction(b_last):
+    rng = np.random.default_rng(6)
+    T, dk, dv = 20, 12, 9
+    q, k, v, g, beta = _rand_chain(rng, T, dk, dv)
+    beta[-1] = b_last
+    _, s_prev = _run(q[:-1], k[:-1], v[:-1], g[:-1], beta[:-1], eps=0.0)
+    _, s_T = _run(q, k, v, g, beta, eps=0.0)
+    kh = _unit(k[-1], eps=0.0)
+    S_tilde = np.exp(g[-1].astype(np.float64))[:, None] * s_prev
+    r_pre = v[-1] - S_tilde.T @ kh
+    r_post = v[-1] - s_T.T @ kh
+    np.testing.assert_allclose(r_post, (1.0 - b_last) * r_pre, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P7 -- a query orthogonal to k_t does not see the delta update
+# ("GDN, KDA の整理", 局所損失, last paragraph)
+# ---------------------------------------------------------------------------
+def test_orthogonal_query():
+    rng = np.random.default_rng(7)
+    T, dk, dv = 15, 10, 6
+    q, k, v, g, beta = _rand_chain(rng, T, dk, dv)
+    kk = k[-1].astype(np.float64)
+    qq = rng.standard_normal(dk)
+    qq -= (qq @ kk) / (kk @ kk) * kk
+    q[-1] = qq.astype(np.float32)
+    qq = q[-1].astype(np.float64)
+    assert abs(qq @ kk) < 1e-5 * np.linalg.norm(qq) * np.linalg.norm(kk)
+    _, s_prev = _run(q[:-1], k[:-1], v[:-1], g[:-1], beta[:-1])
+    o, _ = _run(q, k, v, g, beta)
+    S_tilde = np.exp(g[-1].astype(np.float64))[:, None] * s_prev
+    np.testing.assert_allclose(o[-1], S_tilde.T @ _unit(qq), atol=1e-6 * np.abs(o[-1]).max() + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P8 -- fixed point of a repeated affine map x* = (I - A)^-1 b
+# ("Kimi K3 の KDA ..." section 2.3.3, item 3)
+# ---------------------------------------------------------------------------
+def test_fixed_point_long_run():
+    rng = np.random.default_rng(8)
+    dk, dv, n = 8, 5, 40000
+    k1 = rng.standard_normal(dk)
+    v1 = rng.standard_normal(dv)
+    g1 = np.full(dk, -1e-3)
+    b1 = 0.5
+    q = np.tile(rng.standard_normal(dk), (n, 1)).astype(np.float32)
+    k = np.tile(k1, (n, 1)).astype(np.float32)
+    v = np.tile(v1, (n, 1)).astype(np.float32)
+    g = np.tile(g1, (n, 1)).astype(np.float32)
+    beta = np.full(n, b1, np.float32)
+    _, sT = _run(q, k, v, g, beta)
+    kh = _unit(k[0])
+    M = oracle.transition(np.exp(g[0].astype(np.float64)), float(beta[0]), kh)
+    Sstar = np.linalg.solve(np.eye(dk) - M, float(beta[0]) * np.outer(kh, v[0]))
+    np.testing.assert_allclose(sT, Sstar, rtol=1e-9, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# P9 / P10 -- associativity (split and hand-off) and the identity (empty
+# segment) of the affine monoid ("Kimi K3 の KDA ..." sections 2.3.4.2,
+# 2.3.4.3 and 2.3.4.5)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("split", [0, 1, 17, 63, 64, 65, 100, 130])
+def test_split_handoff(split):
+    rng = np.random.default_rng(9)
+    T, dk, dv = 130, 16, 16
+    q, k, v, g, beta = _rand_chain(rng, T, dk, dv)
+    S0 = rng.standard_normal((dk, dv))
+    o, sT = _run(q, k, v, g, beta, S0)
+    o1, s1 = _run(q[:split], k[:split], v[:split], g[:split], beta[:split], S0)
+    o2, s2 = _run(q[split:], k[split:], v[split:], g[split:], beta[split:], s1)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s2, sT, rtol=1e-12, atol=1e-13)
+
+
+def test_empty_sequence_is_identity_and_varlen_packing():
+    rng = np.random.default_rng(10)
+    H, dk, dv = 3, 8, 6
+    lens = [5, 0, 70, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = rng.standard_normal((1, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((1, T, H, dk)).astype(np.float32)
+    v = rng.standard_normal((1, T, H, dv)).astype(np.float32)
+    g = rng.uniform(-5, 0, (1, T, H, dk)).astype(np.float32)
+    beta = rng.uniform(0, 1, (1, T, H)).astype(np.float32)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    o, sT = oracle.forward_arrays(q, k, v, g, beta, S0, cu)
+    np.testing.assert_array_equal(sT[1], S0[1])
+    for n, L in enumerate(lens):
+        a, b = cu[n], cu[n + 1]
+        on, sn = oracle.forward_arrays(q[:, a:b], k[:, a:b], v[:, a:b], g[:, a:b], beta[:, a:b], S0[n:n + 1])
+        np.testing.assert_array_equal(sn[0], sT[n])
+        np.testing.assert_array_equal(on[0], o[0, a:b])
+
+
+# ---------------------------------------------------------------------------
+# P11 -- column independence: the d_v columns are independent affine systems
+# sharing one transition ("Kimi K3 の KDA ..." section 2.3.2)
+# ---------------------------------------------------------------------------
+def test_column_independence():
+    rng = np.random.default_rng(11)
+    T, dk, dv = 90, 12, 10
+    q, k, v, g, beta = _rand_chain(rng, T, dk, dv)
+    S0 = rng.standard_normal((dk, dv))
+    o, sT = _run(q, k, v, g, beta, S0)
+    J = [1, 4, 9]
+    oj, sj = _run(q, k, np.ascontiguousarray(v[:, J]), g, beta, np.ascontiguousarray(S0[:, J]))
+    np.testing.assert_array_equal(oj, o[:, J])
+    np.testing.assert_array_equal(sj, sT[:, J])
+
+
+# ---------------------------------------------------------------------------
+# P12 -- non-commutativity: order matters ("Kimi K3 の KDA ..." section 2.3.4.6)
+# ---------------------------------------------------------------------------
+def test_order_sensitivity():
+    rng = np.random.default_rng(12)
+    T, dk, dv = 6, 6, 4
+    q, k, v, g, beta = _rand_chain(rng, T, dk, dv)
+    _, sT = _run(q, k, v, g, beta)
+    perm = np.array([0, 1, 3, 2, 4, 5])
+    _, sP = _run(q[perm], k[perm], v[perm], g[perm], beta[perm])
+    assert np.abs(sT - sP).max() > 1e-3
+    # the decay matrices alone commute
+    a, b = np.diag(np.exp(g[2])), np.diag(np.exp(g[3]))
+    np.testing.assert_allclose(a @ b, b @ a)
+
+
+# ---------------------------------------------------------------------------
+# P13 -- two formulations agree: innovation form (C) vs explicit product of
+# transition matrices (NumPy) -- page 1 section 1.2.1 (innovation) and
+# "GDN, KDA の整理" section "Online learning" (gradient step on the decayed state)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scale", [1.0, 0.125])
+def test_innovation_vs_product_form(scale):
+    rng = np.random.default_rng(13)
+    T, dk, dv = 77, 32, 24
+    q, k, v, g, beta = _rand_chain(rng, T, dk, dv)
+    S0 = 0.1 * rng.standard_normal((dk, dv))
+    o, sT = _run(q, k, v, g, beta, S0, scale=scale)
+    op, sp = oracle.product_form(q, k, v, g, beta, S0, scale=scale)
+    np.testing.assert_allclose(o, op, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(sT, sp, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P14 -- the chunk algebra (WY/UT form with 16-token sub-tile references)
+# equals the token recurrence, including partial chunks
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,gate", [(1, "k3"), (16, "k3"), (63, "sigmoid"), (64, "k3"),
+                                    (65, "slow"), (200, "k3"), (257, "sigmoid")])
+def test_chunk_model_matches_token_oracle(T, gate):
+    inp = kda_inputs.make_prefill(21 + T, 1, T, 2, 32, 24, dtype="bf16", gate=gate, s0_std=0.02)
+    o, sT = oracle.forward(inp)
+    for h in range(2):
+        oc, sc = chunk_model.chunk_chain(inp.f32("q")[0, :, h], inp.f32("k")[0, :, h], inp.f32("v")[0, :, h],
+                                         inp.g[0, :, h], inp.beta[0, :, h], inp.f32("init_state")[0, h])
+        scale = np.sqrt(np.mean(o[0, :, h] ** 2))
+        assert np.abs(oc - o[0, :, h]).max() <= 1e-12 * max(scale, 1e-30) + 1e-15
+        assert np.abs(sc - sT[0, h]).max() <= 1e-12
+
+
+def test_chunk_model_bounded_factors_at_gmin():
+    """All gates at the lower bound -5 (the worst case the pages allow): the
+    sub-tile factors stay finite in fp32 and the model still matches."""
+    rng = np.random.default_rng(14)
+    T, dk, dv = 128, 16, 8
+    q, k, v, _, beta = _rand_chain(rng, T, dk, dv)
+    g = np.full((T, dk), -5.0, np.float32)
+    o, sT = _run(q, k, v, g, beta)
+    oc, sc = chunk_model.chunk_chain(q, k, v, g, beta, prec=dict(aqk="f32", akk="f32"))
+    assert np.all(np.isfinite(oc))
+    np.testing.assert_allclose(oc, o, rtol=1e-4, atol=1e-6)
+    np.testing.assert_allclose(sc, sT, rtol=1e-4, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# input generator sanity (not a pin of the method)
+# ---------------------------------------------------------------------------
+def test_bf16_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e38], np.float32)
+    bits = kda_inputs.bf16_bits(x)
+    back = kda_inputs.bf16_to_f32(bits)
+    assert back[0] == 1.0
+    assert back[1] == 1.0                       # tie -> even (mantissa 0)
+    assert back[2] == 1.0 + 4 * 2 ** -8         # tie -> even (round up)
+    assert back[3] == -2.5
+
+
+def test_generator_is_deterministic_and_blocked():
+    a = kda_inputs.make_prefill(7, 1, 5000, 2, 16, 16, gate="k3", s0_std=0.02)
+    b = kda_inputs.make_prefill(7, 1, 5000, 2, 16, 16, gate="k3", s0_std=0.02)
+    for name in ("q", "k", "v", "g", "beta", "init_state"):
+        np.testing.assert_array_equal(getattr(a, name), getattr(b, name))
+    assert a.g.min() >= -5.0 and a.g.max() <= 0.0
+    assert a.beta.min() > 0.0 and a.beta.max() < 1.0
+    lens = kda_inputs.varlen_lengths()
+    assert len(lens) == 16 and lens.min() >= 512 and lens.max() <= 16384
