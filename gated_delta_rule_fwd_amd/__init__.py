@@ -1,0 +1,198 @@
+"""gated_delta_rule_fwd_amd -- Python binding of libkda.so (KDA forward on MI355X).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI declared in include/kda.h.  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if libkda.so is not
+built, importing the library raises.
+
+  chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, ...)
+      -> (o, final_state)                       [kda_chunk_fwd]
+  recurrent_step(q, k, v, g, beta, state, ...)
+      -> o   (state updated in place)           [kda_recurrent_step]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["chunk_fwd", "recurrent_step", "workspace_bytes", "lib_path", "load", "KDAError",
+           "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "STATUS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+FLAG_QK_L2NORM = 0x1
+FLAG_VALIDATE = 0x2
+FLAG_FP32_PATH = 0x4
+KDA_F32, KDA_BF16 = 0, 1
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
+          4: "KDA_ERR_RANGE", 5: "KDA_ERR_HIP"}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+class ChunkDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int),
+                ("d_v", ctypes.c_int), ("num_seqs", ctypes.c_int), ("in_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float), ("flags", ctypes.c_uint)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libkda.so is not built (%s); run __graft_entry__.build() or "
+                          "python gated_delta_rule_fwd_amd/build.py" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, F, U, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
+    lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 9 + [P, S, P]
+    lib.kda_chunk_fwd_workspace_bytes.restype = S
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+    lib.kda_recurrent_step.restype = I
+    lib.kda_recurrent_step.argtypes = [I, I, I, I, I, I, F, U] + [P] * 7 + [P]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [I]
+    lib.kda_last_hip_error.restype = I
+    lib.kda_last_hip_error.argtypes = []
+    lib.kda_version.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load()
+        msg = lib.kda_status_str(status).decode()
+        if status == 5:
+            msg += " (hipError %d)" % lib.kda_last_hip_error()
+        raise KDAError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % dt)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, shape=None):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _desc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, scale, flags) -> ChunkDesc:
+    return ChunkDesc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, float(scale), flags)
+
+
+def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True, scale=1.0, flags=FLAG_QK_L2NORM):
+    d = _desc(B, T, H, dk, dv, num_seqs, KDA_BF16 if in_bf16 else KDA_F32, KDA_BF16 if out_bf16 else KDA_F32,
+              scale, flags)
+    return int(load().kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
+
+
+def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
+              normalize=True, output_final_state=True, validate=False, fp32_path=False, o=None,
+              final_state=None, workspace=None, stream=None):
+    """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
+    beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
+    [N+1] device tensor or None (then N = B).  Returns (o, final_state)."""
+    torch = _torch()
+    lib = load()
+    _need(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, H, dv))
+    _need(g, "g", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (N, H, dk, dv))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _need(o, "o", out_dtype, (B, T, H, dv))
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_VALIDATE if validate else 0) | \
+        (FLAG_FP32_PATH if fp32_path else 0)
+    d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(out_dtype),
+              scale, flags)
+    ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
+    if ws > 0 and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
+                           _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
+                           ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream))
+    _check(st)
+    return o, final_state
+
+
+def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, o=None, stream=None):
+    """One fused decode step.  q, k, g: [N,H,d_k]; v: [N,H,d_v]; beta: [N,H];
+    state: [N,H,d_k,d_v] fp32, updated in place.  Returns o [N,H,d_v]."""
+    torch = _torch()
+    lib = load()
+    _need(q, "q")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (N, H, dv))
+    _need(g, "g", torch.float32, (N, H, dk))
+    _need(beta, "beta", torch.float32, (N, H))
+    _need(state, "state", torch.float32, (N, H, dk, dv))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
+    _need(o, "o", out_dtype, (N, H, dv))
+    st = lib.kda_recurrent_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale),
+                                FLAG_QK_L2NORM if normalize else 0, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
+    _check(st)
+    return o

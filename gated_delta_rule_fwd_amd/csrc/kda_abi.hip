@@ -1,0 +1,138 @@
+// kda_abi.hip -- the extern "C" boundary of libkda.so: argument checks,
+// kernel selection and error reporting.  See include/kda.h for the contract.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
+
+constexpr unsigned kKnownFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH;
+constexpr size_t kValidateBytes = 256;
+
+kda_status hip_fail(hipError_t e)
+{
+    g_last_hip_error = static_cast<int>(e);
+    return KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+
+int kda_last_hip_error(void) { return g_last_hip_error; }
+
+const char* kda_status_str(kda_status s)
+{
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_INVALID_ARG: return "invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or flag";
+    case KDA_ERR_WORKSPACE: return "workspace too small";
+    case KDA_ERR_RANGE: return "input out of range (g outside [-5,0], beta outside [0,1] or bad cu_seqlens)";
+    case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d)
+{
+    if (!d) return static_cast<size_t>(-1);
+    return (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+}
+
+kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* init_state,
+                         const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                         size_t ws_bytes, hipStream_t stream)
+{
+    if (!d) return KDA_ERR_INVALID_ARG;
+    if (d->flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d->d_k) || !head_dim_ok(d->d_v)) return KDA_ERR_UNSUPPORTED;
+    if (d->B <= 0 || d->T < 0 || d->H <= 0) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens && (d->B != 1 || d->num_seqs < 0)) return KDA_ERR_INVALID_ARG;
+    const long long N = cu_seqlens ? d->num_seqs : d->B;
+    const long long tokens = static_cast<long long>(d->B) * d->T;
+    if (tokens * d->H * (d->d_k > d->d_v ? d->d_k : d->d_v) >= (1LL << 40)) return KDA_ERR_INVALID_ARG;
+    if (N * d->H > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, init_state, o, final_state, cu_seqlens};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (ws_bytes < kda_chunk_fwd_workspace_bytes(d)) return KDA_ERR_WORKSPACE;
+    if ((d->flags & KDA_FLAG_VALIDATE) && !workspace) return KDA_ERR_WORKSPACE;
+    if (N == 0) return KDA_OK;
+
+    kda::ChunkArgs a{};
+    a.B = d->B;
+    a.T = d->T;
+    a.H = d->H;
+    a.dk = d->d_k;
+    a.dv = d->d_v;
+    a.num_seqs = cu_seqlens ? d->num_seqs : d->B;
+    a.in_bf16 = d->in_dtype == KDA_BF16;
+    a.out_bf16 = d->out_dtype == KDA_BF16;
+    a.scale = d->scale;
+    a.normalize = (d->flags & KDA_FLAG_QK_L2NORM) ? 1 : 0;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.init_state = init_state;
+    a.cu_seqlens = cu_seqlens;
+    a.o = o;
+    a.final_state = final_state;
+
+    hipError_t e;
+    if (d->flags & KDA_FLAG_VALIDATE) {
+        unsigned int* counters = static_cast<unsigned int*>(workspace);
+        e = kda::launch_validate(a, counters, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        unsigned int host[4] = {0, 0, 0, 0};
+        e = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e);
+        if (host[0] || host[1] || host[2]) return KDA_ERR_RANGE;
+    }
+
+    if (!(d->flags & KDA_FLAG_FP32_PATH) && kda::chunk_mfma_supported(a))
+        e = kda::launch_chunk_mfma(a, stream);
+    else
+        e = kda::launch_chunk_fp32(a, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return KDA_OK;
+}
+
+kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, unsigned flags, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, float* state, void* o, hipStream_t stream)
+{
+    if (flags & ~(KDA_FLAG_QK_L2NORM)) return KDA_ERR_UNSUPPORTED;
+    if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
+    if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
+    if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
+    if (static_cast<long long>(N) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (N == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::launch_decode(d_k, d_v, in_dtype == KDA_BF16, out_dtype == KDA_BF16, N * H, q, k, v, g,
+                                      beta, state, o, scale, (flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    return KDA_OK;
+}
+
+}  // extern "C"

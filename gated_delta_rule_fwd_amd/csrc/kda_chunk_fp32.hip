@@ -1,0 +1,256 @@
+// kda_chunk_fp32.hip -- chunkwise KDA forward, fp32 arithmetic throughout.
+//
+// This is the exact-arithmetic path: it serves fp32 inputs (where the output
+// tolerance is ~1e-4 of RMS) and any head-dim / dtype combination the matrix
+// core path does not cover.  It follows the chunkwise form of
+// "Kimi K3 模型结构（2）：序列维度（下）" (Q&A on the chunkwise algorithm and on
+// A[t] / O[t]); for one chunk of L <= 64 tokens with start state S:
+//
+//   b_r = sum_{u<=r} g_u  (per key channel),  Gamma_r = exp(b_r),  gamma = Gamma_L
+//   A_qk[r,s] = sum_i q^_ri k^_si exp(b_ri - b_si)            s <= r
+//   A_kk[r,s] = beta_r sum_i k^_ri k^_si exp(b_ri - b_si)     s <  r
+//   (I + A_kk) X = Diag(beta) (V - (K^ * Gamma) S)            X = U~ of the WY form
+//   O  = (Q^ * Gamma) S + A_qk X
+//   S' = Diag(gamma) S + (K^ * gamma / Gamma)^T X
+//
+// The intra-chunk decay ratios are formed per position pair in log space, the
+// fp32 route that page 1 (section 1.2.1, on the lower-bounded decay) names as
+// the costly one; it needs no bound on g.  The triangular system is solved by
+// forward substitution, i.e. the UT transform applied to the right-hand side.
+//
+// One workgroup owns one (chain, 32-column slice of d_v); d_v columns are
+// independent affine systems ("Kimi K3 の KDA ..." section 2.3.2), so the
+// slices never communicate.  The state slice lives in LDS for the whole chain.
+#include "kda_device.h"
+#include "kda_kernels.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = 64;     // chunk length
+constexpr int DVS = 32;   // d_v columns per workgroup
+
+template <int DK, int DV, typename Tin, typename Tout>
+__global__ void __launch_bounds__(256)
+chunk_fp32_kernel(ChunkArgs a)
+{
+    constexpr int NS = DV / DVS;
+    constexpr int LD = DK + 1;  // padded row stride (bank spread)
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int chain = blockIdx.x / NS;
+    const int j0 = (blockIdx.x % NS) * DVS;
+    const int H = a.H;
+    const int n = chain / H, h = chain % H;
+
+    long tok_begin, tok_end;
+    if (a.cu_seqlens) {
+        int b0 = a.cu_seqlens[n], b1 = a.cu_seqlens[n + 1];
+        b0 = min(max(b0, 0), a.T);
+        b1 = min(max(b1, b0), a.T);
+        tok_begin = b0;
+        tok_end = b1;
+    } else {
+        tok_begin = static_cast<long>(n) * a.T;
+        tok_end = tok_begin + a.T;
+    }
+
+    const Tin* q = static_cast<const Tin*>(a.q);
+    const Tin* k = static_cast<const Tin*>(a.k);
+    const Tin* v = static_cast<const Tin*>(a.v);
+    Tout* o = static_cast<Tout*>(a.o);
+
+    __shared__ float sQ[C][LD];
+    __shared__ float sK[C][LD];
+    __shared__ float sB[C][LD];
+    __shared__ float sA[C][C + 1];   // lower+diag: A_qk[r][s];  upper: A_kk[r][s] at [s][r]
+    __shared__ float sV[C][DVS];     // v -> right-hand side -> X
+    __shared__ float sS[DK][DVS];    // state slice
+    __shared__ float sBeta[C];
+    __shared__ float sGam[DK];       // b_L, then gamma = exp(b_L)
+
+    const size_t state_base = static_cast<size_t>(chain) * DK * DV + j0;
+    for (int e = t; e < DK * DVS; e += 256) {
+        const int i = e / DVS, j = e % DVS;
+        sS[i][j] = a.init_state ? a.init_state[state_base + static_cast<size_t>(i) * DV + j] : 0.f;
+    }
+
+    for (long c0 = tok_begin; c0 < tok_end; c0 += C) {
+        const int L = static_cast<int>(min(static_cast<long>(C), tok_end - c0));
+        __syncthreads();
+        // 1. stage the chunk (rows >= L are zero: they then change nothing)
+        for (int e = t; e < C * DK; e += 256) {
+            const int r = e / DK, i = e % DK;
+            float qv = 0.f, kv = 0.f, gv = 0.f;
+            if (r < L) {
+                const size_t idx = (static_cast<size_t>(c0 + r) * H + h) * DK + i;
+                qv = Elem<Tin>::load(q, idx);
+                kv = Elem<Tin>::load(k, idx);
+                gv = a.g[idx];
+            }
+            sQ[r][i] = qv;
+            sK[r][i] = kv;
+            sB[r][i] = gv;
+        }
+        for (int e = t; e < C * DVS; e += 256) {
+            const int r = e / DVS, j = e % DVS;
+            sV[r][j] = (r < L) ? Elem<Tin>::load(v, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + j) : 0.f;
+        }
+        if (t < C) sBeta[t] = (t < L) ? a.beta[static_cast<size_t>(c0 + t) * H + h] : 0.f;
+        __syncthreads();
+
+        // 2. per-row L2 normalisation of q and k; 3. running sum of g
+        if (a.normalize) {
+            for (int rr = 0; rr < C / 4; ++rr) {
+                const int r = wave * (C / 4) + rr;
+                float sq = 0.f, sk = 0.f;
+                for (int i = lane; i < DK; i += 64) {
+                    sq += sQ[r][i] * sQ[r][i];
+                    sk += sK[r][i] * sK[r][i];
+                }
+                const float rq = rsqrtf(wave_sum(sq) + kNormEps);
+                const float rk = rsqrtf(wave_sum(sk) + kNormEps);
+                for (int i = lane; i < DK; i += 64) {
+                    sQ[r][i] *= rq;
+                    sK[r][i] *= rk;
+                }
+            }
+        }
+        if (t < DK) {
+            float acc = 0.f;
+            for (int r = 0; r < C; ++r) {
+                acc += sB[r][t];
+                sB[r][t] = acc;
+            }
+            sGam[t] = acc;
+        }
+        __syncthreads();
+
+        // 4. intra-chunk matrices, one position pair per thread-iteration
+        for (int p = t; p < C * (C + 1) / 2; p += 256) {
+            int r = static_cast<int>((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+            while (r * (r + 1) / 2 > p) --r;
+            while ((r + 1) * (r + 2) / 2 <= p) ++r;
+            const int s = p - r * (r + 1) / 2;
+            float aq = 0.f, ak = 0.f;
+            for (int i = 0; i < DK; ++i) {
+                const float ks = sK[s][i] * __expf(sB[r][i] - sB[s][i]);
+                aq += sQ[r][i] * ks;
+                ak += sK[r][i] * ks;
+            }
+            sA[r][s] = aq;
+            if (s < r) sA[s][r] = sBeta[r] * ak;
+        }
+        __syncthreads();
+
+        // 5. decay-weighted operands: Q^*Gamma, K^*Gamma, K^*gamma/Gamma
+        for (int e = t; e < C * DK; e += 256) {
+            const int r = e / DK, i = e % DK;
+            const float b = sB[r][i];
+            const float kv = sK[r][i];
+            const float gm = __expf(b);
+            sQ[r][i] *= gm;
+            sK[r][i] = kv * gm;
+            sB[r][i] = kv * __expf(sGam[i] - b);
+        }
+        __syncthreads();
+        if (t < DK) sGam[t] = __expf(sGam[t]);
+
+        // 6. right-hand side  beta_r (v_r - (K^*Gamma)_r S)
+        {
+            const int j = t % DVS, rg = t / DVS;
+            for (int rr = 0; rr < C / 8; ++rr) {
+                const int r = rg * (C / 8) + rr;
+                float acc = 0.f;
+                for (int i = 0; i < DK; ++i) acc += sK[r][i] * sS[i][j];
+                sV[r][j] = sBeta[r] * (sV[r][j] - acc);
+            }
+        }
+        __syncthreads();
+
+        // 7. forward substitution (I + A_kk) X = rhs, 8 lanes per column
+        {
+            const int j = t / 8, part = t % 8;
+            float xs[C / 8];
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < C / 8; ++m) {
+                    const int s = part + 8 * m;
+                    if (s < r) acc += sA[s][r] * xs[m];
+                }
+                acc += __shfl_xor(acc, 1, 64);
+                acc += __shfl_xor(acc, 2, 64);
+                acc += __shfl_xor(acc, 4, 64);
+                const float x = sV[r][j] - acc;
+                if ((r & 7) == part) xs[r >> 3] = x;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < C / 8; ++m) sV[part + 8 * m][j] = xs[m];
+        }
+        __syncthreads();
+
+        // 8. output  O = (Q^*Gamma) S + A_qk X
+        {
+            const int j = t % DVS, rg = t / DVS;
+            for (int rr = 0; rr < C / 8; ++rr) {
+                const int r = rg * (C / 8) + rr;
+                if (r >= L) break;
+                float acc = 0.f;
+                for (int i = 0; i < DK; ++i) acc += sQ[r][i] * sS[i][j];
+                for (int s = 0; s <= r; ++s) acc += sA[r][s] * sV[s][j];
+                Elem<Tout>::store(o, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + j, a.scale * acc);
+            }
+        }
+        __syncthreads();
+
+        // 9. state  S' = Diag(gamma) S + (K^*gamma/Gamma)^T X
+        {
+            const int j = t % DVS, ig = t / DVS;
+            for (int ii = 0; ii < DK / 8; ++ii) {
+                const int i = ig * (DK / 8) + ii;
+                float acc = sGam[i] * sS[i][j];
+                for (int r = 0; r < C; ++r) acc += sB[r][i] * sV[r][j];
+                sS[i][j] = acc;
+            }
+        }
+    }
+    __syncthreads();
+    if (a.final_state) {
+        for (int e = t; e < DK * DVS; e += 256) {
+            const int i = e / DVS, j = e % DVS;
+            a.final_state[state_base + static_cast<size_t>(i) * DV + j] = sS[i][j];
+        }
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const ChunkArgs& a, hipStream_t stream)
+{
+    const int chains = (a.cu_seqlens ? a.num_seqs : a.B) * a.H;
+    const dim3 grid(chains * (DV / DVS)), block(256);
+    if (a.in_bf16 && a.out_bf16)
+        chunk_fp32_kernel<DK, DV, uint16_t, uint16_t><<<grid, block, 0, stream>>>(a);
+    else if (a.in_bf16)
+        chunk_fp32_kernel<DK, DV, uint16_t, float><<<grid, block, 0, stream>>>(a);
+    else if (a.out_bf16)
+        chunk_fp32_kernel<DK, DV, float, uint16_t><<<grid, block, 0, stream>>>(a);
+    else
+        chunk_fp32_kernel<DK, DV, float, float><<<grid, block, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t stream)
+{
+    if (a.dk == 128 && a.dv == 128) return launch_dims<128, 128>(a, stream);
+    if (a.dk == 128 && a.dv == 64) return launch_dims<128, 64>(a, stream);
+    if (a.dk == 64 && a.dv == 128) return launch_dims<64, 128>(a, stream);
+    return launch_dims<64, 64>(a, stream);
+}
+
+}  // namespace kda

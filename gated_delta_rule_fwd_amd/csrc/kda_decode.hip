@@ -1,0 +1,179 @@
+// kda_decode.hip -- fused single-token recurrent step (decode) for gfx950.
+//
+// Per chain (n, h), with the state S (d_k x d_v fp32, row i = key channel i):
+//   q^, k^ = L2-normalised q, k ("Kimi K3 の KDA ..." section 1.2.1)
+//   S~ = Diag(exp g) S                              (decay first)
+//   p  = S~^T k^,  r = S~^T q^                      (two reductions over d_k)
+//   u  = beta (v - p)                               (innovation times rate)
+//   S  <- S~ + k^ u^T                               (erase + write, in place)
+//   o  = scale * (r + (k^ . q^) u)  == scale * S_new^T q^  (read after write)
+// ("Kimi K3 模型结构（2）", Q&A: decode runs this recurrent form one token at a
+// time.)
+//
+// The step is a pure stream over the state: 2 * 4 * d_k * d_v bytes per
+// chain against ~7 d_k d_v flops, so it is HBM-bound.  One workgroup of 256
+// threads owns one chain; each thread keeps RPT rows x 4 columns of S in
+// registers between the reductions and the store, so S is read once and
+// written once with 16-byte accesses, and both reductions share the one pass
+// (o is rebuilt from S~^T q^ instead of re-reading S_new).
+#include "kda_device.h"
+#include "kda_kernels.h"
+
+namespace kda {
+
+template <int DK, int DV, typename Tin, typename Tout>
+__global__ void __launch_bounds__(256)
+decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+                   const float* __restrict__ g, const float* __restrict__ beta,
+                   float* __restrict__ state, Tout* __restrict__ o, float scale, int normalize)
+{
+    constexpr int CG = DV / 4;        // float4 column groups
+    constexpr int RG = 256 / CG;      // row groups
+    constexpr int RPT = DK / RG;      // rows per thread
+    constexpr int RG_PER_WAVE = 64 / CG;
+    static_assert(RPT >= 1 && DK % RG == 0, "shape");
+
+    const int c = blockIdx.x;         // chain = n * H + h
+    const int t = threadIdx.x;
+    const int cg = t % CG, rg = t / CG;
+    const int lane = t & 63, wave = t >> 6;
+
+    float4* S4 = reinterpret_cast<float4*>(state + static_cast<size_t>(c) * DK * DV);
+
+    // Issue the state loads first so their latency overlaps the vector work.
+    float4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) s[m] = S4[(rg + RG * m) * CG + cg];
+
+    __shared__ float sq[DK], sk[DK], sa[DK];
+    __shared__ float red[2][4][DV];
+    __shared__ float sdot;
+
+    if (wave == 0) {
+        constexpr int PER = DK / 64;
+        float qv[PER], kv[PER], ss_q = 0.f, ss_k = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int i = lane + 64 * e;
+            qv[e] = Elem<Tin>::load(q, static_cast<size_t>(c) * DK + i);
+            kv[e] = Elem<Tin>::load(k, static_cast<size_t>(c) * DK + i);
+            sa[i] = __expf(g[static_cast<size_t>(c) * DK + i]);
+            ss_q += qv[e] * qv[e];
+            ss_k += kv[e] * kv[e];
+        }
+        float rq = 1.f, rk = 1.f;
+        if (normalize) {
+            rq = rsqrtf(wave_sum(ss_q) + kNormEps);
+            rk = rsqrtf(wave_sum(ss_k) + kNormEps);
+        }
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int i = lane + 64 * e;
+            sq[i] = qv[e] * rq;
+            sk[i] = kv[e] * rk;
+            dot += (qv[e] * rq) * (kv[e] * rk);
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) sdot = dot;
+    }
+    __syncthreads();
+
+    // decay in registers, then partial reductions over this thread's rows
+    float p[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const float a = sa[i], kk = sk[i], qq = sq[i];
+        s[m].x *= a; s[m].y *= a; s[m].z *= a; s[m].w *= a;
+        p[0] += kk * s[m].x; p[1] += kk * s[m].y; p[2] += kk * s[m].z; p[3] += kk * s[m].w;
+        r[0] += qq * s[m].x; r[1] += qq * s[m].y; r[2] += qq * s[m].z; r[3] += qq * s[m].w;
+    }
+    // reduce across the row groups that share this wave
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[e] += __shfl_xor(p[e], off, 64);
+            r[e] += __shfl_xor(r[e], off, 64);
+        }
+    }
+    if (lane < CG) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            red[0][wave][4 * cg + e] = p[e];
+            red[1][wave][4 * cg + e] = r[e];
+        }
+    }
+    __syncthreads();
+
+    const float b = beta[c];
+    const float dot = sdot;
+    float u[4], ov[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int j = 4 * cg + e;
+        const float pj = red[0][0][j] + red[0][1][j] + red[0][2][j] + red[0][3][j];
+        const float rj = red[1][0][j] + red[1][1][j] + red[1][2][j] + red[1][3][j];
+        const float vj = Elem<Tin>::load(v, static_cast<size_t>(c) * DV + j);
+        u[e] = b * (vj - pj);
+        ov[e] = scale * (rj + dot * u[e]);
+    }
+    (void)RG_PER_WAVE;
+
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const float kk = sk[i];
+        float4 w;
+        w.x = s[m].x + kk * u[0];
+        w.y = s[m].y + kk * u[1];
+        w.z = s[m].z + kk * u[2];
+        w.w = s[m].w + kk * u[3];
+        S4[i * CG + cg] = w;
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Elem<Tout>::store(o, static_cast<size_t>(c) * DV + 4 * cg + e, ov[e]);
+    }
+}
+
+template <int DK, int DV, typename Tin, typename Tout>
+static hipError_t launch_decode_t(int chains, const void* q, const void* k, const void* v, const float* g,
+                                  const float* beta, float* state, void* o, float scale, int normalize,
+                                  hipStream_t stream)
+{
+    decode_step_kernel<DK, DV, Tin, Tout><<<dim3(chains), dim3(256), 0, stream>>>(
+        static_cast<const Tin*>(q), static_cast<const Tin*>(k), static_cast<const Tin*>(v), g, beta, state,
+        static_cast<Tout*>(o), scale, normalize);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_decode_d(bool in_bf16, bool out_bf16, int chains, const void* q, const void* k,
+                                  const void* v, const float* g, const float* beta, float* state, void* o,
+                                  float scale, int normalize, hipStream_t stream)
+{
+    if (in_bf16 && out_bf16)
+        return launch_decode_t<DK, DV, uint16_t, uint16_t>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    if (in_bf16)
+        return launch_decode_t<DK, DV, uint16_t, float>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    if (out_bf16)
+        return launch_decode_t<DK, DV, float, uint16_t>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    return launch_decode_t<DK, DV, float, float>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+}
+
+hipError_t launch_decode(int dk, int dv, bool in_bf16, bool out_bf16, int chains, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta, float* state, void* o, float scale,
+                         int normalize, hipStream_t stream)
+{
+    if (dk == 128 && dv == 128)
+        return launch_decode_d<128, 128>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    if (dk == 128 && dv == 64)
+        return launch_decode_d<128, 64>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    if (dk == 64 && dv == 128)
+        return launch_decode_d<64, 128>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    return launch_decode_d<64, 64>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,156 @@
+/*
+ * kda.h -- C ABI of libkda.so: the Kimi Delta Attention (KDA) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (one chain per (sequence n, head h), state S in R^{d_k x d_v}):
+ *
+ *   q^_t = scale-free L2 normalisation of q_t over d_k, likewise k^_t
+ *   S_t  = (I - beta_t k^_t k^_t^T) Diag(exp g_t) S_{t-1} + beta_t k^_t v_t^T
+ *   o_t  = scale * S_t^T q^_t
+ *
+ * Sources (cited by page title and section):
+ *   - "Kimi K3 の KDA が Gated MLA と AttnRes との連携を解説", section 1.2.1:
+ *     q and k are L2-normalised per head inside the kernel; the recurrence is
+ *     decay -> erase -> write; each token reads the state after its own
+ *     write; beta is a per-head fp32 scalar; recurrence quantities stay fp32.
+ *   - "GDN, KDA の整理", section "Kimi Delta Attention": the update rule with
+ *     D_t = Diag(alpha_t) and S_t in R^{d_k x d_v}, o_t = S_t^T q_t; the
+ *     bounded log-decay -5 < g < 0.
+ *   - "Kimi K3 模型结构（2）：序列维度（下）", Q&A: the chunkwise form (C = 64,
+ *     WY representation + UT transform) serves training and prefill, the
+ *     recurrent form serves one-token decode; the caller picks the mode.
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
+ *     contiguous in the layouts given below.  The caller owns every buffer;
+ *     the library allocates nothing and keeps no state between calls other
+ *     than a read-only cache of device properties.  Entry points are
+ *     thread-safe.
+ *   - Work is enqueued on `stream` and runs asynchronously; there is no host
+ *     synchronisation except under KDA_FLAG_VALIDATE.
+ *   - Every argument is checked on the host before anything is launched, so a
+ *     call that returns an error other than KDA_ERR_HIP / KDA_ERR_RANGE has had
+ *     no side effect.
+ *   - bf16 is stored as its 16-bit pattern; outputs are rounded to bf16 with
+ *     round-to-nearest-even.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_API __attribute__((visibility("default")))
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misaligned pointer, bad layout */
+    KDA_ERR_UNSUPPORTED = 2,  /* head dims other than 64/128, unknown dtype or flag */
+    KDA_ERR_WORKSPACE = 3,    /* workspace smaller than kda_chunk_fwd_workspace_bytes() */
+    KDA_ERR_RANGE = 4,        /* only with KDA_FLAG_VALIDATE: g outside [-5, 0], beta outside
+                                 [0, 1], or cu_seqlens not a monotone partition of [0, T] */
+    KDA_ERR_HIP = 5           /* a HIP launch/runtime error; see kda_last_hip_error() */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/* q and k are L2-normalised over d_k inside the kernel (eps = 1e-6 under the
+ * square root).  Mirrors the model's use_qk_l2norm_in_kernel switch (page 1,
+ * section 1.2.1).  Without it q and k are used as given. */
+#define KDA_FLAG_QK_L2NORM 0x1u
+/* Debug: before the forward pass, check on the device that every g is in
+ * [-5, 0], every beta in [0, 1] and that cu_seqlens is monotone from 0 to T;
+ * synchronises the stream and returns KDA_ERR_RANGE on failure (nothing else
+ * is written then).  Needs kda_chunk_fwd_workspace_bytes() bytes of workspace. */
+#define KDA_FLAG_VALIDATE 0x2u
+/* Use the fp32 (per-position-pair) arithmetic path even for bf16 inputs. */
+#define KDA_FLAG_FP32_PATH 0x4u
+
+typedef struct kda_chunk_desc {
+    int B;              /* batch (must be 1 when cu_seqlens is given) */
+    int T;              /* tokens per batch row, or total packed tokens when varlen */
+    int H;              /* heads */
+    int d_k;            /* key/query head dim: 64 or 128 */
+    int d_v;            /* value head dim: 64 or 128 */
+    int num_seqs;       /* number of packed sequences when cu_seqlens != NULL, else ignored */
+    kda_dtype in_dtype;  /* dtype of q, k, v */
+    kda_dtype out_dtype; /* dtype of o */
+    float scale;        /* output scale (1.0 = the pages' form) */
+    unsigned flags;     /* KDA_FLAG_* */
+} kda_chunk_desc;
+
+/* Bytes of device workspace kda_chunk_fwd needs for this descriptor (0 unless
+ * KDA_FLAG_VALIDATE is set).  Returns (size_t)-1 for a null descriptor. */
+KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
+
+/*
+ * Chunkwise forward for training/prefill ("Kimi K3 模型结构（2）", Q&A on the
+ * chunkwise algorithm and on which form each phase uses).  Chunks of 64
+ * tokens restart at every sequence start; the last chunk of a sequence may be
+ * partial; a zero-length sequence passes its initial state through unchanged.
+ *
+ *   q, k        [B, T, H, d_k]  in_dtype
+ *   v           [B, T, H, d_v]  in_dtype
+ *   g           [B, T, H, d_k]  fp32, natural-log decay per key channel; the
+ *                               fast path requires g >= -5 (the bounded decay
+ *                               map keeps 16-token rescaling factors below
+ *                               e^80, inside bf16/fp32 range)
+ *   beta        [B, T, H]       fp32 write strength (after the sigmoid)
+ *   init_state  [N, H, d_k, d_v] fp32, nullable (zeros); N = B, or num_seqs
+ *               when cu_seqlens is given; may alias final_state
+ *   cu_seqlens  [num_seqs + 1]  int32 device array, nullable; sequence n is
+ *               tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed axis.
+ *               Values are clamped into [0, T] on the device.
+ *   o           [B, T, H, d_v]  out_dtype, fully overwritten; must not alias
+ *               any input
+ *   final_state [N, H, d_k, d_v] fp32, nullable
+ *   workspace   device buffer of ws_bytes >= kda_chunk_fwd_workspace_bytes()
+ */
+KDA_API kda_status kda_chunk_fwd(const kda_chunk_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* init_state, const int32_t* cu_seqlens,
+                         void* o, float* final_state,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * One fused recurrent step for decode (one new token per sequence), updating
+ * the state in place ("Kimi K3 模型结构（2）", Q&A: decode uses the recurrent
+ * form).  Per (n, h): S~ = Diag(exp g) S; u = beta (v - S~^T k^);
+ * S <- S~ + k^ u^T; o = scale * S^T q^.
+ *
+ *   q, k, g  [N, H, d_k]  (q, k in in_dtype; g fp32)
+ *   v        [N, H, d_v]  in_dtype
+ *   beta     [N, H]       fp32
+ *   state    [N, H, d_k, d_v] fp32, read and overwritten in place
+ *   o        [N, H, d_v]  out_dtype
+ */
+KDA_API kda_status kda_recurrent_step(int N, int H, int d_k, int d_v,
+                              kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, unsigned flags,
+                              const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              float* state, void* o, hipStream_t stream);
+
+/* Static description of a status code. */
+KDA_API const char* kda_status_str(kda_status status);
+
+/* The hipError_t behind the calling thread's last KDA_ERR_HIP (0 if none). */
+KDA_API int kda_last_hip_error(void);
+
+/* Library version string. */
+KDA_API const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (CPU only, no GPU): the library loads, exports
+every entry point include/kda.h declares, and rejects bad arguments before
+launching anything.  Device pointers here are fake addresses that the
+library never dereferences, because every call below fails its host checks."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_fwd_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.lib_path()):
+        pytest.skip("libkda.so not built")
+    return kda.load()
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step",
+                                  "kda_status_str", "kda_last_hip_error", "kda_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.lib_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(kda_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.kda_status_str(code)
+    assert b"ok" == lib.kda_status_str(0)
+    assert lib.kda_version().startswith(b"kda-mi355x")
+    assert lib.kda_last_hip_error() == 0
+
+
+def _desc(**kw):
+    base = dict(B=1, T=64, H=2, d_k=128, d_v=128, num_seqs=0, in_dtype=1, out_dtype=1, scale=1.0,
+                flags=kda.FLAG_QK_L2NORM)
+    base.update(kw)
+    return kda.ChunkDesc(**base)
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def _call(lib, d, ptrs=None, ws=None, ws_bytes=0, cu=None):
+    p = [FAKE + 0x100000 * i for i in range(9)]
+    if ptrs:
+        for i, val in ptrs.items():
+            p[i] = val
+    args = [ctypes.c_void_p(x) if x is not None else None for x in p]
+    # slots: q k v g beta init o final
+    return lib.kda_chunk_fwd(None if d is None else ctypes.byref(d), args[0], args[1], args[2], args[3], args[4],
+                             args[5], None if cu is None else ctypes.c_void_p(cu), args[6], args[7],
+                             None if ws is None else ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_chunk_fwd_rejects_bad_arguments(lib):
+    assert _call(lib, None) == 1
+    assert _call(lib, _desc(d_k=96)) == 2                     # unsupported head dim
+    assert _call(lib, _desc(d_v=32)) == 2
+    assert _call(lib, _desc(in_dtype=7)) == 2                 # unknown dtype
+    assert _call(lib, _desc(flags=0x80)) == 2                 # unknown flag
+    assert _call(lib, _desc(B=0)) == 1
+    assert _call(lib, _desc(H=0)) == 1
+    assert _call(lib, _desc(T=-1)) == 1
+    assert _call(lib, _desc(), ptrs={0: None}) == 1           # null q
+    assert _call(lib, _desc(), ptrs={3: FAKE + 4}) == 1       # misaligned g
+    assert _call(lib, _desc(B=2, num_seqs=2), cu=FAKE) == 1   # varlen needs B == 1
+    assert _call(lib, _desc(B=1, num_seqs=-1), cu=FAKE) == 1
+    d = _desc(flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE)
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert _call(lib, d, ws=FAKE, ws_bytes=need - 1) == 3      # workspace too small
+    assert _call(lib, d, ws=None, ws_bytes=need) == 3
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc())) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(None) == ctypes.c_size_t(-1).value
+
+
+def test_chunk_fwd_empty_batch_is_a_no_op(lib):
+    # zero packed sequences: nothing to compute, no launch, no pointer touched
+    assert _call(lib, _desc(B=1, T=0, num_seqs=0), ptrs={i: None for i in range(8)}, cu=FAKE) == 0
+
+
+def test_recurrent_step_rejects_bad_arguments(lib):
+    P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(7)]
+
+    def call(N=4, H=2, dk=128, dv=128, it=1, ot=1, flags=kda.FLAG_QK_L2NORM, ptrs=P):
+        return lib.kda_recurrent_step(N, H, dk, dv, it, ot, 1.0, flags, *ptrs, None)
+
+    assert call(dk=32) == 2
+    assert call(it=3) == 2
+    assert call(flags=kda.FLAG_VALIDATE) == 2
+    assert call(N=-1) == 1
+    assert call(H=0) == 1
+    assert call(ptrs=[None] + P[1:]) == 1
+    assert call(ptrs=P[:5] + [ctypes.c_void_p(FAKE + 8)] + P[6:]) == 1   # misaligned state
+    assert call(N=0, ptrs=[None] * 7) == 0                               # nothing to do
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(kda, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kda, "_lib", None)
+    with pytest.raises(ImportError):
+        kda.load()

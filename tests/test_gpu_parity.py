@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on
+the same seeded inputs.  Marked ``gpu``; run on an MI355X."""
+import numpy as np
+import pytest
+
+import kda_inputs
+import oracle
+from gpu_util import check, check_state, dev, host64, inputs_to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_fwd_amd as m
+    m.load()
+    return m
+
+
+def _run(kda, inp, out_dtype=None, **kw):
+    import torch
+    d = inputs_to_device(inp)
+    o, s = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["init_state"], d["cu_seqlens"],
+                         out_dtype=out_dtype, **kw)
+    torch.cuda.synchronize()
+    return o, s
+
+
+def _parity(kda, inp, name, tol, heads=None, out_dtypes=None, **kw):
+    import torch
+    o_ref, s_ref = oracle.forward(inp, heads)
+    hs = slice(None) if heads is None else heads
+    outs = out_dtypes or ([torch.float32] if inp.dtype == "f32" else [torch.bfloat16, torch.float32])
+    recs = []
+    for odt in outs:
+        o, s = _run(kda, inp, out_dtype=odt, **kw)
+        recs.append(check("%s/%s" % (name, str(odt).split(".")[-1]), host64(o[:, :, hs]), o_ref,
+                          host64(s[:, hs]), s_ref, tol, bf16_store=(odt == torch.bfloat16)))
+    return recs
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+def test_tiny_fp32(kda):
+    """B=1, H=2, T=256, d=64, all fp32, seed 0."""
+    _parity(kda, kda_inputs.workload("tiny_f32"), "tiny_f32", TOL_F32)
+
+
+def test_mid_bf16(kda):
+    """B=1, H=32, T=4096, d=128, bf16 q/k/v, seed 1."""
+    _parity(kda, kda_inputs.workload("mid_bf16"), "mid_bf16", TOL_BF16)
+
+
+def test_mid_bf16_fp32_path(kda):
+    import torch
+    inp = kda_inputs.workload("mid_bf16", T=1024, H=4)
+    _parity(kda, inp, "mid_bf16_fp32path", TOL_F32 * 10, out_dtypes=[torch.float32], fp32_path=True)
+
+
+def test_long_bf16_sampled_heads(kda):
+    """Full-size launch (B=1, H=96, T=65536), oracle on three sampled heads."""
+    import torch
+    inp = kda_inputs.workload("long_bf16")
+    o, s = _run(kda, inp, out_dtype=torch.bfloat16)
+    for h in (0, 47, 95):
+        heads = slice(h, h + 1)
+        o_ref, s_ref = oracle.forward(inp, heads)
+        check("long_bf16/h%d" % h, host64(o[:, :, heads]), o_ref, host64(s[:, heads]), s_ref, TOL_BF16,
+              bf16_store=True)
+
+
+def test_varlen_bf16_sampled_heads(kda):
+    """16 packed sequences, lengths U[512, 16384] (seed 3), H=32."""
+    inp = kda_inputs.workload("varlen_bf16")
+    _parity(kda, inp, "varlen_bf16", TOL_BF16, heads=slice(5, 8))
+
+
+def test_decode_128_steps(kda):
+    """N=256, H=96, d=128, 128 in-place steps; every step's o and the final
+    states checked on the first 6 sequences (all heads)."""
+    import torch
+    w = kda_inputs.DECODE_WORKLOAD
+    N, H, d, steps, seed = w["N"], w["H"], w["d"], w["steps"], w["seed"]
+    S0 = kda_inputs.decode_initial_state(seed, N, H, d, w["s0_std"])
+    state = dev(S0)
+    ns = 6
+    s_ref = S0[:ns].astype(np.float64)
+    worst = 0.0
+    for step in range(steps):
+        x = kda_inputs.decode_step(seed, step, N, H, d)
+        o = kda.recurrent_step(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), state)
+        o_ref, s_ref = oracle.decode_steps(s_ref, kda_inputs.bf16_to_f32(x.q[:ns]), kda_inputs.bf16_to_f32(x.k[:ns]),
+                                           kda_inputs.bf16_to_f32(x.v[:ns]), x.g[:ns], x.beta[:ns])
+        if step % 16 == 0 or step == steps - 1:
+            rec = check("decode/step%d" % step, host64(o[:ns]), o_ref, None, None, TOL_BF16, bf16_store=True)
+            worst = max(worst, rec["o_err"])
+    torch.cuda.synchronize()
+    check_state("decode/final_state", host64(state[:ns]), s_ref, TOL_BF16)
+
+
+# ---------------------------------------------------------------------------
+# edge cases and probes
+# ---------------------------------------------------------------------------
+def test_ragged_and_empty_sequences(kda):
+    lens = [1, 15, 16, 17, 0, 63, 64, 65, 130, 0, 200]
+    inp = kda_inputs.make_prefill(31, 1, 0, 4, 128, 128, gate="k3", s0_std=0.02, lengths=lens)
+    _parity(kda, inp, "ragged", TOL_BF16)
+    # a zero-length sequence returns its initial state unchanged (bitwise)
+    o, s = _run(kda, inp)
+    np.testing.assert_array_equal(host64(s[4]), inp.init_state[4].astype(np.float64))
+    np.testing.assert_array_equal(host64(s[9]), inp.init_state[9].astype(np.float64))
+
+
+def test_slow_gate_long_memory(kda):
+    inp = kda_inputs.make_prefill(32, 1, 2048, 4, 128, 128, gate="slow", s0_std=0.02)
+    _parity(kda, inp, "slow_gate", TOL_BF16)
+
+
+def test_batch_dense(kda):
+    inp = kda_inputs.make_prefill(33, 3, 200, 2, 128, 128, gate="k3", s0_std=0.02)
+    _parity(kda, inp, "batch3", TOL_BF16)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_dims(kda, dk, dv, dtype):
+    inp = kda_inputs.make_prefill(34, 1, 300, 3, dk, dv, dtype=dtype, gate="k3", s0_std=0.02)
+    _parity(kda, inp, "dims%d_%d_%s" % (dk, dv, dtype), TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+def test_split_resume_matches_one_shot(kda):
+    import torch
+    inp = kda_inputs.make_prefill(35, 1, 700, 2, 128, 128, gate="k3", s0_std=0.02)
+    d = inputs_to_device(inp)
+    o_full, s_full = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["init_state"],
+                                   out_dtype=torch.float32)
+    o_ref, s_ref = oracle.forward(inp)
+    for split in (100, 128, 333):
+        sl = [slice(None), slice(0, split)]
+        sr = [slice(None), slice(split, None)]
+        o1, s1 = kda.chunk_fwd(*(d[n][tuple(sl)].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                               d["init_state"], out_dtype=torch.float32)
+        o2, s2 = kda.chunk_fwd(*(d[n][tuple(sr)].contiguous() for n in ("q", "k", "v", "g", "beta")),
+                               s1, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_cat = np.concatenate([host64(o1), host64(o2)], axis=1)
+        check("split%d" % split, o_cat, o_ref, host64(s2), s_ref, TOL_BF16, bf16_store=False)
+
+
+def test_init_state_may_alias_final_state(kda):
+    import torch
+    inp = kda_inputs.make_prefill(36, 1, 150, 2, 128, 128, gate="k3", s0_std=0.02)
+    d = inputs_to_device(inp)
+    o_ref, s_ref = oracle.forward(inp)
+    st = d["init_state"].clone()
+    o, s = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, final_state=st, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check("alias", host64(o), o_ref, host64(st), s_ref, TOL_BF16, bf16_store=False)
+
+
+def test_deterministic(kda):
+    inp = kda_inputs.make_prefill(37, 1, 500, 3, 128, 128, gate="k3", s0_std=0.02)
+    o1, s1 = _run(kda, inp)
+    o2, s2 = _run(kda, inp)
+    import torch
+    assert torch.equal(o1, o2)
+    assert torch.equal(s1, s2)
+
+
+def test_validate_flag(kda):
+    import torch
+    inp = kda_inputs.make_prefill(38, 1, 130, 2, 128, 128, gate="k3")
+    d = inputs_to_device(inp)
+    kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], validate=True)
+    bad = d["g"].clone()
+    bad[0, 7, 1, 3] = -5.5
+    with pytest.raises(kda.KDAError) as e:
+        kda.chunk_fwd(d["q"], d["k"], d["v"], bad, d["beta"], validate=True)
+    assert e.value.status == 4
+    badb = d["beta"].clone()
+    badb[0, 3, 0] = 1.5
+    with pytest.raises(kda.KDAError):
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], badb, validate=True)
+    cu = torch.tensor([0, 100, 60, 130], dtype=torch.int32, device="cuda")
+    with pytest.raises(kda.KDAError):
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], cu_seqlens=cu, validate=True)
+
+
+def test_long_fixed_point(kda):
+    """One token repeated 16384 times with slow decay: the state converges to
+    the fixed point (I - M)^-1 beta k^ v^T of the repeated affine map
+    ("Kimi K3 の KDA ..." section 2.3.3, item 3)."""
+    import torch
+    T, dk = 16384, 128
+    rng = np.random.default_rng(39)
+    k1 = rng.standard_normal(dk).astype(np.float32)
+    v1 = rng.standard_normal(dk).astype(np.float32)
+    q1 = rng.standard_normal(dk).astype(np.float32)
+    kb, vb, qb = (kda_inputs.bf16_bits(x) for x in (k1, v1, q1))
+    g1 = np.full(dk, -2e-3, np.float32)
+    b1 = np.float32(0.6)
+    q = np.tile(qb, (1, T, 1, 1))
+    k = np.tile(kb, (1, T, 1, 1))
+    v = np.tile(vb, (1, T, 1, 1))
+    g = np.tile(g1, (1, T, 1, 1))
+    beta = np.full((1, T, 1), b1, np.float32)
+    o, s = kda.chunk_fwd(dev(q), dev(k), dev(v), dev(g), dev(beta), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kf = kda_inputs.bf16_to_f32(kb).astype(np.float64)
+    kh = kf / np.sqrt(kf @ kf + oracle.EPS)
+    M = oracle.transition(np.exp(g1.astype(np.float64)), float(b1), kh)
+    Sstar = np.linalg.solve(np.eye(dk) - M, float(b1) * np.outer(kh, kda_inputs.bf16_to_f32(vb)))
+    err = np.abs(host64(s)[0, 0] - Sstar).max() / np.sqrt(np.mean(Sstar ** 2))
+    print("fixed point rel err", err, flush=True)
+    assert err < TOL_BF16
+
+
+def test_decode_dims_and_dtypes(kda):
+    import torch
+    for dk, dv, dt in [(128, 128, "f32"), (64, 64, "bf16"), (64, 128, "f32"), (128, 64, "bf16")]:
+        N, H = 5, 3
+        rng = np.random.default_rng(40 + dk + dv)
+        S0 = (0.02 * rng.standard_normal((N, H, dk, dv))).astype(np.float32)
+        state = dev(S0)
+        s_ref = S0.astype(np.float64)
+        for step in range(4):
+            x = [rng.standard_normal((N, H, d)).astype(np.float32) for d in (dk, dk, dv)]
+            if dt == "bf16":
+                x = [kda_inputs.bf16_bits(a) for a in x]
+            g = (-5.0 / (1.0 + np.exp(-rng.standard_normal((N, H, dk))))).astype(np.float32)
+            beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((N, H))))).astype(np.float32)
+            o = kda.recurrent_step(dev(x[0]), dev(x[1]), dev(x[2]), dev(g), dev(beta), state,
+                                   out_dtype=torch.float32)
+            xf = [kda_inputs.bf16_to_f32(a) if a.dtype == np.uint16 else a for a in x]
+            o_ref, s_ref = oracle.decode_steps(s_ref, xf[0], xf[1], xf[2], g, beta)
+            check("decode%d_%d_%s/%d" % (dk, dv, dt, step), host64(o), o_ref, None, None, TOL_F32,
+                  bf16_store=False)
+        torch.cuda.synchronize()
+        check_state("decode%d_%d_%s/state" % (dk, dv, dt), host64(state), s_ref, TOL_F32)
