@@ -33,11 +33,24 @@ def _compile(src: str, extra) -> str:
     return out
 
 
-def build(extra_flags=(), verbose: bool = False) -> str:
-    """Compile every HIP source and link libkda.so; always rebuilds."""
+def _stale(src: str) -> bool:
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(out):
+        return True
+    t = os.path.getmtime(out)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
+    deps.append(os.path.join(ROOT, "include", "kda.h"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(extra_flags=(), verbose: bool = False, incremental: bool = False) -> str:
+    """Compile the HIP sources and link libkda.so.  By default every source is
+    recompiled; ``incremental`` skips objects newer than their sources."""
     os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
+    todo = [s for s in SOURCES if not incremental or _stale(s)]
+    with ThreadPoolExecutor(max_workers=max(1, min(8, len(todo)))) as ex:
+        list(ex.map(lambda s: _compile(s, extra_flags), todo))
+    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,4 +63,6 @@ def build(extra_flags=(), verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(sys.argv[1:], verbose=True)
+    args = sys.argv[1:]
+    inc = "--incremental" in args
+    build([a for a in args if a != "--incremental"], verbose=True, incremental=inc)

@@ -11,6 +11,7 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
 
@@ -66,9 +67,10 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     if (tokens * d->H * (d->d_k > d->d_v ? d->d_k : d->d_v) >= (1LL << 40)) return KDA_ERR_INVALID_ARG;
     if (N * d->H > (1LL << 30)) return KDA_ERR_INVALID_ARG;
     if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, g, beta, init_state, o, final_state, cu_seqlens};
-    for (const void* p : ptrs)
+    const void* rows[] = {q, k, v, g, init_state, o, final_state};  // row-vectorised tensors
+    for (const void* p : rows)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_INVALID_ARG;
     if (ws_bytes < kda_chunk_fwd_workspace_bytes(d)) return KDA_ERR_WORKSPACE;
     if ((d->flags & KDA_FLAG_VALIDATE) && !workspace) return KDA_ERR_WORKSPACE;
     if (N == 0) return KDA_OK;
@@ -126,9 +128,10 @@ kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype
     if (static_cast<long long>(N) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
-    const void* ptrs[] = {q, k, v, g, beta, state, o};
-    for (const void* p : ptrs)
+    const void* rows[] = {q, k, v, g, state, o};
+    for (const void* p : rows)
         if (!aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (!aligned4(beta)) return KDA_ERR_INVALID_ARG;
     hipError_t e = kda::launch_decode(d_k, d_v, in_dtype == KDA_BF16, out_dtype == KDA_BF16, N * H, q, k, v, g,
                                       beta, state, o, scale, (flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, stream);
     if (e != hipSuccess) return hip_fail(e);

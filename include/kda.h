@@ -21,8 +21,9 @@
  *     recurrent form serves one-token decode; the caller picks the mode.
  *
  * Conventions for every entry point
- *   - All tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
- *     contiguous in the layouts given below.  The caller owns every buffer;
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous in
+ *     the layouts given below; beta and cu_seqlens must be 4-byte aligned,
+ *     every other tensor 16-byte aligned.  The caller owns every buffer;
  *     the library allocates nothing and keeps no state between calls other
  *     than a read-only cache of device properties.  Entry points are
  *     thread-safe.

@@ -82,6 +82,7 @@ def test_chunk_fwd_rejects_bad_arguments(lib):
     assert _call(lib, _desc(T=-1)) == 1
     assert _call(lib, _desc(), ptrs={0: None}) == 1           # null q
     assert _call(lib, _desc(), ptrs={3: FAKE + 4}) == 1       # misaligned g
+    assert _call(lib, _desc(), ptrs={4: FAKE + 2}) == 1       # misaligned beta
     assert _call(lib, _desc(B=2, num_seqs=2), cu=FAKE) == 1   # varlen needs B == 1
     assert _call(lib, _desc(B=1, num_seqs=-1), cu=FAKE) == 1
     d = _desc(flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE)
