@@ -1,11 +1,709 @@
-// kda_chunk_mfma.hip -- matrix-core chunkwise path (bf16 inputs, d = 128).
+// kda_chunk_mfma.hip -- chunkwise KDA forward on the gfx950 matrix cores.
+//
+// Scope: bf16 q/k/v, d_k = d_v = 128, log-decay g in [-5, 0].  One workgroup
+// (4 waves) owns one chain (sequence, head) and a 64-column slice of d_v; the
+// d_v columns are independent affine systems sharing one transition ("Kimi K3
+// の KDA ..." section 2.3.2), so the two slices of a chain never talk.  Each
+// wave keeps a 128 x 16 fp32 strip of the state in MFMA accumulators for the
+// whole chain and walks the 64-token chunks in order.
+//
+// Per chunk (C = 64, tokens r, s; "Kimi K3 模型结构（2）" Q&A on the chunkwise
+// algorithm, on A[t] and O[t]; page 1 section 1.2.1 on the two paths):
+//   b     = running sum of g inside the chunk (per key channel), Gamma = e^b
+//   A_kk  = StrictTril(Diag(beta) (K^ Gamma)(K^ / Gamma)^T)
+//   A_qk  = Tril((Q^ Gamma)(K^ / Gamma)^T)                (diagonal kept)
+//   T'    = (I + A_kk)^-1 Diag(beta)                      (UT transform)
+//   U~    = T' (V - (K^ Gamma) S)          (= U - W S with W = T' K^ Gamma, U = T' V)
+//   O     = (Q^ Gamma) S + A_qk U~
+//   S    <- Diag(gamma) S + (K^ gamma / Gamma)^T U~
+//
+// The ratios Gamma_r / Gamma_s are formed per 16-token sub-tile with a
+// reference point between s and r ("Kimi K3 の KDA ..." section 1.2.1 on the
+// lower-bounded decay; "Kimi K3 模型结构（2）" Q&A on the -5 bound): with
+// ref_j the running decay at the end of sub-tile j, tile (i, j <= i) is
+//   [X_r exp(b_r - ref_{j+1})] . [K_s exp(ref_{j+1} - b_s)]
+// where the right factor is <= 1 and the left one is <= 1 off the diagonal and
+// <= e^80 on it (16 steps of g >= -5): both are dense bf16 matrix products.
+//
+// Precision (fp32 accumulate everywhere).  Each product's operands are
+// rounded only as far as the output tolerance allows; a pair "x3" is
+// hi*hi + hi*lo + lo*hi with x = hi + lo:
+//   A_kk                bf16                     (damped through T)
+//   A_qk factors        bf16 x3                  (diagonal factor up to e^80)
+//   T' (V - K Gamma S)  bf16 x3                  (T may be large; near a fixed
+//                                                 point of the recurrence V and
+//                                                 K Gamma S nearly cancel)
+//   K Gamma S, Q Gamma S  fp16 operand x fp16 hi/lo state
+//   A_qk U~             fp16 hi/lo x fp16
+//   K'^T U~             fp16 x fp16              (|K'| <= 1, U~ bounded)
+// fp16 carries 3 more mantissa bits than bf16 at the same MFMA rate; it is
+// used only where both operands are bounded well inside its range.
+
+// Data layout: every MFMA operand is staged in LDS in the exact per-lane
+// order of v_mfma_f32_16x16x32_bf16 (A: lane = row + 16*kgroup, 8 consecutive
+// k per lane; B: lane = column + 16*kgroup), so each operand fetch is one
+// 16-byte LDS read per lane.  The contraction order over k is free, so the
+// state's channel order and the U~ token order are permuted to match the
+// accumulator layout they come from: the state never leaves registers and U~
+// feeds the next products without an LDS round trip.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
 namespace kda {
 
-bool chunk_mfma_supported(const ChunkArgs&) { return false; }
+namespace {
 
-hipError_t launch_chunk_mfma(const ChunkArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = 64;       // chunk length
+constexpr int DK = 128;
+constexpr int DV = 128;
+constexpr int DVS = 64;     // value columns per workgroup: 4 waves x 16
+constexpr int NSLICE = DV / DVS;
+constexpr int NT = 256;
+
+struct alignas(16) Smem {
+    __bf16 vs[C][DVS];                   // V slice, plain [token][column]
+    union {
+        bf16x8 kf[2][4][4][64];          // K^ e^(ref-b)   B-frags [hi/lo][token tile][chan kb][lane]
+        f16x8 kp[8][2][64];              // (K^ gamma/Gamma)^T A-frags [chan tile][token kb][lane]
+        float tot[4][DK];                // sum of g over each sub-tile (preprocess only)
+    } u1;
+    float akk[C][C + 1];                 // A_kk (fp32), then T = (I + A_kk)^-1 in place
+    f16x8 aqk[2][4][2][64];              // A_qk       A-frags [hi/lo][token tile][token kb][lane]
+    bf16x8 tp[2][4][2][64];              // T'         A-frags [hi/lo][token tile][token kb][lane]
+    f16x8 qg[4][4][64];                  // Q^ Gamma   A-frags [token tile][chan kb][lane]
+    f16x8 kgn[4][4][64];                 // -K^ Gamma  A-frags [token tile][chan kb][lane]
+    float ref[5][DK];                    // running decay at sub-tile boundaries
+    float dlt[4][DK];                    // exp(sum of g over sub-tile w)
+    float gam[DK];                       // gamma = exp(b at the chunk end)
+    float beta[C];
+};
+
+__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mmh(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma32(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split(float x, __bf16& hi, __bf16& lo)
+{
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+__device__ __forceinline__ void splith(float x, _Float16& hi, _Float16& lo)
+{
+    hi = static_cast<_Float16>(x);
+    lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+// 8 consecutive floats from LDS (16-byte aligned)
+__device__ __forceinline__ void lds8(const float* p, float* out)
+{
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+
+// hi*hi + hi*lo + lo*hi
+__device__ __forceinline__ f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c)
+{
+    c = mma(ah, bh, c);
+    c = mma(ah, bl, c);
+    return mma(al, bh, c);
+}
+
+// Inclusive prefix sum over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row_scan16(float x)
+{
+    int v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));  // row_shr:1
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));  // row_shr:2
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));  // row_shr:4
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));  // row_shr:8
+    return x;
+}
+
+// m ? x : 1 for m in {0, 1}, without a branch and without rounding x
+__device__ __forceinline__ float sel(float m, float x) { return fmaf(m, x, 1.f - m); }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One chunk's raw inputs for the lane's token row r = 16*wave + (lane % 16):
+// channels 32*kb + 8*(lane/16) + 0..7 of q, k, g, and value columns
+// 16*(lane/16) + 0..15 of this workgroup's slice.
+struct Raw {
+    uint4 q[4], k[4];
+    float4 g[8];
+    uint4 v[2];
+    float beta;
+};
+
+template <typename Tout>
+__global__ void __launch_bounds__(NT, 1)
+chunk_mfma_kernel(ChunkArgs a)
+{
+    __shared__ Smem s;
+
+    const int t = threadIdx.x;
+    // the wave index is uniform across the wave: keep it in a scalar register
+    // so branches on it stay scalar
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l = t & 63, g = l >> 4, n = l & 15;
+    const int H = a.H;
+    // Workgroup -> (chain, slice).  Both slices of a chain get ids that are
+    // equal mod 8, so they are dispatched to the same XCD and the second read
+    // of the chain's q/k/g hits that XCD's L2.
+    const int bid = blockIdx.x;
+    const int slice = (bid >> 3) & (NSLICE - 1);
+    const int chain = ((bid >> 4) << 3) | (bid & 7);
+    const int nchains = (a.cu_seqlens ? a.num_seqs : a.B) * H;
+    if (chain >= nchains) return;
+    const int j0 = slice * DVS;
+    const int seq = chain / H, h = chain % H;
+
+    long tok0, tok1;
+    if (a.cu_seqlens) {
+        int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
+        b0 = min(max(b0, 0), a.T);
+        b1 = min(max(b1, b0), a.T);
+        tok0 = b0;
+        tok1 = b1;
+    } else {
+        tok0 = static_cast<long>(seq) * a.T;
+        tok1 = tok0 + a.T;
+    }
+
+    const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
+    const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k);
+    const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
+    const float* __restrict__ gp = a.g;
+    const float* __restrict__ bp = a.beta;
+    Tout* __restrict__ op = static_cast<Tout*>(a.o);
+
+    const int row = 16 * w + n;   // this lane's token row inside the chunk
+    // 0/1 masks of the (wave-uniform) sub-tile index, used as arithmetic selects
+    float mlt[4], meq[4], mgt[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        mlt[u] = (u < w) ? 1.f : 0.f;
+        meq[u] = (u == w) ? 1.f : 0.f;
+        mgt[u] = (u > w) ? 1.f : 0.f;
+    }
+
+    auto load_raw = [&](Raw& R, long c0) {
+        const long tk = c0 + row;
+        if (tk < tok1) {
+            const size_t base = (static_cast<size_t>(tk) * H + h);
+            const uint16_t* qr = qp + base * DK + 8 * g;
+            const uint16_t* kr = kp + base * DK + 8 * g;
+            const float* gr = gp + base * DK + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                R.q[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
+                R.k[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+                R.g[2 * kb] = *reinterpret_cast<const float4*>(gr + 32 * kb);
+                R.g[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
+            }
+            const uint16_t* vr = vp + base * DV + j0 + 16 * g;
+            R.v[0] = *reinterpret_cast<const uint4*>(vr);
+            R.v[1] = *reinterpret_cast<const uint4*>(vr + 8);
+            R.beta = bp[base];
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                R.q[kb] = make_uint4(0, 0, 0, 0);
+                R.k[kb] = make_uint4(0, 0, 0, 0);
+                R.g[2 * kb] = make_float4(0.f, 0.f, 0.f, 0.f);
+                R.g[2 * kb + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            R.v[0] = make_uint4(0, 0, 0, 0);
+            R.v[1] = make_uint4(0, 0, 0, 0);
+            R.beta = 0.f;
+        }
+    };
+
+    // ---- state strip: channels 16*mt + 4*g + i, column j0 + 16*w + n
+    f32x4 sacc[8];
+    {
+        const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sacc[mt][i] = a.init_state ? a.init_state[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] : 0.f;
+    }
+
+    Raw R;
+    if (tok0 < tok1) load_raw(R, tok0);
+
+    for (long c0 = tok0; c0 < tok1; c0 += C) {
+        const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
+
+        // ================= P: preprocess this lane's row ==================
+        float qv[32], kv[32], bv[32];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint32_t qw[4] = {R.q[kb].x, R.q[kb].y, R.q[kb].z, R.q[kb].w};
+            const uint32_t kw[4] = {R.k[kb].x, R.k[kb].y, R.k[kb].z, R.k[kb].w};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                qv[8 * kb + 2 * e2] = bf_lo(qw[e2]);
+                qv[8 * kb + 2 * e2 + 1] = bf_hi(qw[e2]);
+                kv[8 * kb + 2 * e2] = bf_lo(kw[e2]);
+                kv[8 * kb + 2 * e2 + 1] = bf_hi(kw[e2]);
+            }
+            bv[8 * kb + 0] = R.g[2 * kb].x;
+            bv[8 * kb + 1] = R.g[2 * kb].y;
+            bv[8 * kb + 2] = R.g[2 * kb].z;
+            bv[8 * kb + 3] = R.g[2 * kb].w;
+            bv[8 * kb + 4] = R.g[2 * kb + 1].x;
+            bv[8 * kb + 5] = R.g[2 * kb + 1].y;
+            bv[8 * kb + 6] = R.g[2 * kb + 1].z;
+            bv[8 * kb + 7] = R.g[2 * kb + 1].w;
+        }
+        const uint4 vraw0 = R.v[0], vraw1 = R.v[1];
+        const float beta_r = R.beta;
+        // prefetch the next chunk; its latency hides behind this chunk's work
+        if (c0 + C < tok1) load_raw(R, c0 + C);
+
+        // L2 norm of q and k over d_k (row spread over the 4 lane groups)
+        {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                sq += qv[e] * qv[e];
+                sk += kv[e] * kv[e];
+            }
+            sq += __shfl_xor(sq, 16, 64);
+            sq += __shfl_xor(sq, 32, 64);
+            sk += __shfl_xor(sk, 16, 64);
+            sk += __shfl_xor(sk, 32, 64);
+            const float rq = a.normalize ? rsqrtf(sq + kNormEps) : 1.f;
+            const float rk = a.normalize ? rsqrtf(sk + kNormEps) : 1.f;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                qv[e] *= rq;
+                kv[e] *= rk;
+            }
+        }
+        // running decay inside the 16-token sub-tile
+#pragma unroll
+        for (int e = 0; e < 32; ++e) bv[e] = row_scan16(bv[e]);
+        if (n == 15) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s.u1.tot[w][32 * kb + 8 * g + e] = bv[8 * kb + e];
+        }
+        if (g == 0) s.beta[row] = beta_r;
+        // V slice, plain layout
+        *reinterpret_cast<uint4*>(&s.vs[row][16 * g]) = vraw0;
+        *reinterpret_cast<uint4*>(&s.vs[row][16 * g + 8]) = vraw1;
+        __syncthreads();
+
+        // per-channel decay tables: ref_w (running decay at the start of
+        // sub-tile w), exp of each sub-tile's total, and gamma
+        {
+            const int c = t & (DK - 1);
+            const float t0 = s.u1.tot[0][c], t1 = s.u1.tot[1][c], t2 = s.u1.tot[2][c], t3 = s.u1.tot[3][c];
+            if (t < DK) {
+                s.ref[0][c] = 0.f;
+                s.ref[1][c] = t0;
+                s.ref[2][c] = t0 + t1;
+                s.ref[3][c] = t0 + t1 + t2;
+                s.ref[4][c] = t0 + t1 + t2 + t3;
+                s.gam[c] = __expf(t0 + t1 + t2 + t3);
+            } else {
+                s.dlt[0][c] = __expf(t0);
+                s.dlt[1][c] = __expf(t1);
+                s.dlt[2][c] = __expf(t2);
+                s.dlt[3][c] = __expf(t3);
+            }
+        }
+        __syncthreads();
+
+        // decay factors for this row; operand fragments for the later phases.
+        // Products of the per-sub-tile factors dlt (each <= 1) give every
+        // longer-range factor without overflow: if one underflows, the term it
+        // scales is below the fp32 range anyway.
+        float dv[32];   // exp(b_r - ref_{w+1}) in [1, e^80]
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int cb = 32 * kb + 8 * g;
+            float rw[8], rw1[8], d0[8], d1[8], d2[8], d3[8];
+            lds8(&s.ref[w][cb], rw);
+            lds8(&s.ref[w + 1][cb], rw1);
+            lds8(&s.dlt[0][cb], d0);
+            lds8(&s.dlt[1][cb], d1);
+            lds8(&s.dlt[2][cb], d2);
+            lds8(&s.dlt[3][cb], d3);
+            bf16x8 kfh, kfl;
+            float qgv[8], kgv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // branch-free selection by the wave index: x^m = m x + (1 - m), exact for m in {0, 1}
+                const float eref = sel(mlt[0], d0[e]) * sel(mlt[1], d1[e]) *
+                                   sel(mlt[2], d2[e]);
+                const float dw = meq[0] * d0[e] + meq[1] * d1[e] + meq[2] * d2[e] + meq[3] * d3[e];
+                const float b = bv[8 * kb + e] + rw[e];
+                const float d = __expf(b - rw1[e]);
+                const float f = __expf(rw1[e] - b);
+                const float gm = d * dw * eref;    // exp(b_r) = exp(b_r - ref_w) exp(ref_w)
+                dv[8 * kb + e] = d;
+                __bf16 hi, lo;
+                split(kv[8 * kb + e] * f, hi, lo);
+                kfh[e] = hi;
+                kfl[e] = lo;
+                qgv[e] = qv[8 * kb + e] * gm;
+                kgv[e] = -kv[8 * kb + e] * gm;
+            }
+            s.u1.kf[0][w][kb][l] = kfh;
+            s.u1.kf[1][w][kb][l] = kfl;
+            // Q^ Gamma and -K^ Gamma into the state's channel order: channel
+            // 32kb + 8g + e goes to lane (2(g&1) + e/4)*16 + n, element 4(g>>1) + e%4
+            {
+                const int eo = 4 * (g >> 1);
+                const int l0 = (2 * (g & 1)) * 16 + n, l1 = l0 + 16;
+                f16x4 q0, q1, k0, k1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    q0[e] = static_cast<_Float16>(qgv[e]);
+                    q1[e] = static_cast<_Float16>(qgv[4 + e]);
+                    k0[e] = static_cast<_Float16>(kgv[e]);
+                    k1[e] = static_cast<_Float16>(kgv[4 + e]);
+                }
+                *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&s.qg[w][kb][l0]) + eo) = q0;
+                *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&s.qg[w][kb][l1]) + eo) = q1;
+                *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&s.kgn[w][kb][l0]) + eo) = k0;
+                *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&s.kgn[w][kb][l1]) + eo) = k1;
+            }
+        }
+        __syncthreads();
+
+        // ================= A: intra-chunk tiles (w, j <= w) ==================
+        for (int j = 0; j <= w; ++j) {
+            f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+            // off-diagonal tiles use exp(b - ref_w) * prod_{j < u < w} dlt_u
+            const float moff = (j < w) ? 1.f : 0.f;
+            const float m1 = (j < 1 && 1 < w) ? 1.f : 0.f;
+            const float m2 = (j < 2 && 2 < w) ? 1.f : 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int cb = 32 * kb + 8 * g;
+                float d0[8], d1[8], d2[8], d3[8];
+                lds8(&s.dlt[0][cb], d0);
+                lds8(&s.dlt[1][cb], d1);
+                lds8(&s.dlt[2][cb], d2);
+                lds8(&s.dlt[3][cb], d3);
+                bf16x8 ka, qh, ql;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // diagonal tile: exp(b - ref_{w+1}); off-diagonal:
+                    // exp(b - ref_w) * exp(ref_w - ref_{j+1})
+                    const float dw = meq[0] * d0[e] + meq[1] * d1[e] + meq[2] * d2[e] + meq[3] * d3[e];
+                    const float off = dw * sel(m1, d1[e]) * sel(m2, d2[e]);
+                    const float fac = dv[8 * kb + e] * sel(moff, off);
+                    ka[e] = static_cast<__bf16>(kv[8 * kb + e] * fac);
+                    __bf16 hi, lo;
+                    split(qv[8 * kb + e] * fac, hi, lo);
+                    qh[e] = hi;
+                    ql[e] = lo;
+                }
+                const bf16x8 bh = s.u1.kf[0][j][kb][l], bl = s.u1.kf[1][j][kb][l];
+                akk = mma(ka, bh, akk);
+                aqk = mma3(qh, ql, bh, bl, aqk);
+            }
+            // lane holds rows r = 16w + 4g + i, column s = 16j + n
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * w + 4 * g + i, sc = 16 * j + n;
+                if (sc < r) s.akk[r][sc] = s.beta[r] * akk[i];
+                const float vq = (sc <= r) ? aqk[i] : 0.f;
+                _Float16 hi, lo;
+                splith(vq, hi, lo);
+                const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (j & 1);
+                reinterpret_cast<_Float16*>(&s.aqk[0][w][j >> 1][lt])[e] = hi;
+                reinterpret_cast<_Float16*>(&s.aqk[1][w][j >> 1][lt])[e] = lo;
+            }
+        }
+        if ((w & 1) == 0) {   // tile (w, w+1) shares a token kb with (w, w): zero it
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4;
+                reinterpret_cast<_Float16*>(&s.aqk[0][w][w >> 1][lt])[e] = static_cast<_Float16>(0.f);
+                reinterpret_cast<_Float16*>(&s.aqk[1][w][w >> 1][lt])[e] = static_cast<_Float16>(0.f);
+            }
+        }
+        __syncthreads();
+
+        // ================= T: (I + A_kk)^-1, blocked, in place ==================
+        // diagonal 16x16 blocks by forward substitution: lane owns column n of
+        // block w and the rows g + 4m of it
+        {
+            float tv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) tv[m] = (g + 4 * m == n) ? 1.f : 0.f;
+            const int b0 = 16 * w;
+#pragma unroll
+            for (int rr = 1; rr < 16; ++rr) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int sr = g + 4 * m;
+                    if (sr < rr) acc += s.akk[b0 + rr][b0 + sr] * tv[m];
+                }
+                acc += __shfl_xor(acc, 16, 64);
+                acc += __shfl_xor(acc, 32, 64);
+                const float tval = (rr > n) ? -acc : ((rr == n) ? 1.f : 0.f);
+                if ((rr & 3) == g) tv[rr >> 2] = tval;
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) s.akk[b0 + g + 4 * m][b0 + n] = tv[m];
+        }
+        __syncthreads();
+
+        // (all waves) (K^ gamma/Gamma)^T A-frags, token order matching U~:
+        // channel c -> frag [c/16][w/2], lane (n/4)*16 + c%16, element n%4 + 4(w%2)
+        {
+            const int e = (n & 3) + 4 * (w & 1);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int cb = 32 * kb + 8 * g;
+                float d1[8], d2[8], d3[8];
+                lds8(&s.dlt[1][cb], d1);
+                lds8(&s.dlt[2][cb], d2);
+                lds8(&s.dlt[3][cb], d3);
+                const int mt = 2 * kb + (g >> 1);
+                const int lb = (n >> 2) * 16 + 8 * (g & 1);
+                _Float16* dst = reinterpret_cast<_Float16*>(&s.u1.kp[mt][w >> 1][0]);
+#pragma unroll
+                for (int ee = 0; ee < 8; ++ee) {
+                    // exp(b_L - b_r) = exp(ref_{w+1} - b_r) exp(b_L - ref_{w+1})
+                    const float eL = sel(mgt[1], d1[ee]) * sel(mgt[2], d2[ee]) *
+                                     sel(mgt[3], d3[ee]);
+                    const float kq = kv[8 * kb + ee] * __builtin_amdgcn_rcpf(dv[8 * kb + ee]) * eL;
+                    dst[(lb + ee) * 8 + e] = static_cast<_Float16>(kq);
+                }
+            }
+        }
+        // level 1: T_{w,w-1} = -T_ww A_{w,w-1} T_{w-1,w-1} for w = 1, 3 (fp32 MFMA)
+        if (w & 1) {
+            const int hi = 16 * w, lo = 16 * (w - 1);
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                p = mma32(s.akk[hi + n][lo + 4 * kk + g], s.akk[lo + 4 * kk + g][lo + n], p);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s.akk[hi + 4 * g + i][lo + n] = p[i];
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's P is in LDS
+            __builtin_amdgcn_wave_barrier();
+            f32x4 q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                q = mma32(s.akk[hi + n][hi + 4 * kk + g], s.akk[hi + 4 * kk + g][lo + n], q);
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s.akk[hi + 4 * g + i][lo + n] = -q[i];
+        }
+        __syncthreads();
+        // level 2: T_BA = -T_BB (A_BA T_AA) on 32x32 blocks; wave -> tile (2 + w/2, w%2)
+        {
+            const int ti = 2 + (w >> 1), tj = w & 1;
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                if (kt < tj) continue;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    p = mma32(s.akk[16 * ti + n][16 * kt + 4 * kk + g], s.akk[16 * kt + 4 * kk + g][16 * tj + n], p);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s.akk[16 * ti + 4 * g + i][16 * tj + n] = p[i];
+            __syncthreads();
+            f32x4 q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 2; kt < 4; ++kt) {
+                if (kt > ti) continue;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    q = mma32(s.akk[16 * ti + n][16 * kt + 4 * kk + g], s.akk[16 * kt + 4 * kk + g][16 * tj + n], q);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s.akk[16 * ti + 4 * g + i][16 * tj + n] = -q[i];
+        }
+        __syncthreads();
+        // T' = T Diag(beta) as A-frags whose token (k) order matches the
+        // accumulator layout of V - K Gamma S: element e of lane group g
+        // holds token 32kb + 16(e/4) + 4g + e%4
+        {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                bf16x8 th, tl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sc = 32 * kb + 16 * (e >> 2) + 4 * g + (e & 3);
+                    const float x = (sc <= row) ? s.akk[row][sc] * s.beta[sc] : 0.f;
+                    __bf16 hi, lo;
+                    split(x, hi, lo);
+                    th[e] = hi;
+                    tl[e] = lo;
+                }
+                s.tp[0][w][kb][l] = th;
+                s.tp[1][w][kb][l] = tl;
+            }
+        }
+        __syncthreads();
+
+        // ================= S: state-dependent part ==================
+        // state as fp16 hi/lo B-frags (channel order of the accumulators)
+        f16x8 sh[4], sl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                _Float16 hi, lo;
+                splith(sacc[2 * kb][i], hi, lo);
+                sh[kb][i] = hi;
+                sl[kb][i] = lo;
+                splith(sacc[2 * kb + 1][i], hi, lo);
+                sh[kb][4 + i] = hi;
+                sl[kb][4 + i] = lo;
+            }
+        }
+        // R = V - (K^ Gamma) S  (rows = tokens 16mt + 4g + i, column n of the strip)
+        f32x4 ut[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const f16x8 ka = s.kgn[mt][kb][l];
+                acc = mmh(ka, sh[kb], acc);
+                acc = mmh(ka, sl[kb], acc);
+            }
+            ut[mt] = acc;
+        }
+        bf16x8 rbh[2], rbl[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __bf16 hi, lo;
+                split(ut[2 * kb][i], hi, lo);
+                rbh[kb][i] = hi;
+                rbl[kb][i] = lo;
+                split(ut[2 * kb + 1][i], hi, lo);
+                rbh[kb][4 + i] = hi;
+                rbl[kb][4 + i] = lo;
+            }
+        }
+        // U~ = T' R
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb <= (mt >> 1); ++kb)
+                acc = mma3(s.tp[0][mt][kb][l], s.tp[1][mt][kb][l], rbh[kb], rbl[kb], acc);
+            ut[mt] = acc;
+        }
+        f16x8 ub[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ub[kb][i] = static_cast<_Float16>(ut[2 * kb][i]);
+                ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
+            }
+        }
+        // O = (Q^ Gamma) S + A_qk U~
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const f16x8 qa = s.qg[mt][kb][l];
+                acc = mmh(qa, sh[kb], acc);
+                acc = mmh(qa, sl[kb], acc);
+            }
+#pragma unroll
+            for (int kb = 0; kb <= (mt >> 1); ++kb) {
+                acc = mmh(s.aqk[0][mt][kb][l], ub[kb], acc);
+                acc = mmh(s.aqk[1][mt][kb][l], ub[kb], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * g + i;
+                if (r < L)
+                    Elem<Tout>::store(op, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + 16 * w + n, a.scale * acc[i]);
+            }
+        }
+        // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const float4 gm4 = *reinterpret_cast<const float4*>(&s.gam[16 * mt + 4 * g]);
+            sacc[mt][0] *= gm4.x;
+            sacc[mt][1] *= gm4.y;
+            sacc[mt][2] *= gm4.z;
+            sacc[mt][3] *= gm4.w;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sacc[mt] = mmh(s.u1.kp[mt][kb][l], ub[kb], sacc[mt]);
+        }
+        __syncthreads();
+    }
+
+    if (a.final_state) {
+        const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.final_state[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] = sacc[mt][i];
+    }
+}
+
+}  // namespace
+
+bool chunk_mfma_supported(const ChunkArgs& a)
+{
+    return a.in_bf16 && a.dk == DK && a.dv == DV;
+}
+
+hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream)
+{
+    const int chains = (a.cu_seqlens ? a.num_seqs : a.B) * a.H;
+    // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
+    const int groups = (chains + 7) / 8;
+    const dim3 grid(groups * 8 * NSLICE), block(NT);
+    if (a.out_bf16)
+        chunk_mfma_kernel<uint16_t><<<grid, block, 0, stream>>>(a);
+    else
+        chunk_mfma_kernel<float><<<grid, block, 0, stream>>>(a);
+    return hipGetLastError();
+}
 
 }  // namespace kda

@@ -88,7 +88,8 @@ def mm(X, Y, mode="f64"):
     raise ValueError(mode)
 
 
-DEFAULT_PREC = dict(akk="f64", aqk="f64", W="f64", U="f64", WS="f64", QS="f64", AU="f64", KU="f64")
+DEFAULT_PREC = dict(akk="f64", aqk="f64", W="f64", U="f64", WS="f64", QS="f64", AU="f64", KU="f64",
+                    KS="f64", TR="f64")
 
 
 # ----------------------------------------------------------------------------
@@ -115,9 +116,12 @@ def _tiled_pair_matrix(X, K, b, mode, strict):
     return np.tril(M, -1 if strict else 0)
 
 
-def chunk_chain(q, k, v, g, beta, S0=None, *, C=64, scale=1.0, eps=EPS, prec=None, tinv="f64"):
+def chunk_chain(q, k, v, g, beta, S0=None, *, C=64, scale=1.0, eps=EPS, prec=None, tinv="f64", form="WU"):
     """Chunkwise forward for one chain.  q, k, g: [T, dk]; v: [T, dv];
-    beta: [T].  Returns (o [T, dv], S_T)."""
+    beta: [T].  Returns (o [T, dv], S_T).
+
+    form="WU": U~ = U - W S with U = Tm Diag(beta) V, W = Tm Diag(beta)(K^ Gamma);
+    form="R":  U~ = (Tm Diag(beta)) (V - (K^ Gamma) S), the same quantity."""
     p = dict(DEFAULT_PREC)
     if prec:
         p.update(prec)
@@ -145,9 +149,13 @@ def chunk_chain(q, k, v, g, beta, S0=None, *, C=64, scale=1.0, eps=EPS, prec=Non
             Tm = np.linalg.inv(np.eye(L) + Akk)
         else:
             Tm = np.linalg.inv((np.eye(L) + Akk).astype(np.float32)).astype(np.float64)
-        W = mm(Tm, bt[:, None] * (K * Gam), p["W"])
-        U = mm(Tm * bt[None, :], V, p["U"])
-        Ut = U - mm(W, S, p["WS"])
+        if form == "WU":
+            W = mm(Tm, bt[:, None] * (K * Gam), p["W"])
+            U = mm(Tm * bt[None, :], V, p["U"])
+            Ut = U - mm(W, S, p["WS"])
+        else:
+            R = V - mm(K * Gam, S, p["KS"])
+            Ut = mm(Tm * bt[None, :], R, p["TR"])
         o[c0:c1] = scale * (mm(Q * Gam, S, p["QS"]) + mm(Aqk, Ut, p["AU"]))
         Kg = K * np.exp(b[L - 1][None, :] - b)
         S = gam[:, None] * S + mm(Kg.T, Ut, p["KU"])
