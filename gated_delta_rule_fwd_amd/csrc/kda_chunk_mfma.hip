@@ -142,6 +142,13 @@ __device__ __forceinline__ float row_scan16(float x)
     return x;
 }
 
+__device__ __forceinline__ void store_out(float* p, float x) { *p = x; }
+// bf16 output: the hardware conversion rounds to nearest even
+__device__ __forceinline__ void store_out(uint16_t* p, float x)
+{
+    *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
 // m ? x : 1 for m in {0, 1}, without a branch and without rounding x
 __device__ __forceinline__ float sel(float m, float x) { return fmaf(m, x, 1.f - m); }
 
@@ -210,36 +217,26 @@ chunk_mfma_kernel(ChunkArgs a)
         mgt[u] = (u > w) ? 1.f : 0.f;
     }
 
+    // Rows past the end of the sequence load the last valid token instead
+    // (no branch, no zero fill); their k, g and beta are masked to zero when
+    // the chunk is unpacked, which makes them the identity of the recurrence.
     auto load_raw = [&](Raw& R, long c0) {
-        const long tk = c0 + row;
-        if (tk < tok1) {
-            const size_t base = (static_cast<size_t>(tk) * H + h);
-            const uint16_t* qr = qp + base * DK + 8 * g;
-            const uint16_t* kr = kp + base * DK + 8 * g;
-            const float* gr = gp + base * DK + 8 * g;
+        const long tk = min(c0 + row, tok1 - 1);
+        const size_t base = (static_cast<size_t>(tk) * H + h);
+        const uint16_t* qr = qp + base * DK + 8 * g;
+        const uint16_t* kr = kp + base * DK + 8 * g;
+        const float* gr = gp + base * DK + 8 * g;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                R.q[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
-                R.k[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
-                R.g[2 * kb] = *reinterpret_cast<const float4*>(gr + 32 * kb);
-                R.g[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
-            }
-            const uint16_t* vr = vp + base * DV + j0 + 16 * g;
-            R.v[0] = *reinterpret_cast<const uint4*>(vr);
-            R.v[1] = *reinterpret_cast<const uint4*>(vr + 8);
-            R.beta = bp[base];
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                R.q[kb] = make_uint4(0, 0, 0, 0);
-                R.k[kb] = make_uint4(0, 0, 0, 0);
-                R.g[2 * kb] = make_float4(0.f, 0.f, 0.f, 0.f);
-                R.g[2 * kb + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-            R.v[0] = make_uint4(0, 0, 0, 0);
-            R.v[1] = make_uint4(0, 0, 0, 0);
-            R.beta = 0.f;
+        for (int kb = 0; kb < 4; ++kb) {
+            R.q[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
+            R.k[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+            R.g[2 * kb] = *reinterpret_cast<const float4*>(gr + 32 * kb);
+            R.g[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
         }
+        const uint16_t* vr = vp + base * DV + j0 + 16 * g;
+        R.v[0] = *reinterpret_cast<const uint4*>(vr);
+        R.v[1] = *reinterpret_cast<const uint4*>(vr + 8);
+        R.beta = bp[base];
     };
 
     // ---- state strip: channels 16*mt + 4*g + i, column j0 + 16*w + n
@@ -282,9 +279,13 @@ chunk_mfma_kernel(ChunkArgs a)
             bv[8 * kb + 7] = R.g[2 * kb + 1].w;
         }
         const uint4 vraw0 = R.v[0], vraw1 = R.v[1];
-        const float beta_r = R.beta;
-        // prefetch the next chunk; its latency hides behind this chunk's work
-        if (c0 + C < tok1) load_raw(R, c0 + C);
+        const float live = (row < L) ? 1.f : 0.f;
+        const float beta_r = R.beta * live;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            kv[e] *= live;
+            bv[e] *= live;
+        }
 
         // L2 norm of q and k over d_k (row spread over the 4 lane groups)
         {
@@ -464,13 +465,19 @@ chunk_mfma_kernel(ChunkArgs a)
 #pragma unroll
             for (int m = 0; m < 4; ++m) tv[m] = (g + 4 * m == n) ? 1.f : 0.f;
             const int b0 = 16 * w;
+            // the block's strictly-lower entries this lane needs, read up front
+            float av[16][4];
+#pragma unroll
+            for (int rr = 1; rr < 16; ++rr)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) av[rr][m] = s.akk[b0 + rr][b0 + g + 4 * m];
 #pragma unroll
             for (int rr = 1; rr < 16; ++rr) {
                 float acc = 0.f;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int sr = g + 4 * m;
-                    if (sr < rr) acc += s.akk[b0 + rr][b0 + sr] * tv[m];
+                    if (sr < rr) acc += av[rr][m] * tv[m];
                 }
                 acc += __shfl_xor(acc, 16, 64);
                 acc += __shfl_xor(acc, 32, 64);
@@ -577,6 +584,10 @@ chunk_mfma_kernel(ChunkArgs a)
         }
         __syncthreads();
 
+        // prefetch the next chunk: its latency hides behind the state phase,
+        // and the raw registers are not live during the phases above
+        if (c0 + C < tok1) load_raw(R, c0 + C);
+
         // ================= S: state-dependent part ==================
         // state as fp16 hi/lo B-frags (channel order of the accumulators)
         f16x8 sh[4], sl[4];
@@ -594,19 +605,30 @@ chunk_mfma_kernel(ChunkArgs a)
             }
         }
         // R = V - (K^ Gamma) S  (rows = tokens 16mt + 4g + i, column n of the strip)
+        // Operand fragments of each step are read from LDS in one batch ahead
+        // of its MFMAs (one wave per SIMD: nothing else hides LDS latency).
         f32x4 ut[4];
+        {
+            f16x8 fa[4][4];
+            float vv[4][4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 acc;
+            for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
+                for (int kb = 0; kb < 4; ++kb) fa[mt][kb] = s.kgn[mt][kb][l];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const f16x8 ka = s.kgn[mt][kb][l];
-                acc = mmh(ka, sh[kb], acc);
-                acc = mmh(ka, sl[kb], acc);
+                for (int i = 0; i < 4; ++i) vv[mt][i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
             }
-            ut[mt] = acc;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc = {vv[mt][0], vv[mt][1], vv[mt][2], vv[mt][3]};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    acc = mmh(fa[mt][kb], sh[kb], acc);
+                    acc = mmh(fa[mt][kb], sl[kb], acc);
+                }
+                ut[mt] = acc;
+            }
         }
         bf16x8 rbh[2], rbl[2];
 #pragma unroll
@@ -623,13 +645,25 @@ chunk_mfma_kernel(ChunkArgs a)
             }
         }
         // U~ = T' R
+        {
+            bf16x8 th[6], tl[6];   // (mt, kb) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < 6; ++p) {
+                const int mt = (p < 2) ? p : 2 + ((p - 2) >> 1), kb = (p < 2) ? 0 : ((p - 2) & 1);
+                th[p] = s.tp[0][mt][kb][l];
+                tl[p] = s.tp[1][mt][kb][l];
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb <= (mt >> 1); ++kb)
-                acc = mma3(s.tp[0][mt][kb][l], s.tp[1][mt][kb][l], rbh[kb], rbl[kb], acc);
-            ut[mt] = acc;
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= (mt >> 1); ++kb) {
+                    const int p = (mt < 2) ? mt : 2 + 2 * (mt - 2) + kb;
+                    acc = mma3(th[p], tl[p], rbh[kb], rbl[kb], acc);
+                }
+                ut[mt] = acc;
+            }
         }
         f16x8 ub[2];
 #pragma unroll
@@ -640,38 +674,66 @@ chunk_mfma_kernel(ChunkArgs a)
                 ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
             }
         }
-        // O = (Q^ Gamma) S + A_qk U~
+        // O = (Q^ Gamma) S + A_qk U~, two token tiles per batch
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int half = 0; half < 2; ++half) {
+            f16x8 qa[2][4], ah[2][2], al[2][2];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const f16x8 qa = s.qg[mt][kb][l];
-                acc = mmh(qa, sh[kb], acc);
-                acc = mmh(qa, sl[kb], acc);
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mt = 2 * half + m2;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.qg[mt][kb][l];
+#pragma unroll
+                for (int kb = 0; kb <= half; ++kb) {
+                    ah[m2][kb] = s.aqk[0][mt][kb][l];
+                    al[m2][kb] = s.aqk[1][mt][kb][l];
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb <= (mt >> 1); ++kb) {
-                acc = mmh(s.aqk[0][mt][kb][l], ub[kb], acc);
-                acc = mmh(s.aqk[1][mt][kb][l], ub[kb], acc);
-            }
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mt = 2 * half + m2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mt + 4 * g + i;
-                if (r < L)
-                    Elem<Tout>::store(op, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + 16 * w + n, a.scale * acc[i]);
+                for (int kb = 0; kb < 4; ++kb) {
+                    acc = mmh(qa[m2][kb], sh[kb], acc);
+                    acc = mmh(qa[m2][kb], sl[kb], acc);
+                }
+#pragma unroll
+                for (int kb = 0; kb <= half; ++kb) {
+                    acc = mmh(ah[m2][kb], ub[kb], acc);
+                    acc = mmh(al[m2][kb], ub[kb], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * g + i;
+                    if (r < L) store_out(op + (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + 16 * w + n, a.scale * acc[i]);
+                }
             }
         }
-        // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~
+        // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~, four channel tiles per batch
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const float4 gm4 = *reinterpret_cast<const float4*>(&s.gam[16 * mt + 4 * g]);
-            sacc[mt][0] *= gm4.x;
-            sacc[mt][1] *= gm4.y;
-            sacc[mt][2] *= gm4.z;
-            sacc[mt][3] *= gm4.w;
+        for (int half = 0; half < 2; ++half) {
+            f16x8 ka[4][2];
+            float4 gm4[4];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) sacc[mt] = mmh(s.u1.kp[mt][kb][l], ub[kb], sacc[mt]);
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const int mt = 4 * half + m4;
+                ka[m4][0] = s.u1.kp[mt][0][l];
+                ka[m4][1] = s.u1.kp[mt][1][l];
+                gm4[m4] = *reinterpret_cast<const float4*>(&s.gam[16 * mt + 4 * g]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const int mt = 4 * half + m4;
+                sacc[mt][0] *= gm4[m4].x;
+                sacc[mt][1] *= gm4[m4].y;
+                sacc[mt][2] *= gm4[m4].z;
+                sacc[mt][3] *= gm4[m4].w;
+                sacc[mt] = mmh(ka[m4][0], ub[0], sacc[mt]);
+                sacc[mt] = mmh(ka[m4][1], ub[1], sacc[mt]);
+            }
         }
         __syncthreads();
     }
