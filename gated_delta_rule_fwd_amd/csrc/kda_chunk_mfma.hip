@@ -69,17 +69,21 @@ constexpr int NT = 256;
 struct alignas(16) Smem {
     __bf16 vs[C][DVS];                   // V slice, plain [token][column]
     union {
-        bf16x8 kf[2][4][4][64];          // K^ e^(ref-b)   B-frags [hi/lo][token tile][chan kb][lane]
+        struct {
+            bf16x8 kf[2][4][4][64];      // K^ e^(ref_{j+1}-b) B-frags [hi/lo][token tile j][chan kb][lane]
+            bf16x8 kfx[2][3][4][64];     // the same rescaled to ref_i for tiles (i,j) = (2,0), (3,0), (3,1)
+        } b;
         f16x8 kp[8][2][64];              // (K^ gamma/Gamma)^T A-frags [chan tile][token kb][lane]
-        float tot[4][DK];                // sum of g over each sub-tile (preprocess only)
     } u1;
+    float tot[4][DK];                    // sum of g over each sub-tile
     float akk[C][C + 1];                 // A_kk (fp32), then T = (I + A_kk)^-1 in place
     f16x8 aqk[2][4][2][64];              // A_qk       A-frags [hi/lo][token tile][token kb][lane]
     bf16x8 tp[2][4][2][64];              // T'         A-frags [hi/lo][token tile][token kb][lane]
     f16x8 qg[4][4][64];                  // Q^ Gamma   A-frags [token tile][chan kb][lane]
     f16x8 kgn[4][4][64];                 // -K^ Gamma  A-frags [token tile][chan kb][lane]
-    float ref[5][DK];                    // running decay at sub-tile boundaries
-    float dlt[4][DK];                    // exp(sum of g over sub-tile w)
+    float fac[4][4][DK];                 // per sub-tile w and channel: tot_w, exp(tot_w),
+                                         //   exp(ref_w), exp(ref_4 - ref_{w+1})
+    float dl12[2][DK];                   // exp(tot_1), exp(tot_2)
     float gam[DK];                       // gamma = exp(b at the chunk end)
     float beta[C];
 };
@@ -149,9 +153,6 @@ __device__ __forceinline__ void store_out(uint16_t* p, float x)
     *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// m ? x : 1 for m in {0, 1}, without a branch and without rounding x
-__device__ __forceinline__ float sel(float m, float x) { return fmaf(m, x, 1.f - m); }
-
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -208,15 +209,6 @@ chunk_mfma_kernel(ChunkArgs a)
     Tout* __restrict__ op = static_cast<Tout*>(a.o);
 
     const int row = 16 * w + n;   // this lane's token row inside the chunk
-    // 0/1 masks of the (wave-uniform) sub-tile index, used as arithmetic selects
-    float mlt[4], meq[4], mgt[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        mlt[u] = (u < w) ? 1.f : 0.f;
-        meq[u] = (u == w) ? 1.f : 0.f;
-        mgt[u] = (u > w) ? 1.f : 0.f;
-    }
-
     // Rows past the end of the sequence load the last valid token instead
     // (no branch, no zero fill); their k, g and beta are masked to zero when
     // the chunk is unpacked, which makes them the identity of the recurrence.
@@ -314,7 +306,7 @@ chunk_mfma_kernel(ChunkArgs a)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) s.u1.tot[w][32 * kb + 8 * g + e] = bv[8 * kb + e];
+                for (int e = 0; e < 8; ++e) s.tot[w][32 * kb + 8 * g + e] = bv[8 * kb + e];
         }
         if (g == 0) s.beta[row] = beta_r;
         // V slice, plain layout
@@ -322,64 +314,109 @@ chunk_mfma_kernel(ChunkArgs a)
         *reinterpret_cast<uint4*>(&s.vs[row][16 * g + 8]) = vraw1;
         __syncthreads();
 
-        // per-channel decay tables: ref_w (running decay at the start of
-        // sub-tile w), exp of each sub-tile's total, and gamma
+        // per-channel decay factors for every sub-tile; each factor is an
+        // exp of a non-positive sum, so none overflows
         {
             const int c = t & (DK - 1);
-            const float t0 = s.u1.tot[0][c], t1 = s.u1.tot[1][c], t2 = s.u1.tot[2][c], t3 = s.u1.tot[3][c];
+            const float t0 = s.tot[0][c], t1 = s.tot[1][c], t2 = s.tot[2][c], t3 = s.tot[3][c];
+            const float r1 = t0, r2 = t0 + t1, r3 = r2 + t2, r4 = r3 + t3;
             if (t < DK) {
-                s.ref[0][c] = 0.f;
-                s.ref[1][c] = t0;
-                s.ref[2][c] = t0 + t1;
-                s.ref[3][c] = t0 + t1 + t2;
-                s.ref[4][c] = t0 + t1 + t2 + t3;
-                s.gam[c] = __expf(t0 + t1 + t2 + t3);
+                s.fac[0][0][c] = t0;
+                s.fac[0][1][c] = __expf(t0);
+                s.fac[0][2][c] = 1.f;
+                s.fac[0][3][c] = __expf(r4 - r1);
+                s.fac[1][0][c] = t1;
+                s.fac[1][1][c] = __expf(t1);
+                s.fac[1][2][c] = __expf(r1);
+                s.fac[1][3][c] = __expf(r4 - r2);
+                s.dl12[0][c] = __expf(t1);
+                s.dl12[1][c] = __expf(t2);
             } else {
-                s.dlt[0][c] = __expf(t0);
-                s.dlt[1][c] = __expf(t1);
-                s.dlt[2][c] = __expf(t2);
-                s.dlt[3][c] = __expf(t3);
+                s.fac[2][0][c] = t2;
+                s.fac[2][1][c] = __expf(t2);
+                s.fac[2][2][c] = __expf(r2);
+                s.fac[2][3][c] = __expf(r4 - r3);
+                s.fac[3][0][c] = t3;
+                s.fac[3][1][c] = __expf(t3);
+                s.fac[3][2][c] = __expf(r3);
+                s.fac[3][3][c] = 1.f;
+                s.gam[c] = __expf(r4);
             }
         }
         __syncthreads();
 
-        // decay factors for this row; operand fragments for the later phases.
-        // Products of the per-sub-tile factors dlt (each <= 1) give every
-        // longer-range factor without overflow: if one underflows, the term it
-        // scales is below the fp32 range anyway.
-        float dv[32];   // exp(b_r - ref_{w+1}) in [1, e^80]
+        // Per element: d = exp(b - ref_{w+1}) in [1, e^80], f = 1/d,
+        // E = exp(b - ref_w) <= 1, Gamma = exp(b).  The diagonal tile (w, w)
+        // is computed right here: both of its operands are in this lane.  The
+        // off-diagonal tiles share one A-operand, X^ E; the extra factor
+        // exp(ref_w - ref_{j+1}) of tiles two or three sub-tiles apart is folded
+        // into their B-operands (kfx).
+        bf16x8 kao[4], qoh[4], qol[4];
+        f16x8 kq16[4];   // K^ gamma/Gamma of this row, channels 32kb + 8g + e
+        f32x4 akd = {0.f, 0.f, 0.f, 0.f}, aqd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int cb = 32 * kb + 8 * g;
-            float rw[8], rw1[8], d0[8], d1[8], d2[8], d3[8];
-            lds8(&s.ref[w][cb], rw);
-            lds8(&s.ref[w + 1][cb], rw1);
-            lds8(&s.dlt[0][cb], d0);
-            lds8(&s.dlt[1][cb], d1);
-            lds8(&s.dlt[2][cb], d2);
-            lds8(&s.dlt[3][cb], d3);
-            bf16x8 kfh, kfl;
+            float tw[8], dw[8], er[8], el[8];
+            lds8(&s.fac[w][0][cb], tw);
+            lds8(&s.fac[w][1][cb], dw);
+            lds8(&s.fac[w][2][cb], er);
+            lds8(&s.fac[w][3][cb], el);
+            bf16x8 kfh, kfl, kad, qdh, qdl;
             float qgv[8], kgv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // branch-free selection by the wave index: x^m = m x + (1 - m), exact for m in {0, 1}
-                const float eref = sel(mlt[0], d0[e]) * sel(mlt[1], d1[e]) *
-                                   sel(mlt[2], d2[e]);
-                const float dw = meq[0] * d0[e] + meq[1] * d1[e] + meq[2] * d2[e] + meq[3] * d3[e];
-                const float b = bv[8 * kb + e] + rw[e];
-                const float d = __expf(b - rw1[e]);
-                const float f = __expf(rw1[e] - b);
-                const float gm = d * dw * eref;    // exp(b_r) = exp(b_r - ref_w) exp(ref_w)
-                dv[8 * kb + e] = d;
+                const float bl = bv[8 * kb + e];         // running sum inside sub-tile w
+                const float d = __expf(bl - tw[e]);      // b - ref_{w+1}
+                const float f = __expf(tw[e] - bl);
+                const float E = d * dw[e];               // exp(b - ref_w)
+                const float gm = E * er[e];              // exp(b)
+                const float kx = kv[8 * kb + e], qx = qv[8 * kb + e];
                 __bf16 hi, lo;
-                split(kv[8 * kb + e] * f, hi, lo);
+                split(kx * f, hi, lo);
                 kfh[e] = hi;
                 kfl[e] = lo;
-                qgv[e] = qv[8 * kb + e] * gm;
-                kgv[e] = -kv[8 * kb + e] * gm;
+                qgv[e] = qx * gm;
+                kgv[e] = -kx * gm;
+                kad[e] = static_cast<__bf16>(kx * d);
+                split(qx * d, hi, lo);
+                qdh[e] = hi;
+                qdl[e] = lo;
+                kao[kb][e] = static_cast<__bf16>(kx * E);
+                split(qx * E, hi, lo);
+                qoh[kb][e] = hi;
+                qol[kb][e] = lo;
+                kq16[kb][e] = static_cast<_Float16>(kx * f * el[e]);
             }
-            s.u1.kf[0][w][kb][l] = kfh;
-            s.u1.kf[1][w][kb][l] = kfl;
+            akd = mma(kad, kfh, akd);
+            aqd = mma3(qdh, qdl, kfh, kfl, aqd);
+            s.u1.b.kf[0][w][kb][l] = kfh;
+            s.u1.b.kf[1][w][kb][l] = kfl;
+            // sub-tiles 0 and 1 also provide their B-operands rescaled to
+            // ref_i for rows two or three sub-tiles below
+            if (w < 2) {
+                float x1[8], x2[8];
+                lds8(&s.dl12[0][cb], x1);
+                lds8(&s.dl12[1][cb], x2);
+#pragma unroll
+                for (int ver = 0; ver < 2; ++ver) {
+                    if (w == 1 && ver == 1) break;
+                    bf16x8 xh, xl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float kf = static_cast<float>(kfh[e]) + static_cast<float>(kfl[e]);
+                        // (i,j) = (2,0): exp(tot_1); (3,0): exp(tot_1 + tot_2); (3,1): exp(tot_2)
+                        const float sc = (w == 0) ? ((ver == 0) ? x1[e] : x1[e] * x2[e]) : x2[e];
+                        __bf16 hi, lo;
+                        split(kf * sc, hi, lo);
+                        xh[e] = hi;
+                        xl[e] = lo;
+                    }
+                    const int vi = (w == 0) ? ver : 2;
+                    s.u1.b.kfx[0][vi][kb][l] = xh;
+                    s.u1.b.kfx[1][vi][kb][l] = xl;
+                }
+            }
             // Q^ Gamma and -K^ Gamma into the state's channel order: channel
             // 32kb + 8g + e goes to lane (2(g&1) + e/4)*16 + n, element 4(g>>1) + e%4
             {
@@ -399,60 +436,50 @@ chunk_mfma_kernel(ChunkArgs a)
                 *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&s.kgn[w][kb][l1]) + eo) = k1;
             }
         }
+        // diagonal tile (w, w): lane holds rows 16w + 4g + i, column 16w + n
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * g + i, sc = 16 * w + n;
+            if (sc < r) s.akk[r][sc] = s.beta[r] * akd[i];
+            _Float16 hi, lo;
+            splith((sc <= r) ? aqd[i] : 0.f, hi, lo);
+            const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (w & 1);
+            reinterpret_cast<_Float16*>(&s.aqk[0][w][w >> 1][lt])[e] = hi;
+            reinterpret_cast<_Float16*>(&s.aqk[1][w][w >> 1][lt])[e] = lo;
+            if ((w & 1) == 0) {   // tile (w, w+1) shares this token kb: zero it
+                reinterpret_cast<_Float16*>(&s.aqk[0][w][w >> 1][lt])[e + 4] = static_cast<_Float16>(0.f);
+                reinterpret_cast<_Float16*>(&s.aqk[1][w][w >> 1][lt])[e + 4] = static_cast<_Float16>(0.f);
+            }
+        }
         __syncthreads();
 
-        // ================= A: intra-chunk tiles (w, j <= w) ==================
-        for (int j = 0; j <= w; ++j) {
+        // ================= A: off-diagonal intra-chunk tiles (w, j < w) ==================
+        for (int j = 0; j < w; ++j) {
             f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-            // off-diagonal tiles use exp(b - ref_w) * prod_{j < u < w} dlt_u
-            const float moff = (j < w) ? 1.f : 0.f;
-            const float m1 = (j < 1 && 1 < w) ? 1.f : 0.f;
-            const float m2 = (j < 2 && 2 < w) ? 1.f : 0.f;
+            // B-operand: sub-tile j's own (j = w - 1), or its copy rescaled to ref_w
+            const bf16x8* bsrc_h = (j + 2 <= w) ? &s.u1.b.kfx[0][(w == 2) ? 0 : j + 1][0][0] : &s.u1.b.kf[0][j][0][0];
+            const bf16x8* bsrc_l = (j + 2 <= w) ? &s.u1.b.kfx[1][(w == 2) ? 0 : j + 1][0][0] : &s.u1.b.kf[1][j][0][0];
+            bf16x8 bh[4], bl[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const int cb = 32 * kb + 8 * g;
-                float d0[8], d1[8], d2[8], d3[8];
-                lds8(&s.dlt[0][cb], d0);
-                lds8(&s.dlt[1][cb], d1);
-                lds8(&s.dlt[2][cb], d2);
-                lds8(&s.dlt[3][cb], d3);
-                bf16x8 ka, qh, ql;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // diagonal tile: exp(b - ref_{w+1}); off-diagonal:
-                    // exp(b - ref_w) * exp(ref_w - ref_{j+1})
-                    const float dw = meq[0] * d0[e] + meq[1] * d1[e] + meq[2] * d2[e] + meq[3] * d3[e];
-                    const float off = dw * sel(m1, d1[e]) * sel(m2, d2[e]);
-                    const float fac = dv[8 * kb + e] * sel(moff, off);
-                    ka[e] = static_cast<__bf16>(kv[8 * kb + e] * fac);
-                    __bf16 hi, lo;
-                    split(qv[8 * kb + e] * fac, hi, lo);
-                    qh[e] = hi;
-                    ql[e] = lo;
-                }
-                const bf16x8 bh = s.u1.kf[0][j][kb][l], bl = s.u1.kf[1][j][kb][l];
-                akk = mma(ka, bh, akk);
-                aqk = mma3(qh, ql, bh, bl, aqk);
+                bh[kb] = bsrc_h[kb * 64 + l];
+                bl[kb] = bsrc_l[kb * 64 + l];
             }
-            // lane holds rows r = 16w + 4g + i, column s = 16j + n
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                akk = mma(kao[kb], bh[kb], akk);
+                aqk = mma3(qoh[kb], qol[kb], bh[kb], bl[kb], aqk);
+            }
+            // lane holds rows r = 16w + 4g + i, column s = 16j + n (all s < r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * w + 4 * g + i, sc = 16 * j + n;
-                if (sc < r) s.akk[r][sc] = s.beta[r] * akk[i];
-                const float vq = (sc <= r) ? aqk[i] : 0.f;
+                s.akk[r][sc] = s.beta[r] * akk[i];
                 _Float16 hi, lo;
-                splith(vq, hi, lo);
+                splith(aqk[i], hi, lo);
                 const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (j & 1);
                 reinterpret_cast<_Float16*>(&s.aqk[0][w][j >> 1][lt])[e] = hi;
                 reinterpret_cast<_Float16*>(&s.aqk[1][w][j >> 1][lt])[e] = lo;
-            }
-        }
-        if ((w & 1) == 0) {   // tile (w, w+1) shares a token kb with (w, w): zero it
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4;
-                reinterpret_cast<_Float16*>(&s.aqk[0][w][w >> 1][lt])[e] = static_cast<_Float16>(0.f);
-                reinterpret_cast<_Float16*>(&s.aqk[1][w][w >> 1][lt])[e] = static_cast<_Float16>(0.f);
             }
         }
         __syncthreads();
@@ -495,22 +522,11 @@ chunk_mfma_kernel(ChunkArgs a)
             const int e = (n & 3) + 4 * (w & 1);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const int cb = 32 * kb + 8 * g;
-                float d1[8], d2[8], d3[8];
-                lds8(&s.dlt[1][cb], d1);
-                lds8(&s.dlt[2][cb], d2);
-                lds8(&s.dlt[3][cb], d3);
                 const int mt = 2 * kb + (g >> 1);
                 const int lb = (n >> 2) * 16 + 8 * (g & 1);
                 _Float16* dst = reinterpret_cast<_Float16*>(&s.u1.kp[mt][w >> 1][0]);
 #pragma unroll
-                for (int ee = 0; ee < 8; ++ee) {
-                    // exp(b_L - b_r) = exp(ref_{w+1} - b_r) exp(b_L - ref_{w+1})
-                    const float eL = sel(mgt[1], d1[ee]) * sel(mgt[2], d2[ee]) *
-                                     sel(mgt[3], d3[ee]);
-                    const float kq = kv[8 * kb + ee] * __builtin_amdgcn_rcpf(dv[8 * kb + ee]) * eL;
-                    dst[(lb + ee) * 8 + e] = static_cast<_Float16>(kq);
-                }
+                for (int ee = 0; ee < 8; ++ee) dst[(lb + ee) * 8 + e] = kq16[kb][ee];
             }
         }
         // level 1: T_{w,w-1} = -T_ww A_{w,w-1} T_{w-1,w-1} for w = 1, 3 (fp32 MFMA)
