@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
-    p.add_argument("--cpu-sample-heads", type=int, default=32)
+    p.add_argument("--cpu-sample-heads", type=int, default=96)
     p.add_argument("--cpu-sample-tokens", type=int, default=65536)
     return p.parse_args()
 

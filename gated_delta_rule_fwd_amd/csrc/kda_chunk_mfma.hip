@@ -153,6 +153,16 @@ __device__ __forceinline__ void store_out(uint16_t* p, float x)
     *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// value of the lane with index ^1 / ^2 inside its quad (DPP quad_perm)
+__device__ __forceinline__ float quad_swap1(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_swap2(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -368,7 +378,7 @@ chunk_mfma_kernel(ChunkArgs a)
             for (int e = 0; e < 8; ++e) {
                 const float bl = bv[8 * kb + e];         // running sum inside sub-tile w
                 const float d = __expf(bl - tw[e]);      // b - ref_{w+1}
-                const float f = __expf(tw[e] - bl);
+                const float f = __builtin_amdgcn_rcpf(d);  // exp(ref_{w+1} - b)
                 const float E = d * dw[e];               // exp(b - ref_w)
                 const float gm = E * er[e];              // exp(b)
                 const float kx = kv[8 * kb + e], qx = qv[8 * kb + e];
@@ -485,34 +495,33 @@ chunk_mfma_kernel(ChunkArgs a)
         __syncthreads();
 
         // ================= T: (I + A_kk)^-1, blocked, in place ==================
-        // diagonal 16x16 blocks by forward substitution: lane owns column n of
-        // block w and the rows g + 4m of it
+        // diagonal 16x16 blocks by forward substitution: lane owns column
+        // l/4 of block w and the rows l%4 + 4m of it; the four partial sums of
+        // a column sit in one lane quad and are reduced with DPP
         {
+            const int col = l >> 2, pr = l & 3;
             float tv[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) tv[m] = (g + 4 * m == n) ? 1.f : 0.f;
+            for (int m = 0; m < 4; ++m) tv[m] = (pr + 4 * m == col) ? 1.f : 0.f;
             const int b0 = 16 * w;
-            // the block's strictly-lower entries this lane needs, read up front
-            float av[16][4];
+            float av[16][4];   // the block's strictly-lower entries this lane needs
 #pragma unroll
             for (int rr = 1; rr < 16; ++rr)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) av[rr][m] = s.akk[b0 + rr][b0 + g + 4 * m];
+                for (int m = 0; m < 4; ++m) av[rr][m] = s.akk[b0 + rr][b0 + pr + 4 * m];
 #pragma unroll
             for (int rr = 1; rr < 16; ++rr) {
                 float acc = 0.f;
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int sr = g + 4 * m;
-                    if (sr < rr) acc += av[rr][m] * tv[m];
-                }
-                acc += __shfl_xor(acc, 16, 64);
-                acc += __shfl_xor(acc, 32, 64);
-                const float tval = (rr > n) ? -acc : ((rr == n) ? 1.f : 0.f);
-                if ((rr & 3) == g) tv[rr >> 2] = tval;
+                for (int m = 0; m < 4; ++m)
+                    if (pr + 4 * m < rr) acc += av[rr][m] * tv[m];
+                acc += quad_swap1(acc);
+                acc += quad_swap2(acc);
+                const float tval = (rr > col) ? -acc : ((rr == col) ? 1.f : 0.f);
+                if ((rr & 3) == pr) tv[rr >> 2] = tval;
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) s.akk[b0 + g + 4 * m][b0 + n] = tv[m];
+            for (int m = 0; m < 4; ++m) s.akk[b0 + pr + 4 * m][b0 + col] = tv[m];
         }
         __syncthreads();
 
