@@ -76,7 +76,8 @@ struct alignas(16) Smem {
         f16x8 kp[8][2][64];              // (K^ gamma/Gamma)^T A-frags [chan tile][token kb][lane]
     } u1;
     float tot[4][DK];                    // sum of g over each sub-tile
-    float akk[C][C + 1];                 // A_kk (fp32), then T = (I + A_kk)^-1 in place
+    float akk[C][C + 4];                 // A_kk (fp32), then T = (I + A_kk)^-1 in place; rows 16-byte aligned;
+                                         // reused to stage the output tile of the state phase
     f16x8 aqk[2][4][2][64];              // A_qk       A-frags [hi/lo][token tile][token kb][lane]
     bf16x8 tp[2][4][2][64];              // T'         A-frags [hi/lo][token tile][token kb][lane]
     f16x8 qg[4][4][64];                  // Q^ Gamma   A-frags [token tile][chan kb][lane]
@@ -146,11 +147,15 @@ __device__ __forceinline__ float row_scan16(float x)
     return x;
 }
 
-__device__ __forceinline__ void store_out(float* p, float x) { *p = x; }
-// bf16 output: the hardware conversion rounds to nearest even
-__device__ __forceinline__ void store_out(uint16_t* p, float x)
+// output tile staging in LDS, [token][column] of the workgroup's 64 columns;
+// bf16 is rounded to nearest even by the hardware conversion
+__device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const float*)
 {
-    *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+    base[r * DVS + c] = x;
+}
+__device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const uint16_t*)
+{
+    reinterpret_cast<uint16_t*>(base)[r * DVS + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // value of the lane with index ^1 / ^2 inside its quad (DPP quad_perm)
@@ -373,7 +378,7 @@ chunk_mfma_kernel(ChunkArgs a)
             lds8(&s.fac[w][2][cb], er);
             lds8(&s.fac[w][3][cb], el);
             bf16x8 kfh, kfl, kad, qdh, qdl;
-            float qgv[8], kgv[8];
+            float qgv[8], kgv[8], kfv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float bl = bv[8 * kb + e];         // running sum inside sub-tile w
@@ -382,6 +387,7 @@ chunk_mfma_kernel(ChunkArgs a)
                 const float E = d * dw[e];               // exp(b - ref_w)
                 const float gm = E * er[e];              // exp(b)
                 const float kx = kv[8 * kb + e], qx = qv[8 * kb + e];
+                kfv[e] = kx * f;
                 __bf16 hi, lo;
                 split(kx * f, hi, lo);
                 kfh[e] = hi;
@@ -414,11 +420,10 @@ chunk_mfma_kernel(ChunkArgs a)
                     bf16x8 xh, xl;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float kf = static_cast<float>(kfh[e]) + static_cast<float>(kfl[e]);
                         // (i,j) = (2,0): exp(tot_1); (3,0): exp(tot_1 + tot_2); (3,1): exp(tot_2)
                         const float sc = (w == 0) ? ((ver == 0) ? x1[e] : x1[e] * x2[e]) : x2[e];
                         __bf16 hi, lo;
-                        split(kf * sc, hi, lo);
+                        split(kfv[e] * sc, hi, lo);
                         xh[e] = hi;
                         xl[e] = lo;
                     }
@@ -594,10 +599,16 @@ chunk_mfma_kernel(ChunkArgs a)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 bf16x8 th, tl;
+                const float4 t0 = *reinterpret_cast<const float4*>(&s.akk[row][32 * kb + 4 * g]);
+                const float4 t1 = *reinterpret_cast<const float4*>(&s.akk[row][32 * kb + 16 + 4 * g]);
+                const float4 b0 = *reinterpret_cast<const float4*>(&s.beta[32 * kb + 4 * g]);
+                const float4 b1 = *reinterpret_cast<const float4*>(&s.beta[32 * kb + 16 + 4 * g]);
+                const float tv8[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
+                                      t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int sc = 32 * kb + 16 * (e >> 2) + 4 * g + (e & 3);
-                    const float x = (sc <= row) ? s.akk[row][sc] * s.beta[sc] : 0.f;
+                    const float x = (sc <= row) ? tv8[e] : 0.f;
                     __bf16 hi, lo;
                     split(x, hi, lo);
                     th[e] = hi;
@@ -731,8 +742,10 @@ chunk_mfma_kernel(ChunkArgs a)
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * mt + 4 * g + i;
-                    if (r < L) store_out(op + (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + 16 * w + n, a.scale * acc[i]);
+                    // stage the output tile in LDS (the A_kk area is free now)
+                    // so that the global stores below write whole rows
+                    stage_out(&s.akk[0][0], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
+                              static_cast<const Tout*>(nullptr));
                 }
             }
         }
@@ -758,6 +771,21 @@ chunk_mfma_kernel(ChunkArgs a)
                 sacc[mt][3] *= gm4[m4].w;
                 sacc[mt] = mmh(ka[m4][0], ub[0], sacc[mt]);
                 sacc[mt] = mmh(ka[m4][1], ub[1], sacc[mt]);
+            }
+        }
+        __syncthreads();
+        // coalesced output rows: 64 tokens x 64 columns of this slice
+        {
+            constexpr int CH = 16 / sizeof(Tout);            // elements per 16-byte piece
+            constexpr int PER_ROW = DVS / CH;
+#pragma unroll
+            for (int pc = t; pc < C * PER_ROW; pc += NT) {
+                const int r = pc / PER_ROW, part = pc % PER_ROW;
+                if (r < L) {
+                    const uint4 val = *reinterpret_cast<const uint4*>(
+                        reinterpret_cast<const char*>(&s.akk[0][0]) + (r * DVS + part * CH) * sizeof(Tout));
+                    *reinterpret_cast<uint4*>(op + (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + part * CH) = val;
+                }
             }
         }
         __syncthreads();
