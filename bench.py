@@ -79,7 +79,8 @@ def time_prefill(kda, torch, d, steps, warmup):
     stream = torch.cuda.current_stream()
 
     def call():
-        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], o=d["o"], final_state=d["sT"])
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], o=d["o"], final_state=d["sT"],
+                      workspace=d["ws"])
 
     for _ in range(warmup):
         call()
@@ -183,6 +184,8 @@ def main():
          "s0": to(inp.init_state)}
     d["o"] = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     d["sT"] = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    # chunk-record workspace of the two-pass matrix-core path, allocated once
+    d["ws"] = torch.empty(kda.workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
 
     total_ms, launches, wall = time_prefill(kda, torch, d, args.steps, args.warmup)
     ms = total_ms / args.steps

@@ -45,10 +45,33 @@ const char* kda_status_str(kda_status s)
     return "unknown status";
 }
 
+namespace {
+
+// The matrix-core path serves bf16 inputs with d_k = d_v = 128 unless the
+// fp32 path is forced; it needs the two-pass record workspace.
+bool uses_two_pass(const kda_chunk_desc* d)
+{
+    return d->in_dtype == KDA_BF16 && d->d_k == 128 && d->d_v == 128 && !(d->flags & KDA_FLAG_FP32_PATH);
+}
+
+// Workspace of one call: validation counters first, then the records.
+size_t workspace_need(const kda_chunk_desc* d, bool packed)
+{
+    size_t bytes = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+    if (uses_two_pass(d)) bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed);
+    return bytes;
+}
+
+}  // namespace
+
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d)
 {
     if (!d) return static_cast<size_t>(-1);
-    return (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+    if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->num_seqs < 0) return 0;   // rejected by kda_chunk_fwd
+    // the descriptor does not say whether cu_seqlens will be passed: cover both
+    const size_t dense = workspace_need(d, false);
+    const size_t packed = (d->B == 1 && d->num_seqs > 0) ? workspace_need(d, true) : 0;
+    return dense > packed ? dense : packed;
 }
 
 kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
@@ -71,9 +94,12 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     for (const void* p : rows)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
     if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_INVALID_ARG;
-    if (ws_bytes < kda_chunk_fwd_workspace_bytes(d)) return KDA_ERR_WORKSPACE;
-    if ((d->flags & KDA_FLAG_VALIDATE) && !workspace) return KDA_ERR_WORKSPACE;
+    const size_t need = workspace_need(d, cu_seqlens != nullptr);
+    if (ws_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
+    if (uses_two_pass(d) && kda::chunk_record_slots(d->B, d->T, d->num_seqs, cu_seqlens != nullptr) * d->H >= (1LL << 24))
+        return KDA_ERR_INVALID_ARG;   // more (chunk, head) workgroups than one launch takes
 
     kda::ChunkArgs a{};
     a.B = d->B;
@@ -109,10 +135,12 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
         if (host[0] || host[1] || host[2]) return KDA_ERR_RANGE;
     }
 
-    if (!(d->flags & KDA_FLAG_FP32_PATH) && kda::chunk_mfma_supported(a))
-        e = kda::launch_chunk_mfma(a, stream);
-    else
+    if (uses_two_pass(d)) {
+        const size_t off = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+        e = kda::launch_chunk_two_pass(a, static_cast<char*>(workspace) + off, stream);
+    } else {
         e = kda::launch_chunk_fp32(a, stream);
+    }
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;
 }

@@ -1,0 +1,850 @@
+// kda_chunk_two_pass.hip -- chunkwise KDA forward on the gfx950 matrix cores,
+// split into a chunk-parallel pass and a sequential pass.
+//
+// Scope: bf16 q/k/v, d_k = d_v = 128, log-decay g in [-5, 0].
+//
+// Per chunk (C = 64, tokens r, s; "Kimi K3 模型结构（2）" Q&A on the chunkwise
+// algorithm, on A[t] and O[t]; "Kimi K3 の KDA ..." section 1.2.1 on the two
+// paths):
+//   b     = running sum of g inside the chunk (per key channel), Gamma = e^b
+//   A_kk  = StrictTril(Diag(beta) (K^ Gamma)(K^ / Gamma)^T)
+//   A_qk  = Tril((Q^ Gamma)(K^ / Gamma)^T)                (diagonal kept)
+//   T'    = (I + A_kk)^-1 Diag(beta)                      (UT transform)
+//   U~    = T' (V - (K^ Gamma) S)          (= U - W S with W = T' K^ Gamma, U = T' V)
+//   O     = (Q^ Gamma) S + A_qk U~
+//   S    <- Diag(gamma) S + (K^ gamma / Gamma)^T U~
+//
+// Only the last three lines involve the carried state S.  Everything above
+// them is local to one chunk, so it is computed for all chunks of all heads
+// at once (pass 1, one workgroup per (chunk, head)) and stored as a
+// ChunkRecord of ready-made MFMA operand fragments.  Pass 2 walks each chain
+// (sequence, head) in chunk order, one workgroup per 64-column slice of d_v
+// (the columns are independent affine systems sharing one transition,
+// "Kimi K3 の KDA ..." section 2.3.2), streaming one record per chunk while
+// the state stays in MFMA accumulators.
+//
+// The ratios Gamma_r / Gamma_s are formed per 16-token sub-tile with a
+// reference point between s and r ("Kimi K3 の KDA ..." section 1.2.1 on the
+// lower-bounded decay; "Kimi K3 模型结构（2）" Q&A on the -5 bound): with
+// ref_j the running decay at the end of sub-tile j, tile (i, j <= i) is
+//   [X_r exp(b_r - ref_i)] . [K_s exp(ref_i - b_s)]          (j < i)
+//   [X_r exp(b_r - ref_{i+1})] . [K_s exp(ref_{i+1} - b_s)]  (j = i)
+// where every factor is <= 1 except the diagonal tile's left one (<= e^80
+// for 16 steps of g >= -5): all are dense bf16 matrix products.
+//
+// Precision (fp32 accumulate everywhere; "x3" = hi*hi + hi*lo + lo*hi with
+// x = hi + lo):
+//   A_kk                bf16
+//   A_qk                bf16 x3                  (diagonal factor up to e^80)
+//   T' (V - K Gamma S)  bf16 x3                  (near a fixed point of the
+//                                                 recurrence V and K Gamma S
+//                                                 nearly cancel)
+//   K Gamma S, Q Gamma S  fp16 operand x fp16 hi/lo state
+//   A_qk U~             fp16 hi/lo x fp16
+//   K'^T U~             fp16 x fp16              (|K'| <= 1, U~ bounded)
+#include "kda_kernels.h"
+#include "kda_mfma.h"
+
+namespace kda {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int DVS = 64;     // value columns per pass-2 workgroup: 4 waves x 16
+constexpr int NSLICE = DV / DVS;
+
+static_assert(sizeof(ChunkRecord) == kChunkRecordBytes, "ChunkRecord layout");
+
+// ---------------------------------------------------------------------------
+// Pass 1: chunk-local operands
+// ---------------------------------------------------------------------------
+
+struct alignas(16) PrepSmem {
+    union {
+        bf16x8 kf[2][4][4][64];      // K^ e^(ref_{j+1}-b) B-frags [hi/lo][token tile j][chan kb][lane]
+        f16x8 kp[8][2][64];          // (K^ gamma/Gamma)^T A-frags, built once kf is dead
+    } u;
+    float akk[C][C + 4];             // A_kk (fp32), then T = (I + A_kk)^-1 in place
+    f16x8 aqk[2][6][64];             // A_qk [hi/lo][tri block][lane]
+    float tot[4][DK];                // sum of g over each sub-tile
+    float fac[4][4][DK];             // per sub-tile w and channel: tot_w, exp(tot_w),
+                                     //   exp(ref_w), exp(ref_4 - ref_{w+1})
+    float dl12[2][DK];               // exp(tot_1), exp(tot_2)
+    float beta[C];
+};
+
+// Packed sequences: slot -> sequence (or -1 for a slot no sequence uses).
+__global__ void slot_map_kernel(const int32_t* __restrict__ cu, int num_seqs, int T, int nslots, int* __restrict__ map)
+{
+    const int slot = blockIdx.x * blockDim.x + threadIdx.x;
+    if (slot >= nslots) return;
+    auto start = [&](int i) { return min(max(cu[i], 0), T); };
+    // largest i with first slot i + start_i / C <= slot
+    int lo = 0, hi = num_seqs - 1, found = -1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        if (mid + start(mid) / C <= slot) {
+            found = mid;
+            lo = mid + 1;
+        } else {
+            hi = mid - 1;
+        }
+    }
+    int seq = -1;
+    if (found >= 0) {
+        const int b0 = start(found), b1 = min(max(cu[found + 1], b0), T);
+        if (slot - (found + b0 / C) < (b1 - b0 + C - 1) / C) seq = found;
+    }
+    map[slot] = seq;
+}
+
+__global__ void __launch_bounds__(NT, 2)
+chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __restrict__ slot_seq, int nslots)
+{
+    __shared__ PrepSmem s;
+
+    const int t = threadIdx.x;
+    // the wave index is uniform across the wave: keep it in a scalar register
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l = t & 63, g = l >> 4, n = l & 15;
+    const int H = a.H;
+    // consecutive workgroups take consecutive heads of one chunk: their
+    // q/k/g rows are adjacent in memory
+    const int h = blockIdx.x % H, slot = blockIdx.x / H;
+
+    long c0, tok1;
+    if (a.cu_seqlens) {
+        const int seq = slot_seq[slot];
+        if (seq < 0) return;
+        int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
+        b0 = min(max(b0, 0), a.T);
+        b1 = min(max(b1, b0), a.T);
+        c0 = b0 + static_cast<long>(slot - (seq + b0 / C)) * C;
+        tok1 = b1;
+    } else {
+        const int nck = (a.T + C - 1) / C;
+        const int seq = slot / nck;
+        c0 = static_cast<long>(seq) * a.T + static_cast<long>(slot - seq * nck) * C;
+        tok1 = static_cast<long>(seq) * a.T + a.T;
+    }
+    if (c0 >= tok1) return;
+    const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
+    ChunkRecord* __restrict__ rg = recs + static_cast<size_t>(h) * nslots + slot;
+
+    // ---- raw inputs of this lane's token row r = 16w + n: channels
+    // 32kb + 8g + 0..7.  Rows past the end of the sequence read the last valid
+    // token and are masked to the identity of the recurrence (k = g = beta = 0).
+    const int row = 16 * w + n;
+    float qv[32], kv[32], bv[32];
+    float beta_r;
+    {
+        const long tk = min(c0 + row, tok1 - 1);
+        const size_t base = static_cast<size_t>(tk) * H + h;
+        const uint16_t* qr = static_cast<const uint16_t*>(a.q) + base * DK + 8 * g;
+        const uint16_t* kr = static_cast<const uint16_t*>(a.k) + base * DK + 8 * g;
+        const float* gr = a.g + base * DK + 8 * g;
+        uint4 rq[4], rk[4];
+        float4 rgv[8];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            rq[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
+            rk[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+            rgv[2 * kb] = *reinterpret_cast<const float4*>(gr + 32 * kb);
+            rgv[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
+        }
+        const float braw = a.beta[base];
+        const float live = (row < L) ? 1.f : 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const uint32_t qw[4] = {rq[kb].x, rq[kb].y, rq[kb].z, rq[kb].w};
+            const uint32_t kw[4] = {rk[kb].x, rk[kb].y, rk[kb].z, rk[kb].w};
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                qv[8 * kb + 2 * e2] = bf_lo(qw[e2]);
+                qv[8 * kb + 2 * e2 + 1] = bf_hi(qw[e2]);
+                kv[8 * kb + 2 * e2] = bf_lo(kw[e2]) * live;
+                kv[8 * kb + 2 * e2 + 1] = bf_hi(kw[e2]) * live;
+            }
+            bv[8 * kb + 0] = rgv[2 * kb].x * live;
+            bv[8 * kb + 1] = rgv[2 * kb].y * live;
+            bv[8 * kb + 2] = rgv[2 * kb].z * live;
+            bv[8 * kb + 3] = rgv[2 * kb].w * live;
+            bv[8 * kb + 4] = rgv[2 * kb + 1].x * live;
+            bv[8 * kb + 5] = rgv[2 * kb + 1].y * live;
+            bv[8 * kb + 6] = rgv[2 * kb + 1].z * live;
+            bv[8 * kb + 7] = rgv[2 * kb + 1].w * live;
+        }
+        beta_r = braw * live;
+    }
+
+    // L2 norm of q and k over d_k (the row is spread over the 4 lane groups)
+    {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            sq += qv[e] * qv[e];
+            sk += kv[e] * kv[e];
+        }
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        sk += __shfl_xor(sk, 16, 64);
+        sk += __shfl_xor(sk, 32, 64);
+        const float rq = a.normalize ? rsqrtf(sq + kNormEps) : 1.f;
+        const float rk = a.normalize ? rsqrtf(sk + kNormEps) : 1.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            qv[e] *= rq;
+            kv[e] *= rk;
+        }
+    }
+    // running decay inside the 16-token sub-tile
+#pragma unroll
+    for (int e = 0; e < 32; ++e) bv[e] = row_scan16(bv[e]);
+    if (n == 15) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s.tot[w][32 * kb + 8 * g + e] = bv[8 * kb + e];
+    }
+    if (g == 0) s.beta[row] = beta_r;
+    __syncthreads();
+
+    // per-channel decay factors for every sub-tile; each factor is an exp of
+    // a non-positive sum, so none overflows
+    {
+        const int c = t & (DK - 1);
+        const float t0 = s.tot[0][c], t1 = s.tot[1][c], t2 = s.tot[2][c], t3 = s.tot[3][c];
+        const float r1 = t0, r2 = t0 + t1, r3 = r2 + t2, r4 = r3 + t3;
+        if (t < DK) {
+            s.fac[0][0][c] = t0;
+            s.fac[0][1][c] = __expf(t0);
+            s.fac[0][2][c] = 1.f;
+            s.fac[0][3][c] = __expf(r4 - r1);
+            s.fac[1][0][c] = t1;
+            s.fac[1][1][c] = __expf(t1);
+            s.fac[1][2][c] = __expf(r1);
+            s.fac[1][3][c] = __expf(r4 - r2);
+            s.dl12[0][c] = __expf(t1);
+            s.dl12[1][c] = __expf(t2);
+        } else {
+            s.fac[2][0][c] = t2;
+            s.fac[2][1][c] = __expf(t2);
+            s.fac[2][2][c] = __expf(r2);
+            s.fac[2][3][c] = __expf(r4 - r3);
+            s.fac[3][0][c] = t3;
+            s.fac[3][1][c] = __expf(t3);
+            s.fac[3][2][c] = __expf(r3);
+            s.fac[3][3][c] = 1.f;
+            rg->gam[c] = __expf(r4);
+        }
+    }
+    __syncthreads();
+
+    // Per element: d = exp(b - ref_{w+1}) in [1, e^80], f = 1/d,
+    // E = exp(b - ref_w) <= 1, Gamma = exp(b).  The diagonal tile (w, w) is
+    // computed right here: both of its operands are in this lane.  The
+    // off-diagonal tiles share one A-operand, X^ E.
+    bf16x8 kao[4], qoh[4], qol[4];
+    f16x8 kq16[4];   // K^ gamma/Gamma of this row, channels 32kb + 8g + e
+    f32x4 akd = {0.f, 0.f, 0.f, 0.f}, aqd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int cb = 32 * kb + 8 * g;
+        float tw[8], dw[8], er[8], el[8];
+        lds8(&s.fac[w][0][cb], tw);
+        lds8(&s.fac[w][1][cb], dw);
+        lds8(&s.fac[w][2][cb], er);
+        lds8(&s.fac[w][3][cb], el);
+        bf16x8 kfh, kfl, kad, qdh, qdl;
+        float qgv[8], kgv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float bl = bv[8 * kb + e];         // running sum inside sub-tile w
+            const float d = __expf(bl - tw[e]);      // b - ref_{w+1}
+            const float f = __builtin_amdgcn_rcpf(d);  // exp(ref_{w+1} - b)
+            const float E = d * dw[e];               // exp(b - ref_w)
+            const float gm = E * er[e];              // exp(b)
+            const float kx = kv[8 * kb + e], qx = qv[8 * kb + e];
+            __bf16 hi, lo;
+            split(kx * f, hi, lo);
+            kfh[e] = hi;
+            kfl[e] = lo;
+            qgv[e] = qx * gm;
+            kgv[e] = -kx * gm;
+            kad[e] = static_cast<__bf16>(kx * d);
+            split(qx * d, hi, lo);
+            qdh[e] = hi;
+            qdl[e] = lo;
+            kao[kb][e] = static_cast<__bf16>(kx * E);
+            split(qx * E, hi, lo);
+            qoh[kb][e] = hi;
+            qol[kb][e] = lo;
+            kq16[kb][e] = static_cast<_Float16>(kx * f * el[e]);
+        }
+        akd = mma(kad, kfh, akd);
+        aqd = mma3(qdh, qdl, kfh, kfl, aqd);
+        s.u.kf[0][w][kb][l] = kfh;
+        s.u.kf[1][w][kb][l] = kfl;
+        // Q^ Gamma and -K^ Gamma, in the state's channel order, straight to
+        // the record: channel 32kb + 8g + e goes to lane (2(g&1) + e/4)*16 + n,
+        // element 4(g>>1) + e%4
+        {
+            const int eo = 4 * (g >> 1);
+            const int l0 = (2 * (g & 1)) * 16 + n, l1 = l0 + 16;
+            f16x4 q0, q1, k0, k1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                q0[e] = static_cast<_Float16>(qgv[e]);
+                q1[e] = static_cast<_Float16>(qgv[4 + e]);
+                k0[e] = static_cast<_Float16>(kgv[e]);
+                k1[e] = static_cast<_Float16>(kgv[4 + e]);
+            }
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->qg[w][kb][l0]) + eo) = q0;
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->qg[w][kb][l1]) + eo) = q1;
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->kgn[w][kb][l0]) + eo) = k0;
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->kgn[w][kb][l1]) + eo) = k1;
+        }
+    }
+    // diagonal tile (w, w): lane holds rows 16w + 4g + i, column 16w + n.
+    // A_qk goes to the A-fragment of U~'s token order: column token
+    // 16j + n of tile (w, j) is element (n&3) + 4(j&1) of lane (n/4)*16 + row%16
+    // in block (w, j/2).
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * g + i, sc = 16 * w + n;
+        if (sc < r) s.akk[r][sc] = s.beta[r] * akd[i];
+        _Float16 hi, lo;
+        splith((sc <= r) ? aqd[i] : 0.f, hi, lo);
+        const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (w & 1);
+        const int p = tri_block(w, w >> 1);
+        reinterpret_cast<_Float16*>(&s.aqk[0][p][lt])[e] = hi;
+        reinterpret_cast<_Float16*>(&s.aqk[1][p][lt])[e] = lo;
+        if ((w & 1) == 0) {   // tile (w, w+1) shares this token block: zero it
+            reinterpret_cast<_Float16*>(&s.aqk[0][p][lt])[e + 4] = static_cast<_Float16>(0.f);
+            reinterpret_cast<_Float16*>(&s.aqk[1][p][lt])[e + 4] = static_cast<_Float16>(0.f);
+        }
+    }
+    __syncthreads();
+
+    // ---- off-diagonal tiles (w, j < w).  The B-operand of sub-tile j is
+    // referenced to ref_{j+1}; tiles two or three sub-tiles apart rescale it
+    // to ref_w by exp(tot_{j+1} + ... + tot_{w-1}) <= 1.
+    for (int j = 0; j < w; ++j) {
+        f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 bh[4], bl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bh[kb] = s.u.kf[0][j][kb][l];
+            bl[kb] = s.u.kf[1][j][kb][l];
+        }
+        if (j + 2 <= w) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                float x1[8], x2[8];
+                lds8(&s.dl12[0][32 * kb + 8 * g], x1);
+                lds8(&s.dl12[1][32 * kb + 8 * g], x2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // (w, j) = (2,0): exp(tot_1); (3,0): exp(tot_1 + tot_2); (3,1): exp(tot_2)
+                    const float sc = (w == 2) ? x1[e] : ((j == 0) ? x1[e] * x2[e] : x2[e]);
+                    const float kf = (static_cast<float>(bh[kb][e]) + static_cast<float>(bl[kb][e])) * sc;
+                    __bf16 hi, lo;
+                    split(kf, hi, lo);
+                    bh[kb][e] = hi;
+                    bl[kb][e] = lo;
+                }
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            akk = mma(kao[kb], bh[kb], akk);
+            aqk = mma3(qoh[kb], qol[kb], bh[kb], bl[kb], aqk);
+        }
+        // lane holds rows r = 16w + 4g + i, column s = 16j + n (all s < r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * g + i, sc = 16 * j + n;
+            s.akk[r][sc] = s.beta[r] * akk[i];
+            _Float16 hi, lo;
+            splith(aqk[i], hi, lo);
+            const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (j & 1);
+            const int p = tri_block(w, j >> 1);
+            reinterpret_cast<_Float16*>(&s.aqk[0][p][lt])[e] = hi;
+            reinterpret_cast<_Float16*>(&s.aqk[1][p][lt])[e] = lo;
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + A_kk)^-1, blocked, in place.  Diagonal 16x16 blocks by
+    // forward substitution: lane owns column l/4 of block w and the rows
+    // l%4 + 4m of it; the four partial sums of a column sit in one lane quad
+    // and are reduced with DPP.
+    {
+        const int col = l >> 2, pr = l & 3;
+        float tv[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) tv[m] = (pr + 4 * m == col) ? 1.f : 0.f;
+        const int b0 = 16 * w;
+        float av[16][4];   // the block's strictly-lower entries this lane needs
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) av[rr][m] = s.akk[b0 + rr][b0 + pr + 4 * m];
+#pragma unroll
+        for (int rr = 1; rr < 16; ++rr) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if (pr + 4 * m < rr) acc += av[rr][m] * tv[m];
+            acc += quad_swap1(acc);
+            acc += quad_swap2(acc);
+            const float tval = (rr > col) ? -acc : ((rr == col) ? 1.f : 0.f);
+            if ((rr & 3) == pr) tv[rr >> 2] = tval;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s.akk[b0 + pr + 4 * m][b0 + col] = tv[m];
+    }
+    __syncthreads();
+
+    // (all waves) (K^ gamma/Gamma)^T A-frags, token order matching U~:
+    // channel c -> frag [c/16][w/2], lane (n/4)*16 + c%16, element n%4 + 4(w%2)
+    {
+        const int e = (n & 3) + 4 * (w & 1);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int mt = 2 * kb + (g >> 1);
+            const int lb = (n >> 2) * 16 + 8 * (g & 1);
+            _Float16* dst = reinterpret_cast<_Float16*>(&s.u.kp[mt][w >> 1][0]);
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) dst[(lb + ee) * 8 + e] = kq16[kb][ee];
+        }
+    }
+    // level 1: T_{w,w-1} = -T_ww A_{w,w-1} T_{w-1,w-1} for w = 1, 3 (fp32 MFMA)
+    if (w & 1) {
+        const int hi = 16 * w, lo = 16 * (w - 1);
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            p = mma32(s.akk[hi + n][lo + 4 * kk + g], s.akk[lo + 4 * kk + g][lo + n], p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.akk[hi + 4 * g + i][lo + n] = p[i];
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's P is in LDS
+        __builtin_amdgcn_wave_barrier();
+        f32x4 q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            q = mma32(s.akk[hi + n][hi + 4 * kk + g], s.akk[hi + 4 * kk + g][lo + n], q);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.akk[hi + 4 * g + i][lo + n] = -q[i];
+    }
+    __syncthreads();
+    // level 2: T_BA = -T_BB (A_BA T_AA) on 32x32 blocks; wave -> tile (2 + w/2, w%2)
+    {
+        const int ti = 2 + (w >> 1), tj = w & 1;
+        f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            if (kt < tj) continue;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                p = mma32(s.akk[16 * ti + n][16 * kt + 4 * kk + g], s.akk[16 * kt + 4 * kk + g][16 * tj + n], p);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.akk[16 * ti + 4 * g + i][16 * tj + n] = p[i];
+        __syncthreads();
+        f32x4 q = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 2; kt < 4; ++kt) {
+            if (kt > ti) continue;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                q = mma32(s.akk[16 * ti + n][16 * kt + 4 * kk + g], s.akk[16 * kt + 4 * kk + g][16 * tj + n], q);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.akk[16 * ti + 4 * g + i][16 * tj + n] = -q[i];
+    }
+    __syncthreads();
+
+    // T' = T Diag(beta) as A-frags whose token (k) order matches the
+    // accumulator layout of V - K Gamma S: element e of lane group g holds
+    // token 32kb + 16(e/4) + 4g + e%4.  Blocks above the diagonal are zero
+    // and not stored.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        if (kb > (w >> 1)) continue;
+        const float4 t0 = *reinterpret_cast<const float4*>(&s.akk[row][32 * kb + 4 * g]);
+        const float4 t1 = *reinterpret_cast<const float4*>(&s.akk[row][32 * kb + 16 + 4 * g]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&s.beta[32 * kb + 4 * g]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&s.beta[32 * kb + 16 + 4 * g]);
+        const float tv8[8] = {t0.x * b0.x, t0.y * b0.y, t0.z * b0.z, t0.w * b0.w,
+                              t1.x * b1.x, t1.y * b1.y, t1.z * b1.z, t1.w * b1.w};
+        bf16x8 th, tl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sc = 32 * kb + 16 * (e >> 2) + 4 * g + (e & 3);
+            const float x = (sc <= row) ? tv8[e] : 0.f;
+            __bf16 hi, lo;
+            split(x, hi, lo);
+            th[e] = hi;
+            tl[e] = lo;
+        }
+        const int p = tri_block(w, kb);
+        rg->tp[0][p][l] = th;
+        rg->tp[1][p][l] = tl;
+    }
+
+    // A_qk and K'^T fragments: LDS -> record, whole 16-byte pieces
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(&s.aqk[0][0][0]);
+        uint4* dst = reinterpret_cast<uint4*>(&rg->aqk[0][0][0]);
+        constexpr int NA = static_cast<int>(sizeof(s.aqk) / 16);
+#pragma unroll
+        for (int i = t; i < NA; i += NT) dst[i] = src[i];
+        const uint4* src2 = reinterpret_cast<const uint4*>(&s.u.kp[0][0][0]);
+        uint4* dst2 = reinterpret_cast<uint4*>(&rg->kp[0][0][0]);
+        constexpr int NK = static_cast<int>(sizeof(s.u.kp) / 16);
+#pragma unroll
+        for (int i = t; i < NK; i += NT) dst2[i] = src2[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: the state recurrence over the records
+// ---------------------------------------------------------------------------
+
+struct alignas(16) ScanSmem {
+    ChunkRecord r;                   // this chunk's operands
+    __bf16 vs[C][DVS];               // V slice, plain [token][column]
+    float obuf[C * DVS];             // output tile staging ([token][column], bf16 or fp32)
+};
+static_assert(sizeof(ScanSmem) == 98816, "scan LDS");
+
+// output tile staging; bf16 is rounded to nearest even by the hardware conversion
+__device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const float*)
+{
+    base[r * DVS + c] = x;
+}
+__device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const uint16_t*)
+{
+    reinterpret_cast<uint16_t*>(base)[r * DVS + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+template <typename Tout>
+__global__ void __launch_bounds__(NT, 1)
+chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
+{
+    __shared__ ScanSmem s;
+
+    const int t = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l = t & 63, g = l >> 4, n = l & 15;
+    const int H = a.H;
+    // Workgroup -> (chain, slice).  Both slices of a chain get ids that are
+    // equal mod 8, so they are dispatched to the same XCD and the second read
+    // of each record hits that XCD's L2.
+    const int bid = blockIdx.x;
+    const int slice = (bid >> 3) & (NSLICE - 1);
+    const int chain = ((bid >> 4) << 3) | (bid & 7);
+    const int nchains = (a.cu_seqlens ? a.num_seqs : a.B) * H;
+    if (chain >= nchains) return;
+    const int j0 = slice * DVS;
+    const int seq = chain / H, h = chain % H;
+
+    long tok0, tok1;
+    int slot0;
+    if (a.cu_seqlens) {
+        int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
+        b0 = min(max(b0, 0), a.T);
+        b1 = min(max(b1, b0), a.T);
+        tok0 = b0;
+        tok1 = b1;
+        slot0 = seq + b0 / C;
+    } else {
+        tok0 = static_cast<long>(seq) * a.T;
+        tok1 = tok0 + a.T;
+        slot0 = seq * ((a.T + C - 1) / C);
+    }
+    const int nch = static_cast<int>((tok1 - tok0 + C - 1) / C);
+    const ChunkRecord* __restrict__ rc = recs + static_cast<size_t>(h) * nslots + slot0;
+    const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
+    Tout* __restrict__ op = static_cast<Tout*>(a.o);
+
+    // ---- state strip: channels 16*mt + 4*g + i, column j0 + 16*w + n
+    f32x4 sacc[8];
+    {
+        const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sacc[mt][i] = a.init_state ? a.init_state[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] : 0.f;
+    }
+
+    // The next chunk's record and V slice travel in registers while the
+    // current chunk is computed, then go to LDS between two barriers.
+    constexpr int RV = static_cast<int>(sizeof(ChunkRecord) / 16);
+    constexpr int RFULL = RV / NT;
+    constexpr int RTAIL = RV - RFULL * NT;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 P[RFULL + 1], PV[2];
+    auto fetch = [&](int j) __attribute__((always_inline)) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(rc + j);
+#pragma unroll
+        for (int i = 0; i < RFULL; ++i) P[i] = src[t + NT * i];
+        if (t < RTAIL) P[RFULL] = src[t + NT * RFULL];
+        const long cb = tok0 + static_cast<long>(j) * C;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = t + NT * u, r = idx >> 3, part = idx & 7;
+            // rows past the end read the last valid token: T' has zero
+            // columns for them, so only finiteness matters
+            const long tk = min(cb + r, tok1 - 1);
+            PV[u] = *reinterpret_cast<const u32x4*>(vp + (static_cast<size_t>(tk) * H + h) * DV + j0 + 8 * part);
+        }
+    };
+    auto commit = [&]() __attribute__((always_inline)) {
+        u32x4* dst = reinterpret_cast<u32x4*>(&s.r);
+#pragma unroll
+        for (int i = 0; i < RFULL; ++i) dst[t + NT * i] = P[i];
+        if (t < RTAIL) dst[t + NT * RFULL] = P[RFULL];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int idx = t + NT * u, r = idx >> 3, part = idx & 7;
+            *reinterpret_cast<u32x4*>(&s.vs[r][8 * part]) = PV[u];
+        }
+    };
+
+    if (nch > 0) {
+        fetch(0);
+        commit();
+        if (nch > 1) fetch(1);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < nch; ++j) {
+        const long c0 = tok0 + static_cast<long>(j) * C;
+        const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
+
+        // state as fp16 hi/lo B-frags (channel order of the accumulators)
+        f16x8 sh[4], sl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                _Float16 hi, lo;
+                splith(sacc[2 * kb][i], hi, lo);
+                sh[kb][i] = hi;
+                sl[kb][i] = lo;
+                splith(sacc[2 * kb + 1][i], hi, lo);
+                sh[kb][4 + i] = hi;
+                sl[kb][4 + i] = lo;
+            }
+        }
+        // R = V - (K^ Gamma) S  (rows = tokens 16mt + 4g + i, column n of the strip).
+        // Operand fragments of each step are read from LDS in one batch ahead
+        // of its MFMAs (one wave per SIMD: nothing else hides LDS latency).
+        f32x4 ut[4];
+        {
+            f16x8 fa[4][4];
+            float vv[4][4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) fa[mt][kb] = s.r.kgn[mt][kb][l];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vv[mt][i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc = {vv[mt][0], vv[mt][1], vv[mt][2], vv[mt][3]};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    acc = mmh(fa[mt][kb], sh[kb], acc);
+                    acc = mmh(fa[mt][kb], sl[kb], acc);
+                }
+                ut[mt] = acc;
+            }
+        }
+        bf16x8 rbh[2], rbl[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __bf16 hi, lo;
+                split(ut[2 * kb][i], hi, lo);
+                rbh[kb][i] = hi;
+                rbl[kb][i] = lo;
+                split(ut[2 * kb + 1][i], hi, lo);
+                rbh[kb][4 + i] = hi;
+                rbl[kb][4 + i] = lo;
+            }
+        }
+        // U~ = T' R
+        {
+            bf16x8 th[6], tl[6];
+#pragma unroll
+            for (int p = 0; p < 6; ++p) {
+                th[p] = s.r.tp[0][p][l];
+                tl[p] = s.r.tp[1][p][l];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb <= (mt >> 1); ++kb) {
+                    const int p = tri_block(mt, kb);
+                    acc = mma3(th[p], tl[p], rbh[kb], rbl[kb], acc);
+                }
+                ut[mt] = acc;
+            }
+        }
+        f16x8 ub[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ub[kb][i] = static_cast<_Float16>(ut[2 * kb][i]);
+                ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
+            }
+        }
+        // O = (Q^ Gamma) S + A_qk U~, two token tiles per batch
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            f16x8 qa[2][4], ah[2][2], al[2][2];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mt = 2 * half + m2;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[mt][kb][l];
+#pragma unroll
+                for (int kb = 0; kb <= half; ++kb) {
+                    ah[m2][kb] = s.r.aqk[0][tri_block(mt, kb)][l];
+                    al[m2][kb] = s.r.aqk[1][tri_block(mt, kb)][l];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mt = 2 * half + m2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    acc = mmh(qa[m2][kb], sh[kb], acc);
+                    acc = mmh(qa[m2][kb], sl[kb], acc);
+                }
+#pragma unroll
+                for (int kb = 0; kb <= half; ++kb) {
+                    acc = mmh(ah[m2][kb], ub[kb], acc);
+                    acc = mmh(al[m2][kb], ub[kb], acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    stage_out(s.obuf, 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
+                              static_cast<const Tout*>(nullptr));
+            }
+        }
+        // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~, four channel tiles per batch
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            f16x8 ka[4][2];
+            float4 gm4[4];
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const int mt = 4 * half + m4;
+                ka[m4][0] = s.r.kp[mt][0][l];
+                ka[m4][1] = s.r.kp[mt][1][l];
+                gm4[m4] = *reinterpret_cast<const float4*>(&s.r.gam[16 * mt + 4 * g]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const int mt = 4 * half + m4;
+                sacc[mt][0] *= gm4[m4].x;
+                sacc[mt][1] *= gm4[m4].y;
+                sacc[mt][2] *= gm4[m4].z;
+                sacc[mt][3] *= gm4[m4].w;
+                sacc[mt] = mmh(ka[m4][0], ub[0], sacc[mt]);
+                sacc[mt] = mmh(ka[m4][1], ub[1], sacc[mt]);
+            }
+        }
+        __syncthreads();
+        // every read of this chunk's record is done: the next one moves in
+        if (j + 1 < nch) commit();
+        // coalesced output rows: 64 tokens x 64 columns of this slice
+        {
+            constexpr int CH = 16 / sizeof(Tout);            // elements per 16-byte piece
+            constexpr int PER_ROW = DVS / CH;
+#pragma unroll
+            for (int pc = t; pc < C * PER_ROW; pc += NT) {
+                const int r = pc / PER_ROW, part = pc % PER_ROW;
+                if (r < L) {
+                    const uint4 val = *reinterpret_cast<const uint4*>(
+                        reinterpret_cast<const char*>(s.obuf) + (r * DVS + part * CH) * sizeof(Tout));
+                    *reinterpret_cast<uint4*>(op + (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + part * CH) = val;
+                }
+            }
+        }
+        if (j + 2 < nch) fetch(j + 2);
+        __syncthreads();
+    }
+
+    if (a.final_state) {
+        const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a.final_state[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] = sacc[mt][i];
+    }
+}
+
+}  // namespace
+
+long long chunk_record_slots(int B, int T, int num_seqs, bool packed)
+{
+    if (packed) return static_cast<long long>(num_seqs) + T / C;
+    return static_cast<long long>(B) * ((T + C - 1) / C);
+}
+
+size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed)
+{
+    const long long slots = chunk_record_slots(B, T, num_seqs, packed);
+    size_t bytes = static_cast<size_t>(slots) * H * kChunkRecordBytes;
+    if (packed) bytes += (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256;
+    return bytes;
+}
+
+hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream)
+{
+    const int chains = (a.cu_seqlens ? a.num_seqs : a.B) * a.H;
+    if (chains == 0) return hipSuccess;
+    const long long slots = chunk_record_slots(a.B, a.T, a.num_seqs, a.cu_seqlens != nullptr);
+    ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
+    if (slots > 0) {
+        int* map = nullptr;
+        if (a.cu_seqlens) {
+            map = reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                         static_cast<size_t>(slots) * a.H * kChunkRecordBytes);
+            slot_map_kernel<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(
+                a.cu_seqlens, a.num_seqs, a.T, static_cast<int>(slots), map);
+        }
+        chunk_prep_kernel<<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
+    }
+    // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
+    const int groups = (chains + 7) / 8;
+    const dim3 grid(groups * 8 * NSLICE), block(NT);
+    if (a.out_bf16)
+        chunk_scan_kernel<uint16_t><<<grid, block, 0, stream>>>(a, recs, static_cast<int>(slots));
+    else
+        chunk_scan_kernel<float><<<grid, block, 0, stream>>>(a, recs, static_cast<int>(slots));
+    return hipGetLastError();
+}
+
+}  // namespace kda

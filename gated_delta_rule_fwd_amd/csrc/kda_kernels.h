@@ -30,9 +30,20 @@ hipError_t launch_decode(int dk, int dv, bool in_bf16, bool out_bf16, int chains
 // fp32 per-position-pair path: any supported head dims and dtypes.
 hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t stream);
 
-// Matrix-core path: bf16 inputs, d_k = d_v = 128, g >= -5.
-bool chunk_mfma_supported(const ChunkArgs& a);
-hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t stream);
+// Matrix-core path: bf16 inputs, d_k = d_v = 128, g >= -5, in two passes.
+//   pass 1 (chunk-parallel): every (chunk, head) writes one ChunkRecord of
+//          chunk-local operands to the workspace;
+//   pass 2 (sequential over chunks): carries the state through the records.
+// Record slots: a dense batch uses B * ceil(T/64) slots per head (sequence b,
+// chunk j -> slot b * ceil(T/64) + j); packed sequences use num_seqs + T/64
+// slots, sequence n starting at slot n + cu_seqlens[n]/64 (a chunk count of
+// ceil(len/64) never reaches the next sequence's first slot).
+constexpr size_t kChunkRecordBytes = 74240;
+long long chunk_record_slots(int B, int T, int num_seqs, bool packed);
+// workspace: records (h * slots + slot), then (packed sequences only) one
+// int32 per slot naming its sequence or -1.
+size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed);
+hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream);
 
 // Device-side range checks for KDA_FLAG_VALIDATE; counts violations into
 // counters[0..2] (g, beta, cu_seqlens); the launcher zeroes them first with

@@ -90,8 +90,31 @@ def test_chunk_fwd_rejects_bad_arguments(lib):
     assert need > 0
     assert _call(lib, d, ws=FAKE, ws_bytes=need - 1) == 3      # workspace too small
     assert _call(lib, d, ws=None, ws_bytes=need) == 3
-    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc())) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(None) == ctypes.c_size_t(-1).value
+    assert _call(lib, _desc()) == 3                            # matrix-core path needs its record workspace
+
+
+RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
+
+
+def test_workspace_sizes(lib):
+    size = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(**kw)))
+    # fp32 arithmetic paths need nothing
+    assert size(in_dtype=0) == 0
+    assert size(d_k=64, d_v=64) == 0
+    assert size(flags=kda.FLAG_QK_L2NORM | kda.FLAG_FP32_PATH) == 0
+    # dense batch: B * ceil(T / 64) chunk records per head
+    assert size(B=3, T=130, H=5) == 3 * 3 * 5 * RECORD
+    # packed sequences: num_seqs + T // 64 slots per head plus one int32 per slot (256-byte rounded);
+    # the descriptor does not say which layout is coming, so the larger need is reported
+    slots = 7 + 1000 // 64
+    assert size(B=1, T=1000, H=4, num_seqs=7) == max(slots * 4 * RECORD + 256, 16 * 4 * RECORD)
+    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 50 * 2 * RECORD + 256 + 3 * 2 * RECORD
+    # validation counters come first
+    assert size(B=2, T=64, H=1, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * RECORD
+    # a misaligned workspace is refused before anything runs
+    d = _desc(B=1, T=64, H=1)
+    assert _call(lib, d, ws=FAKE + 8, ws_bytes=RECORD) == 1
 
 
 def test_chunk_fwd_empty_batch_is_a_no_op(lib):
