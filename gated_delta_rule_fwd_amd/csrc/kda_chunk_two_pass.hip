@@ -520,9 +520,8 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 struct alignas(16) ScanSmem {
     ChunkRecord r;                   // this chunk's operands
     __bf16 vs[C][DVS];               // V slice, plain [token][column]
-    float obuf[C * DVS];             // output tile staging ([token][column], bf16 or fp32)
+    float obuf[2][C * DVS];          // output tile staging ([token][column], bf16 or fp32), two chunks
 };
-static_assert(sizeof(ScanSmem) == 98816, "scan LDS");
 
 // output tile staging; bf16 is rounded to nearest even by the hardware conversion
 __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const float*)
@@ -586,17 +585,25 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     }
 
     // The next chunk's record and V slice travel in registers while the
-    // current chunk is computed, then go to LDS between two barriers.
+    // current chunk is computed (issued in pieces between the compute steps
+    // so the loads overlap them), then go to LDS between two barriers.
     constexpr int RV = static_cast<int>(sizeof(ChunkRecord) / 16);
     constexpr int RFULL = RV / NT;
     constexpr int RTAIL = RV - RFULL * NT;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 P[RFULL + 1], PV[2];
-    auto fetch = [&](int j) __attribute__((always_inline)) {
+    // record pieces i in [i0, i1) of chunk j; piece RFULL is the partial one
+    auto fetch = [&](int j, int i0, int i1) __attribute__((always_inline)) {
         const u32x4* src = reinterpret_cast<const u32x4*>(rc + j);
 #pragma unroll
-        for (int i = 0; i < RFULL; ++i) P[i] = src[t + NT * i];
-        if (t < RTAIL) P[RFULL] = src[t + NT * RFULL];
+        for (int i = i0; i < i1; ++i) {
+            if (i < RFULL)
+                P[i] = src[t + NT * i];
+            else if (t < RTAIL)
+                P[i] = src[t + NT * i];
+        }
+    };
+    auto fetch_v = [&](int j) __attribute__((always_inline)) {
         const long cb = tok0 + static_cast<long>(j) * C;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -620,16 +627,134 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     };
 
     if (nch > 0) {
-        fetch(0);
+        fetch(0, 0, RFULL + 1);
+        fetch_v(0);
         commit();
-        if (nch > 1) fetch(1);
     }
     __syncthreads();
 
+    // Output tiles are staged in LDS (alternating buffers) and written out as
+    // whole rows during the next chunk, or after the loop for the last one.
+    auto store_tile = [&](int buf, long cbase, int rows) __attribute__((always_inline)) {
+        constexpr int CH = 16 / sizeof(Tout);            // elements per 16-byte piece
+        constexpr int PER_ROW = DVS / CH;
+        const char* src = reinterpret_cast<const char*>(s.obuf[buf]);
+#pragma unroll
+        for (int pc = t; pc < C * PER_ROW; pc += NT) {
+            const int r = pc / PER_ROW, part = pc % PER_ROW;
+            if (r < rows) {
+                const uint4 val = *reinterpret_cast<const uint4*>(src + (r * DVS + part * CH) * sizeof(Tout));
+                *reinterpret_cast<uint4*>(op + (static_cast<size_t>(cbase + r) * H + h) * DV + j0 + part * CH) = val;
+            }
+        }
+    };
+    // operand fragments of the R step for token tiles 2mh, 2mh + 1
+    auto load_r = [&](int mh, f16x8 (&fa)[2][4], float (&vv)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int mt = 2 * mh + m2;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) fa[m2][kb] = s.r.kgn[mt][kb][l];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vv[m2][i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
+        }
+    };
+    // R = V - (K^ Gamma) S for token tiles 2mh, 2mh + 1 (rows 16mt + 4g + i, column n of the strip)
+    auto step_r = [&](int mh, const f16x8 (&fa)[2][4], const float (&vv)[2][4], const f16x8 (&sh)[4],
+                      const f16x8 (&sl)[4], f32x4 (&ut)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            f32x4 acc = {vv[m2][0], vv[m2][1], vv[m2][2], vv[m2][3]};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                acc = mmh(fa[m2][kb], sh[kb], acc);
+                acc = mmh(fa[m2][kb], sl[kb], acc);
+            }
+            ut[2 * mh + m2] = acc;
+        }
+    };
+    // operand fragments of the O step for token tiles 2half, 2half + 1
+    auto load_o = [&](int half, f16x8 (&qa)[2][4], f16x8 (&ah)[2][2], f16x8 (&al)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int mt = 2 * half + m2;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[mt][kb][l];
+#pragma unroll
+            for (int kb = 0; kb <= half; ++kb) {
+                ah[m2][kb] = s.r.aqk[0][tri_block(mt, kb)][l];
+                al[m2][kb] = s.r.aqk[1][tri_block(mt, kb)][l];
+            }
+        }
+    };
+    // O = (Q^ Gamma) S + A_qk U~ for token tiles 2half, 2half + 1, staged in LDS
+    auto step_o = [&](int half, int buf, const f16x8 (&qa)[2][4], const f16x8 (&ah)[2][2], const f16x8 (&al)[2][2],
+                      const f16x8 (&sh)[4], const f16x8 (&sl)[4], const f16x8 (&ub)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            const int mt = 2 * half + m2;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                acc = mmh(qa[m2][kb], sh[kb], acc);
+                acc = mmh(qa[m2][kb], sl[kb], acc);
+            }
+#pragma unroll
+            for (int kb = 0; kb <= half; ++kb) {
+                acc = mmh(ah[m2][kb], ub[kb], acc);
+                acc = mmh(al[m2][kb], ub[kb], acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                stage_out(s.obuf[buf], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
+                          static_cast<const Tout*>(nullptr));
+        }
+    };
+    // operand fragments of the state update for channel tiles 4half .. 4half + 3
+    auto load_k = [&](int half, f16x8 (&ka)[4][2], float4 (&gm4)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const int mt = 4 * half + m4;
+            ka[m4][0] = s.r.kp[mt][0][l];
+            ka[m4][1] = s.r.kp[mt][1][l];
+            gm4[m4] = *reinterpret_cast<const float4*>(&s.r.gam[16 * mt + 4 * g]);
+        }
+    };
+    // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~ for channel tiles 4half .. 4half + 3
+    auto step_k = [&](int half, const f16x8 (&ka)[4][2], const float4 (&gm4)[4], const f16x8 (&ub)[2])
+        __attribute__((always_inline)) {
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const int mt = 4 * half + m4;
+            sacc[mt][0] *= gm4[m4].x;
+            sacc[mt][1] *= gm4[m4].y;
+            sacc[mt][2] *= gm4[m4].z;
+            sacc[mt][3] *= gm4[m4].w;
+            sacc[mt] = mmh(ka[m4][0], ub[0], sacc[mt]);
+            sacc[mt] = mmh(ka[m4][1], ub[1], sacc[mt]);
+        }
+    };
+
+    // Each chunk is software-pipelined inside the wave: the LDS fragments of
+    // the next step are requested before the matrix products of the current
+    // one, so the LDS and the matrix cores work at the same time (one wave
+    // per SIMD: nothing else would hide the LDS latency).
+    long prev_c0 = 0;
+    int prev_L = 0;
     for (int j = 0; j < nch; ++j) {
         const long c0 = tok0 + static_cast<long>(j) * C;
         const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
+        const bool more = j + 1 < nch;
+        const int buf = j & 1;
 
+        f16x8 fa0[2][4], fa1[2][4];
+        float vv0[2][4], vv1[2][4];
+        load_r(0, fa0, vv0);
+        if (more) {
+            fetch_v(j + 1);
+            fetch(j + 1, 0, 5);
+        }
+        if (j > 0) store_tile(buf ^ 1, prev_c0, prev_L);
         // state as fp16 hi/lo B-frags (channel order of the accumulators)
         f16x8 sh[4], sl[4];
 #pragma unroll
@@ -645,32 +770,22 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
                 sl[kb][4 + i] = lo;
             }
         }
-        // R = V - (K^ Gamma) S  (rows = tokens 16mt + 4g + i, column n of the strip).
-        // Operand fragments of each step are read from LDS in one batch ahead
-        // of its MFMAs (one wave per SIMD: nothing else hides LDS latency).
+        __builtin_amdgcn_sched_barrier(0);
+        load_r(1, fa1, vv1);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 ut[4];
-        {
-            f16x8 fa[4][4];
-            float vv[4][4];
+        step_r(0, fa0, vv0, sh, sl, ut);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 th[6], tl[6];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) fa[mt][kb] = s.r.kgn[mt][kb][l];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vv[mt][i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 acc = {vv[mt][0], vv[mt][1], vv[mt][2], vv[mt][3]};
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    acc = mmh(fa[mt][kb], sh[kb], acc);
-                    acc = mmh(fa[mt][kb], sl[kb], acc);
-                }
-                ut[mt] = acc;
-            }
+        for (int p = 0; p < 6; ++p) {
+            th[p] = s.r.tp[0][p][l];
+            tl[p] = s.r.tp[1][p][l];
         }
+        if (more) fetch(j + 1, 5, 10);
+        __builtin_amdgcn_sched_barrier(0);
+        step_r(1, fa1, vv1, sh, sl, ut);
+        // R as bf16 hi/lo B-frags, token order of the accumulators
         bf16x8 rbh[2], rbl[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -685,25 +800,20 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
                 rbl[kb][4 + i] = lo;
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 qa0[2][4], ah0[2][2], al0[2][2];
+        load_o(0, qa0, ah0, al0);
+        __builtin_amdgcn_sched_barrier(0);
         // U~ = T' R
-        {
-            bf16x8 th[6], tl[6];
 #pragma unroll
-            for (int p = 0; p < 6; ++p) {
-                th[p] = s.r.tp[0][p][l];
-                tl[p] = s.r.tp[1][p][l];
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb <= (mt >> 1); ++kb) {
+                const int p = tri_block(mt, kb);
+                acc = mma3(th[p], tl[p], rbh[kb], rbl[kb], acc);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb <= (mt >> 1); ++kb) {
-                    const int p = tri_block(mt, kb);
-                    acc = mma3(th[p], tl[p], rbh[kb], rbl[kb], acc);
-                }
-                ut[mt] = acc;
-            }
+            ut[mt] = acc;
         }
         f16x8 ub[2];
 #pragma unroll
@@ -714,86 +824,34 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
                 ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
             }
         }
-        // O = (Q^ Gamma) S + A_qk U~, two token tiles per batch
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f16x8 qa[2][4], ah[2][2], al[2][2];
-#pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) {
-                const int mt = 2 * half + m2;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[mt][kb][l];
-#pragma unroll
-                for (int kb = 0; kb <= half; ++kb) {
-                    ah[m2][kb] = s.r.aqk[0][tri_block(mt, kb)][l];
-                    al[m2][kb] = s.r.aqk[1][tri_block(mt, kb)][l];
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) {
-                const int mt = 2 * half + m2;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    acc = mmh(qa[m2][kb], sh[kb], acc);
-                    acc = mmh(qa[m2][kb], sl[kb], acc);
-                }
-#pragma unroll
-                for (int kb = 0; kb <= half; ++kb) {
-                    acc = mmh(ah[m2][kb], ub[kb], acc);
-                    acc = mmh(al[m2][kb], ub[kb], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    stage_out(s.obuf, 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
-                              static_cast<const Tout*>(nullptr));
-            }
-        }
-        // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~, four channel tiles per batch
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            f16x8 ka[4][2];
-            float4 gm4[4];
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const int mt = 4 * half + m4;
-                ka[m4][0] = s.r.kp[mt][0][l];
-                ka[m4][1] = s.r.kp[mt][1][l];
-                gm4[m4] = *reinterpret_cast<const float4*>(&s.r.gam[16 * mt + 4 * g]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const int mt = 4 * half + m4;
-                sacc[mt][0] *= gm4[m4].x;
-                sacc[mt][1] *= gm4[m4].y;
-                sacc[mt][2] *= gm4[m4].z;
-                sacc[mt][3] *= gm4[m4].w;
-                sacc[mt] = mmh(ka[m4][0], ub[0], sacc[mt]);
-                sacc[mt] = mmh(ka[m4][1], ub[1], sacc[mt]);
-            }
-        }
+        if (more) fetch(j + 1, 10, 15);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 qa1[2][4], ah1[2][2], al1[2][2];
+        load_o(1, qa1, ah1, al1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_o(0, buf, qa0, ah0, al0, sh, sl, ub);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 ka0[4][2];
+        float4 gm0[4];
+        load_k(0, ka0, gm0);
+        if (more) fetch(j + 1, 15, RFULL + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_o(1, buf, qa1, ah1, al1, sh, sl, ub);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 ka1[4][2];
+        float4 gm1[4];
+        load_k(1, ka1, gm1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_k(0, ka0, gm0, ub);
+        step_k(1, ka1, gm1, ub);
         __syncthreads();
         // every read of this chunk's record is done: the next one moves in
-        if (j + 1 < nch) commit();
-        // coalesced output rows: 64 tokens x 64 columns of this slice
-        {
-            constexpr int CH = 16 / sizeof(Tout);            // elements per 16-byte piece
-            constexpr int PER_ROW = DVS / CH;
-#pragma unroll
-            for (int pc = t; pc < C * PER_ROW; pc += NT) {
-                const int r = pc / PER_ROW, part = pc % PER_ROW;
-                if (r < L) {
-                    const uint4 val = *reinterpret_cast<const uint4*>(
-                        reinterpret_cast<const char*>(s.obuf) + (r * DVS + part * CH) * sizeof(Tout));
-                    *reinterpret_cast<uint4*>(op + (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + part * CH) = val;
-                }
-            }
-        }
-        if (j + 2 < nch) fetch(j + 2);
+        if (more) commit();
+        prev_c0 = c0;
+        prev_L = L;
         __syncthreads();
     }
+    if (nch > 0) store_tile((nch - 1) & 1, prev_c0, prev_L);
 
     if (a.final_state) {
         const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
