@@ -99,6 +99,11 @@ __global__ void slot_map_kernel(const int32_t* __restrict__ cu, int num_seqs, in
     map[slot] = seq;
 }
 
+// Staging slots of the scattered fragment writes (A_qk, K'^T) are permuted
+// inside groups of eight, so the lanes of one 2-byte write instruction fall
+// into different LDS banks; the copy to the record undoes it.
+__device__ __forceinline__ int swz(int slot) { return slot ^ ((slot >> 3) & 7); }
+
 __global__ void __launch_bounds__(NT, 2)
 chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __restrict__ slot_seq, int nslots)
 {
@@ -106,7 +111,11 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 
     const int t = threadIdx.x;
     // the wave index is uniform across the wave: keep it in a scalar register
-    const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+    // Sub-tile w of this wave.  The sub-tiles carry unequal work (tile rows
+    // further down have more off-diagonal tiles), so the mapping rotates with
+    // the workgroup id: two workgroups sharing a CU then rarely put their
+    // heaviest waves on the same SIMD.
+    const int w = (__builtin_amdgcn_readfirstlane(t >> 6) + static_cast<int>(blockIdx.x & 3)) & 3;
     const int l = t & 63, g = l >> 4, n = l & 15;
     const int H = a.H;
     // consecutive workgroups take consecutive heads of one chunk: their
@@ -318,11 +327,11 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         splith((sc <= r) ? aqd[i] : 0.f, hi, lo);
         const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (w & 1);
         const int p = tri_block(w, w >> 1);
-        reinterpret_cast<_Float16*>(&s.aqk[0][p][lt])[e] = hi;
-        reinterpret_cast<_Float16*>(&s.aqk[1][p][lt])[e] = lo;
+        reinterpret_cast<_Float16*>(&s.aqk[0][p][swz(lt)])[e] = hi;
+        reinterpret_cast<_Float16*>(&s.aqk[1][p][swz(lt)])[e] = lo;
         if ((w & 1) == 0) {   // tile (w, w+1) shares this token block: zero it
-            reinterpret_cast<_Float16*>(&s.aqk[0][p][lt])[e + 4] = static_cast<_Float16>(0.f);
-            reinterpret_cast<_Float16*>(&s.aqk[1][p][lt])[e + 4] = static_cast<_Float16>(0.f);
+            reinterpret_cast<_Float16*>(&s.aqk[0][p][swz(lt)])[e + 4] = static_cast<_Float16>(0.f);
+            reinterpret_cast<_Float16*>(&s.aqk[1][p][swz(lt)])[e + 4] = static_cast<_Float16>(0.f);
         }
     }
     __syncthreads();
@@ -370,8 +379,8 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             splith(aqk[i], hi, lo);
             const int lt = (n >> 2) * 16 + 4 * g + i, e = (n & 3) + 4 * (j & 1);
             const int p = tri_block(w, j >> 1);
-            reinterpret_cast<_Float16*>(&s.aqk[0][p][lt])[e] = hi;
-            reinterpret_cast<_Float16*>(&s.aqk[1][p][lt])[e] = lo;
+            reinterpret_cast<_Float16*>(&s.aqk[0][p][swz(lt)])[e] = hi;
+            reinterpret_cast<_Float16*>(&s.aqk[1][p][swz(lt)])[e] = lo;
         }
     }
     __syncthreads();
@@ -417,7 +426,7 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             const int lb = (n >> 2) * 16 + 8 * (g & 1);
             _Float16* dst = reinterpret_cast<_Float16*>(&s.u.kp[mt][w >> 1][0]);
 #pragma unroll
-            for (int ee = 0; ee < 8; ++ee) dst[(lb + ee) * 8 + e] = kq16[kb][ee];
+            for (int ee = 0; ee < 8; ++ee) dst[swz(lb + ee) * 8 + e] = kq16[kb][ee];
         }
     }
     // level 1: T_{w,w-1} = -T_ww A_{w,w-1} T_{w-1,w-1} for w = 1, 3 (fp32 MFMA)
@@ -504,12 +513,12 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         uint4* dst = reinterpret_cast<uint4*>(&rg->aqk[0][0][0]);
         constexpr int NA = static_cast<int>(sizeof(s.aqk) / 16);
 #pragma unroll
-        for (int i = t; i < NA; i += NT) dst[i] = src[i];
+        for (int i = t; i < NA; i += NT) dst[i] = src[(i & ~63) | swz(i & 63)];
         const uint4* src2 = reinterpret_cast<const uint4*>(&s.u.kp[0][0][0]);
         uint4* dst2 = reinterpret_cast<uint4*>(&rg->kp[0][0][0]);
         constexpr int NK = static_cast<int>(sizeof(s.u.kp) / 16);
 #pragma unroll
-        for (int i = t; i < NK; i += NT) dst2[i] = src2[i];
+        for (int i = t; i < NK; i += NT) dst2[i] = src2[(i & ~63) | swz(i & 63)];
     }
 }
 
