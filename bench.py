@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-sample-heads", type=int, default=96)
     p.add_argument("--cpu-sample-tokens", type=int, default=65536)
+    p.add_argument("--no-extra", action="store_true", help="skip the mid/varlen prefill timings and the copy kernel")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/traffic.json from two rocprofv3 --pmc runs of this bench "
+                        "(FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
     return p.parse_args()
 
 
@@ -156,13 +160,166 @@ def cpu_baseline(inp_full, heads, tokens):
     oracle.forward(sub, threads=threads)
     dt = time.perf_counter() - t0
     token_heads_per_s = tokens * heads / dt
+    # one core: one head, the first 16384 tokens
+    one = kda_inputs.PrefillInputs(
+        B=1, T=16384, H=1, dk=D, dv=D, dtype="bf16", q=np.ascontiguousarray(sub.q[:, :16384, :1]),
+        k=np.ascontiguousarray(sub.k[:, :16384, :1]), v=np.ascontiguousarray(sub.v[:, :16384, :1]),
+        g=np.ascontiguousarray(sub.g[:, :16384, :1]), beta=np.ascontiguousarray(sub.beta[:, :16384, :1]),
+        init_state=np.ascontiguousarray(sub.init_state[:, :1]), cu_seqlens=None)
+    t1 = time.perf_counter()
+    oracle.forward(one, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": token_heads_per_s / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "first %d tokens x %d of 96 heads of the same workload (fp64 token recurrence, "
-                      "OpenMP over heads); %.1f s wall; scaled to 96-head tokens/s" % (tokens, heads, dt)}
+                      "OpenMP over heads); %.1f s wall; scaled to 96-head tokens/s" % (tokens, heads, dt),
+            "one_core_tokens_per_s": 16384 / dt1 / H,
+            "one_core_sample": "first 16384 tokens of head 0, 1 thread, %.2f s; scaled to 96-head tokens/s" % dt1,
+            "host": host_info()}
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def cpu_decode_baseline(n_sample=32):
+    """The fp64 oracle's decode step on the first n_sample of the 256
+    sequences (all 96 heads), scaled to ms per full step."""
+    import oracle
+    import kda_inputs
+    w = kda_inputs.DECODE_WORKLOAD
+    S0 = kda_inputs.decode_initial_state(w["seed"], n_sample, DEC_H, D, w["s0_std"]).astype(np.float64)
+    x = kda_inputs.decode_step(w["seed"], 0, n_sample, DEC_H, D)
+    f = lambda a: kda_inputs.bf16_to_f32(a) if a.dtype == np.uint16 else a
+    threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.decode_steps(S0, f(x.q), f(x.k), f(x.v), x.g, x.beta, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"ms_per_step": dt * 1e3 * DEC_N / n_sample, "cores": threads, "kind": "oracle",
+            "sample": "%d of 256 sequences x 96 heads, one step, %.2f s; scaled to the full step" % (n_sample, dt)}
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def write_traffic(fetch_dir, write_dir):
+    """HBM bytes per call of each path from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch).  Each counter is scaled by what it reads for the bench's
+    own device-to-device copy of COPY_BYTES, whose true traffic is COPY_BYTES
+    read + COPY_BYTES written."""
+    groups = {"chunk_fwd": ("chunk_prep_kernel", "chunk_scan_kernel"), "decode": ("decode_step_kernel",)}
+    copy_names = ("copyBuffer", "copy_kernel", "CopyBuffer")
+    out = {}
+    scale = {}
+    per = {}
+    for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == ctr]
+        copy = [float(r["Counter_Value"]) * 1024 for r in rows if any(c in r["Kernel_Name"] for c in copy_names)]
+        if not copy:
+            raise SystemExit("no copy-kernel dispatch with %s under %s" % (ctr, d))
+        scale[ctr] = COPY_BYTES / max(copy)   # the largest copy is the bench's calibration copy
+        for key, names in groups.items():
+            vals = [float(r["Counter_Value"]) * 1024 for r in rows if any(n in r["Kernel_Name"] for n in names)]
+            # one call = one dispatch of each kernel of the group
+            ncalls = max(1, min(sum(1 for r in rows if n in r["Kernel_Name"]) for n in names))
+            per.setdefault(key, {})[ctr] = sum(vals) / ncalls
+    for key, v in per.items():
+        if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+            rd = v["FETCH_SIZE"] * scale["FETCH_SIZE"]
+            wr = v["WRITE_SIZE"] * scale["WRITE_SIZE"]
+            out[key] = {"source_hash": kernel_source_hash(), "hbm_bytes_per_launch": rd + wr, "read_bytes": rd,
+                        "write_bytes": wr, "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
+COPY_BYTES = 1 << 30
+
+
+def copy_bandwidth(torch):
+    """Achievable HBM rate of a plain device-to-device copy of 1 GiB."""
+    x = torch.ones(COPY_BYTES // 4, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        y.copy_(x)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del x, y
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * COPY_BYTES, "ms_median": ms, "gbs": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
+
+
+def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
+    """Median call time of one prefill workload; with several input sets the
+    calls rotate over them (a 200 MB working set would otherwise stay in the
+    256 MB Infinity Cache)."""
+    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    ins = []
+    for k in range(sets):
+        inp = kda_inputs.workload(name, seed=kda_inputs.WORKLOADS[name]["seed"] + 100 * k)
+        d = {f: to(getattr(inp, f)) for f in ("q", "k", "v", "g", "beta")}
+        d["cu"] = to(inp.cu_seqlens) if inp.cu_seqlens is not None else None
+        d["s0"] = to(inp.init_state) if inp.init_state is not None else None
+        ins.append(d)
+    tokens, H = inp.B * inp.T, inp.H
+    n_seq = (inp.cu_seqlens.shape[0] - 1) if inp.cu_seqlens is not None else inp.B
+    o = torch.empty((inp.B, inp.T, H, inp.dv), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((n_seq, H, inp.dk, inp.dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(inp.B, inp.T, H, inp.dk, inp.dv, num_seqs=n_seq if d["cu"] is not None else 0),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda d: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["cu"], o=o,
+                                   final_state=sT, workspace=ws)
+    for i in range(warm):
+        call(ins[i % sets])
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call(ins[i % sets])
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    algo = BYTES_PER_TOKEN_HEAD * tokens * H + 2 * STATE_BYTES * n_seq * H
+    del ins, o, sT, ws
+    torch.cuda.empty_cache()
+    return {"tokens": tokens, "heads": H, "sequences": n_seq, "input_sets": sets, "ms_median": ms,
+            "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)), "tokens_per_s": tokens / (ms * 1e-3),
+            "algorithmic_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
@@ -206,15 +363,24 @@ def main():
                      "traffic": load_traffic("chunk_fwd"), "bytes_per_launch": bytes_launch},
         "mfma": {"achieved_tflops_algorithmic": tfl, "peak_bf16_tflops": BF16_MFMA_PEAK_TFLOPS,
                  "frac": tfl / BF16_MFMA_PEAK_TFLOPS, "flops_per_launch": flops_launch},
-        "launch_ms_mean": launch_ms, "launch_ms_min": float(np.min(launches)),
-        "launch_ms_max": float(np.max(launches)), "wall_s_timed": wall,
+        "launch_ms_mean": launch_ms, "launch_ms_median": float(np.median(launches)),
+        "launch_ms_min": float(np.min(launches)), "launch_ms_max": float(np.max(launches)), "wall_s_timed": wall,
     }
     del d
     torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = time_decode(kda, torch, kda_inputs)
+    if not args.no_extra:
+        out["prefill_mid"] = dict(workload="B=1 H=32 T=4096 d=128 bf16, seed 1; two input sets rotated",
+                                  **time_workload(kda, torch, kda_inputs, "mid_bf16", sets=2))
+        out["prefill_varlen"] = dict(workload="16 packed sequences, lengths U[512,16384] from seed 3, H=32 d=128 bf16",
+                                     **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1))
+    # the copy also calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE (see --traffic-from)
+    out["copy_kernel"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_heads, args.cpu_sample_tokens)
+        if not args.no_decode:
+            out["decode"]["cpu_baseline"] = cpu_decode_baseline()
     print(json.dumps(out), flush=True)
 
 
