@@ -315,6 +315,46 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
             "algorithmic_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+# gated prefill: bf16 decay logits z replace fp32 g (2 d instead of 4 d bytes), beta as fp32 logits
+BYTES_PER_TOKEN_HEAD_GATED = 2 * (2 * D + 2 * D) + 2 * D + 4
+
+
+def time_gated(kda, torch, kda_inputs, reps=20, warm=5):
+    """The headline shape through kda_chunk_fwd_gated (gate map and beta
+    sigmoid in the kernel), same seed as the headline workload."""
+    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    gi = kda_inputs.make_gated_prefill(2, B, T, H, D, D, s0_std=0.02)
+    d = {f: to(getattr(gi, f)) for f in ("q", "k", "v", "z", "A_log", "dt_bias", "beta_logits", "init_state")}
+    del gi
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
+    call = lambda: kda.chunk_fwd_gated(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta_logits"], d["init_state"],
+                                       dt_bias=d["dt_bias"], beta_logits=True, o=o, final_state=sT, workspace=ws)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    algo = BYTES_PER_TOKEN_HEAD_GATED * B * T * H + 2 * STATE_BYTES * B * H
+    del d, o, sT, ws
+    torch.cuda.empty_cache()
+    return {"workload": "long prefill B=1 H=96 T=65536 d=128 via the gated entry point: bf16 decay logits z, "
+                        "A_log, dt_bias, beta logits (seed 2)",
+            "ms_median": ms, "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)),
+            "tokens_per_s": B * T / (ms * 1e-3), "bytes_per_launch": algo,
+            "roofline": {"bound": "hbm", "achieved": algo / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -375,6 +415,7 @@ def main():
                                   **time_workload(kda, torch, kda_inputs, "mid_bf16", sets=2))
         out["prefill_varlen"] = dict(workload="16 packed sequences, lengths U[512,16384] from seed 3, H=32 d=128 bf16",
                                      **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1))
+        out["prefill_gated"] = time_gated(kda, torch, kda_inputs)
     # the copy also calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE (see --traffic-from)
     out["copy_kernel"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:

@@ -9,14 +9,18 @@ built, importing the library raises.
       -> (o, final_state)                       [kda_chunk_fwd]
   recurrent_step(q, k, v, g, beta, state, ...)
       -> o   (state updated in place)           [kda_recurrent_step]
+  chunk_fwd_gated(q, k, v, z, A_log, beta, ..., dt_bias=None)
+      -> (o, final_state)                       [kda_chunk_fwd_gated]
+  recurrent_step_gated(q, k, v, z, A_log, beta, state, ..., dt_bias=None)
+      -> o                                      [kda_recurrent_step_gated]
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "recurrent_step", "workspace_bytes", "lib_path", "load", "KDAError",
-           "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "STATUS"]
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_gated", "recurrent_step_gated", "workspace_bytes", "lib_path",
+           "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -24,6 +28,7 @@ _LIB_PATH = os.path.join(_PKG, "libkda.so")
 FLAG_QK_L2NORM = 0x1
 FLAG_VALIDATE = 0x2
 FLAG_FP32_PATH = 0x4
+FLAG_BETA_LOGITS = 0x8
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_RANGE", 5: "KDA_ERR_HIP"}
@@ -64,6 +69,10 @@ def load():
     lib.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
     lib.kda_recurrent_step.restype = I
     lib.kda_recurrent_step.argtypes = [I, I, I, I, I, I, F, U] + [P] * 7 + [P]
+    lib.kda_chunk_fwd_gated.restype = I
+    lib.kda_chunk_fwd_gated.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 11 + [P, S, P]
+    lib.kda_recurrent_step_gated.restype = I
+    lib.kda_recurrent_step_gated.argtypes = [I, I, I, I, I, I, F, U] + [P] * 9 + [P]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_status_str.argtypes = [I]
     lib.kda_last_hip_error.restype = I
@@ -132,11 +141,27 @@ def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True,
 
 
 def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
-              normalize=True, output_final_state=True, validate=False, fp32_path=False, o=None,
+              normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False, o=None,
               final_state=None, workspace=None, stream=None):
     """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
     beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
     [N+1] device tensor or None (then N = B).  Returns (o, final_state)."""
+    return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
+                  validate, fp32_path, beta_logits, o, final_state, workspace, stream)
+
+
+def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *, dt_bias=None, out_dtype=None,
+                    scale=1.0, normalize=True, output_final_state=True, validate=False, fp32_path=False,
+                    beta_logits=False, o=None, final_state=None, workspace=None, stream=None):
+    """As chunk_fwd, with g = -5 sigmoid(exp(A_log[h]) (z + dt_bias[h, c]))
+    computed in the kernel: z [B,T,H,d_k] in q's dtype, A_log [H] fp32,
+    dt_bias [H,d_k] fp32 or None."""
+    return _chunk(q, k, v, None, (z, A_log, dt_bias), beta, init_state, cu_seqlens, out_dtype, scale, normalize,
+                  output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, stream)
+
+
+def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
+           validate, fp32_path, beta_logits, o, final_state, workspace, stream):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -144,7 +169,14 @@ def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=N
     dv = v.shape[-1]
     _need(k, "k", q.dtype, q.shape)
     _need(v, "v", q.dtype, (B, T, H, dv))
-    _need(g, "g", torch.float32, (B, T, H, dk))
+    if gate is None:
+        _need(g, "g", torch.float32, (B, T, H, dk))
+    else:
+        z, A_log, dt_bias = gate
+        _need(z, "z", q.dtype, (B, T, H, dk))
+        _need(A_log, "A_log", torch.float32, (H,))
+        if dt_bias is not None:
+            _need(dt_bias, "dt_bias", torch.float32, (H, dk))
     _need(beta, "beta", torch.float32, (B, T, H))
     N = B
     if cu_seqlens is not None:
@@ -161,22 +193,39 @@ def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=N
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_VALIDATE if validate else 0) | \
-        (FLAG_FP32_PATH if fp32_path else 0)
+        (FLAG_FP32_PATH if fp32_path else 0) | (FLAG_BETA_LOGITS if beta_logits else 0)
     d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(out_dtype),
               scale, flags)
     ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
     if ws > 0 and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
-                           _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace),
-                           ctypes.c_size_t(0 if workspace is None else workspace.numel()), _stream(stream))
+    wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if gate is None:
+        st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
+                               _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace), wsb, _stream(stream))
+    else:
+        st = lib.kda_chunk_fwd_gated(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias),
+                                     _ptr(beta), _ptr(init_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
+                                     _ptr(workspace), wsb, _stream(stream))
     _check(st)
     return o, final_state
 
 
-def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, o=None, stream=None):
+def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, beta_logits=False, o=None,
+                   stream=None):
     """One fused decode step.  q, k, g: [N,H,d_k]; v: [N,H,d_v]; beta: [N,H];
     state: [N,H,d_k,d_v] fp32, updated in place.  Returns o [N,H,d_v]."""
+    return _step(q, k, v, g, None, beta, state, out_dtype, scale, normalize, beta_logits, o, stream)
+
+
+def recurrent_step_gated(q, k, v, z, A_log, beta, state, *, dt_bias=None, out_dtype=None, scale=1.0, normalize=True,
+                         beta_logits=False, o=None, stream=None):
+    """As recurrent_step, with g computed in the kernel from z [N,H,d_k],
+    A_log [H] and dt_bias [H,d_k] (or None)."""
+    return _step(q, k, v, None, (z, A_log, dt_bias), beta, state, out_dtype, scale, normalize, beta_logits, o, stream)
+
+
+def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, stream):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -184,15 +233,28 @@ def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normal
     dv = v.shape[-1]
     _need(k, "k", q.dtype, q.shape)
     _need(v, "v", q.dtype, (N, H, dv))
-    _need(g, "g", torch.float32, (N, H, dk))
+    if gate is None:
+        _need(g, "g", torch.float32, (N, H, dk))
+    else:
+        z, A_log, dt_bias = gate
+        _need(z, "z", q.dtype, (N, H, dk))
+        _need(A_log, "A_log", torch.float32, (H,))
+        if dt_bias is not None:
+            _need(dt_bias, "dt_bias", torch.float32, (H, dk))
     _need(beta, "beta", torch.float32, (N, H))
     _need(state, "state", torch.float32, (N, H, dk, dv))
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
     _need(o, "o", out_dtype, (N, H, dv))
-    st = lib.kda_recurrent_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale),
-                                FLAG_QK_L2NORM if normalize else 0, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
+    flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_BETA_LOGITS if beta_logits else 0)
+    if gate is None:
+        st = lib.kda_recurrent_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale), flags,
+                                    _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+                                    _stream(stream))
+    else:
+        st = lib.kda_recurrent_step_gated(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale),
+                                          flags, _ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(dt_bias),
+                                          _ptr(beta), _ptr(state), _ptr(o), _stream(stream))
     _check(st)
     return o

@@ -15,7 +15,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
 
-constexpr unsigned kKnownFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH;
+constexpr unsigned kKnownFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH | KDA_FLAG_BETA_LOGITS;
 constexpr size_t kValidateBytes = 256;
 
 kda_status hip_fail(hipError_t e)
@@ -74,10 +74,20 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d)
     return dense > packed ? dense : packed;
 }
 
-kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, const float* init_state,
-                         const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
-                         size_t ws_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Gate inputs of the gated entry points (all null for the plain ones).
+struct Gate {
+    const void* z;
+    const float* A_log;
+    const float* dt_bias;
+};
+
+kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const float* g,
+                          const Gate* gate, const float* beta, const float* init_state, const int32_t* cu_seqlens,
+                          void* o, float* final_state, void* workspace, size_t ws_bytes, hipStream_t stream)
 {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
@@ -89,11 +99,14 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     const long long tokens = static_cast<long long>(d->B) * d->T;
     if (tokens * d->H * (d->d_k > d->d_v ? d->d_k : d->d_v) >= (1LL << 40)) return KDA_ERR_INVALID_ARG;
     if (N * d->H > (1LL << 30)) return KDA_ERR_INVALID_ARG;
-    if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
-    const void* rows[] = {q, k, v, g, init_state, o, final_state};  // row-vectorised tensors
+    const void* decay = gate ? gate->z : static_cast<const void*>(g);
+    if (tokens > 0 && (!q || !k || !v || !decay || !beta || !o)) return KDA_ERR_INVALID_ARG;
+    if (gate && tokens > 0 && !gate->A_log) return KDA_ERR_INVALID_ARG;
+    const void* rows[] = {q, k, v, decay, init_state, o, final_state, gate ? gate->dt_bias : nullptr};
     for (const void* p : rows)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
     if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_INVALID_ARG;
+    if (gate && gate->A_log && !aligned4(gate->A_log)) return KDA_ERR_INVALID_ARG;
     const size_t need = workspace_need(d, cu_seqlens != nullptr);
     if (ws_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
@@ -121,6 +134,11 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     a.cu_seqlens = cu_seqlens;
     a.o = o;
     a.final_state = final_state;
+    a.gated = gate ? 1 : 0;
+    a.z = gate ? gate->z : nullptr;
+    a.A_log = gate ? gate->A_log : nullptr;
+    a.dt_bias = gate ? gate->dt_bias : nullptr;
+    a.beta_logits = (d->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
 
     hipError_t e;
     if (d->flags & KDA_FLAG_VALIDATE) {
@@ -145,25 +163,88 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     return KDA_OK;
 }
 
-kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
-                              float scale, unsigned flags, const void* q, const void* k, const void* v,
-                              const float* g, const float* beta, float* state, void* o, hipStream_t stream)
+kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
+                               unsigned flags, const void* q, const void* k, const void* v, const float* g,
+                               const Gate* gate, const float* beta, float* state, void* o, hipStream_t stream)
 {
-    if (flags & ~(KDA_FLAG_QK_L2NORM)) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_LOGITS)) return KDA_ERR_UNSUPPORTED;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
     if (static_cast<long long>(N) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
-    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
-    const void* rows[] = {q, k, v, g, state, o};
+    const void* decay = gate ? gate->z : static_cast<const void*>(g);
+    if (!q || !k || !v || !decay || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (gate && !gate->A_log) return KDA_ERR_INVALID_ARG;
+    const void* rows[] = {q, k, v, decay, state, o};
     for (const void* p : rows)
         if (!aligned16(p)) return KDA_ERR_INVALID_ARG;
     if (!aligned4(beta)) return KDA_ERR_INVALID_ARG;
-    hipError_t e = kda::launch_decode(d_k, d_v, in_dtype == KDA_BF16, out_dtype == KDA_BF16, N * H, q, k, v, g,
-                                      beta, state, o, scale, (flags & KDA_FLAG_QK_L2NORM) ? 1 : 0, stream);
+    if (gate && (!aligned4(gate->A_log) || (gate->dt_bias && !aligned4(gate->dt_bias)))) return KDA_ERR_INVALID_ARG;
+    kda::DecodeArgs a{};
+    a.dk = d_k;
+    a.dv = d_v;
+    a.chains = N * H;
+    a.H = H;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.scale = scale;
+    a.normalize = (flags & KDA_FLAG_QK_L2NORM) ? 1 : 0;
+    a.gated = gate ? 1 : 0;
+    a.z = gate ? gate->z : nullptr;
+    a.A_log = gate ? gate->A_log : nullptr;
+    a.dt_bias = gate ? gate->dt_bias : nullptr;
+    a.beta_logits = (flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
+    hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* init_state, const int32_t* cu_seqlens, void* o,
+                         float* final_state, void* workspace, size_t ws_bytes, hipStream_t stream)
+{
+    return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, o, final_state, workspace, ws_bytes,
+                          stream);
+}
+
+kda_status kda_chunk_fwd_gated(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const void* z,
+                               const float* A_log, const float* dt_bias, const float* beta, const float* init_state,
+                               const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                               size_t ws_bytes, hipStream_t stream)
+{
+    const Gate gate{z, A_log, dt_bias};
+    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, o, final_state, workspace,
+                          ws_bytes, stream);
+}
+
+kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, unsigned flags, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, float* state, void* o, hipStream_t stream)
+{
+    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, state, o,
+                               stream);
+}
+
+kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                                    float scale, unsigned flags, const void* q, const void* k, const void* v,
+                                    const void* z, const float* A_log, const float* dt_bias, const float* beta,
+                                    float* state, void* o, hipStream_t stream)
+{
+    const Gate gate{z, A_log, dt_bias};
+    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, nullptr, &gate, beta,
+                               state, o, stream);
 }
 
 }  // extern "C"

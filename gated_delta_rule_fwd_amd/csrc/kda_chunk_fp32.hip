@@ -87,7 +87,9 @@ chunk_fp32_kernel(ChunkArgs a)
                 const size_t idx = (static_cast<size_t>(c0 + r) * H + h) * DK + i;
                 qv = Elem<Tin>::load(q, idx);
                 kv = Elem<Tin>::load(k, idx);
-                gv = a.g[idx];
+                gv = a.gated ? gate_log_decay(Elem<Tin>::load(static_cast<const Tin*>(a.z), idx),
+                                              a.dt_bias ? a.dt_bias[h * DK + i] : 0.f, __expf(a.A_log[h]))
+                             : a.g[idx];
             }
             sQ[r][i] = qv;
             sK[r][i] = kv;
@@ -97,7 +99,14 @@ chunk_fp32_kernel(ChunkArgs a)
             const int r = e / DVS, j = e % DVS;
             sV[r][j] = (r < L) ? Elem<Tin>::load(v, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + j) : 0.f;
         }
-        if (t < C) sBeta[t] = (t < L) ? a.beta[static_cast<size_t>(c0 + t) * H + h] : 0.f;
+        if (t < C) {
+            float bt = 0.f;
+            if (t < L) {
+                bt = a.beta[static_cast<size_t>(c0 + t) * H + h];
+                if (a.beta_logits) bt = beta_from_logit(bt);
+            }
+            sBeta[t] = bt;
+        }
         __syncthreads();
 
         // 2. per-row L2 normalisation of q and k; 3. running sum of g

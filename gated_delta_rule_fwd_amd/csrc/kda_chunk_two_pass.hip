@@ -152,17 +152,39 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         const size_t base = static_cast<size_t>(tk) * H + h;
         const uint16_t* qr = static_cast<const uint16_t*>(a.q) + base * DK + 8 * g;
         const uint16_t* kr = static_cast<const uint16_t*>(a.k) + base * DK + 8 * g;
-        const float* gr = a.g + base * DK + 8 * g;
         uint4 rq[4], rk[4];
         float4 rgv[8];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             rq[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
             rk[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
-            rgv[2 * kb] = *reinterpret_cast<const float4*>(gr + 32 * kb);
-            rgv[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
         }
-        const float braw = a.beta[base];
+        if (a.gated) {
+            // g = -5 sigmoid(e^{A_h} (z + dt_bias)) from bf16 z
+            const uint16_t* zr = static_cast<const uint16_t*>(a.z) + base * DK + 8 * g;
+            const float ea = __expf(a.A_log[h]);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint4 rz = *reinterpret_cast<const uint4*>(zr + 32 * kb);
+                float4 b0 = make_float4(0.f, 0.f, 0.f, 0.f), b1 = b0;
+                if (a.dt_bias) {
+                    b0 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g);
+                    b1 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g + 4);
+                }
+                rgv[2 * kb] = make_float4(gate_log_decay(bf_lo(rz.x), b0.x, ea), gate_log_decay(bf_hi(rz.x), b0.y, ea),
+                                          gate_log_decay(bf_lo(rz.y), b0.z, ea), gate_log_decay(bf_hi(rz.y), b0.w, ea));
+                rgv[2 * kb + 1] = make_float4(gate_log_decay(bf_lo(rz.z), b1.x, ea), gate_log_decay(bf_hi(rz.z), b1.y, ea),
+                                              gate_log_decay(bf_lo(rz.w), b1.z, ea), gate_log_decay(bf_hi(rz.w), b1.w, ea));
+            }
+        } else {
+            const float* gr = a.g + base * DK + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                rgv[2 * kb] = *reinterpret_cast<const float4*>(gr + 32 * kb);
+                rgv[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
+            }
+        }
+        const float braw = a.beta_logits ? beta_from_logit(a.beta[base]) : a.beta[base];
         const float live = (row < L) ? 1.f : 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {

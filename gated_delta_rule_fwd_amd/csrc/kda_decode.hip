@@ -23,10 +23,17 @@ namespace kda {
 
 template <int DK, int DV, typename Tin, typename Tout>
 __global__ void __launch_bounds__(256)
-decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
-                   const float* __restrict__ g, const float* __restrict__ beta,
-                   float* __restrict__ state, Tout* __restrict__ o, float scale, int normalize)
+decode_step_kernel(DecodeArgs a)
 {
+    const Tin* __restrict__ q = static_cast<const Tin*>(a.q);
+    const Tin* __restrict__ k = static_cast<const Tin*>(a.k);
+    const Tin* __restrict__ v = static_cast<const Tin*>(a.v);
+    const float* __restrict__ g = a.g;
+    const float* __restrict__ beta = a.beta;
+    float* __restrict__ state = a.state;
+    Tout* __restrict__ o = static_cast<Tout*>(a.o);
+    const float scale = a.scale;
+    const int normalize = a.normalize;
     constexpr int CG = DV / 4;        // float4 column groups
     constexpr int RG = 256 / CG;      // row groups
     constexpr int RPT = DK / RG;      // rows per thread
@@ -57,7 +64,15 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
             const int i = lane + 64 * e;
             qv[e] = Elem<Tin>::load(q, static_cast<size_t>(c) * DK + i);
             kv[e] = Elem<Tin>::load(k, static_cast<size_t>(c) * DK + i);
-            sa[i] = __expf(g[static_cast<size_t>(c) * DK + i]);
+            float gi;
+            if (a.gated) {   // bounded decay map of the gated entry point
+                const int h = c % a.H;
+                gi = gate_log_decay(Elem<Tin>::load(static_cast<const Tin*>(a.z), static_cast<size_t>(c) * DK + i),
+                                    a.dt_bias ? a.dt_bias[h * DK + i] : 0.f, __expf(a.A_log[h]));
+            } else {
+                gi = g[static_cast<size_t>(c) * DK + i];
+            }
+            sa[i] = __expf(gi);
             ss_q += qv[e] * qv[e];
             ss_k += kv[e] * kv[e];
         }
@@ -107,7 +122,7 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     }
     __syncthreads();
 
-    const float b = beta[c];
+    const float b = a.beta_logits ? beta_from_logit(beta[c]) : beta[c];
     const float dot = sdot;
     float u[4], ov[4];
 #pragma unroll
@@ -139,41 +154,27 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 }
 
 template <int DK, int DV, typename Tin, typename Tout>
-static hipError_t launch_decode_t(int chains, const void* q, const void* k, const void* v, const float* g,
-                                  const float* beta, float* state, void* o, float scale, int normalize,
-                                  hipStream_t stream)
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream)
 {
-    decode_step_kernel<DK, DV, Tin, Tout><<<dim3(chains), dim3(256), 0, stream>>>(
-        static_cast<const Tin*>(q), static_cast<const Tin*>(k), static_cast<const Tin*>(v), g, beta, state,
-        static_cast<Tout*>(o), scale, normalize);
+    decode_step_kernel<DK, DV, Tin, Tout><<<dim3(a.chains), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
-static hipError_t launch_decode_d(bool in_bf16, bool out_bf16, int chains, const void* q, const void* k,
-                                  const void* v, const float* g, const float* beta, float* state, void* o,
-                                  float scale, int normalize, hipStream_t stream)
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream)
 {
-    if (in_bf16 && out_bf16)
-        return launch_decode_t<DK, DV, uint16_t, uint16_t>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
-    if (in_bf16)
-        return launch_decode_t<DK, DV, uint16_t, float>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
-    if (out_bf16)
-        return launch_decode_t<DK, DV, float, uint16_t>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
-    return launch_decode_t<DK, DV, float, float>(chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    if (a.in_bf16 && a.out_bf16) return launch_decode_t<DK, DV, uint16_t, uint16_t>(a, stream);
+    if (a.in_bf16) return launch_decode_t<DK, DV, uint16_t, float>(a, stream);
+    if (a.out_bf16) return launch_decode_t<DK, DV, float, uint16_t>(a, stream);
+    return launch_decode_t<DK, DV, float, float>(a, stream);
 }
 
-hipError_t launch_decode(int dk, int dv, bool in_bf16, bool out_bf16, int chains, const void* q, const void* k,
-                         const void* v, const float* g, const float* beta, float* state, void* o, float scale,
-                         int normalize, hipStream_t stream)
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)
 {
-    if (dk == 128 && dv == 128)
-        return launch_decode_d<128, 128>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
-    if (dk == 128 && dv == 64)
-        return launch_decode_d<128, 64>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
-    if (dk == 64 && dv == 128)
-        return launch_decode_d<64, 128>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
-    return launch_decode_d<64, 64>(in_bf16, out_bf16, chains, q, k, v, g, beta, state, o, scale, normalize, stream);
+    if (a.dk == 128 && a.dv == 128) return launch_decode_d<128, 128>(a, stream);
+    if (a.dk == 128 && a.dv == 64) return launch_decode_d<128, 64>(a, stream);
+    if (a.dk == 64 && a.dv == 128) return launch_decode_d<64, 128>(a, stream);
+    return launch_decode_d<64, 64>(a, stream);
 }
 
 }  // namespace kda

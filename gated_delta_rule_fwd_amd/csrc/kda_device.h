@@ -35,6 +35,17 @@ template <> struct Elem<uint16_t> {
     __device__ __forceinline__ static void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
 };
 
+// Gate prologue of the gated entry points ("Kimi K3 模型结构（2）", Q&A on the
+// lower bound; "Kimi K3 の KDA ..." section 1.2.1 on A_log, dt_bias and the
+// in-kernel sigmoid of beta):
+//   g    = -5 sigmoid(e^{A_h} (z + dt_bias[h, c]))   in (-5, 0)
+//   beta = sigmoid(logit)
+// exp(-x) overflowing to +inf gives g = -0 and beta = 0, the right limits.
+__device__ __forceinline__ float gate_log_decay(float z, float bias, float exp_a) {
+    return -5.f / (1.f + __expf(-exp_a * (z + bias)));
+}
+__device__ __forceinline__ float beta_from_logit(float b) { return 1.f / (1.f + __expf(-b)); }
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);

@@ -21,11 +21,35 @@ struct ChunkArgs {
     const int32_t* cu_seqlens;
     void* o;
     float* final_state;
+    // gated entry point: g is computed from z (in_dtype, [tokens, H, d_k]),
+    // A_log [H] and dt_bias [H, d_k] (nullable) instead of being read
+    const void* z;
+    const float* A_log;
+    const float* dt_bias;
+    int gated;
+    int beta_logits;    // beta holds logits; the kernels apply the sigmoid
 };
 
-hipError_t launch_decode(int dk, int dv, bool in_bf16, bool out_bf16, int chains, const void* q,
-                         const void* k, const void* v, const float* g, const float* beta, float* state,
-                         void* o, float scale, int normalize, hipStream_t stream);
+// Inputs of one decode step; z/A_log/dt_bias replace g when gated.
+struct DecodeArgs {
+    int dk, dv, chains, H;
+    bool in_bf16, out_bf16;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;
+    void* o;
+    float scale;
+    int normalize;
+    const void* z;
+    const float* A_log;
+    const float* dt_bias;
+    int gated;
+    int beta_logits;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // fp32 per-position-pair path: any supported head dims and dtypes.
 hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t stream);

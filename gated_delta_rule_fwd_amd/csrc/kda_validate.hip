@@ -4,7 +4,9 @@
 // [-5, 0], so 16 consecutive tokens rescale by at most e^80, inside the bf16
 // and fp32 range ("Kimi K3 模型结构（2）", Q&A on the -5 bound).  beta is a
 // write strength in [0, 1] ("Kimi K3 の KDA ..." section 1.2.1).  Packed
-// sequences must partition [0, T] monotonically.
+// sequences must partition [0, T] monotonically.  The gated entry point maps
+// z into (-5, 0) itself, so only beta (or, for logits, finiteness) and the
+// sequence partition are checked there.
 #include "kda_kernels.h"
 
 namespace kda {
@@ -17,7 +19,7 @@ __global__ void zero_counters(unsigned int* c)
 }
 
 __global__ void __launch_bounds__(256)
-validate_kernel(const float* __restrict__ g, size_t ng, const float* __restrict__ beta, size_t nb,
+validate_kernel(const float* __restrict__ g, size_t ng, const float* __restrict__ beta, size_t nb, int beta_logits,
                 const int32_t* __restrict__ cu, int nseq, int T, unsigned int* counters)
 {
     unsigned int bad_g = 0, bad_b = 0, bad_cu = 0;
@@ -28,7 +30,7 @@ validate_kernel(const float* __restrict__ g, size_t ng, const float* __restrict_
     }
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nb; i += stride) {
         const float x = beta[i];
-        bad_b += !(x >= 0.0f && x <= 1.0f);
+        bad_b += beta_logits ? !(x == x && fabsf(x) <= 3.4e38f) : !(x >= 0.0f && x <= 1.0f);
     }
     if (cu && blockIdx.x == 0) {
         for (int n = threadIdx.x; n <= nseq; n += blockDim.x) {
@@ -51,8 +53,9 @@ hipError_t launch_validate(const ChunkArgs& a, unsigned int* counters, hipStream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t tokens = static_cast<size_t>(a.B) * a.T;
-    const size_t ng = tokens * a.H * a.dk, nb = tokens * a.H;
-    validate_kernel<<<1024, 256, 0, stream>>>(a.g, ng, a.beta, nb, a.cu_seqlens, a.num_seqs, a.T, counters);
+    const size_t ng = a.gated ? 0 : tokens * a.H * a.dk, nb = tokens * a.H;
+    validate_kernel<<<1024, 256, 0, stream>>>(a.g, ng, a.beta, nb, a.beta_logits, a.cu_seqlens, a.num_seqs, a.T,
+                                              counters);
     return hipGetLastError();
 }
 

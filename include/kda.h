@@ -74,6 +74,11 @@ typedef enum kda_dtype {
 #define KDA_FLAG_VALIDATE 0x2u
 /* Use the fp32 (per-position-pair) arithmetic path even for bf16 inputs. */
 #define KDA_FLAG_FP32_PATH 0x4u
+/* beta holds write-strength logits; the kernel applies the sigmoid, as the
+ * model does in-kernel (page 1, section 1.2.1: beta is a per-head fp32 scalar
+ * passed through a sigmoid inside the kernel).  Accepted by every prefill and
+ * decode entry point. */
+#define KDA_FLAG_BETA_LOGITS 0x8u
 
 typedef struct kda_chunk_desc {
     int B;              /* batch (must be 1 when cu_seqlens is given) */
@@ -139,6 +144,44 @@ KDA_API kda_status kda_recurrent_step(int N, int H, int d_k, int d_v,
                               float scale, unsigned flags,
                               const void* q, const void* k, const void* v,
                               const float* g, const float* beta,
+                              float* state, void* o, hipStream_t stream);
+
+/*
+ * Gate prologue fused into the forward pass ("Kimi K3 模型结构（2）", Q&A on
+ * the scaled-sigmoid decay map with its -5 lower bound; "Kimi K3 の KDA ..."
+ * section 1.2.1 on A_log and dt_bias).  Instead of g, these take the decay
+ * logits z and compute, per token, head h and key channel c,
+ *
+ *   g = -5 * sigmoid(exp(A_log[h]) * (z + dt_bias[h, c]))      in (-5, 0)
+ *
+ * which saves the g tensor's traffic (bf16 z is half of fp32 g).  Where
+ * dt_bias enters is not legible on the pages; adding it to z before the
+ * scale is this library's reading.
+ *
+ *   z        [B, T, H, d_k] (prefill) / [N, H, d_k] (decode), in_dtype,
+ *            16-byte aligned
+ *   A_log    [H] fp32, 4-byte aligned, required
+ *   dt_bias  [H, d_k] fp32, nullable (zero), 16-byte aligned
+ *
+ * Every other argument, layout, flag, workspace rule and error is that of
+ * kda_chunk_fwd / kda_recurrent_step; with KDA_FLAG_VALIDATE the g range
+ * check is skipped (the map cannot leave (-5, 0)) and beta logits are only
+ * checked to be finite.
+ */
+KDA_API kda_status kda_chunk_fwd_gated(const kda_chunk_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const void* z, const float* A_log, const float* dt_bias,
+                         const float* beta,
+                         const float* init_state, const int32_t* cu_seqlens,
+                         void* o, float* final_state,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+KDA_API kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v,
+                              kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, unsigned flags,
+                              const void* q, const void* k, const void* v,
+                              const void* z, const float* A_log, const float* dt_bias,
+                              const float* beta,
                               float* state, void* o, hipStream_t stream);
 
 /* Static description of a status code. */

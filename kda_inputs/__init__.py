@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 BLOCK_T = 4096  # tokens per independently seeded block
-_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7}
+_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7, "dt_bias": 8}
 
 
 # ----------------------------------------------------------------------------
@@ -244,3 +244,81 @@ def decode_step(seed: int, step: int, N: int, H: int, d: int, dtype: str = "bf16
     g = (np.float32(-5.0) * _sigmoid32(np.exp(A)[None, :, None].astype(np.float32) * z)).astype(np.float32)
     beta = _sigmoid32(_rng(seed, "beta", blk).standard_normal((N, H), dtype=np.float32))
     return DecodeStep(q=qkv("q"), k=qkv("k"), v=qkv("v"), g=g, beta=beta)
+
+
+# ----------------------------------------------------------------------------
+# Raw gate inputs (decay logits z, A_log, dt_bias, beta logits) for the gated
+# entry points.  These are draws only: the gate map itself is applied by the
+# code under test and by the oracle.
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class GatedPrefillInputs:
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    dtype: str
+    q: np.ndarray                   # [B,T,H,dk] (bf16 bits or float32)
+    k: np.ndarray
+    v: np.ndarray
+    z: np.ndarray                   # [B,T,H,dk] decay logits, same storage as q
+    A_log: np.ndarray               # [H] float32
+    dt_bias: np.ndarray             # [H,dk] float32
+    beta_logits: np.ndarray         # [B,T,H] float32
+    init_state: Optional[np.ndarray]
+    cu_seqlens: Optional[np.ndarray]
+
+    def f32(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return bf16_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def make_gated_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int, *, dtype: str = "bf16",
+                       s0_std: float = 0.0, lengths=None, bias_std: float = 0.5) -> GatedPrefillInputs:
+    """q, k, v, S0 and the packing as make_prefill (same streams); z ~ N(0,1)
+    stored like q; A_log ~ U(-1, 1) per head; dt_bias ~ N(0, bias_std^2) per
+    (head, channel); beta logits ~ N(0,1)."""
+    base = make_prefill(seed, B, T, H, dk, dv, dtype=dtype, gate="sigmoid", s0_std=s0_std, lengths=lengths)
+    T = base.T
+    store = np.float32 if dtype == "f32" else np.uint16
+    z = np.empty((B, T, H, dk), dtype=store)
+    _fill_blocked(z, seed, "z", lambda rng, shape, t0, t1: (
+        lambda x: x if dtype == "f32" else bf16_bits(x))(rng.standard_normal(shape, dtype=np.float32)), T)
+    A_log = _rng(seed, "A", 0).uniform(-1.0, 1.0, size=H).astype(np.float32)
+    dt_bias = (_rng(seed, "dt_bias", 0).standard_normal((H, dk), dtype=np.float32)
+               * np.float32(bias_std)).astype(np.float32)
+    bl = np.empty((B, T, H), dtype=np.float32)
+    _fill_blocked(bl, seed, "beta", lambda rng, shape, t0, t1: rng.standard_normal(shape, dtype=np.float32), T)
+    return GatedPrefillInputs(B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, q=base.q, k=base.k, v=base.v, z=z,
+                              A_log=A_log, dt_bias=dt_bias, beta_logits=bl, init_state=base.init_state,
+                              cu_seqlens=base.cu_seqlens)
+
+
+@dataclasses.dataclass
+class GatedDecodeStep:
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    z: np.ndarray           # [N,H,d] decay logits, same storage as q
+    beta_logits: np.ndarray  # [N,H] float32
+
+
+def gated_decode_step(seed: int, step: int, N: int, H: int, d: int, dtype: str = "bf16") -> GatedDecodeStep:
+    blk = 1_000_000 + step
+
+    def draw(name, shape):
+        x = _rng(seed, name, blk).standard_normal(shape, dtype=np.float32)
+        return x if dtype == "f32" else bf16_bits(x)
+
+    return GatedDecodeStep(q=draw("q", (N, H, d)), k=draw("k", (N, H, d)), v=draw("v", (N, H, d)),
+                           z=draw("z", (N, H, d)),
+                           beta_logits=_rng(seed, "beta", blk).standard_normal((N, H), dtype=np.float32))
+
+
+def gate_params(seed: int, H: int, d: int, bias_std: float = 0.5):
+    """A_log [H] ~ U(-1, 1) and dt_bias [H,d] ~ N(0, bias_std^2)."""
+    A_log = _rng(seed, "A", 0).uniform(-1.0, 1.0, size=H).astype(np.float32)
+    dt_bias = (_rng(seed, "dt_bias", 0).standard_normal((H, d), dtype=np.float32)
+               * np.float32(bias_std)).astype(np.float32)
+    return A_log, dt_bias

@@ -14,6 +14,12 @@ Contents
   * ``decode_steps``: the same recurrence, one token per call, carrying the
     fp64 state between calls (the recurrent form that the chunkwise page
     assigns to decode: "Kimi K3 模型结构（2）", Q&A on train/prefill/decode).
+  * ``gate_map`` / ``beta_from_logits`` / ``forward_gated`` / ``decode_gated``:
+    the gate prologue of the gated entry points, g = -5 sigmoid(e^{A_h} (z +
+    dt_bias)) and beta = sigmoid(logit), evaluated in fp64 ("Kimi K3 模型结构
+    （2）", Q&A on the scaled sigmoid with g_min = -5; "Kimi K3 の KDA ..."
+    section 1.2.1 on A_log, dt_bias and the in-kernel sigmoid of beta), then
+    the recurrence above.
   * ``product_form``: a second, independently written NumPy formulation that
     builds each transition matrix (I - beta k k^T) Diag(alpha) explicitly
     (page 1, section 2.3.5: the state map is the ordered product of per-token
@@ -127,6 +133,53 @@ def decode_steps(state, q, k, v, g, beta, *, scale=1.0, threads=0):
                            np.reshape(v, (N, 1, H, dv)), np.reshape(g, (N, 1, H, dk)),
                            np.reshape(beta, (N, 1, H)), state, scale=scale, threads=threads)
     return o[:, 0], sT
+
+
+# ----------------------------------------------------------------------------
+# Gate prologue
+# ----------------------------------------------------------------------------
+def sigmoid(x):
+    """1 / (1 + e^-x) in fp64, written so that neither branch overflows."""
+    x = np.asarray(x, np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gate_map(z, A_log, dt_bias=None):
+    """Per-channel log-decay of the bounded map: g = g_min sigmoid(e^A x) with
+    g_min = -5 and x the decay logit ("Kimi K3 模型结构（2）", Q&A: K3 replaces
+    the unbounded negative softplus by a scaled sigmoid with g_min = -5, range
+    (-5, 0)).  A = A_log[h] is the per-head log-scale and dt_bias[h, c] the
+    per-(head, channel) bias ("Kimi K3 の KDA ..." section 1.2.1).  Reading:
+    the bias is added to the logit before the scale, x = z + dt_bias.
+    z: [..., H, d_k]; A_log: [H]; dt_bias: [H, d_k] or None.  fp64 result."""
+    z = np.asarray(z, np.float64)
+    x = z if dt_bias is None else z + np.asarray(dt_bias, np.float64)
+    return -5.0 * sigmoid(np.exp(np.asarray(A_log, np.float64))[:, None] * x)
+
+
+def beta_from_logits(b):
+    """beta = sigmoid(logit) ("Kimi K3 の KDA ..." section 1.2.1: the per-head
+    write strength goes through a sigmoid inside the kernel)."""
+    return sigmoid(b)
+
+
+def forward_gated(inp, heads: Optional[slice] = None, *, beta_logits=True, scale=1.0, want_o=True, threads=0):
+    """Oracle on a kda_inputs.GatedPrefillInputs: the gate map in fp64, then
+    the recurrence (which reads g and beta as fp32, one rounding each)."""
+    hs = slice(None) if heads is None else heads
+    g = gate_map(inp.f32("z")[:, :, hs], inp.A_log[hs], inp.dt_bias[hs])
+    b = beta_from_logits(inp.beta_logits[:, :, hs]) if beta_logits else inp.beta_logits[:, :, hs]
+    s0 = inp.init_state[:, hs] if inp.init_state is not None else None
+    return forward_arrays(inp.f32("q")[:, :, hs], inp.f32("k")[:, :, hs], inp.f32("v")[:, :, hs], g, b, s0,
+                          inp.cu_seqlens, scale=scale, want_o=want_o, threads=threads)
+
+
+def decode_gated(state, q, k, v, z, A_log, dt_bias, beta_logits, *, scale=1.0, threads=0):
+    """One gated decode step: gate map on z [N,H,d_k], sigmoid on the beta
+    logits [N,H], then decode_steps."""
+    return decode_steps(state, q, k, v, gate_map(z, A_log, dt_bias), beta_from_logits(beta_logits),
+                        scale=scale, threads=threads)
 
 
 # ----------------------------------------------------------------------------

@@ -28,8 +28,9 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step",
-                                  "kda_status_str", "kda_last_hip_error", "kda_version"])
+    assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_workspace_bytes",
+                                  "kda_recurrent_step", "kda_recurrent_step_gated", "kda_status_str",
+                                  "kda_last_hip_error", "kda_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -143,3 +144,35 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(kda, "_lib", None)
     with pytest.raises(ImportError):
         kda.load()
+
+
+def _call_gated(lib, d, z=FAKE + 0x900000, a_log=FAKE + 0xA00000, dt_bias=None, beta=FAKE + 0xB00000, ws=None,
+                ws_bytes=0):
+    p = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(3)]
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_fwd_gated(ctypes.byref(d), p[0], p[1], p[2], vp(z), vp(a_log), vp(dt_bias), vp(beta),
+                                   None, None, ctypes.c_void_p(FAKE + 0xC00000), None, vp(ws),
+                                   ctypes.c_size_t(ws_bytes), None)
+
+
+def test_gated_entry_points_reject_bad_arguments(lib):
+    d = _desc(flags=kda.FLAG_QK_L2NORM | kda.FLAG_BETA_LOGITS)
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert _call_gated(lib, d, z=None, ws=FAKE, ws_bytes=need) == 1          # z required
+    assert _call_gated(lib, d, a_log=None, ws=FAKE, ws_bytes=need) == 1      # A_log required
+    assert _call_gated(lib, d, z=FAKE + 8, ws=FAKE, ws_bytes=need) == 1      # z misaligned
+    assert _call_gated(lib, d, a_log=FAKE + 2, ws=FAKE, ws_bytes=need) == 1  # A_log misaligned
+    assert _call_gated(lib, d, dt_bias=FAKE + 4, ws=FAKE, ws_bytes=need) == 1
+    assert _call_gated(lib, d, ws=None, ws_bytes=0) == 3                     # same workspace rule
+    assert _call_gated(lib, _desc(flags=0x80)) == 2
+    P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(9)]
+
+    def step(z=P[3], a_log=P[4], flags=kda.FLAG_QK_L2NORM):
+        return lib.kda_recurrent_step_gated(4, 2, 128, 128, 1, 1, 1.0, flags, P[0], P[1], P[2], z, a_log, None,
+                                            P[5], P[6], P[7], None)
+
+    assert step(z=None) == 1
+    assert step(a_log=None) == 1
+    assert step(flags=kda.FLAG_VALIDATE) == 2
+    assert lib.kda_recurrent_step_gated(0, 2, 128, 128, 1, 1, 1.0, 1, *([None] * 9), None) == 0

@@ -365,3 +365,95 @@ def test_generator_is_deterministic_and_blocked():
     assert a.beta.min() > 0.0 and a.beta.max() < 1.0
     lens = kda_inputs.varlen_lengths()
     assert len(lens) == 16 and lens.min() >= 512 and lens.max() <= 16384
+
+
+# ---------------------------------------------------------------------------
+# Gate prologue of the gated entry points: g = -5 sigmoid(e^A (z + dt_bias)),
+# beta = sigmoid(logit) ("Kimi K3 模型结构（2）", Q&A: the scaled sigmoid with
+# g_min = -5 and range (-5, 0); "Kimi K3 の KDA ..." section 1.2.1: A_log,
+# dt_bias and the in-kernel sigmoid of beta).  Each test checks a value the
+# formula fixes without evaluating the formula the same way.
+# ---------------------------------------------------------------------------
+def _gate_case(seed=11, H=3, d=8, n=5):
+    rng = np.random.default_rng(seed)
+    z = rng.standard_normal((n, H, d))
+    A = rng.uniform(-1, 1, H)
+    b = rng.standard_normal((H, d))
+    return z, A, b
+
+
+def test_gate_map_midpoint_is_half_of_the_bound():
+    # sigmoid(0) = 1/2: a logit that cancels the bias gives exactly g_min / 2
+    _, A, b = _gate_case()
+    g = oracle.gate_map(-b[None], A, b)
+    np.testing.assert_array_equal(g, np.full(g.shape, -2.5))
+
+
+def test_gate_map_reflection():
+    # sigmoid(x) + sigmoid(-x) = 1  =>  g(x) + g(-x) = g_min for x = e^A (z + b)
+    z, A, b = _gate_case()
+    g_pos = oracle.gate_map(z, A, b)
+    g_neg = oracle.gate_map(-z - 2 * b, A, b)          # z + b -> -(z + b)
+    np.testing.assert_allclose(g_pos + g_neg, -5.0, rtol=0, atol=1e-14)
+
+
+def test_gate_map_bounds_limits_and_monotonicity():
+    z, A, b = _gate_case()
+    g = oracle.gate_map(z, A, b)
+    assert np.all(g < 0) and np.all(g > -5)             # the open range (-5, 0)
+    big = np.full_like(z, 60.0)
+    np.testing.assert_allclose(oracle.gate_map(big, A, None), -5.0, rtol=0, atol=1e-8)   # no-forget limit: -5
+    np.testing.assert_allclose(oracle.gate_map(-big, A, None), 0.0, rtol=0, atol=1e-8)   # and 0 at -inf
+    # strictly decreasing in z for every head scale e^A > 0
+    np.testing.assert_array_less(oracle.gate_map(z + 1e-3, A, b), g)
+
+
+def test_gate_map_scale_enters_as_exp_of_a_log():
+    # e^(A + ln 2) (z/2 + b/2) = e^A (z + b): halving the logit and the bias
+    # while adding ln 2 to A_log leaves g unchanged
+    z, A, b = _gate_case()
+    np.testing.assert_allclose(oracle.gate_map(z / 2, A + np.log(2.0), b / 2), oracle.gate_map(z, A, b),
+                               rtol=1e-14, atol=1e-15)
+
+
+def test_gate_map_without_bias_is_the_printed_k3_map():
+    # with no bias the map is exactly g_min * sigmoid(e^A z), checked against
+    # a logistic evaluated through tanh: sigmoid(x) = (1 + tanh(x/2)) / 2
+    z, A, _ = _gate_case()
+    x = np.exp(A)[:, None] * z
+    np.testing.assert_allclose(oracle.gate_map(z, A, None), -5.0 * 0.5 * (1.0 + np.tanh(x / 2)), rtol=1e-14)
+
+
+def test_beta_from_logits():
+    assert oracle.beta_from_logits(0.0) == 0.5
+    b = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(oracle.beta_from_logits(b) + oracle.beta_from_logits(-b), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(oracle.beta_from_logits(b), 0.5 * (1.0 + np.tanh(b / 2)), rtol=1e-13, atol=1e-15)
+    assert oracle.beta_from_logits(-1000.0) == 0.0 and oracle.beta_from_logits(1000.0) == 1.0   # no overflow
+
+
+def test_gated_oracle_composes_map_and_recurrence():
+    # the gated oracle equals the plain one fed with the mapped decay and
+    # strength; and a logit of +inf-like size gives beta = 1, i.e. S^T k^ = v
+    inp = kda_inputs.make_gated_prefill(5, 1, 70, 2, 8, 4, dtype="f32", s0_std=0.1)
+    o1, s1 = oracle.forward_gated(inp)
+    g = oracle.gate_map(inp.z, inp.A_log, inp.dt_bias)
+    o2, s2 = oracle.forward_arrays(inp.q, inp.k, inp.v, g, oracle.beta_from_logits(inp.beta_logits),
+                                   inp.init_state)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1, s2)
+    inp.beta_logits[:] = 80.0
+    _, sT = oracle.forward_gated(inp)
+    kl = inp.k[0, -1].astype(np.float64)
+    kh = kl / np.sqrt(np.sum(kl * kl, axis=-1, keepdims=True) + oracle.EPS)
+    # |k^|^2 = 1 - eps / (|k|^2 + eps) leaves a residual of order 1e-7 here
+    for h in range(2):
+        np.testing.assert_allclose(sT[0, h].T @ kh[h], inp.v[0, -1, h], rtol=2e-6, atol=2e-6)
+
+
+def test_gated_generator_draws_raw_inputs():
+    a = kda_inputs.make_gated_prefill(7, 1, 300, 2, 16, 16, s0_std=0.02)
+    b = kda_inputs.make_gated_prefill(7, 1, 300, 2, 16, 16, s0_std=0.02)
+    for name in ("q", "k", "v", "z", "A_log", "dt_bias", "beta_logits", "init_state"):
+        np.testing.assert_array_equal(getattr(a, name), getattr(b, name))
+    assert a.z.dtype == np.uint16 and a.beta_logits.min() < 0 < a.beta_logits.max()   # raw logits, not sigmoids
