@@ -355,6 +355,42 @@ def time_gated(kda, torch, kda_inputs, reps=20, warm=5):
                          "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
+def time_signed(kda, torch, kda_inputs, reps=20, warm=5):
+    """The headline shape as Complex KDA (KDA_FLAG_SIGNED_ALPHA): signed
+    decay alpha (a quarter of the entries negative), beta in (0, 2)."""
+    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
+    si = kda_inputs.make_signed_prefill(2, B, T, H, D, D, s0_std=0.02)
+    d = {f: to(getattr(si, f)) for f in ("q", "k", "v", "g", "beta", "init_state")}
+    del si
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
+    call = lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["init_state"], signed_alpha=True,
+                                 o=o, final_state=sT, workspace=ws)
+    for _ in range(warm):
+        call()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    algo = BYTES_PER_TOKEN_HEAD * B * T * H + 2 * STATE_BYTES * B * H
+    del d, o, sT, ws
+    torch.cuda.empty_cache()
+    return {"workload": "long prefill B=1 H=96 T=65536 d=128 as Complex KDA: signed alpha (25 % negative, "
+                        "|alpha| >= e^-5), beta in (0, 2) (seed 2)",
+            "ms_median": ms, "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)),
+            "tokens_per_s": B * T / (ms * 1e-3), "bytes_per_launch": algo,
+            "roofline": {"bound": "hbm", "achieved": algo / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -416,6 +452,7 @@ def main():
         out["prefill_varlen"] = dict(workload="16 packed sequences, lengths U[512,16384] from seed 3, H=32 d=128 bf16",
                                      **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1))
         out["prefill_gated"] = time_gated(kda, torch, kda_inputs)
+        out["prefill_complex_kda"] = time_signed(kda, torch, kda_inputs)
     # the copy also calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE (see --traffic-from)
     out["copy_kernel"] = copy_bandwidth(torch)
     if not args.no_cpu_baseline:

@@ -20,7 +20,8 @@ import ctypes
 import os
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_gated", "recurrent_step_gated", "workspace_bytes", "lib_path",
-           "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS", "STATUS"]
+           "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS",
+           "FLAG_SIGNED_ALPHA", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -29,6 +30,7 @@ FLAG_QK_L2NORM = 0x1
 FLAG_VALIDATE = 0x2
 FLAG_FP32_PATH = 0x4
 FLAG_BETA_LOGITS = 0x8
+FLAG_SIGNED_ALPHA = 0x10
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_RANGE", 5: "KDA_ERR_HIP"}
@@ -141,13 +143,15 @@ def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True,
 
 
 def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
-              normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False, o=None,
-              final_state=None, workspace=None, stream=None):
+              normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False,
+              signed_alpha=False, o=None, final_state=None, workspace=None, stream=None):
     """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
     beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
-    [N+1] device tensor or None (then N = B).  Returns (o, final_state)."""
+    [N+1] device tensor or None (then N = B).  With signed_alpha (Complex KDA)
+    g holds the signed decay alpha in [-1, 1] and beta may lie in [0, 2].
+    Returns (o, final_state)."""
     return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
-                  validate, fp32_path, beta_logits, o, final_state, workspace, stream)
+                  validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha)
 
 
 def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *, dt_bias=None, out_dtype=None,
@@ -161,7 +165,7 @@ def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *
 
 
 def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
-           validate, fp32_path, beta_logits, o, final_state, workspace, stream):
+           validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -193,7 +197,8 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_VALIDATE if validate else 0) | \
-        (FLAG_FP32_PATH if fp32_path else 0) | (FLAG_BETA_LOGITS if beta_logits else 0)
+        (FLAG_FP32_PATH if fp32_path else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
+        (FLAG_SIGNED_ALPHA if signed_alpha else 0)
     d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(out_dtype),
               scale, flags)
     ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
@@ -211,11 +216,12 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     return o, final_state
 
 
-def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, beta_logits=False, o=None,
-                   stream=None):
+def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, beta_logits=False,
+                   signed_alpha=False, o=None, stream=None):
     """One fused decode step.  q, k, g: [N,H,d_k]; v: [N,H,d_v]; beta: [N,H];
-    state: [N,H,d_k,d_v] fp32, updated in place.  Returns o [N,H,d_v]."""
-    return _step(q, k, v, g, None, beta, state, out_dtype, scale, normalize, beta_logits, o, stream)
+    state: [N,H,d_k,d_v] fp32, updated in place.  With signed_alpha g holds
+    the signed decay alpha.  Returns o [N,H,d_v]."""
+    return _step(q, k, v, g, None, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha)
 
 
 def recurrent_step_gated(q, k, v, z, A_log, beta, state, *, dt_bias=None, out_dtype=None, scale=1.0, normalize=True,
@@ -225,7 +231,7 @@ def recurrent_step_gated(q, k, v, z, A_log, beta, state, *, dt_bias=None, out_dt
     return _step(q, k, v, None, (z, A_log, dt_bias), beta, state, out_dtype, scale, normalize, beta_logits, o, stream)
 
 
-def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, stream):
+def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha=False):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -247,7 +253,8 @@ def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logit
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
     _need(o, "o", out_dtype, (N, H, dv))
-    flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_BETA_LOGITS if beta_logits else 0)
+    flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
+        (FLAG_SIGNED_ALPHA if signed_alpha else 0)
     if gate is None:
         st = lib.kda_recurrent_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale), flags,
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),

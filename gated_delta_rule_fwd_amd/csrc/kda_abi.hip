@@ -15,7 +15,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
 
-constexpr unsigned kKnownFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH | KDA_FLAG_BETA_LOGITS;
+constexpr unsigned kKnownFlags =
+    KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH | KDA_FLAG_BETA_LOGITS | KDA_FLAG_SIGNED_ALPHA;
 constexpr size_t kValidateBytes = 256;
 
 kda_status hip_fail(hipError_t e)
@@ -91,6 +92,7 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
 {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    if (gate && (d->flags & KDA_FLAG_SIGNED_ALPHA)) return KDA_ERR_UNSUPPORTED;
     if (!dtype_ok(d->in_dtype) || !dtype_ok(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(d->d_k) || !head_dim_ok(d->d_v)) return KDA_ERR_UNSUPPORTED;
     if (d->B <= 0 || d->T < 0 || d->H <= 0) return KDA_ERR_INVALID_ARG;
@@ -139,6 +141,7 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     a.A_log = gate ? gate->A_log : nullptr;
     a.dt_bias = gate ? gate->dt_bias : nullptr;
     a.beta_logits = (d->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
+    a.signed_alpha = (d->flags & KDA_FLAG_SIGNED_ALPHA) ? 1 : 0;
 
     hipError_t e;
     if (d->flags & KDA_FLAG_VALIDATE) {
@@ -167,7 +170,8 @@ kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtyp
                                unsigned flags, const void* q, const void* k, const void* v, const float* g,
                                const Gate* gate, const float* beta, float* state, void* o, hipStream_t stream)
 {
-    if (flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_LOGITS)) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_LOGITS | KDA_FLAG_SIGNED_ALPHA)) return KDA_ERR_UNSUPPORTED;
+    if (gate && (flags & KDA_FLAG_SIGNED_ALPHA)) return KDA_ERR_UNSUPPORTED;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
@@ -202,6 +206,7 @@ kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtyp
     a.A_log = gate ? gate->A_log : nullptr;
     a.dt_bias = gate ? gate->dt_bias : nullptr;
     a.beta_logits = (flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
+    a.signed_alpha = (flags & KDA_FLAG_SIGNED_ALPHA) ? 1 : 0;
     hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;

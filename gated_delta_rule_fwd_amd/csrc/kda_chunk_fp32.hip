@@ -69,6 +69,7 @@ chunk_fp32_kernel(ChunkArgs a)
     __shared__ float sS[DK][DVS];    // state slice
     __shared__ float sBeta[C];
     __shared__ float sGam[DK];       // b_L, then gamma = exp(b_L)
+    __shared__ float sSgL[DK];       // chunk-end sign of the decay (Complex KDA)
 
     const size_t state_base = static_cast<size_t>(chain) * DK * DV + j0;
     for (int e = t; e < DK * DVS; e += 256) {
@@ -126,11 +127,29 @@ chunk_fp32_kernel(ChunkArgs a)
                 }
             }
         }
+        if (a.signed_alpha) __syncthreads();   // the normalised rows are read below
         if (t < DK) {
             float acc = 0.f;
-            for (int r = 0; r < C; ++r) {
-                acc += sB[r][t];
-                sB[r][t] = acc;
+            if (a.signed_alpha) {
+                // Complex KDA: sB holds alpha; Gamma_r = sigma_r e^{b_r} with
+                // sigma_r the running sign.  sigma_r goes into q^ and k^ of row
+                // r, so every pair factor Gamma_r / Gamma_s gets sigma_r sigma_s;
+                // the chunk-end sign sigma_L goes into gamma and K^ gamma/Gamma.
+                float sg = 1.f;
+                for (int r = 0; r < C; ++r) {
+                    const float al = (r < L) ? sB[r][t] : 1.f;
+                    if (al < 0.f) sg = -sg;
+                    acc += __logf(fabsf(al));
+                    sB[r][t] = acc;
+                    sQ[r][t] *= sg;
+                    sK[r][t] *= sg;
+                }
+                sSgL[t] = sg;
+            } else {
+                for (int r = 0; r < C; ++r) {
+                    acc += sB[r][t];
+                    sB[r][t] = acc;
+                }
             }
             sGam[t] = acc;
         }
@@ -161,10 +180,10 @@ chunk_fp32_kernel(ChunkArgs a)
             const float gm = __expf(b);
             sQ[r][i] *= gm;
             sK[r][i] = kv * gm;
-            sB[r][i] = kv * __expf(sGam[i] - b);
+            sB[r][i] = kv * __expf(sGam[i] - b) * (a.signed_alpha ? sSgL[i] : 1.f);
         }
         __syncthreads();
-        if (t < DK) sGam[t] = __expf(sGam[t]);
+        if (t < DK) sGam[t] = __expf(sGam[t]) * (a.signed_alpha ? sSgL[t] : 1.f);
 
         // 6. right-hand side  beta_r (v_r - (K^*Gamma)_r S)
         {

@@ -34,7 +34,9 @@
 //
 // Precision (fp32 accumulate everywhere; "x3" = hi*hi + hi*lo + lo*hi with
 // x = hi + lo):
-//   A_kk                bf16
+//   A_kk                bf16 (x3 for Complex KDA: with |alpha| near 1 the
+//                            chain is undamped and single-bf16 A_kk rounding
+//                            accumulates)
 //   A_qk                bf16 x3                  (diagonal factor up to e^80)
 //   T' (V - K Gamma S)  bf16 x3                  (near a fixed point of the
 //                                                 recurrence V and K Gamma S
@@ -72,6 +74,8 @@ struct alignas(16) PrepSmem {
                                      //   exp(ref_w), exp(ref_4 - ref_{w+1})
     float dl12[2][DK];               // exp(tot_1), exp(tot_2)
     float beta[C];
+    float tsg[4][DK];                // Complex KDA: sign of the decay product over each sub-tile
+    float psg[4][DK];                //   and over the sub-tiles before each one
 };
 
 // Packed sequences: slot -> sequence (or -1 for a slot no sequence uses).
@@ -104,6 +108,24 @@ __global__ void slot_map_kernel(const int32_t* __restrict__ cu, int num_seqs, in
 // into different LDS banks; the copy to the record undoes it.
 __device__ __forceinline__ int swz(int slot) { return slot ^ ((slot >> 3) & 7); }
 
+// Inclusive prefix product of +-1 signs over the 16 lanes of a DPP row
+// (lanes with no source keep the identity 1).
+__device__ __forceinline__ float row_sign_scan16(float x)
+{
+    const int one = __float_as_int(1.f);
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x111, 0xf, 0xf, false));  // row_shr:1
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x112, 0xf, 0xf, false));  // row_shr:2
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x114, 0xf, 0xf, false));  // row_shr:4
+    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x118, 0xf, 0xf, false));  // row_shr:8
+    return x;
+}
+
+// SIGNED: Complex KDA, g holds the signed decay alpha.  With sigma_r the sign
+// of alpha's running product, Gamma_r = sigma_r e^{b_r}; sigma_r is folded
+// into q^ and k^ of row r, which gives every pair factor its sigma_r sigma_s,
+// and the chunk-end sign sigma_L into gamma and K^ gamma/Gamma.  All the
+// exponential factors stay those of b = sum log|alpha|.
+template <bool SIGNED>
 __global__ void __launch_bounds__(NT, 2)
 chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __restrict__ slot_seq, int nslots)
 {
@@ -146,6 +168,7 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
     // token and are masked to the identity of the recurrence (k = g = beta = 0).
     const int row = 16 * w + n;
     float qv[32], kv[32], bv[32];
+    float sgn[SIGNED ? 32 : 1];
     float beta_r;
     {
         const long tk = min(c0 + row, tok1 - 1);
@@ -197,14 +220,26 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
                 kv[8 * kb + 2 * e2] = bf_lo(kw[e2]) * live;
                 kv[8 * kb + 2 * e2 + 1] = bf_hi(kw[e2]) * live;
             }
-            bv[8 * kb + 0] = rgv[2 * kb].x * live;
-            bv[8 * kb + 1] = rgv[2 * kb].y * live;
-            bv[8 * kb + 2] = rgv[2 * kb].z * live;
-            bv[8 * kb + 3] = rgv[2 * kb].w * live;
-            bv[8 * kb + 4] = rgv[2 * kb + 1].x * live;
-            bv[8 * kb + 5] = rgv[2 * kb + 1].y * live;
-            bv[8 * kb + 6] = rgv[2 * kb + 1].z * live;
-            bv[8 * kb + 7] = rgv[2 * kb + 1].w * live;
+            bv[8 * kb + 0] = rgv[2 * kb].x;
+            bv[8 * kb + 1] = rgv[2 * kb].y;
+            bv[8 * kb + 2] = rgv[2 * kb].z;
+            bv[8 * kb + 3] = rgv[2 * kb].w;
+            bv[8 * kb + 4] = rgv[2 * kb + 1].x;
+            bv[8 * kb + 5] = rgv[2 * kb + 1].y;
+            bv[8 * kb + 6] = rgv[2 * kb + 1].z;
+            bv[8 * kb + 7] = rgv[2 * kb + 1].w;
+        }
+        if constexpr (SIGNED) {
+            // alpha -> (sign, log|alpha|); rows past the end act as alpha = 1
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                const float al = bv[e];
+                sgn[e] = (row < L && al < 0.f) ? -1.f : 1.f;
+                bv[e] = (row < L) ? __logf(fabsf(al)) : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 32; ++e) bv[e] *= live;
         }
         beta_r = braw * live;
     }
@@ -238,6 +273,16 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 #pragma unroll
             for (int e = 0; e < 8; ++e) s.tot[w][32 * kb + 8 * g + e] = bv[8 * kb + e];
     }
+    if constexpr (SIGNED) {
+        // running sign inside the sub-tile, folded into q^ and k^ of this row
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const float sc = row_sign_scan16(sgn[e]);
+            qv[e] *= sc;
+            kv[e] *= sc;
+            if (n == 15) s.tsg[w][32 * (e >> 3) + 8 * g + (e & 7)] = sc;
+        }
+    }
     if (g == 0) s.beta[row] = beta_r;
     __syncthreads();
 
@@ -269,6 +314,22 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             s.fac[3][3][c] = 1.f;
             rg->gam[c] = __expf(r4);
         }
+        if constexpr (SIGNED) {
+            const float p1 = s.tsg[0][c], p2 = p1 * s.tsg[1][c], p3 = p2 * s.tsg[2][c], sL = p3 * s.tsg[3][c];
+            __syncthreads();   // every fac entry above is written before it is rescaled
+            if (t < DK) {
+                s.psg[0][c] = 1.f;
+                s.psg[1][c] = p1;
+                s.fac[0][3][c] *= sL;
+                s.fac[1][3][c] *= sL;
+            } else {
+                s.psg[2][c] = p2;
+                s.psg[3][c] = p3;
+                s.fac[2][3][c] *= sL;
+                s.fac[3][3][c] = sL;
+                rg->gam[c] *= sL;
+            }
+        }
     }
     __syncthreads();
 
@@ -276,7 +337,9 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
     // E = exp(b - ref_w) <= 1, Gamma = exp(b).  The diagonal tile (w, w) is
     // computed right here: both of its operands are in this lane.  The
     // off-diagonal tiles share one A-operand, X^ E.
-    bf16x8 kao[4], qoh[4], qol[4];
+    // Complex KDA also keeps the low half of the A_kk operands: with |alpha|
+    // near 1 nothing damps the rounding of single-bf16 A_kk over a long chain
+    bf16x8 kao[4], qoh[4], qol[4], kaol[SIGNED ? 4 : 1];
     f16x8 kq16[4];   // K^ gamma/Gamma of this row, channels 32kb + 8g + e
     f32x4 akd = {0.f, 0.f, 0.f, 0.f}, aqd = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -287,7 +350,9 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         lds8(&s.fac[w][1][cb], dw);
         lds8(&s.fac[w][2][cb], er);
         lds8(&s.fac[w][3][cb], el);
-        bf16x8 kfh, kfl, kad, qdh, qdl;
+        float ps[8];
+        if constexpr (SIGNED) lds8(&s.psg[w][cb], ps);
+        bf16x8 kfh, kfl, kad, kadl, qdh, qdl;
         float qgv[8], kgv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -296,24 +361,40 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             const float f = __builtin_amdgcn_rcpf(d);  // exp(ref_{w+1} - b)
             const float E = d * dw[e];               // exp(b - ref_w)
             const float gm = E * er[e];              // exp(b)
-            const float kx = kv[8 * kb + e], qx = qv[8 * kb + e];
+            const float kx = SIGNED ? kv[8 * kb + e] * ps[e] : kv[8 * kb + e];
+            const float qx = SIGNED ? qv[8 * kb + e] * ps[e] : qv[8 * kb + e];
             __bf16 hi, lo;
             split(kx * f, hi, lo);
             kfh[e] = hi;
             kfl[e] = lo;
             qgv[e] = qx * gm;
             kgv[e] = -kx * gm;
-            kad[e] = static_cast<__bf16>(kx * d);
+            if constexpr (SIGNED) {
+                split(kx * d, hi, lo);
+                kad[e] = hi;
+                kadl[e] = lo;
+            } else {
+                kad[e] = static_cast<__bf16>(kx * d);
+            }
             split(qx * d, hi, lo);
             qdh[e] = hi;
             qdl[e] = lo;
-            kao[kb][e] = static_cast<__bf16>(kx * E);
+            if constexpr (SIGNED) {
+                split(kx * E, hi, lo);
+                kao[kb][e] = hi;
+                kaol[kb][e] = lo;
+            } else {
+                kao[kb][e] = static_cast<__bf16>(kx * E);
+            }
             split(qx * E, hi, lo);
             qoh[kb][e] = hi;
             qol[kb][e] = lo;
             kq16[kb][e] = static_cast<_Float16>(kx * f * el[e]);
         }
-        akd = mma(kad, kfh, akd);
+        if constexpr (SIGNED)
+            akd = mma3(kad, kadl, kfh, kfl, akd);
+        else
+            akd = mma(kad, kfh, akd);
         aqd = mma3(qdh, qdl, kfh, kfl, aqd);
         s.u.kf[0][w][kb][l] = kfh;
         s.u.kf[1][w][kb][l] = kfl;
@@ -389,7 +470,10 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         }
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            akk = mma(kao[kb], bh[kb], akk);
+            if constexpr (SIGNED)
+                akk = mma3(kao[kb], kaol[kb], bh[kb], bl[kb], akk);
+            else
+                akk = mma(kao[kb], bh[kb], akk);
             aqk = mma3(qoh[kb], qol[kb], bh[kb], bl[kb], aqk);
         }
         // lane holds rows r = 16w + 4g + i, column s = 16j + n (all s < r)
@@ -924,7 +1008,12 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_
             slot_map_kernel<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(
                 a.cu_seqlens, a.num_seqs, a.T, static_cast<int>(slots), map);
         }
-        chunk_prep_kernel<<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
+        if (a.signed_alpha)
+            chunk_prep_kernel<true><<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map,
+                                                                                            static_cast<int>(slots));
+        else
+            chunk_prep_kernel<false><<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map,
+                                                                                             static_cast<int>(slots));
     }
     // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
     const int groups = (chains + 7) / 8;

@@ -72,7 +72,8 @@ decode_step_kernel(DecodeArgs a)
             } else {
                 gi = g[static_cast<size_t>(c) * DK + i];
             }
-            sa[i] = __expf(gi);
+            // Complex KDA passes the signed decay alpha itself
+            sa[i] = a.signed_alpha ? gi : __expf(gi);
             ss_q += qv[e] * qv[e];
             ss_k += kv[e] * kv[e];
         }

@@ -28,6 +28,7 @@ struct ChunkArgs {
     const float* dt_bias;
     int gated;
     int beta_logits;    // beta holds logits; the kernels apply the sigmoid
+    int signed_alpha;   // g holds the signed decay alpha (Complex KDA), not its log
 };
 
 // Inputs of one decode step; z/A_log/dt_bias replace g when gated.
@@ -48,6 +49,7 @@ struct DecodeArgs {
     const float* dt_bias;
     int gated;
     int beta_logits;
+    int signed_alpha;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

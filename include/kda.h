@@ -79,6 +79,14 @@ typedef enum kda_dtype {
  * passed through a sigmoid inside the kernel).  Accepted by every prefill and
  * decode entry point. */
 #define KDA_FLAG_BETA_LOGITS 0x8u
+/* Complex KDA ("[논문리뷰] Complex KDA ..." page: the gate range widened to
+ * [-1, 1] and beta to [0, 2]): the g argument holds the signed per-channel
+ * decay alpha itself instead of its logarithm, and beta may lie in [0, 2].
+ * The transition stays (I - beta k^ k^T) Diag(alpha).  Prefill requires
+ * exp(-5) <= |alpha| <= 1 (the bounded-decay range of the chunk kernels;
+ * checked under KDA_FLAG_VALIDATE).  Not combinable with the gated entry
+ * points. */
+#define KDA_FLAG_SIGNED_ALPHA 0x10u
 
 typedef struct kda_chunk_desc {
     int B;              /* batch (must be 1 when cu_seqlens is given) */

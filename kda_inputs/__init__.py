@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 BLOCK_T = 4096  # tokens per independently seeded block
-_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7, "dt_bias": 8}
+_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7, "dt_bias": 8, "sign": 9}
 
 
 # ----------------------------------------------------------------------------
@@ -322,3 +322,33 @@ def gate_params(seed: int, H: int, d: int, bias_std: float = 0.5):
     dt_bias = (_rng(seed, "dt_bias", 0).standard_normal((H, d), dtype=np.float32)
                * np.float32(bias_std)).astype(np.float32)
     return A_log, dt_bias
+
+
+# ----------------------------------------------------------------------------
+# Complex KDA inputs: signed decay alpha and beta in (0, 2)
+# ----------------------------------------------------------------------------
+def make_signed_prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int, *, dtype: str = "bf16",
+                        s0_std: float = 0.0, lengths=None, p_negative: float = 0.25) -> PrefillInputs:
+    """As make_prefill (same streams), then the decay is given as a signed
+    alpha: |alpha| = e^g with g from the bounded map (so |alpha| >= e^-5) and
+    a negative sign with probability p_negative per (token, head, channel);
+    beta = 2 sigmoid(N(0,1)) in (0, 2).  Returned in the g and beta fields."""
+    base = make_prefill(seed, B, T, H, dk, dv, dtype=dtype, gate="k3", s0_std=s0_std, lengths=lengths)
+    T = base.T
+    alpha = np.exp(base.g).astype(np.float32)
+    neg = np.empty(alpha.shape, dtype=bool)
+    _fill_blocked(neg, seed, "sign", lambda rng, shape, t0, t1: rng.uniform(size=shape) < p_negative, T)
+    alpha[neg] = -alpha[neg]
+    base.g = alpha
+    base.beta = (np.float32(2.0) * base.beta).astype(np.float32)
+    return base
+
+
+def signed_decode_step(seed: int, step: int, N: int, H: int, d: int, dtype: str = "bf16",
+                       p_negative: float = 0.25) -> DecodeStep:
+    """decode_step with the decay given as signed alpha and beta in (0, 2)."""
+    x = decode_step(seed, step, N, H, d, dtype)
+    alpha = np.exp(x.g).astype(np.float32)
+    neg = _rng(seed, "sign", 1_000_000 + step).uniform(size=alpha.shape) < p_negative
+    alpha[neg] = -alpha[neg]
+    return DecodeStep(q=x.q, k=x.k, v=x.v, g=alpha, beta=(np.float32(2.0) * x.beta).astype(np.float32))

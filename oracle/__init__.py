@@ -20,6 +20,9 @@ Contents
     （2）", Q&A on the scaled sigmoid with g_min = -5; "Kimi K3 の KDA ..."
     section 1.2.1 on A_log, dt_bias and the in-kernel sigmoid of beta), then
     the recurrence above.
+  * ``forward_signed``: the same recurrence with the decay given as a signed
+    alpha in [-1, 1] and beta in [0, 2] (Complex KDA, "[논문리뷰] Complex KDA
+    ..." page).
   * ``product_form``: a second, independently written NumPy formulation that
     builds each transition matrix (I - beta k k^T) Diag(alpha) explicitly
     (page 1, section 2.3.5: the state map is the ordered product of per-token
@@ -61,12 +64,12 @@ def _load():
     if _lib is None:
         build()
         lib = ctypes.CDLL(_LIB)
-        f = lib.kda_oracle_forward
-        f.restype = ctypes.c_int
         P = ctypes.c_void_p
-        f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int, P] + [P] * 5 + [P, ctypes.c_double,
-                                                                         ctypes.c_double, ctypes.c_int,
-                                                                         P, P, ctypes.c_int]
+        for f in (lib.kda_oracle_forward, lib.kda_oracle_forward_signed):
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int] * 5 + [ctypes.c_int, P] + [P] * 5 + [P, ctypes.c_double,
+                                                                             ctypes.c_double, ctypes.c_int,
+                                                                             P, P, ctypes.c_int]
         lib.kda_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -81,10 +84,11 @@ def _ptr(a: Optional[np.ndarray]):
 
 
 def forward_arrays(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, scale=1.0, eps=EPS,
-                   normalize=True, want_o=True, threads=0):
+                   normalize=True, want_o=True, threads=0, alpha_given=False):
     """Run the recurrence.  q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H]
     (all converted to fp32, which is exact for bf16 values); init_state
-    [N,H,dk,dv] (converted to fp64).  Returns (o fp64 [B,T,H,dv] or None,
+    [N,H,dk,dv] (converted to fp64).  With alpha_given, g holds the signed
+    decay alpha itself (Complex KDA).  Returns (o fp64 [B,T,H,dv] or None,
     final_state fp64 [N,H,dk,dv])."""
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
@@ -107,9 +111,9 @@ def forward_arrays(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, scale=
         assert s0.shape == (N, H, dk, dv)
     o = np.empty((B, T, H, dv), dtype=np.float64) if want_o else None
     sT = np.empty((N, H, dk, dv), dtype=np.float64)
-    rc = lib.kda_oracle_forward(B, T, H, dk, dv, N, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                _ptr(beta), _ptr(s0), float(scale), float(eps), int(bool(normalize)),
-                                _ptr(o), _ptr(sT), int(threads))
+    fn = lib.kda_oracle_forward_signed if alpha_given else lib.kda_oracle_forward
+    rc = fn(B, T, H, dk, dv, N, _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0), float(scale),
+            float(eps), int(bool(normalize)), _ptr(o), _ptr(sT), int(threads))
     if rc != 0:
         raise ValueError("kda_oracle_forward rejected its arguments")
     return o, sT
@@ -124,14 +128,21 @@ def forward(inp, heads: Optional[slice] = None, *, scale=1.0, want_o=True, threa
                           s0, inp.cu_seqlens, scale=scale, want_o=want_o, threads=threads)
 
 
-def decode_steps(state, q, k, v, g, beta, *, scale=1.0, threads=0):
+def forward_signed(q, k, v, alpha, beta, init_state=None, cu_seqlens=None, **kw):
+    """Complex KDA: the recurrence with signed per-channel decay alpha in
+    [-1, 1] and beta in [0, 2] ("[논문리뷰] Complex KDA ..." page, Method:
+    the transition stays (I - beta k^ k^T) Diag(alpha))."""
+    return forward_arrays(q, k, v, alpha, beta, init_state, cu_seqlens, alpha_given=True, **kw)
+
+
+def decode_steps(state, q, k, v, g, beta, *, scale=1.0, threads=0, alpha_given=False):
     """One recurrent step for every (n, h): q, k, g [N,H,dk]; v [N,H,dv];
     beta [N,H]; state fp64 [N,H,dk,dv].  Returns (o [N,H,dv], new state)."""
     N, H, dk = np.shape(q)
     dv = np.shape(v)[-1]
     o, sT = forward_arrays(np.reshape(q, (N, 1, H, dk)), np.reshape(k, (N, 1, H, dk)),
                            np.reshape(v, (N, 1, H, dv)), np.reshape(g, (N, 1, H, dk)),
-                           np.reshape(beta, (N, 1, H)), state, scale=scale, threads=threads)
+                           np.reshape(beta, (N, 1, H)), state, scale=scale, threads=threads, alpha_given=alpha_given)
     return o[:, 0], sT
 
 
@@ -195,9 +206,10 @@ def transition(alpha, beta, k):
     return (np.eye(d) - beta * np.outer(k, k)) @ np.diag(alpha)
 
 
-def product_form(q, k, v, g, beta, S0=None, *, scale=1.0, eps=EPS):
+def product_form(q, k, v, g, beta, S0=None, *, scale=1.0, eps=EPS, alpha_given=False):
     """One chain, explicit matrices: S_t = M_t S_{t-1} + beta_t k^_t v_t^T with
-    M_t = (I - beta_t k^_t k^_t^T) Diag(exp g_t); o_t = scale * S_t^T q^_t.
+    M_t = (I - beta_t k^_t k^_t^T) Diag(alpha_t), alpha_t = exp g_t (or g_t
+    itself with alpha_given); o_t = scale * S_t^T q^_t.
     q, k, g: [T, dk]; v: [T, dv]; beta: [T].  Returns (o [T, dv], S_T)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -211,7 +223,7 @@ def product_form(q, k, v, g, beta, S0=None, *, scale=1.0, eps=EPS):
     for t in range(T):
         qh = q[t] / np.sqrt(q[t] @ q[t] + eps)
         kh = k[t] / np.sqrt(k[t] @ k[t] + eps)
-        M = transition(np.exp(g[t]), beta[t], kh)
+        M = transition(g[t] if alpha_given else np.exp(g[t]), beta[t], kh)
         S = M @ S + beta[t] * np.outer(kh, v[t])
         o[t] = scale * (S.T @ qh)
     return o, S

@@ -34,6 +34,12 @@
  *   cu_seqlens (nullable): int32 [N+1]; when given, B must be 1 and chain n
  *   covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed axis.
  *
+ * kda_oracle_forward_signed is the same recurrence with the per-channel
+ * decay given directly as alpha (any sign) in place of g, for the Complex KDA
+ * range alpha in [-1, 1], beta in [0, 2] ("[논문리뷰] Complex KDA ..." page:
+ * the gate range widened to [-1, 1] and beta to [0, 2]; the transition is
+ * still (I - beta k^ k^T) Diag(alpha)).
+ *
  * Returns 0 on success, -1 on an invalid argument.
  */
 #include <math.h>
@@ -47,7 +53,7 @@
 #endif
 
 static void run_chain(int len, int H, int dk, int dv, size_t tok_stride_h,
-                      const float* q, const float* k, const float* v, const float* g,
+                      const float* q, const float* k, const float* v, const float* g, int alpha_given,
                       const float* beta, const double* s0, double scale, double eps,
                       int normalize, double* o, double* sT, double* S, double* work)
 {
@@ -74,9 +80,10 @@ static void run_chain(int len, int H, int dk, int dv, size_t tok_stride_h,
         const double rk = normalize ? 1.0 / sqrt(sk + eps) : 1.0;
         for (int i = 0; i < dk; ++i) { qh[i] = qt[i] * rq; kh[i] = kt[i] * rk; }
 
-        /* decay: row i of S (key channel i) scaled by alpha_i = exp(g_i) */
+        /* decay: row i of S (key channel i) scaled by alpha_i = exp(g_i),
+           or by the given signed alpha_i */
         for (int i = 0; i < dk; ++i) {
-            const double a = exp((double)gt[i]);
+            const double a = alpha_given ? (double)gt[i] : exp((double)gt[i]);
             double* Si = S + (size_t)i * dv;
             for (int j = 0; j < dv; ++j) Si[j] *= a;
         }
@@ -105,12 +112,12 @@ static void run_chain(int len, int H, int dk, int dv, size_t tok_stride_h,
     if (sT) memcpy(sT, S, nS * sizeof(double));
 }
 
-int kda_oracle_forward(int B, int T, int H, int dk, int dv,
-                       int num_seqs, const int32_t* cu_seqlens,
-                       const float* q, const float* k, const float* v,
-                       const float* g, const float* beta,
-                       const double* init_state, double scale, double eps, int normalize,
-                       double* o, double* final_state, int num_threads)
+static int forward(int B, int T, int H, int dk, int dv,
+                   int num_seqs, const int32_t* cu_seqlens,
+                   const float* q, const float* k, const float* v,
+                   const float* g, int alpha_given, const float* beta,
+                   const double* init_state, double scale, double eps, int normalize,
+                   double* o, double* final_state, int num_threads)
 {
     if (B <= 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     if (!q || !k || !v || !g || !beta) return -1;
@@ -149,7 +156,7 @@ int kda_oracle_forward(int B, int T, int H, int dk, int dv,
                 else            { tok0 = (size_t)n * T;         len = T; }
                 const size_t base = tok0 * H + h;   /* token-head index */
                 run_chain(len, H, dk, dv, (size_t)H,
-                          q + base * dk, k + base * dk, v + base * dv, g + base * dk, beta + base,
+                          q + base * dk, k + base * dk, v + base * dv, g + base * dk, alpha_given, beta + base,
                           init_state ? init_state + (size_t)c * nS : NULL,
                           scale, eps, normalize,
                           o ? o + base * dv : NULL,
@@ -160,6 +167,28 @@ int kda_oracle_forward(int B, int T, int H, int dk, int dv,
         free(work);
     }
     return ok ? 0 : -1;
+}
+
+int kda_oracle_forward(int B, int T, int H, int dk, int dv,
+                       int num_seqs, const int32_t* cu_seqlens,
+                       const float* q, const float* k, const float* v,
+                       const float* g, const float* beta,
+                       const double* init_state, double scale, double eps, int normalize,
+                       double* o, double* final_state, int num_threads)
+{
+    return forward(B, T, H, dk, dv, num_seqs, cu_seqlens, q, k, v, g, 0, beta, init_state, scale, eps,
+                   normalize, o, final_state, num_threads);
+}
+
+int kda_oracle_forward_signed(int B, int T, int H, int dk, int dv,
+                              int num_seqs, const int32_t* cu_seqlens,
+                              const float* q, const float* k, const float* v,
+                              const float* alpha, const float* beta,
+                              const double* init_state, double scale, double eps, int normalize,
+                              double* o, double* final_state, int num_threads)
+{
+    return forward(B, T, H, dk, dv, num_seqs, cu_seqlens, q, k, v, alpha, 1, beta, init_state, scale, eps,
+                   normalize, o, final_state, num_threads);
 }
 
 int kda_oracle_num_threads(void)

@@ -166,6 +166,7 @@ def test_gated_entry_points_reject_bad_arguments(lib):
     assert _call_gated(lib, d, dt_bias=FAKE + 4, ws=FAKE, ws_bytes=need) == 1
     assert _call_gated(lib, d, ws=None, ws_bytes=0) == 3                     # same workspace rule
     assert _call_gated(lib, _desc(flags=0x80)) == 2
+    assert _call_gated(lib, _desc(flags=kda.FLAG_QK_L2NORM | kda.FLAG_SIGNED_ALPHA), ws=FAKE, ws_bytes=need) == 2
     P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(9)]
 
     def step(z=P[3], a_log=P[4], flags=kda.FLAG_QK_L2NORM):

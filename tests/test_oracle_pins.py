@@ -457,3 +457,72 @@ def test_gated_generator_draws_raw_inputs():
     for name in ("q", "k", "v", "z", "A_log", "dt_bias", "beta_logits", "init_state"):
         np.testing.assert_array_equal(getattr(a, name), getattr(b, name))
     assert a.z.dtype == np.uint16 and a.beta_logits.min() < 0 < a.beta_logits.max()   # raw logits, not sigmoids
+
+
+# ---------------------------------------------------------------------------
+# Complex KDA: signed decay alpha in [-1, 1], beta in [0, 2] ("[논문리뷰]
+# Complex KDA ..." page: the gate range widened to [-1, 1] and beta to [0, 2];
+# one update (I - beta k k^T) Diag(alpha) stays diagonal-plus-rank-one and
+# non-expansive; Figure 1's 90 degree rotation).
+# ---------------------------------------------------------------------------
+def test_signed_oracle_runs_the_printed_rotation():
+    # Figure 1 through the C recurrence: one token with v = 0 maps S0 = I to
+    # the transition itself, the rotation by 90 degrees
+    with open(os.path.join(GOLDEN, "rotation_90.json")) as f:
+        ex = json.load(f)
+    q = np.array([[[[1.0, 0.0]]]], np.float32)
+    k = np.array([[[ex["k"]]]], np.float32)
+    v = np.zeros((1, 1, 1, 2), np.float32)
+    alpha = np.array([[[ex["alpha"]]]], np.float32)
+    beta = np.full((1, 1, 1), ex["beta"], np.float32)
+    _, sT = oracle.forward_signed(q, k, v, alpha, beta, np.eye(2)[None, None], eps=0.0)
+    np.testing.assert_allclose(sT[0, 0], np.array(ex["expected_transition"]), atol=1e-7)
+
+
+@pytest.mark.parametrize("d,T", [(2, 7), (3, 5), (8, 12)])
+def test_signed_oracle_matches_explicit_products(d, T):
+    rng = np.random.default_rng(100 + d)
+    q = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    k = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    v = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    alpha = rng.uniform(-1, 1, (1, T, 1, d)).astype(np.float32)
+    beta = rng.uniform(0, 2, (1, T, 1)).astype(np.float32)
+    s0 = rng.standard_normal((1, 1, d, d))
+    o, sT = oracle.forward_signed(q, k, v, alpha, beta, s0)
+    op, sp = oracle.product_form(q[0, :, 0], k[0, :, 0], v[0, :, 0], alpha[0, :, 0], beta[0, :, 0], s0[0, 0],
+                                 alpha_given=True)
+    np.testing.assert_allclose(o[0, :, 0], op, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sT[0, 0], sp, rtol=1e-12, atol=1e-12)
+
+
+def test_signed_transitions_are_non_expansive_and_orthogonal_at_the_ends():
+    rng = np.random.default_rng(7)
+    d, T = 6, 40
+    q = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    k = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    v = np.zeros((1, T, 1, d), np.float32)
+    s0 = rng.standard_normal((1, 1, d, d))
+    # |alpha| <= 1, beta in [0, 2]: ||S_t||_F never grows (v = 0)
+    alpha = rng.uniform(-1, 1, (1, T, 1, d)).astype(np.float32)
+    beta = rng.uniform(0, 2, (1, T, 1)).astype(np.float32)
+    norms = [np.linalg.norm(s0)]
+    for t in range(1, T + 1):
+        _, s = oracle.forward_signed(q[:, :t], k[:, :t], v[:, :t], alpha[:, :t], beta[:, :t], s0, eps=0.0)
+        norms.append(np.linalg.norm(s))
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(norms, norms[1:]))
+    # alpha in {-1, +1} and beta = 2: a reflection times a signed permutation-free
+    # diagonal is orthogonal, so the norm is kept exactly
+    alpha = np.where(rng.uniform(size=(1, T, 1, d)) < 0.5, -1.0, 1.0).astype(np.float32)
+    beta = np.full((1, T, 1), 2.0, np.float32)
+    _, s = oracle.forward_signed(q, k, v, alpha, beta, s0, eps=0.0)
+    assert abs(np.linalg.norm(s) / np.linalg.norm(s0) - 1.0) < 1e-5
+
+
+def test_signed_oracle_with_positive_alpha_is_the_log_oracle():
+    inp = kda_inputs.make_prefill(3, 1, 90, 2, 8, 8, dtype="f32", s0_std=0.1)
+    o1, s1 = oracle.forward_arrays(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.init_state)
+    alpha = np.exp(inp.g.astype(np.float64)).astype(np.float32)
+    o2, s2 = oracle.forward_signed(inp.q, inp.k, inp.v, alpha, inp.beta, inp.init_state)
+    # alpha rounded to fp32 once: agreement to fp32 rounding of the decay
+    np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(s2, s1, rtol=1e-5, atol=1e-6)
