@@ -107,7 +107,13 @@ def time_prefill(kda, torch, d, steps, warmup):
     return total_ms, launches, wall
 
 
-def time_decode(kda, torch, kda_inputs):
+def _dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def time_decode(kda, torch, kda_inputs, norm=False):
     w = kda_inputs.DECODE_WORKLOAD
     S0 = kda_inputs.decode_initial_state(w["seed"], DEC_N, DEC_H, D, w["s0_std"])
     state = torch.from_numpy(S0).cuda()
@@ -115,33 +121,39 @@ def time_decode(kda, torch, kda_inputs):
     xs = []
     for s in range(8):  # 8 distinct seeded step inputs, cycled over the 128 steps
         x = kda_inputs.decode_step(w["seed"], s, DEC_N, DEC_H, D)
-        xs.append(tuple(torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-                        if a.dtype == np.uint16 else torch.from_numpy(a).cuda()
-                        for a in (x.q, x.k, x.v, x.g, x.beta)))
+        xs.append(tuple(_dev(torch, a) for a in (x.q, x.k, x.v, x.g, x.beta)))
+    kws = [{}] * 8
+    if norm:
+        wt = _dev(torch, kda_inputs.norm_weight(w["seed"], D))
+        kws = [dict(out_gate=_dev(torch, kda_inputs.make_out_gate(w["seed"] + s, (DEC_N, DEC_H, D))),
+                    norm_weight=wt, norm_eps=1e-5) for s in range(8)]
     o = torch.empty((DEC_N, DEC_H, D), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     for s in range(4):
-        kda.recurrent_step(*xs[s % 8], state, o=o)
+        kda.recurrent_step(*xs[s % 8], state, o=o, **kws[s % 8])
     torch.cuda.synchronize()
     evs = []
     for s in range(DEC_STEPS):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        kda.recurrent_step(*xs[s % 8], state, o=o)
+        kda.recurrent_step(*xs[s % 8], state, o=o, **kws[s % 8])
         e1.record(stream)
         evs.append((e0, e1))
     torch.cuda.synchronize()
     us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     med = float(np.median(us))
-    bytes_step = DEC_BYTES_PER_CHAIN * DEC_N * DEC_H
+    bytes_step = (DEC_BYTES_PER_CHAIN + (2 * D if norm else 0)) * DEC_N * DEC_H
     gbs = bytes_step / (med * 1e-6) / 1e9
-    return {
-        "workload": "decode N=256 H=96 d_k=d_v=128, bf16 q/k/v/o, fp32 g/beta/state in place, 128 steps",
+    line = {
+        "workload": "decode N=256 H=96 d_k=d_v=128, bf16 q/k/v/o, fp32 g/beta/state in place, 128 steps" +
+                    (", output norm fused (bf16 gate logits, fp32 gain)" if norm else ""),
         "us_per_step_median": med, "us_per_step_min": float(us.min()), "us_per_step_max": float(us.max()),
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic("decode"),
-                     "bytes_per_launch": bytes_step},
+                     "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_step},
     }
+    if not norm:
+        line["roofline"]["traffic"] = load_traffic("decode")
+    return line
 
 
 def cpu_baseline(inp_full, heads, tokens):
@@ -317,21 +329,13 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
 
 # gated prefill: bf16 decay logits z replace fp32 g (2 d instead of 4 d bytes), beta as fp32 logits
 BYTES_PER_TOKEN_HEAD_GATED = 2 * (2 * D + 2 * D) + 2 * D + 4
+# ... plus the output norm's bf16 gate logits (the gain is d_v floats per call)
+BYTES_PER_TOKEN_HEAD_LAYER = BYTES_PER_TOKEN_HEAD_GATED + 2 * D
 
 
-def time_gated(kda, torch, kda_inputs, reps=20, warm=5):
-    """The headline shape through kda_chunk_fwd_gated (gate map and beta
-    sigmoid in the kernel), same seed as the headline workload."""
-    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
-    gi = kda_inputs.make_gated_prefill(2, B, T, H, D, D, s0_std=0.02)
-    d = {f: to(getattr(gi, f)) for f in ("q", "k", "v", "z", "A_log", "dt_bias", "beta_logits", "init_state")}
-    del gi
-    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
-    sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
-    call = lambda: kda.chunk_fwd_gated(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta_logits"], d["init_state"],
-                                       dt_bias=d["dt_bias"], beta_logits=True, o=o, final_state=sT, workspace=ws)
+def _time_calls(torch, call, reps, warm):
+    """Per-call HIP-event times (ms) on torch's current stream, which the
+    binding launches on."""
     for _ in range(warm):
         call()
     torch.cuda.synchronize()
@@ -343,52 +347,62 @@ def time_gated(kda, torch, kda_inputs, reps=20, warm=5):
         e1.record()
         e1.synchronize()
         ts.append(e0.elapsed_time(e1))
+    return ts
+
+
+def _line(workload, ts, algo):
     ms = float(np.median(ts))
-    algo = BYTES_PER_TOKEN_HEAD_GATED * B * T * H + 2 * STATE_BYTES * B * H
-    del d, o, sT, ws
-    torch.cuda.empty_cache()
-    return {"workload": "long prefill B=1 H=96 T=65536 d=128 via the gated entry point: bf16 decay logits z, "
-                        "A_log, dt_bias, beta logits (seed 2)",
-            "ms_median": ms, "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)),
+    return {"workload": workload, "ms_median": ms, "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)),
             "tokens_per_s": B * T / (ms * 1e-3), "bytes_per_launch": algo,
             "roofline": {"bound": "hbm", "achieved": algo / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
+def time_gated(kda, torch, kda_inputs, reps=20, warm=5, norm=False):
+    """The headline shape through the gated entry point (gate map and beta
+    sigmoid in the kernel), same seed as the headline workload; with norm,
+    also the output norm at the store of o (the fused layer core)."""
+    gi = kda_inputs.make_gated_prefill(2, B, T, H, D, D, s0_std=0.02)
+    d = {f: _dev(torch, getattr(gi, f)) for f in ("q", "k", "v", "z", "A_log", "dt_bias", "beta_logits",
+                                                  "init_state")}
+    del gi
+    kw = {}
+    if norm:
+        kw = dict(out_gate=_dev(torch, kda_inputs.make_out_gate(2, (B, T, H, D))),
+                  norm_weight=_dev(torch, kda_inputs.norm_weight(2, D)), norm_eps=1e-5)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D, flags=kda.FLAG_QK_L2NORM | kda.FLAG_BETA_LOGITS |
+                                         (kda.FLAG_OUT_NORM if norm else 0)), dtype=torch.uint8, device="cuda")
+    call = lambda: kda.chunk_fwd_gated(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta_logits"], d["init_state"],
+                                       dt_bias=d["dt_bias"], beta_logits=True, o=o, final_state=sT, workspace=ws, **kw)
+    ts = _time_calls(torch, call, reps, warm)
+    del d, o, sT, ws, kw
+    torch.cuda.empty_cache()
+    if norm:
+        return _line("long prefill B=1 H=96 T=65536 d=128, gated entry point with the output norm fused: bf16 decay "
+                     "logits z, A_log, dt_bias, beta logits, bf16 output-gate logits, fp32 gain (seed 2)",
+                     ts, BYTES_PER_TOKEN_HEAD_LAYER * B * T * H + 2 * STATE_BYTES * B * H + 4 * D)
+    return _line("long prefill B=1 H=96 T=65536 d=128 via the gated entry point: bf16 decay logits z, A_log, "
+                 "dt_bias, beta logits (seed 2)", ts, BYTES_PER_TOKEN_HEAD_GATED * B * T * H + 2 * STATE_BYTES * B * H)
+
+
 def time_signed(kda, torch, kda_inputs, reps=20, warm=5):
     """The headline shape as Complex KDA (KDA_FLAG_SIGNED_ALPHA): signed
     decay alpha (a quarter of the entries negative), beta in (0, 2)."""
-    to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
-                    if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
     si = kda_inputs.make_signed_prefill(2, B, T, H, D, D, s0_std=0.02)
-    d = {f: to(getattr(si, f)) for f in ("q", "k", "v", "g", "beta", "init_state")}
+    d = {f: _dev(torch, getattr(si, f)) for f in ("q", "k", "v", "g", "beta", "init_state")}
     del si
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     ws = torch.empty(kda.workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
     call = lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["init_state"], signed_alpha=True,
                                  o=o, final_state=sT, workspace=ws)
-    for _ in range(warm):
-        call()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        e1.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ms = float(np.median(ts))
-    algo = BYTES_PER_TOKEN_HEAD * B * T * H + 2 * STATE_BYTES * B * H
+    ts = _time_calls(torch, call, reps, warm)
     del d, o, sT, ws
     torch.cuda.empty_cache()
-    return {"workload": "long prefill B=1 H=96 T=65536 d=128 as Complex KDA: signed alpha (25 % negative, "
-                        "|alpha| >= e^-5), beta in (0, 2) (seed 2)",
-            "ms_median": ms, "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)),
-            "tokens_per_s": B * T / (ms * 1e-3), "bytes_per_launch": algo,
-            "roofline": {"bound": "hbm", "achieved": algo / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    return _line("long prefill B=1 H=96 T=65536 d=128 as Complex KDA: signed alpha (25 % negative, |alpha| >= e^-5), "
+                 "beta in (0, 2) (seed 2)", ts, BYTES_PER_TOKEN_HEAD * B * T * H + 2 * STATE_BYTES * B * H)
 
 
 def main():
@@ -446,12 +460,15 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = time_decode(kda, torch, kda_inputs)
+        if not args.no_extra:
+            out["decode_out_norm"] = time_decode(kda, torch, kda_inputs, norm=True)
     if not args.no_extra:
         out["prefill_mid"] = dict(workload="B=1 H=32 T=4096 d=128 bf16, seed 1; two input sets rotated",
                                   **time_workload(kda, torch, kda_inputs, "mid_bf16", sets=2))
         out["prefill_varlen"] = dict(workload="16 packed sequences, lengths U[512,16384] from seed 3, H=32 d=128 bf16",
                                      **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1))
         out["prefill_gated"] = time_gated(kda, torch, kda_inputs)
+        out["prefill_gated_out_norm"] = time_gated(kda, torch, kda_inputs, norm=True)
         out["prefill_complex_kda"] = time_signed(kda, torch, kda_inputs)
     # the copy also calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE (see --traffic-from)
     out["copy_kernel"] = copy_bandwidth(torch)

@@ -13,6 +13,11 @@ built, importing the library raises.
       -> (o, final_state)                       [kda_chunk_fwd_gated]
   recurrent_step_gated(q, k, v, z, A_log, beta, state, ..., dt_bias=None)
       -> o                                      [kda_recurrent_step_gated]
+
+Each of them takes ``out_gate=`` (with ``norm_weight=``, ``norm_eps=``) to
+fuse the output norm o <- RMSNorm(o) * norm_weight * sigmoid(out_gate) at the
+store of o; such calls go through kda_chunk_fwd_fused /
+kda_recurrent_step_fused.
 """
 from __future__ import annotations
 
@@ -21,7 +26,7 @@ import os
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_gated", "recurrent_step_gated", "workspace_bytes", "lib_path",
            "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS",
-           "FLAG_SIGNED_ALPHA", "STATUS"]
+           "FLAG_SIGNED_ALPHA", "FLAG_OUT_NORM", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -31,6 +36,7 @@ FLAG_VALIDATE = 0x2
 FLAG_FP32_PATH = 0x4
 FLAG_BETA_LOGITS = 0x8
 FLAG_SIGNED_ALPHA = 0x10
+FLAG_OUT_NORM = 0x20
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_RANGE", 5: "KDA_ERR_HIP"}
@@ -46,6 +52,14 @@ class ChunkDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int),
                 ("d_v", ctypes.c_int), ("num_seqs", ctypes.c_int), ("in_dtype", ctypes.c_int),
                 ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float), ("flags", ctypes.c_uint)]
+
+
+class DecayGate(ctypes.Structure):
+    _fields_ = [("z", ctypes.c_void_p), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+class OutNorm(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 _lib = None
@@ -75,6 +89,12 @@ def load():
     lib.kda_chunk_fwd_gated.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 11 + [P, S, P]
     lib.kda_recurrent_step_gated.restype = I
     lib.kda_recurrent_step_gated.argtypes = [I, I, I, I, I, I, F, U] + [P] * 9 + [P]
+    lib.kda_chunk_fwd_fused.restype = I
+    lib.kda_chunk_fwd_fused.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 4 + [ctypes.POINTER(DecayGate)] + \
+        [P] * 3 + [ctypes.POINTER(OutNorm)] + [P, P, P, S, P]
+    lib.kda_recurrent_step_fused.restype = I
+    lib.kda_recurrent_step_fused.argtypes = [I, I, I, I, I, I, F, U] + [P] * 4 + [ctypes.POINTER(DecayGate), P,
+                                                                                  ctypes.POINTER(OutNorm), P, P, P]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_status_str.argtypes = [I]
     lib.kda_last_hip_error.restype = I
@@ -144,28 +164,47 @@ def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True,
 
 def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
               normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False,
-              signed_alpha=False, o=None, final_state=None, workspace=None, stream=None):
+              signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, final_state=None,
+              workspace=None, stream=None):
     """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
     beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
     [N+1] device tensor or None (then N = B).  With signed_alpha (Complex KDA)
     g holds the signed decay alpha in [-1, 1] and beta may lie in [0, 2].
-    Returns (o, final_state)."""
+    out_gate ([B,T,H,d_v], q's dtype) fuses the output norm, with norm_weight
+    ([d_v] fp32 or None) and norm_eps.  Returns (o, final_state)."""
     return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
-                  validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha)
+                  validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha,
+                  (out_gate, norm_weight, norm_eps))
 
 
 def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *, dt_bias=None, out_dtype=None,
                     scale=1.0, normalize=True, output_final_state=True, validate=False, fp32_path=False,
-                    beta_logits=False, o=None, final_state=None, workspace=None, stream=None):
+                    beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, final_state=None,
+                    workspace=None, stream=None):
     """As chunk_fwd, with g = -5 sigmoid(exp(A_log[h]) (z + dt_bias[h, c]))
     computed in the kernel: z [B,T,H,d_k] in q's dtype, A_log [H] fp32,
     dt_bias [H,d_k] fp32 or None."""
     return _chunk(q, k, v, None, (z, A_log, dt_bias), beta, init_state, cu_seqlens, out_dtype, scale, normalize,
-                  output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, stream)
+                  output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, stream, False,
+                  (out_gate, norm_weight, norm_eps))
+
+
+def _norm_args(norm, o_shape, in_dtype, dv):
+    """Checks the output-norm tensors; returns an OutNorm or None."""
+    torch = _torch()
+    out_gate, weight, eps = norm if norm is not None else (None, None, 0.0)
+    if out_gate is None:
+        if weight is not None:
+            raise ValueError("norm_weight needs out_gate")
+        return None
+    _need(out_gate, "out_gate", in_dtype, o_shape)
+    if weight is not None:
+        _need(weight, "norm_weight", torch.float32, (dv,))
+    return OutNorm(out_gate.data_ptr(), None if weight is None else weight.data_ptr(), float(eps))
 
 
 def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
-           validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False):
+           validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False, norm=None):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -196,16 +235,23 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    on = _norm_args(norm, (B, T, H, dv), q.dtype, dv)
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_VALIDATE if validate else 0) | \
         (FLAG_FP32_PATH if fp32_path else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
-        (FLAG_SIGNED_ALPHA if signed_alpha else 0)
+        (FLAG_SIGNED_ALPHA if signed_alpha else 0) | (FLAG_OUT_NORM if on is not None else 0)
     d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(out_dtype),
               scale, flags)
     ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
     if ws > 0 and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
-    if gate is None:
+    if on is not None:
+        dg = None if gate is None else ctypes.byref(DecayGate(z.data_ptr(), A_log.data_ptr(),
+                                                              None if dt_bias is None else dt_bias.data_ptr()))
+        st = lib.kda_chunk_fwd_fused(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), dg, _ptr(beta),
+                                     _ptr(init_state), _ptr(cu_seqlens), ctypes.byref(on), _ptr(o),
+                                     _ptr(final_state), _ptr(workspace), wsb, _stream(stream))
+    elif gate is None:
         st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
                                _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace), wsb, _stream(stream))
     else:
@@ -217,21 +263,25 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
 
 
 def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, beta_logits=False,
-                   signed_alpha=False, o=None, stream=None):
+                   signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, stream=None):
     """One fused decode step.  q, k, g: [N,H,d_k]; v: [N,H,d_v]; beta: [N,H];
     state: [N,H,d_k,d_v] fp32, updated in place.  With signed_alpha g holds
-    the signed decay alpha.  Returns o [N,H,d_v]."""
-    return _step(q, k, v, g, None, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha)
+    the signed decay alpha.  out_gate [N,H,d_v] fuses the output norm.
+    Returns o [N,H,d_v]."""
+    return _step(q, k, v, g, None, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha,
+                 (out_gate, norm_weight, norm_eps))
 
 
 def recurrent_step_gated(q, k, v, z, A_log, beta, state, *, dt_bias=None, out_dtype=None, scale=1.0, normalize=True,
-                         beta_logits=False, o=None, stream=None):
+                         beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, stream=None):
     """As recurrent_step, with g computed in the kernel from z [N,H,d_k],
     A_log [H] and dt_bias [H,d_k] (or None)."""
-    return _step(q, k, v, None, (z, A_log, dt_bias), beta, state, out_dtype, scale, normalize, beta_logits, o, stream)
+    return _step(q, k, v, None, (z, A_log, dt_bias), beta, state, out_dtype, scale, normalize, beta_logits, o, stream,
+                 False, (out_gate, norm_weight, norm_eps))
 
 
-def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha=False):
+def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha=False,
+          norm=None):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -253,9 +303,16 @@ def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logit
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
     _need(o, "o", out_dtype, (N, H, dv))
+    on = _norm_args(norm, (N, H, dv), q.dtype, dv)
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
-        (FLAG_SIGNED_ALPHA if signed_alpha else 0)
-    if gate is None:
+        (FLAG_SIGNED_ALPHA if signed_alpha else 0) | (FLAG_OUT_NORM if on is not None else 0)
+    if on is not None:
+        dg = None if gate is None else ctypes.byref(DecayGate(z.data_ptr(), A_log.data_ptr(),
+                                                              None if dt_bias is None else dt_bias.data_ptr()))
+        st = lib.kda_recurrent_step_fused(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale),
+                                          flags, _ptr(q), _ptr(k), _ptr(v), _ptr(g), dg, _ptr(beta), ctypes.byref(on),
+                                          _ptr(state), _ptr(o), _stream(stream))
+    elif gate is None:
         st = lib.kda_recurrent_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale), flags,
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
                                     _stream(stream))

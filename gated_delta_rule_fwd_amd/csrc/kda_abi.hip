@@ -15,8 +15,9 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 bool dtype_ok(kda_dtype t) { return t == KDA_F32 || t == KDA_BF16; }
 
-constexpr unsigned kKnownFlags =
-    KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH | KDA_FLAG_BETA_LOGITS | KDA_FLAG_SIGNED_ALPHA;
+constexpr unsigned kKnownFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FLAG_FP32_PATH | KDA_FLAG_BETA_LOGITS |
+                                 KDA_FLAG_SIGNED_ALPHA | KDA_FLAG_OUT_NORM;
+constexpr unsigned kDecodeFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_LOGITS | KDA_FLAG_SIGNED_ALPHA | KDA_FLAG_OUT_NORM;
 constexpr size_t kValidateBytes = 256;
 
 kda_status hip_fail(hipError_t e)
@@ -55,12 +56,27 @@ bool uses_two_pass(const kda_chunk_desc* d)
     return d->in_dtype == KDA_BF16 && d->d_k == 128 && d->d_v == 128 && !(d->flags & KDA_FLAG_FP32_PATH);
 }
 
-// Workspace of one call: validation counters first, then the records.
+// Workspace of one call: validation counters first, then the records (matrix
+// core path) or the fp32 path's temporary output (output norm only).
 size_t workspace_need(const kda_chunk_desc* d, bool packed)
 {
     size_t bytes = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
-    if (uses_two_pass(d)) bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed);
+    if (uses_two_pass(d))
+        bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed);
+    else if (d->flags & KDA_FLAG_OUT_NORM)
+        bytes += static_cast<size_t>(d->B) * d->T * d->H * d->d_v * sizeof(float);
     return bytes;
+}
+
+// Checks shared by the prefill and decode entry points for the output norm.
+bool out_norm_ok(const kda_out_norm* norm, unsigned flags, const void* o)
+{
+    if (!norm) return !(flags & KDA_FLAG_OUT_NORM);
+    if (!(flags & KDA_FLAG_OUT_NORM)) return false;
+    if (!(norm->eps >= 0.f) || norm->eps > 3.0e38f) return false;   // rejects NaN and inf too
+    if (norm->gate && (!aligned16(norm->gate) || norm->gate == o)) return false;
+    if (norm->weight && !aligned16(norm->weight)) return false;
+    return true;
 }
 
 }  // namespace
@@ -88,7 +104,8 @@ struct Gate {
 
 kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const float* g,
                           const Gate* gate, const float* beta, const float* init_state, const int32_t* cu_seqlens,
-                          void* o, float* final_state, void* workspace, size_t ws_bytes, hipStream_t stream)
+                          const kda_out_norm* norm, void* o, float* final_state, void* workspace, size_t ws_bytes,
+                          hipStream_t stream)
 {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
@@ -104,6 +121,8 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     const void* decay = gate ? gate->z : static_cast<const void*>(g);
     if (tokens > 0 && (!q || !k || !v || !decay || !beta || !o)) return KDA_ERR_INVALID_ARG;
     if (gate && tokens > 0 && !gate->A_log) return KDA_ERR_INVALID_ARG;
+    if (!out_norm_ok(norm, d->flags, o)) return KDA_ERR_INVALID_ARG;
+    if (norm && tokens > 0 && !norm->gate) return KDA_ERR_INVALID_ARG;
     const void* rows[] = {q, k, v, decay, init_state, o, final_state, gate ? gate->dt_bias : nullptr};
     for (const void* p : rows)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
@@ -142,6 +161,10 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     a.dt_bias = gate ? gate->dt_bias : nullptr;
     a.beta_logits = (d->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
     a.signed_alpha = (d->flags & KDA_FLAG_SIGNED_ALPHA) ? 1 : 0;
+    a.out_norm = norm ? 1 : 0;
+    a.out_gate = norm ? norm->gate : nullptr;
+    a.norm_w = norm ? norm->weight : nullptr;
+    a.norm_eps = norm ? norm->eps : 0.f;
 
     hipError_t e;
     if (d->flags & KDA_FLAG_VALIDATE) {
@@ -156,27 +179,30 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
         if (host[0] || host[1] || host[2]) return KDA_ERR_RANGE;
     }
 
-    if (uses_two_pass(d)) {
-        const size_t off = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+    const size_t off = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+    if (uses_two_pass(d))
         e = kda::launch_chunk_two_pass(a, static_cast<char*>(workspace) + off, stream);
-    } else {
-        e = kda::launch_chunk_fp32(a, stream);
-    }
+    else
+        e = kda::launch_chunk_fp32(a, norm ? reinterpret_cast<float*>(static_cast<char*>(workspace) + off) : nullptr,
+                                   stream);
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;
 }
 
 kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
                                unsigned flags, const void* q, const void* k, const void* v, const float* g,
-                               const Gate* gate, const float* beta, float* state, void* o, hipStream_t stream)
+                               const Gate* gate, const float* beta, const kda_out_norm* norm, float* state, void* o,
+                               hipStream_t stream)
 {
-    if (flags & ~(KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_LOGITS | KDA_FLAG_SIGNED_ALPHA)) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~kDecodeFlags) return KDA_ERR_UNSUPPORTED;
     if (gate && (flags & KDA_FLAG_SIGNED_ALPHA)) return KDA_ERR_UNSUPPORTED;
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
     if (static_cast<long long>(N) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (!out_norm_ok(norm, flags, o)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
+    if (norm && !norm->gate) return KDA_ERR_INVALID_ARG;
     const void* decay = gate ? gate->z : static_cast<const void*>(g);
     if (!q || !k || !v || !decay || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
     if (gate && !gate->A_log) return KDA_ERR_INVALID_ARG;
@@ -207,6 +233,10 @@ kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtyp
     a.dt_bias = gate ? gate->dt_bias : nullptr;
     a.beta_logits = (flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
     a.signed_alpha = (flags & KDA_FLAG_SIGNED_ALPHA) ? 1 : 0;
+    a.out_norm = norm ? 1 : 0;
+    a.out_gate = norm ? norm->gate : nullptr;
+    a.norm_w = norm ? norm->weight : nullptr;
+    a.norm_eps = norm ? norm->eps : 0.f;
     hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;
@@ -220,8 +250,8 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
                          const float* beta, const float* init_state, const int32_t* cu_seqlens, void* o,
                          float* final_state, void* workspace, size_t ws_bytes, hipStream_t stream)
 {
-    return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, o, final_state, workspace, ws_bytes,
-                          stream);
+    return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, nullptr, o, final_state, workspace,
+                          ws_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_gated(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const void* z,
@@ -230,7 +260,21 @@ kda_status kda_chunk_fwd_gated(const kda_chunk_desc* d, const void* q, const voi
                                size_t ws_bytes, hipStream_t stream)
 {
     const Gate gate{z, A_log, dt_bias};
-    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, o, final_state, workspace,
+    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, nullptr, o, final_state, workspace,
+                          ws_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_fused(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const float* g,
+                               const kda_decay_gate* decay_gate, const float* beta, const float* init_state,
+                               const int32_t* cu_seqlens, const kda_out_norm* norm, void* o, float* final_state,
+                               void* workspace, size_t ws_bytes, hipStream_t stream)
+{
+    if (decay_gate && g) return KDA_ERR_INVALID_ARG;
+    if (!decay_gate)
+        return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, norm, o, final_state, workspace,
+                              ws_bytes, stream);
+    const Gate gate{decay_gate->z, decay_gate->A_log, decay_gate->dt_bias};
+    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, norm, o, final_state, workspace,
                           ws_bytes, stream);
 }
 
@@ -238,8 +282,8 @@ kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype
                               float scale, unsigned flags, const void* q, const void* k, const void* v,
                               const float* g, const float* beta, float* state, void* o, hipStream_t stream)
 {
-    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, state, o,
-                               stream);
+    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, nullptr,
+                               state, o, stream);
 }
 
 kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
@@ -249,6 +293,20 @@ kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v, kda_dtype in
 {
     const Gate gate{z, A_log, dt_bias};
     return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, nullptr, &gate, beta,
+                               nullptr, state, o, stream);
+}
+
+kda_status kda_recurrent_step_fused(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
+                                    float scale, unsigned flags, const void* q, const void* k, const void* v,
+                                    const float* g, const kda_decay_gate* decay_gate, const float* beta,
+                                    const kda_out_norm* norm, float* state, void* o, hipStream_t stream)
+{
+    if (decay_gate && g) return KDA_ERR_INVALID_ARG;
+    if (!decay_gate)
+        return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, norm,
+                                   state, o, stream);
+    const Gate gate{decay_gate->z, decay_gate->A_log, decay_gate->dt_bias};
+    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, nullptr, &gate, beta, norm,
                                state, o, stream);
 }
 

@@ -53,10 +53,13 @@ namespace {
 
 using namespace mfma;
 
-constexpr int DVS = 64;     // value columns per pass-2 workgroup: 4 waves x 16
-constexpr int NSLICE = DV / DVS;
-
 static_assert(sizeof(ChunkRecord) == kChunkRecordBytes, "ChunkRecord layout");
+
+#ifndef KDA_PLAIN_SCAN_WAVES
+#define KDA_PLAIN_SCAN_WAVES 4
+#endif
+// waves per pass-2 workgroup without the output norm (4: two workgroups per chain)
+constexpr int kPlainScanWaves = KDA_PLAIN_SCAN_WAVES;
 
 // ---------------------------------------------------------------------------
 // Pass 1: chunk-local operands
@@ -632,6 +635,8 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 // Pass 2: the state recurrence over the records
 // ---------------------------------------------------------------------------
 
+// Pass-2 workgroups of NW waves own 16 * NW value columns each.
+template <int DVS>
 struct alignas(16) ScanSmem {
     ChunkRecord r;                   // this chunk's operands
     __bf16 vs[C][DVS];               // V slice, plain [token][column]
@@ -639,31 +644,47 @@ struct alignas(16) ScanSmem {
 };
 
 // output tile staging; bf16 is rounded to nearest even by the hardware conversion
+template <int DVS>
 __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const float*)
 {
     base[r * DVS + c] = x;
 }
+template <int DVS>
 __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const uint16_t*)
 {
     reinterpret_cast<uint16_t*>(base)[r * DVS + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-template <typename Tout>
-__global__ void __launch_bounds__(NT, 1)
+__device__ __forceinline__ float bf16_bits_to_f32(unsigned int bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// NW = 4: two workgroups per chain (64 columns each); NW = 8: one workgroup
+// per chain holding all 128 columns (two waves per SIMD), which the output
+// norm needs since it reduces over a whole row of o.
+template <typename Tout, int NW, bool NORM>
+__global__ void __launch_bounds__(64 * NW, 1)
 chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
 {
-    __shared__ ScanSmem s;
+    constexpr int NTS = 64 * NW;
+    constexpr int DVS = 16 * NW;
+    constexpr int NSLICE = DV / DVS;
+    static_assert(NSLICE == 1 || NSLICE == 2, "pass-2 slicing");
+    static_assert(!NORM || NSLICE == 1, "the output norm needs whole rows");
+    using Tstage = typename std::conditional<NORM, float, Tout>::type;
+    __shared__ ScanSmem<DVS> s;
 
     const int t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l = t & 63, g = l >> 4, n = l & 15;
     const int H = a.H;
-    // Workgroup -> (chain, slice).  Both slices of a chain get ids that are
-    // equal mod 8, so they are dispatched to the same XCD and the second read
-    // of each record hits that XCD's L2.
+    // Workgroup -> (chain, slice).  With two slices, both slices of a chain
+    // get ids that are equal mod 8, so they are dispatched to the same XCD
+    // and the second read of each record hits that XCD's L2.
     const int bid = blockIdx.x;
-    const int slice = (bid >> 3) & (NSLICE - 1);
-    const int chain = ((bid >> 4) << 3) | (bid & 7);
+    const int slice = NSLICE == 1 ? 0 : (bid >> 3) & 1;
+    const int chain = NSLICE == 1 ? bid : (((bid >> 4) << 3) | (bid & 7));
     const int nchains = (a.cu_seqlens ? a.num_seqs : a.B) * H;
     if (chain >= nchains) return;
     const int j0 = slice * DVS;
@@ -703,8 +724,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     // current chunk is computed (issued in pieces between the compute steps
     // so the loads overlap them), then go to LDS between two barriers.
     constexpr int RV = static_cast<int>(sizeof(ChunkRecord) / 16);
-    constexpr int RFULL = RV / NT;
-    constexpr int RTAIL = RV - RFULL * NT;
+    constexpr int RFULL = RV / NTS;
+    constexpr int RTAIL = RV - RFULL * NTS;
+    constexpr int PPR = DVS / 8;                   // 16-byte pieces per V row
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 P[RFULL + 1], PV[2];
     // record pieces i in [i0, i1) of chunk j; piece RFULL is the partial one
@@ -713,16 +735,16 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
             if (i < RFULL)
-                P[i] = src[t + NT * i];
+                P[i] = src[t + NTS * i];
             else if (t < RTAIL)
-                P[i] = src[t + NT * i];
+                P[i] = src[t + NTS * i];
         }
     };
     auto fetch_v = [&](int j) __attribute__((always_inline)) {
         const long cb = tok0 + static_cast<long>(j) * C;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int idx = t + NT * u, r = idx >> 3, part = idx & 7;
+            const int idx = t + NTS * u, r = idx / PPR, part = idx % PPR;
             // rows past the end read the last valid token: T' has zero
             // columns for them, so only finiteness matters
             const long tk = min(cb + r, tok1 - 1);
@@ -732,11 +754,11 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     auto commit = [&]() __attribute__((always_inline)) {
         u32x4* dst = reinterpret_cast<u32x4*>(&s.r);
 #pragma unroll
-        for (int i = 0; i < RFULL; ++i) dst[t + NT * i] = P[i];
-        if (t < RTAIL) dst[t + NT * RFULL] = P[RFULL];
+        for (int i = 0; i < RFULL; ++i) dst[t + NTS * i] = P[i];
+        if (t < RTAIL) dst[t + NTS * RFULL] = P[RFULL];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int idx = t + NT * u, r = idx >> 3, part = idx & 7;
+            const int idx = t + NTS * u, r = idx / PPR, part = idx % PPR;
             *reinterpret_cast<u32x4*>(&s.vs[r][8 * part]) = PV[u];
         }
     };
@@ -755,13 +777,82 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         constexpr int PER_ROW = DVS / CH;
         const char* src = reinterpret_cast<const char*>(s.obuf[buf]);
 #pragma unroll
-        for (int pc = t; pc < C * PER_ROW; pc += NT) {
+        for (int pc = t; pc < C * PER_ROW; pc += NTS) {
             const int r = pc / PER_ROW, part = pc % PER_ROW;
             if (r < rows) {
                 const uint4 val = *reinterpret_cast<const uint4*>(src + (r * DVS + part * CH) * sizeof(Tout));
                 *reinterpret_cast<uint4*>(op + (static_cast<size_t>(cbase + r) * H + h) * DV + j0 + part * CH) = val;
             }
         }
+    };
+    // Output norm ("Kimi K3 の KDA ..." section 1.2.1, the gated RMSNorm after
+    // the kernel): o <- o / sqrt(mean_c o_c^2 + eps) * w_c * sigmoid(gate_c)
+    // over the d_v columns of one (token, head).  Thread t owns row t / 8 and
+    // columns 4 (t % 8 + 8 i) .. + 3, i < 4, so the 8 threads of a row read
+    // 128 contiguous bytes of the staged tile per step; the gate of chunk j
+    // is loaded during chunk j and used when its tile is stored.
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int nr = t >> 3, np = t & 7;
+    u32x2 G[4];
+    float4 WR[4];
+    if constexpr (NORM) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            WR[i] = a.norm_w ? *reinterpret_cast<const float4*>(a.norm_w + 4 * (np + 8 * i))
+                             : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+    auto fetch_gate = [&](long cbase) __attribute__((always_inline)) {
+        if constexpr (NORM) {
+            const long tk = min(cbase + nr, tok1 - 1);
+            const uint16_t* gp = static_cast<const uint16_t*>(a.out_gate) + (static_cast<size_t>(tk) * H + h) * DV;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[i] = *reinterpret_cast<const u32x2*>(gp + 4 * (np + 8 * i));
+        }
+    };
+    auto store_tile_norm = [&](int buf, long cbase, int rows) __attribute__((always_inline)) {
+        if constexpr (NORM) {
+            const float* src = s.obuf[buf] + nr * DVS;
+            float4 x[4];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = *reinterpret_cast<const float4*>(src + 4 * (np + 8 * i));
+                ss += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
+            }
+            ss += __shfl_xor(ss, 1, 64);
+            ss += __shfl_xor(ss, 2, 64);
+            ss += __shfl_xor(ss, 4, 64);
+            const float rs = rsqrtf(ss * (1.f / DV) + a.norm_eps);
+            if (nr < rows) {
+                Tout* dst = op + (static_cast<size_t>(cbase + nr) * H + h) * DV;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float gt[4] = {bf16_bits_to_f32(G[i].x & 0xffffu), bf16_bits_to_f32(G[i].x >> 16),
+                                         bf16_bits_to_f32(G[i].y & 0xffffu), bf16_bits_to_f32(G[i].y >> 16)};
+                    const float xv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+                    const float wv[4] = {WR[i].x, WR[i].y, WR[i].z, WR[i].w};
+                    float y[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = xv[e] * rs * wv[e] / (1.f + __expf(-gt[e]));
+                    if constexpr (sizeof(Tout) == 4) {
+                        *reinterpret_cast<float4*>(dst + 4 * (np + 8 * i)) = make_float4(y[0], y[1], y[2], y[3]);
+                    } else {
+                        u32x2 pk;
+                        pk.x = static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[0]))) |
+                               (static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[1]))) << 16);
+                        pk.y = static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[2]))) |
+                               (static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[3]))) << 16);
+                        *reinterpret_cast<u32x2*>(dst + 4 * (np + 8 * i)) = pk;
+                    }
+                }
+            }
+        }
+    };
+    auto store_out = [&](int buf, long cbase, int rows) __attribute__((always_inline)) {
+        if constexpr (NORM)
+            store_tile_norm(buf, cbase, rows);
+        else
+            store_tile(buf, cbase, rows);
     };
     // operand fragments of the R step for token tiles 2mh, 2mh + 1
     auto load_r = [&](int mh, f16x8 (&fa)[2][4], float (&vv)[2][4]) __attribute__((always_inline)) {
@@ -821,8 +912,8 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                stage_out(s.obuf[buf], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
-                          static_cast<const Tout*>(nullptr));
+                stage_out<DVS>(s.obuf[buf], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
+                               static_cast<const Tstage*>(nullptr));
         }
     };
     // operand fragments of the state update for channel tiles 4half .. 4half + 3
@@ -850,28 +941,8 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         }
     };
 
-    // Each chunk is software-pipelined inside the wave: the LDS fragments of
-    // the next step are requested before the matrix products of the current
-    // one, so the LDS and the matrix cores work at the same time (one wave
-    // per SIMD: nothing else would hide the LDS latency).
-    long prev_c0 = 0;
-    int prev_L = 0;
-    for (int j = 0; j < nch; ++j) {
-        const long c0 = tok0 + static_cast<long>(j) * C;
-        const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
-        const bool more = j + 1 < nch;
-        const int buf = j & 1;
-
-        f16x8 fa0[2][4], fa1[2][4];
-        float vv0[2][4], vv1[2][4];
-        load_r(0, fa0, vv0);
-        if (more) {
-            fetch_v(j + 1);
-            fetch(j + 1, 0, 5);
-        }
-        if (j > 0) store_tile(buf ^ 1, prev_c0, prev_L);
-        // state as fp16 hi/lo B-frags (channel order of the accumulators)
-        f16x8 sh[4], sl[4];
+    // state as fp16 hi/lo B-frags (channel order of the accumulators)
+    auto split_state = [&](f16x8 (&sh)[4], f16x8 (&sl)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
@@ -885,22 +956,18 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
                 sl[kb][4 + i] = lo;
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        load_r(1, fa1, vv1);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x4 ut[4];
-        step_r(0, fa0, vv0, sh, sl, ut);
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 th[6], tl[6];
+    };
+    auto load_t = [&](bf16x8 (&th)[6], bf16x8 (&tl)[6]) __attribute__((always_inline)) {
 #pragma unroll
         for (int p = 0; p < 6; ++p) {
             th[p] = s.r.tp[0][p][l];
             tl[p] = s.r.tp[1][p][l];
         }
-        if (more) fetch(j + 1, 5, 10);
-        __builtin_amdgcn_sched_barrier(0);
-        step_r(1, fa1, vv1, sh, sl, ut);
-        // R as bf16 hi/lo B-frags, token order of the accumulators
+    };
+    // U~ = T' R with R as bf16 hi/lo B-frags (token order of the
+    // accumulators); the result goes out as fp16 B-frags
+    auto step_t = [&](const bf16x8 (&th)[6], const bf16x8 (&tl)[6], f32x4 (&ut)[4], f16x8 (&ub)[2])
+        __attribute__((always_inline)) {
         bf16x8 rbh[2], rbl[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -915,11 +982,6 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
                 rbl[kb][4 + i] = lo;
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        f16x8 qa0[2][4], ah0[2][2], al0[2][2];
-        load_o(0, qa0, ah0, al0);
-        __builtin_amdgcn_sched_barrier(0);
-        // U~ = T' R
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -930,7 +992,6 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             }
             ut[mt] = acc;
         }
-        f16x8 ub[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -939,26 +1000,110 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
                 ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
             }
         }
-        if (more) fetch(j + 1, 10, 15);
-        __builtin_amdgcn_sched_barrier(0);
-        f16x8 qa1[2][4], ah1[2][2], al1[2][2];
-        load_o(1, qa1, ah1, al1);
-        __builtin_amdgcn_sched_barrier(0);
-        step_o(0, buf, qa0, ah0, al0, sh, sl, ub);
-        __builtin_amdgcn_sched_barrier(0);
-        f16x8 ka0[4][2];
-        float4 gm0[4];
-        load_k(0, ka0, gm0);
-        if (more) fetch(j + 1, 15, RFULL + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        step_o(1, buf, qa1, ah1, al1, sh, sl, ub);
-        __builtin_amdgcn_sched_barrier(0);
-        f16x8 ka1[4][2];
-        float4 gm1[4];
-        load_k(1, ka1, gm1);
-        __builtin_amdgcn_sched_barrier(0);
-        step_k(0, ka0, gm0, ub);
-        step_k(1, ka1, gm1, ub);
+    };
+
+    long prev_c0 = 0;
+    int prev_L = 0;
+    for (int j = 0; j < nch; ++j) {
+        const long c0 = tok0 + static_cast<long>(j) * C;
+        const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
+        const bool more = j + 1 < nch;
+        const int buf = j & 1;
+
+        if constexpr (NW == 4) {
+            // One wave per SIMD: each chunk is software-pipelined inside the
+            // wave (the LDS fragments of the next step are requested before
+            // the matrix products of the current one), since nothing else
+            // would hide the LDS latency.
+            f16x8 fa0[2][4], fa1[2][4];
+            float vv0[2][4], vv1[2][4];
+            load_r(0, fa0, vv0);
+            if (more) {
+                fetch_v(j + 1);
+                fetch(j + 1, 0, 5);
+            }
+            if (j > 0) store_out(buf ^ 1, prev_c0, prev_L);
+            f16x8 sh[4], sl[4];
+            split_state(sh, sl);
+            __builtin_amdgcn_sched_barrier(0);
+            load_r(1, fa1, vv1);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 ut[4];
+            step_r(0, fa0, vv0, sh, sl, ut);
+            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 th[6], tl[6];
+            load_t(th, tl);
+            if (more) fetch(j + 1, 5, 10);
+            __builtin_amdgcn_sched_barrier(0);
+            step_r(1, fa1, vv1, sh, sl, ut);
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 qa0[2][4], ah0[2][2], al0[2][2];
+            load_o(0, qa0, ah0, al0);
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 ub[2];
+            step_t(th, tl, ut, ub);
+            if (more) fetch(j + 1, 10, 15);
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 qa1[2][4], ah1[2][2], al1[2][2];
+            load_o(1, qa1, ah1, al1);
+            __builtin_amdgcn_sched_barrier(0);
+            step_o(0, buf, qa0, ah0, al0, sh, sl, ub);
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 ka0[4][2];
+            float4 gm0[4];
+            load_k(0, ka0, gm0);
+            if (more) fetch(j + 1, 15, RFULL + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            step_o(1, buf, qa1, ah1, al1, sh, sl, ub);
+            __builtin_amdgcn_sched_barrier(0);
+            f16x8 ka1[4][2];
+            float4 gm1[4];
+            load_k(1, ka1, gm1);
+            __builtin_amdgcn_sched_barrier(0);
+            step_k(0, ka0, gm0, ub);
+            step_k(1, ka1, gm1, ub);
+        } else {
+            // Two waves per SIMD hide each other's LDS latency: the steps run
+            // in order and reuse one set of fragment registers.
+            if (more) {
+                fetch_v(j + 1);
+                fetch(j + 1, 0, RFULL + 1);
+            }
+            if (j > 0) store_out(buf ^ 1, prev_c0, prev_L);
+            fetch_gate(c0);
+            f16x8 sh[4], sl[4];
+            split_state(sh, sl);
+            f32x4 ut[4];
+            {
+                f16x8 fa[2][4];
+                float vv[2][4];
+                load_r(0, fa, vv);
+                step_r(0, fa, vv, sh, sl, ut);
+                load_r(1, fa, vv);
+                step_r(1, fa, vv, sh, sl, ut);
+            }
+            f16x8 ub[2];
+            {
+                bf16x8 th[6], tl[6];
+                load_t(th, tl);
+                step_t(th, tl, ut, ub);
+            }
+            {
+                f16x8 qa[2][4], ah[2][2], al[2][2];
+                load_o(0, qa, ah, al);
+                step_o(0, buf, qa, ah, al, sh, sl, ub);
+                load_o(1, qa, ah, al);
+                step_o(1, buf, qa, ah, al, sh, sl, ub);
+            }
+            {
+                f16x8 ka[4][2];
+                float4 gm[4];
+                load_k(0, ka, gm);
+                step_k(0, ka, gm, ub);
+                load_k(1, ka, gm);
+                step_k(1, ka, gm, ub);
+            }
+        }
         __syncthreads();
         // every read of this chunk's record is done: the next one moves in
         if (more) commit();
@@ -966,7 +1111,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         prev_L = L;
         __syncthreads();
     }
-    if (nch > 0) store_tile((nch - 1) & 1, prev_c0, prev_L);
+    if (nch > 0) store_out((nch - 1) & 1, prev_c0, prev_L);
 
     if (a.final_state) {
         const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
@@ -1015,13 +1160,29 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_
             chunk_prep_kernel<false><<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map,
                                                                                              static_cast<int>(slots));
     }
-    // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
-    const int groups = (chains + 7) / 8;
-    const dim3 grid(groups * 8 * NSLICE), block(NT);
-    if (a.out_bf16)
-        chunk_scan_kernel<uint16_t><<<grid, block, 0, stream>>>(a, recs, static_cast<int>(slots));
-    else
-        chunk_scan_kernel<float><<<grid, block, 0, stream>>>(a, recs, static_cast<int>(slots));
+    const int ns = static_cast<int>(slots);
+    if (a.out_norm) {
+        // one 8-wave workgroup per chain (whole rows of o for the norm)
+        const dim3 grid(chains), block(512);
+        if (a.out_bf16)
+            chunk_scan_kernel<uint16_t, 8, true><<<grid, block, 0, stream>>>(a, recs, ns);
+        else
+            chunk_scan_kernel<float, 8, true><<<grid, block, 0, stream>>>(a, recs, ns);
+    } else if (kPlainScanWaves == 8) {
+        const dim3 grid(chains), block(512);
+        if (a.out_bf16)
+            chunk_scan_kernel<uint16_t, 8, false><<<grid, block, 0, stream>>>(a, recs, ns);
+        else
+            chunk_scan_kernel<float, 8, false><<<grid, block, 0, stream>>>(a, recs, ns);
+    } else {
+        // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
+        const int groups = (chains + 7) / 8;
+        const dim3 grid(groups * 16), block(256);
+        if (a.out_bf16)
+            chunk_scan_kernel<uint16_t, 4, false><<<grid, block, 0, stream>>>(a, recs, ns);
+        else
+            chunk_scan_kernel<float, 4, false><<<grid, block, 0, stream>>>(a, recs, ns);
+    }
     return hipGetLastError();
 }
 

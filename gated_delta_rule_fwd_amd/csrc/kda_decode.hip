@@ -7,6 +7,7 @@
 //   u  = beta (v - p)                               (innovation times rate)
 //   S  <- S~ + k^ u^T                               (erase + write, in place)
 //   o  = scale * (r + (k^ . q^) u)  == scale * S_new^T q^  (read after write)
+//   optional output norm: o <- o / sqrt(mean(o^2) + eps) * w * sigmoid(gate)
 // ("Kimi K3 模型结构（2）", Q&A: decode runs this recurrent form one token at a
 // time.)
 //
@@ -149,6 +150,19 @@ decode_step_kernel(DecodeArgs a)
         S4[i * CG + cg] = w;
     }
     if (rg == 0) {
+        if (a.out_norm) {
+            // output norm over the d_v columns, held by the CG lanes of wave 0
+            float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+            for (int off = 1; off < CG; off <<= 1) ss += __shfl_xor(ss, off, 64);
+            const float rs = rsqrtf(ss * (1.f / DV) + a.norm_eps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * cg + e;
+                const float gt = Elem<Tin>::load(static_cast<const Tin*>(a.out_gate), static_cast<size_t>(c) * DV + j);
+                ov[e] = ov[e] * rs * (a.norm_w ? a.norm_w[j] : 1.f) / (1.f + __expf(-gt));
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Elem<Tout>::store(o, static_cast<size_t>(c) * DV + 4 * cg + e, ov[e]);
     }

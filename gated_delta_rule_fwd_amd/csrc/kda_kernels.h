@@ -29,6 +29,13 @@ struct ChunkArgs {
     int gated;
     int beta_logits;    // beta holds logits; the kernels apply the sigmoid
     int signed_alpha;   // g holds the signed decay alpha (Complex KDA), not its log
+    // output norm: o <- o / sqrt(mean(o^2) + norm_eps) * norm_w * sigmoid(out_gate)
+    // per (token, head) over d_v; out_gate in in_dtype [tokens, H, d_v],
+    // norm_w [d_v] fp32 (nullable: ones)
+    const void* out_gate;
+    const float* norm_w;
+    float norm_eps;
+    int out_norm;
 };
 
 // Inputs of one decode step; z/A_log/dt_bias replace g when gated.
@@ -50,11 +57,17 @@ struct DecodeArgs {
     int gated;
     int beta_logits;
     int signed_alpha;
+    const void* out_gate;   // output norm, as in ChunkArgs ([chains, d_v])
+    const float* norm_w;
+    float norm_eps;
+    int out_norm;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
-// fp32 per-position-pair path: any supported head dims and dtypes.
-hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t stream);
+// fp32 per-position-pair path: any supported head dims and dtypes.  With
+// a.out_norm it writes fp32 o to o_tmp ([tokens, H, d_v]) and then applies
+// the output norm in a second kernel that writes a.o.
+hipError_t launch_chunk_fp32(const ChunkArgs& a, float* o_tmp, hipStream_t stream);
 
 // Matrix-core path: bf16 inputs, d_k = d_v = 128, g >= -5, in two passes.
 //   pass 1 (chunk-parallel): every (chunk, head) writes one ChunkRecord of

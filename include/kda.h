@@ -87,6 +87,11 @@ typedef enum kda_dtype {
  * checked under KDA_FLAG_VALIDATE).  Not combinable with the gated entry
  * points. */
 #define KDA_FLAG_SIGNED_ALPHA 0x10u
+/* The call carries an output norm (kda_out_norm below).  Must be set exactly
+ * when a norm is passed to kda_chunk_fwd_fused / kda_recurrent_step_fused;
+ * it is part of the descriptor so that kda_chunk_fwd_workspace_bytes() can
+ * size the fp32 path's temporary output. */
+#define KDA_FLAG_OUT_NORM 0x20u
 
 typedef struct kda_chunk_desc {
     int B;              /* batch (must be 1 when cu_seqlens is given) */
@@ -101,8 +106,14 @@ typedef struct kda_chunk_desc {
     unsigned flags;     /* KDA_FLAG_* */
 } kda_chunk_desc;
 
-/* Bytes of device workspace kda_chunk_fwd needs for this descriptor (0 unless
- * KDA_FLAG_VALIDATE is set).  Returns (size_t)-1 for a null descriptor. */
+/* Bytes of device workspace the chunkwise entry points need for this
+ * descriptor: the matrix-core path (bf16 inputs, d_k = d_v = 128, no
+ * KDA_FLAG_FP32_PATH) keeps one 74,240-byte record per (64-token chunk,
+ * head) there; the fp32 path needs none, except B*T*H*d_v fp32 values for
+ * its temporary output under KDA_FLAG_OUT_NORM; KDA_FLAG_VALIDATE adds 256
+ * bytes.  When num_seqs > 0 and B == 1 the figure covers both the dense and
+ * the packed (cu_seqlens) layout.  Returns 0 for a descriptor the entry
+ * points reject and (size_t)-1 for a null descriptor. */
 KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
 
 /*
@@ -190,6 +201,66 @@ KDA_API kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v,
                               const void* q, const void* k, const void* v,
                               const void* z, const float* A_log, const float* dt_bias,
                               const float* beta,
+                              float* state, void* o, hipStream_t stream);
+
+/*
+ * Decay-gate inputs of the fused entry points (the map of kda_chunk_fwd_gated:
+ * g = -5 sigmoid(exp(A_log[h]) (z + dt_bias[h, c])); layouts as given there).
+ */
+typedef struct kda_decay_gate {
+    const void* z;          /* [B, T, H, d_k] / [N, H, d_k], in_dtype */
+    const float* A_log;     /* [H], required */
+    const float* dt_bias;   /* [H, d_k], nullable (zero) */
+} kda_decay_gate;
+
+/*
+ * Output norm fused at the store of o ("Kimi K3 の KDA ..." section 1.2.1:
+ * after the kernel, the model applies a per-head RMSNorm over the head's
+ * value dimension, a sigmoid on the output gate, and their elementwise
+ * product).  Per token (and sequence) t, head h and value channel c, with o
+ * the forward pass's output (scale included):
+ *
+ *   o'[t,h,c] = o[t,h,c] / sqrt(mean_c' o[t,h,c']^2 + eps) * weight[c]
+ *               * sigmoid(gate[t,h,c])
+ *
+ *   gate    same layout as o ([B, T, H, d_v] prefill, [N, H, d_v] decode),
+ *           in_dtype, 16-byte aligned: the output-gate logits
+ *   weight  [d_v] fp32 per-channel gain shared by all heads, nullable
+ *           (ones), 16-byte aligned
+ *   eps     >= 0, added to the mean square (the pages give no value)
+ */
+typedef struct kda_out_norm {
+    const void* gate;
+    const float* weight;
+    float eps;
+} kda_out_norm;
+
+/*
+ * The forward pass with both of the model's adjacent steps fused: the
+ * decay-gate prologue (when decay_gate is given; g must then be NULL) and the
+ * output norm (when norm is given; KDA_FLAG_OUT_NORM must then be set in the
+ * flags, and only then).  With decay_gate == NULL and norm == NULL this is
+ * kda_chunk_fwd / kda_recurrent_step.  Every other argument, layout, flag,
+ * workspace rule and error is that of those entry points; a norm with a
+ * null gate or a negative or non-finite eps is KDA_ERR_INVALID_ARG, as is a
+ * mismatch between norm and KDA_FLAG_OUT_NORM.  o must not alias the norm's
+ * gate.
+ */
+KDA_API kda_status kda_chunk_fwd_fused(const kda_chunk_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const kda_decay_gate* decay_gate,
+                         const float* beta,
+                         const float* init_state, const int32_t* cu_seqlens,
+                         const kda_out_norm* norm,
+                         void* o, float* final_state,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+KDA_API kda_status kda_recurrent_step_fused(int N, int H, int d_k, int d_v,
+                              kda_dtype in_dtype, kda_dtype out_dtype,
+                              float scale, unsigned flags,
+                              const void* q, const void* k, const void* v,
+                              const float* g, const kda_decay_gate* decay_gate,
+                              const float* beta, const kda_out_norm* norm,
                               float* state, void* o, hipStream_t stream);
 
 /* Static description of a status code. */

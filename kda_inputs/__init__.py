@@ -30,7 +30,8 @@ from typing import Optional
 import numpy as np
 
 BLOCK_T = 4096  # tokens per independently seeded block
-_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7, "dt_bias": 8, "sign": 9}
+_TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7, "dt_bias": 8, "sign": 9,
+              "out_gate": 10, "norm_w": 11}
 
 
 # ----------------------------------------------------------------------------
@@ -352,3 +353,23 @@ def signed_decode_step(seed: int, step: int, N: int, H: int, d: int, dtype: str 
     neg = _rng(seed, "sign", 1_000_000 + step).uniform(size=alpha.shape) < p_negative
     alpha[neg] = -alpha[neg]
     return DecodeStep(q=x.q, k=x.k, v=x.v, g=alpha, beta=(np.float32(2.0) * x.beta).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# Output-norm inputs: the output-gate logits and the norm's per-channel gain
+# ----------------------------------------------------------------------------
+def make_out_gate(seed: int, shape, dtype: str = "bf16") -> np.ndarray:
+    """Output-gate logits ~ N(0, 1) of the shape of o ([B,T,H,d_v] or
+    [N,H,d_v]), bf16 bits or fp32; drawn in token blocks like q, k, v."""
+    out = np.empty(tuple(shape), np.float32)
+    if len(shape) == 4:
+        _fill_blocked(out, seed, "out_gate",
+                      lambda rng, shp, t0, t1: rng.standard_normal(shp, dtype=np.float32), shape[1])
+    else:
+        out[:] = _rng(seed, "out_gate", 0).standard_normal(out.shape, dtype=np.float32)
+    return bf16_bits(out) if dtype == "bf16" else out
+
+
+def norm_weight(seed: int, dv: int) -> np.ndarray:
+    """The norm's per-channel gain [d_v] ~ U(0.5, 1.5), fp32."""
+    return _rng(seed, "norm_w", 0).uniform(0.5, 1.5, size=dv).astype(np.float32)

@@ -23,6 +23,9 @@ Contents
   * ``forward_signed``: the same recurrence with the decay given as a signed
     alpha in [-1, 1] and beta in [0, 2] (Complex KDA, "[논문리뷰] Complex KDA
     ..." page).
+  * ``out_norm``: the gated RMSNorm that follows the kernel in the model,
+    o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) per (token, head) row
+    ("Kimi K3 の KDA ..." section 1.2.1, the output gate).
   * ``product_form``: a second, independently written NumPy formulation that
     builds each transition matrix (I - beta k k^T) Diag(alpha) explicitly
     (page 1, section 2.3.5: the state map is the ordered product of per-token
@@ -191,6 +194,27 @@ def decode_gated(state, q, k, v, z, A_log, dt_bias, beta_logits, *, scale=1.0, t
     logits [N,H], then decode_steps."""
     return decode_steps(state, q, k, v, gate_map(z, A_log, dt_bias), beta_from_logits(beta_logits),
                         scale=scale, threads=threads)
+
+
+# ----------------------------------------------------------------------------
+# Output norm epilogue
+# ----------------------------------------------------------------------------
+def out_norm(o, gate, weight=None, eps=1e-5):
+    """The gated RMSNorm applied to the kernel's output ("Kimi K3 の KDA ..."
+    section 1.2.1: per head, RMSNorm over the head's value dimension, a
+    sigmoid on the output gate, and the elementwise product; the norm comes
+    before the gate).  For every (token, head) row over the last axis c:
+
+        y_c = o_c / sqrt(mean_c' o_c'^2 + eps) * weight_c * sigmoid(gate_c)
+
+    Reading: weight is the norm's per-channel gain [d_v], shared by all heads
+    (None means ones); eps is the caller's (the pages give none).  fp64."""
+    o = np.asarray(o, np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    y = o / np.sqrt(ms + eps)
+    if weight is not None:
+        y = y * np.asarray(weight, np.float64)
+    return y * sigmoid(gate)
 
 
 # ----------------------------------------------------------------------------

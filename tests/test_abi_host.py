@@ -28,9 +28,9 @@ def lib():
 
 
 def test_header_declares_expected_entry_points():
-    assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_workspace_bytes",
-                                  "kda_recurrent_step", "kda_recurrent_step_gated", "kda_status_str",
-                                  "kda_last_hip_error", "kda_version"])
+    assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
+                                  "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step", "kda_recurrent_step_gated",
+                                  "kda_recurrent_step_fused", "kda_status_str", "kda_last_hip_error", "kda_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -177,3 +177,58 @@ def test_gated_entry_points_reject_bad_arguments(lib):
     assert step(a_log=None) == 1
     assert step(flags=kda.FLAG_VALIDATE) == 2
     assert lib.kda_recurrent_step_gated(0, 2, 128, 128, 1, 1, 1.0, 1, *([None] * 9), None) == 0
+
+
+def test_workspace_for_the_output_norm(lib):
+    size = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(**kw)))
+    on = kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM
+    # matrix-core path: the norm is applied in the scan pass, no extra bytes
+    assert size(B=2, T=100, H=3, flags=on) == size(B=2, T=100, H=3)
+    # fp32 path: fp32 o for every (token, head) row as a temporary
+    assert size(B=2, T=100, H=3, d_k=64, d_v=64, flags=on) == 2 * 100 * 3 * 64 * 4
+    assert size(B=1, T=10, H=1, in_dtype=0, flags=on | kda.FLAG_VALIDATE) == 256 + 10 * 128 * 4
+
+
+def _call_fused(lib, d, g=FAKE + 0x300000, dg=None, norm=None, ws=FAKE, ws_bytes=1 << 40):
+    p = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(3)]
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_fwd_fused(ctypes.byref(d), p[0], p[1], p[2], vp(g), None if dg is None else ctypes.byref(dg),
+                                   ctypes.c_void_p(FAKE + 0x400000), None, None,
+                                   None if norm is None else ctypes.byref(norm), ctypes.c_void_p(FAKE + 0x600000),
+                                   None, vp(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_fused_entry_points_reject_bad_arguments(lib):
+    on = kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM
+    good = kda.OutNorm(FAKE + 0x800000, None, 1e-5)
+    assert _call_fused(lib, _desc(flags=on), norm=None) == 1                        # flag without a norm
+    assert _call_fused(lib, _desc(), norm=good) == 1                               # norm without the flag
+    assert _call_fused(lib, _desc(flags=on), norm=kda.OutNorm(None, None, 1e-5)) == 1        # gate required
+    assert _call_fused(lib, _desc(flags=on), norm=kda.OutNorm(FAKE + 8, None, 1e-5)) == 1    # gate misaligned
+    assert _call_fused(lib, _desc(flags=on), norm=kda.OutNorm(FAKE + 0x800000, FAKE + 4, 1e-5)) == 1
+    assert _call_fused(lib, _desc(flags=on), norm=kda.OutNorm(FAKE + 0x800000, None, -1.0)) == 1
+    assert _call_fused(lib, _desc(flags=on), norm=kda.OutNorm(FAKE + 0x800000, None, float("nan"))) == 1
+    assert _call_fused(lib, _desc(flags=on), norm=kda.OutNorm(FAKE + 0x600000, None, 1e-5)) == 1  # gate is o
+    dg = kda.DecayGate(FAKE + 0x900000, FAKE + 0xA00000, None)
+    assert _call_fused(lib, _desc(), dg=dg) == 1                                   # g and a decay gate
+    assert _call_fused(lib, _desc(flags=on), g=None, dg=kda.DecayGate(FAKE + 0x900000, None, None),
+                       norm=good) == 1                                             # A_log required
+    assert _call_fused(lib, _desc(flags=on), norm=good, ws=None, ws_bytes=0) == 3  # same workspace rule
+    assert _call_fused(lib, _desc(flags=on | kda.FLAG_SIGNED_ALPHA), g=None, dg=dg, norm=good) == 2
+    # the plain and gated entry points take no norm
+    assert _call(lib, _desc(flags=on), ws=FAKE, ws_bytes=1 << 40) == 1
+    P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(9)]
+
+    def step(flags=on, norm=good, g=P[3], dg=None, N=4):
+        return lib.kda_recurrent_step_fused(N, 2, 128, 128, 1, 1, 1.0, flags, P[0], P[1], P[2], g,
+                                            None if dg is None else ctypes.byref(dg), P[4],
+                                            None if norm is None else ctypes.byref(norm), P[5], P[6], None)
+
+    assert step(norm=None) == 1
+    assert step(flags=kda.FLAG_QK_L2NORM) == 1
+    assert step(norm=kda.OutNorm(None, None, 0.0)) == 1
+    assert step(norm=kda.OutNorm(FAKE + 0x800000, None, float("inf"))) == 1
+    assert step(dg=dg) == 1
+    assert step(flags=on | kda.FLAG_VALIDATE) == 2
+    assert step(N=0) == 0
+    assert lib.kda_recurrent_step(4, 2, 128, 128, 1, 1, 1.0, on, *P[:7], None) == 1

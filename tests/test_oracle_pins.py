@@ -526,3 +526,61 @@ def test_signed_oracle_with_positive_alpha_is_the_log_oracle():
     # alpha rounded to fp32 once: agreement to fp32 rounding of the decay
     np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(s2, s1, rtol=1e-5, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Output norm ("Kimi K3 の KDA ..." section 1.2.1: per-head RMSNorm over the
+# value dimension, sigmoid of the output gate, elementwise product; the norm
+# before the gate)
+# ---------------------------------------------------------------------------
+def test_out_norm_worked_by_hand():
+    # o = (1, 2, 2): mean square 3; with eps = 1 the scale is 1/sqrt(4) = 1/2,
+    # so RMSNorm(o) = (0.5, 1, 1).  weight (2, 1, 0.5) and gate (0, ln 3,
+    # -ln 3), whose sigmoids are (1/2, 3/4, 1/4), give (0.5, 0.75, 0.125).
+    y = oracle.out_norm(np.array([1.0, 2.0, 2.0]), np.array([0.0, np.log(3.0), -np.log(3.0)]),
+                        np.array([2.0, 1.0, 0.5]), eps=1.0)
+    np.testing.assert_allclose(y, [0.5, 0.75, 0.125], rtol=1e-15, atol=0)
+
+
+def test_out_norm_scale_invariance_and_unit_rms():
+    rng = np.random.default_rng(77)
+    o = rng.standard_normal((5, 3, 16))
+    gate = rng.standard_normal((5, 3, 16))
+    y = oracle.out_norm(o, gate, eps=0.0)
+    np.testing.assert_allclose(oracle.out_norm(7.5 * o, gate, eps=0.0), y, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(oracle.out_norm(-o, gate, eps=0.0), -y, rtol=1e-15, atol=0)
+    # a saturated gate (sigmoid = 1) leaves the plain RMSNorm: unit RMS per row
+    y1 = oracle.out_norm(o, np.full_like(o, 60.0), eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y1 * y1, axis=-1)), 1.0, rtol=1e-14, atol=0)
+    # sigmoid(x) + sigmoid(-x) = 1: the two gates add up to the plain norm
+    np.testing.assert_allclose(oracle.out_norm(o, gate, eps=0.0) + oracle.out_norm(o, -gate, eps=0.0), y1,
+                               rtol=1e-13, atol=1e-15)
+    # eps keeps a zero row at zero
+    assert np.all(oracle.out_norm(np.zeros((2, 8)), np.zeros((2, 8)), eps=1e-5) == 0.0)
+
+
+def test_out_norm_reduces_each_row_over_the_last_axis_with_a_shared_weight():
+    rng = np.random.default_rng(78)
+    u = rng.standard_normal(16)
+    c = rng.uniform(0.1, 10.0, (4, 3, 1))
+    y = oracle.out_norm(c * u, np.zeros((4, 3, 16)), eps=0.0)   # every row a positive multiple of u
+    np.testing.assert_allclose(y, np.broadcast_to(y[0, 0], y.shape), rtol=1e-14, atol=0)
+    w = np.zeros(16)
+    w[5] = 2.0
+    y = oracle.out_norm(rng.standard_normal((4, 3, 16)), rng.standard_normal((4, 3, 16)), w, eps=1e-5)
+    assert np.all(np.delete(y, 5, axis=-1) == 0.0) and np.all(y[..., 5] != 0.0)
+
+
+def test_out_norm_after_one_token_from_zero_state():
+    # from S = 0 the first output is o = scale beta (k^ . q^) v, so its norm
+    # with eps = 0 is sign(beta k^.q^) v / rms(v) * w * sigmoid(gate)
+    rng = np.random.default_rng(79)
+    d = 8
+    q, k, v, g, beta = _rand_chain(rng, 1, d, d)
+    o, _ = _run(q, k, v, g, beta, scale=0.5)
+    gate = rng.standard_normal(d)
+    w = rng.uniform(0.5, 1.5, d)
+    vv = v[0].astype(np.float64)
+    sign = np.sign(float(beta[0]) * float(_unit(k[0]) @ _unit(q[0])))
+    expect = sign * vv / np.sqrt(np.mean(vv * vv)) * w / (1.0 + np.exp(-gate))
+    np.testing.assert_allclose(oracle.out_norm(o[0], gate, w, eps=0.0), expect, rtol=1e-12, atol=1e-14)
