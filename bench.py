@@ -358,10 +358,11 @@ def _line(workload, ts, algo):
                          "frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
-def time_gated(kda, torch, kda_inputs, reps=20, warm=5, norm=False):
+def time_gated(kda, torch, kda_inputs, reps=20, warm=5, norm=False, conv=False):
     """The headline shape through the gated entry point (gate map and beta
     sigmoid in the kernel), same seed as the headline workload; with norm,
-    also the output norm at the store of o (the fused layer core)."""
+    also the output norm at the store of o; with conv, also the short
+    convolution of q, k, v at their load (the whole fused layer core)."""
     gi = kda_inputs.make_gated_prefill(2, B, T, H, D, D, s0_std=0.02)
     d = {f: _dev(torch, getattr(gi, f)) for f in ("q", "k", "v", "z", "A_log", "dt_bias", "beta_logits",
                                                   "init_state")}
@@ -370,21 +371,52 @@ def time_gated(kda, torch, kda_inputs, reps=20, warm=5, norm=False):
     if norm:
         kw = dict(out_gate=_dev(torch, kda_inputs.make_out_gate(2, (B, T, H, D))),
                   norm_weight=_dev(torch, kda_inputs.norm_weight(2, D)), norm_eps=1e-5)
+    if conv:
+        kw["conv_weights"] = tuple(_dev(torch, w) for w in kda_inputs.conv_weights(2, H, D, D))
+        kw["conv_init"] = tuple(_dev(torch, c) for c in kda_inputs.conv_states(2, B, H, D, D))
+        kw["conv_final"] = tuple(torch.empty_like(c) for c in kw["conv_init"])
     o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
     sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D, flags=kda.FLAG_QK_L2NORM | kda.FLAG_BETA_LOGITS |
-                                         (kda.FLAG_OUT_NORM if norm else 0)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D, flags=kda.FLAG_QK_L2NORM | (kda.FLAG_OUT_NORM if norm else 0)),
+                     dtype=torch.uint8, device="cuda")
     call = lambda: kda.chunk_fwd_gated(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta_logits"], d["init_state"],
                                        dt_bias=d["dt_bias"], beta_logits=True, o=o, final_state=sT, workspace=ws, **kw)
     ts = _time_calls(torch, call, reps, warm)
     del d, o, sT, ws, kw
     torch.cuda.empty_cache()
+    if conv:
+        return _line("long prefill B=1 H=96 T=65536 d=128, the fused layer core: short convolution + SiLU of raw bf16 "
+                     "q, k, v with conv states in and out, decay-gate prologue, output norm pass (seed 2)",
+                     ts, BYTES_PER_TOKEN_HEAD_LAYER * B * T * H + 2 * STATE_BYTES * B * H + 4 * D +
+                     2 * 3 * 3 * H * D * 2 + 3 * 4 * 4 * H * D)
     if norm:
-        return _line("long prefill B=1 H=96 T=65536 d=128, gated entry point with the output norm fused: bf16 decay "
+        return _line("long prefill B=1 H=96 T=65536 d=128, gated entry point with the output norm: bf16 decay "
                      "logits z, A_log, dt_bias, beta logits, bf16 output-gate logits, fp32 gain (seed 2)",
                      ts, BYTES_PER_TOKEN_HEAD_LAYER * B * T * H + 2 * STATE_BYTES * B * H + 4 * D)
     return _line("long prefill B=1 H=96 T=65536 d=128 via the gated entry point: bf16 decay logits z, A_log, "
                  "dt_bias, beta logits (seed 2)", ts, BYTES_PER_TOKEN_HEAD_GATED * B * T * H + 2 * STATE_BYTES * B * H)
+
+
+def time_conv(kda, torch, kda_inputs, reps=20, warm=5):
+    """The headline workload with the short convolution fused (raw q, k, v;
+    conv states in and out); g and beta as in the headline call."""
+    inp = kda_inputs.workload("long_bf16")
+    d = {f: _dev(torch, getattr(inp, f)) for f in ("q", "k", "v", "g", "beta", "init_state")}
+    del inp
+    ws_ = tuple(_dev(torch, w) for w in kda_inputs.conv_weights(2, H, D, D))
+    ci = tuple(_dev(torch, c) for c in kda_inputs.conv_states(2, B, H, D, D))
+    cf = tuple(torch.empty_like(c) for c in ci)
+    o = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+    sT = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(B, T, H, D, D), dtype=torch.uint8, device="cuda")
+    call = lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["init_state"], o=o, final_state=sT,
+                                 workspace=ws, conv_weights=ws_, conv_init=ci, conv_final=cf)
+    ts = _time_calls(torch, call, reps, warm)
+    del d, o, sT, ws
+    torch.cuda.empty_cache()
+    return _line("long prefill B=1 H=96 T=65536 d=128 with the short convolution + SiLU fused at the load of raw "
+                 "bf16 q, k, v (conv states in and out; seed 2)", ts,
+                 BYTES_PER_TOKEN_HEAD * B * T * H + 2 * STATE_BYTES * B * H + 2 * 3 * 3 * H * D * 2 + 3 * 4 * 4 * H * D)
 
 
 def time_signed(kda, torch, kda_inputs, reps=20, warm=5):
@@ -469,6 +501,8 @@ def main():
                                      **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1))
         out["prefill_gated"] = time_gated(kda, torch, kda_inputs)
         out["prefill_gated_out_norm"] = time_gated(kda, torch, kda_inputs, norm=True)
+        out["prefill_layer_core"] = time_gated(kda, torch, kda_inputs, norm=True, conv=True)
+        out["prefill_conv"] = time_conv(kda, torch, kda_inputs)
         out["prefill_complex_kda"] = time_signed(kda, torch, kda_inputs)
     # the copy also calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE (see --traffic-from)
     out["copy_kernel"] = copy_bandwidth(torch)

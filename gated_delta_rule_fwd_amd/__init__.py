@@ -15,8 +15,11 @@ built, importing the library raises.
       -> o                                      [kda_recurrent_step_gated]
 
 Each of them takes ``out_gate=`` (with ``norm_weight=``, ``norm_eps=``) to
-fuse the output norm o <- RMSNorm(o) * norm_weight * sigmoid(out_gate) at the
-store of o; such calls go through kda_chunk_fwd_fused /
+apply the output norm o <- RMSNorm(o) * norm_weight * sigmoid(out_gate), and ``conv_weights=(w_q, w_k, w_v)`` to fuse the short
+convolution + SiLU at the load of q, k, v (then raw projections); the
+prefill calls take ``conv_init=`` / ``conv_final=`` (three [N, 3, H*d]
+tensors each, entries may be None), the decode calls ``conv_state=`` (updated
+in place).  Such calls go through kda_chunk_fwd_fused /
 kda_recurrent_step_fused.
 """
 from __future__ import annotations
@@ -58,6 +61,11 @@ class DecayGate(ctypes.Structure):
     _fields_ = [("z", ctypes.c_void_p), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
 
 
+class ShortConv(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p * 3), ("init_state", ctypes.c_void_p * 3),
+                ("final_state", ctypes.c_void_p * 3)]
+
+
 class OutNorm(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
@@ -91,10 +99,10 @@ def load():
     lib.kda_recurrent_step_gated.argtypes = [I, I, I, I, I, I, F, U] + [P] * 9 + [P]
     lib.kda_chunk_fwd_fused.restype = I
     lib.kda_chunk_fwd_fused.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 4 + [ctypes.POINTER(DecayGate)] + \
-        [P] * 3 + [ctypes.POINTER(OutNorm)] + [P, P, P, S, P]
+        [P] * 3 + [ctypes.POINTER(ShortConv), ctypes.POINTER(OutNorm)] + [P, P, P, S, P]
     lib.kda_recurrent_step_fused.restype = I
-    lib.kda_recurrent_step_fused.argtypes = [I, I, I, I, I, I, F, U] + [P] * 4 + [ctypes.POINTER(DecayGate), P,
-                                                                                  ctypes.POINTER(OutNorm), P, P, P]
+    lib.kda_recurrent_step_fused.argtypes = [I, I, I, I, I, I, F, U] + [P] * 4 + [
+        ctypes.POINTER(DecayGate), P, ctypes.POINTER(ShortConv), ctypes.POINTER(OutNorm), P, P, P]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_status_str.argtypes = [I]
     lib.kda_last_hip_error.restype = I
@@ -164,29 +172,32 @@ def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True,
 
 def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
               normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False,
-              signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, final_state=None,
-              workspace=None, stream=None):
+              signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
+              conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None):
     """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
     beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
     [N+1] device tensor or None (then N = B).  With signed_alpha (Complex KDA)
     g holds the signed decay alpha in [-1, 1] and beta may lie in [0, 2].
     out_gate ([B,T,H,d_v], q's dtype) fuses the output norm, with norm_weight
-    ([d_v] fp32 or None) and norm_eps.  Returns (o, final_state)."""
+    ([d_v] fp32 or None) and norm_eps.  conv_weights ([H*d,4] fp32 for q, k,
+    v) fuses the short convolution: q, k, v are then the raw projections,
+    conv_init / conv_final the [N,3,H*d] conv states read / written.
+    Returns (o, final_state)."""
     return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
                   validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha,
-                  (out_gate, norm_weight, norm_eps))
+                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final))
 
 
 def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *, dt_bias=None, out_dtype=None,
                     scale=1.0, normalize=True, output_final_state=True, validate=False, fp32_path=False,
-                    beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, final_state=None,
-                    workspace=None, stream=None):
+                    beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
+                    conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None):
     """As chunk_fwd, with g = -5 sigmoid(exp(A_log[h]) (z + dt_bias[h, c]))
     computed in the kernel: z [B,T,H,d_k] in q's dtype, A_log [H] fp32,
     dt_bias [H,d_k] fp32 or None."""
     return _chunk(q, k, v, None, (z, A_log, dt_bias), beta, init_state, cu_seqlens, out_dtype, scale, normalize,
                   output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, stream, False,
-                  (out_gate, norm_weight, norm_eps))
+                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final))
 
 
 def _norm_args(norm, o_shape, in_dtype, dv):
@@ -203,8 +214,30 @@ def _norm_args(norm, o_shape, in_dtype, dv):
     return OutNorm(out_gate.data_ptr(), None if weight is None else weight.data_ptr(), float(eps))
 
 
+def _conv_args(conv, N, H, dk, dv, dtype):
+    """Checks the short-convolution tensors; returns a ShortConv or None."""
+    torch = _torch()
+    weights, inits, finals = conv if conv is not None else (None, None, None)
+    if weights is None:
+        if inits is not None or finals is not None:
+            raise ValueError("conv states need conv_weights")
+        return None
+    inits = inits or (None, None, None)
+    finals = finals or (None, None, None)
+    sc = ShortConv()
+    for i, (name, d) in enumerate((("q", dk), ("k", dk), ("v", dv))):
+        _need(weights[i], "conv weight of " + name, torch.float32, (H * d, 4))
+        sc.weight[i] = weights[i].data_ptr()
+        for lst, field, what in ((inits, sc.init_state, "conv_init"), (finals, sc.final_state, "conv_final")):
+            if lst[i] is not None:
+                _need(lst[i], "%s of %s" % (what, name), dtype, (N, 3, H * d))
+                field[i] = lst[i].data_ptr()
+    return sc
+
+
 def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
-           validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False, norm=None):
+           validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False, norm=None,
+           conv=None):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -236,6 +269,7 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     if final_state is not None:
         _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
     on = _norm_args(norm, (B, T, H, dv), q.dtype, dv)
+    sc = _conv_args(conv, N, H, dk, dv, q.dtype)
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_VALIDATE if validate else 0) | \
         (FLAG_FP32_PATH if fp32_path else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
         (FLAG_SIGNED_ALPHA if signed_alpha else 0) | (FLAG_OUT_NORM if on is not None else 0)
@@ -245,12 +279,13 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     if ws > 0 and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
-    if on is not None:
+    if on is not None or sc is not None:
         dg = None if gate is None else ctypes.byref(DecayGate(z.data_ptr(), A_log.data_ptr(),
                                                               None if dt_bias is None else dt_bias.data_ptr()))
         st = lib.kda_chunk_fwd_fused(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), dg, _ptr(beta),
-                                     _ptr(init_state), _ptr(cu_seqlens), ctypes.byref(on), _ptr(o),
-                                     _ptr(final_state), _ptr(workspace), wsb, _stream(stream))
+                                     _ptr(init_state), _ptr(cu_seqlens), None if sc is None else ctypes.byref(sc),
+                                     None if on is None else ctypes.byref(on), _ptr(o), _ptr(final_state),
+                                     _ptr(workspace), wsb, _stream(stream))
     elif gate is None:
         st = lib.kda_chunk_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(init_state),
                                _ptr(cu_seqlens), _ptr(o), _ptr(final_state), _ptr(workspace), wsb, _stream(stream))
@@ -263,25 +298,29 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
 
 
 def recurrent_step(q, k, v, g, beta, state, *, out_dtype=None, scale=1.0, normalize=True, beta_logits=False,
-                   signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, stream=None):
+                   signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
+                   conv_state=None, o=None, stream=None):
     """One fused decode step.  q, k, g: [N,H,d_k]; v: [N,H,d_v]; beta: [N,H];
     state: [N,H,d_k,d_v] fp32, updated in place.  With signed_alpha g holds
-    the signed decay alpha.  out_gate [N,H,d_v] fuses the output norm.
+    the signed decay alpha.  out_gate [N,H,d_v] fuses the output norm;
+    conv_weights the short convolution, with conv_state (three [N,3,H*d]
+    caches, or None for zeros and no update) advanced in place.
     Returns o [N,H,d_v]."""
     return _step(q, k, v, g, None, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha,
-                 (out_gate, norm_weight, norm_eps))
+                 (out_gate, norm_weight, norm_eps), (conv_weights, conv_state, conv_state))
 
 
 def recurrent_step_gated(q, k, v, z, A_log, beta, state, *, dt_bias=None, out_dtype=None, scale=1.0, normalize=True,
-                         beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, o=None, stream=None):
+                         beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
+                         conv_state=None, o=None, stream=None):
     """As recurrent_step, with g computed in the kernel from z [N,H,d_k],
     A_log [H] and dt_bias [H,d_k] (or None)."""
     return _step(q, k, v, None, (z, A_log, dt_bias), beta, state, out_dtype, scale, normalize, beta_logits, o, stream,
-                 False, (out_gate, norm_weight, norm_eps))
+                 False, (out_gate, norm_weight, norm_eps), (conv_weights, conv_state, conv_state))
 
 
 def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, stream, signed_alpha=False,
-          norm=None):
+          norm=None, conv=None):
     torch = _torch()
     lib = load()
     _need(q, "q")
@@ -304,14 +343,17 @@ def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logit
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
     _need(o, "o", out_dtype, (N, H, dv))
     on = _norm_args(norm, (N, H, dv), q.dtype, dv)
+    sc = _conv_args(conv, N, H, dk, dv, q.dtype)
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
         (FLAG_SIGNED_ALPHA if signed_alpha else 0) | (FLAG_OUT_NORM if on is not None else 0)
-    if on is not None:
+    if on is not None or sc is not None:
         dg = None if gate is None else ctypes.byref(DecayGate(z.data_ptr(), A_log.data_ptr(),
                                                               None if dt_bias is None else dt_bias.data_ptr()))
         st = lib.kda_recurrent_step_fused(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale),
-                                          flags, _ptr(q), _ptr(k), _ptr(v), _ptr(g), dg, _ptr(beta), ctypes.byref(on),
-                                          _ptr(state), _ptr(o), _stream(stream))
+                                          flags, _ptr(q), _ptr(k), _ptr(v), _ptr(g), dg, _ptr(beta),
+                                          None if sc is None else ctypes.byref(sc),
+                                          None if on is None else ctypes.byref(on), _ptr(state), _ptr(o),
+                                          _stream(stream))
     elif gate is None:
         st = lib.kda_recurrent_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out_dtype), float(scale), flags,
                                     _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_abi.hip", "kda_decode.hip", "kda_chunk_fp32.hip", "kda_chunk_two_pass.hip", "kda_validate.hip"]
+SOURCES = ["kda_abi.hip", "kda_decode.hip", "kda_chunk_fp32.hip", "kda_chunk_two_pass.hip", "kda_validate.hip",
+           "kda_conv.hip", "kda_norm.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

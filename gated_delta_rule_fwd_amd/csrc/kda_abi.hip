@@ -56,16 +56,32 @@ bool uses_two_pass(const kda_chunk_desc* d)
     return d->in_dtype == KDA_BF16 && d->d_k == 128 && d->d_v == 128 && !(d->flags & KDA_FLAG_FP32_PATH);
 }
 
-// Workspace of one call: validation counters first, then the records (matrix
-// core path) or the fp32 path's temporary output (output norm only).
+// fp32 staging of o for the norm pass (a bf16 o with KDA_FLAG_OUT_NORM)
+size_t norm_staging_bytes(const kda_chunk_desc* d)
+{
+    if (!(d->flags & KDA_FLAG_OUT_NORM) || d->out_dtype != KDA_BF16) return 0;
+    return static_cast<size_t>(d->B) * d->T * d->H * d->d_v * sizeof(float);
+}
+
+// Workspace of one call: validation counters, the records (matrix-core
+// path), then the norm staging.
 size_t workspace_need(const kda_chunk_desc* d, bool packed)
 {
     size_t bytes = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
-    if (uses_two_pass(d))
-        bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed);
-    else if (d->flags & KDA_FLAG_OUT_NORM)
-        bytes += static_cast<size_t>(d->B) * d->T * d->H * d->d_v * sizeof(float);
-    return bytes;
+    if (uses_two_pass(d)) bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed);
+    return bytes + norm_staging_bytes(d);
+}
+
+// Conv pointers: every weight present, everything 16-byte aligned.
+bool conv_ok(const kda_short_conv* conv)
+{
+    if (!conv) return true;
+    for (int i = 0; i < 3; ++i) {
+        if (!conv->weight[i] || !aligned16(conv->weight[i])) return false;
+        if (conv->init_state[i] && !aligned16(conv->init_state[i])) return false;
+        if (conv->final_state[i] && !aligned16(conv->final_state[i])) return false;
+    }
+    return true;
 }
 
 // Checks shared by the prefill and decode entry points for the output norm.
@@ -104,8 +120,8 @@ struct Gate {
 
 kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const float* g,
                           const Gate* gate, const float* beta, const float* init_state, const int32_t* cu_seqlens,
-                          const kda_out_norm* norm, void* o, float* final_state, void* workspace, size_t ws_bytes,
-                          hipStream_t stream)
+                          const kda_short_conv* conv, const kda_out_norm* norm, void* o, float* final_state,
+                          void* workspace, size_t ws_bytes, hipStream_t stream)
 {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
@@ -123,6 +139,7 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     if (gate && tokens > 0 && !gate->A_log) return KDA_ERR_INVALID_ARG;
     if (!out_norm_ok(norm, d->flags, o)) return KDA_ERR_INVALID_ARG;
     if (norm && tokens > 0 && !norm->gate) return KDA_ERR_INVALID_ARG;
+    if (!conv_ok(conv)) return KDA_ERR_INVALID_ARG;
     const void* rows[] = {q, k, v, decay, init_state, o, final_state, gate ? gate->dt_bias : nullptr};
     for (const void* p : rows)
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
@@ -165,6 +182,11 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     a.out_gate = norm ? norm->gate : nullptr;
     a.norm_w = norm ? norm->weight : nullptr;
     a.norm_eps = norm ? norm->eps : 0.f;
+    a.conv = conv ? 1 : 0;
+    for (int i = 0; i < 3; ++i) {
+        a.conv_w[i] = conv ? conv->weight[i] : nullptr;
+        a.conv_init[i] = conv ? conv->init_state[i] : nullptr;
+    }
 
     hipError_t e;
     if (d->flags & KDA_FLAG_VALIDATE) {
@@ -180,19 +202,35 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     }
 
     const size_t off = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+    const size_t recs = uses_two_pass(d) ? kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs,
+                                                                          cu_seqlens != nullptr)
+                                         : 0;
+    // with a norm, the forward pass writes fp32 o (to the staging area when
+    // o is bf16), then the norm pass writes o
+    kda::ChunkArgs fw = a;
+    if (norm) {
+        fw.out_norm = 0;
+        fw.out_bf16 = false;
+        if (a.out_bf16) fw.o = static_cast<char*>(workspace) + off + recs;
+    }
     if (uses_two_pass(d))
-        e = kda::launch_chunk_two_pass(a, static_cast<char*>(workspace) + off, stream);
+        e = kda::launch_chunk_two_pass(fw, static_cast<char*>(workspace) + off, stream);
     else
-        e = kda::launch_chunk_fp32(a, norm ? reinterpret_cast<float*>(static_cast<char*>(workspace) + off) : nullptr,
-                                   stream);
+        e = kda::launch_chunk_fp32(fw, stream);
+    if (e == hipSuccess && norm) e = kda::launch_out_norm(a, static_cast<const float*>(fw.o), stream);
     if (e != hipSuccess) return hip_fail(e);
+    if (conv) {
+        // after every kernel that reads the incoming conv state
+        e = kda::launch_conv_final(a, conv->final_state, stream);
+        if (e != hipSuccess) return hip_fail(e);
+    }
     return KDA_OK;
 }
 
 kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype, float scale,
                                unsigned flags, const void* q, const void* k, const void* v, const float* g,
-                               const Gate* gate, const float* beta, const kda_out_norm* norm, float* state, void* o,
-                               hipStream_t stream)
+                               const Gate* gate, const float* beta, const kda_short_conv* conv,
+                               const kda_out_norm* norm, float* state, void* o, hipStream_t stream)
 {
     if (flags & ~kDecodeFlags) return KDA_ERR_UNSUPPORTED;
     if (gate && (flags & KDA_FLAG_SIGNED_ALPHA)) return KDA_ERR_UNSUPPORTED;
@@ -201,6 +239,7 @@ kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtyp
     if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
     if (static_cast<long long>(N) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
     if (!out_norm_ok(norm, flags, o)) return KDA_ERR_INVALID_ARG;
+    if (!conv_ok(conv)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
     if (norm && !norm->gate) return KDA_ERR_INVALID_ARG;
     const void* decay = gate ? gate->z : static_cast<const void*>(g);
@@ -237,6 +276,12 @@ kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtyp
     a.out_gate = norm ? norm->gate : nullptr;
     a.norm_w = norm ? norm->weight : nullptr;
     a.norm_eps = norm ? norm->eps : 0.f;
+    a.conv = conv ? 1 : 0;
+    for (int i = 0; i < 3; ++i) {
+        a.conv_w[i] = conv ? conv->weight[i] : nullptr;
+        a.conv_init[i] = conv ? conv->init_state[i] : nullptr;
+        a.conv_final[i] = conv ? conv->final_state[i] : nullptr;
+    }
     hipError_t e = kda::launch_decode(a, stream);
     if (e != hipSuccess) return hip_fail(e);
     return KDA_OK;
@@ -250,8 +295,8 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
                          const float* beta, const float* init_state, const int32_t* cu_seqlens, void* o,
                          float* final_state, void* workspace, size_t ws_bytes, hipStream_t stream)
 {
-    return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, nullptr, o, final_state, workspace,
-                          ws_bytes, stream);
+    return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, nullptr, nullptr, o, final_state,
+                          workspace, ws_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_gated(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const void* z,
@@ -260,22 +305,22 @@ kda_status kda_chunk_fwd_gated(const kda_chunk_desc* d, const void* q, const voi
                                size_t ws_bytes, hipStream_t stream)
 {
     const Gate gate{z, A_log, dt_bias};
-    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, nullptr, o, final_state, workspace,
-                          ws_bytes, stream);
+    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, nullptr, nullptr, o, final_state,
+                          workspace, ws_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_fused(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const float* g,
                                const kda_decay_gate* decay_gate, const float* beta, const float* init_state,
-                               const int32_t* cu_seqlens, const kda_out_norm* norm, void* o, float* final_state,
-                               void* workspace, size_t ws_bytes, hipStream_t stream)
+                               const int32_t* cu_seqlens, const kda_short_conv* conv, const kda_out_norm* norm,
+                               void* o, float* final_state, void* workspace, size_t ws_bytes, hipStream_t stream)
 {
     if (decay_gate && g) return KDA_ERR_INVALID_ARG;
     if (!decay_gate)
-        return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, norm, o, final_state, workspace,
-                              ws_bytes, stream);
+        return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, conv, norm, o, final_state,
+                              workspace, ws_bytes, stream);
     const Gate gate{decay_gate->z, decay_gate->A_log, decay_gate->dt_bias};
-    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, norm, o, final_state, workspace,
-                          ws_bytes, stream);
+    return chunk_fwd_impl(d, q, k, v, nullptr, &gate, beta, init_state, cu_seqlens, conv, norm, o, final_state,
+                          workspace, ws_bytes, stream);
 }
 
 kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
@@ -283,7 +328,7 @@ kda_status kda_recurrent_step(int N, int H, int d_k, int d_v, kda_dtype in_dtype
                               const float* g, const float* beta, float* state, void* o, hipStream_t stream)
 {
     return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, nullptr,
-                               state, o, stream);
+                               nullptr, state, o, stream);
 }
 
 kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
@@ -293,21 +338,22 @@ kda_status kda_recurrent_step_gated(int N, int H, int d_k, int d_v, kda_dtype in
 {
     const Gate gate{z, A_log, dt_bias};
     return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, nullptr, &gate, beta,
-                               nullptr, state, o, stream);
+                               nullptr, nullptr, state, o, stream);
 }
 
 kda_status kda_recurrent_step_fused(int N, int H, int d_k, int d_v, kda_dtype in_dtype, kda_dtype out_dtype,
                                     float scale, unsigned flags, const void* q, const void* k, const void* v,
                                     const float* g, const kda_decay_gate* decay_gate, const float* beta,
-                                    const kda_out_norm* norm, float* state, void* o, hipStream_t stream)
+                                    const kda_short_conv* conv, const kda_out_norm* norm, float* state, void* o,
+                                    hipStream_t stream)
 {
     if (decay_gate && g) return KDA_ERR_INVALID_ARG;
     if (!decay_gate)
-        return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, norm,
-                                   state, o, stream);
+        return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, g, nullptr, beta, conv,
+                                   norm, state, o, stream);
     const Gate gate{decay_gate->z, decay_gate->A_log, decay_gate->dt_bias};
-    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, nullptr, &gate, beta, norm,
-                               state, o, stream);
+    return recurrent_step_impl(N, H, d_k, d_v, in_dtype, out_dtype, scale, flags, q, k, v, nullptr, &gate, beta, conv,
+                               norm, state, o, stream);
 }
 
 }  // extern "C"

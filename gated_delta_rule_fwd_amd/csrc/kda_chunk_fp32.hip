@@ -18,6 +18,9 @@
 // the costly one; it needs no bound on g.  The triangular system is solved by
 // forward substitution, i.e. the UT transform applied to the right-hand side.
 //
+// With the short convolution, q, k and v are the SiLU of a causal width-4
+// convolution of the raw inputs, formed as they are staged.
+//
 // One workgroup owns one (chain, 32-column slice of d_v); d_v columns are
 // independent affine systems ("Kimi K3 の KDA ..." section 2.3.2), so the
 // slices never communicate.  The state slice lives in LDS for the whole chain.
@@ -86,8 +89,16 @@ chunk_fp32_kernel(ChunkArgs a)
             float qv = 0.f, kv = 0.f, gv = 0.f;
             if (r < L) {
                 const size_t idx = (static_cast<size_t>(c0 + r) * H + h) * DK + i;
-                qv = Elem<Tin>::load(q, idx);
-                kv = Elem<Tin>::load(k, idx);
+                if (a.conv) {   // silu(causal width-4 conv) of the raw projections
+                    const size_t col = static_cast<size_t>(h) * DK + i, w = static_cast<size_t>(H) * DK;
+                    qv = conv_silu(q, static_cast<const Tin*>(a.conv_init[0]), a.conv_w[0], c0 + r, tok_begin, w,
+                                   3 * static_cast<size_t>(n), col);
+                    kv = conv_silu(k, static_cast<const Tin*>(a.conv_init[1]), a.conv_w[1], c0 + r, tok_begin, w,
+                                   3 * static_cast<size_t>(n), col);
+                } else {
+                    qv = Elem<Tin>::load(q, idx);
+                    kv = Elem<Tin>::load(k, idx);
+                }
                 gv = a.gated ? gate_log_decay(Elem<Tin>::load(static_cast<const Tin*>(a.z), idx),
                                               a.dt_bias ? a.dt_bias[h * DK + i] : 0.f, __expf(a.A_log[h]))
                              : a.g[idx];
@@ -98,7 +109,13 @@ chunk_fp32_kernel(ChunkArgs a)
         }
         for (int e = t; e < C * DVS; e += 256) {
             const int r = e / DVS, j = e % DVS;
-            sV[r][j] = (r < L) ? Elem<Tin>::load(v, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + j) : 0.f;
+            float vv = 0.f;
+            if (r < L)
+                vv = a.conv ? conv_silu(v, static_cast<const Tin*>(a.conv_init[2]), a.conv_w[2], c0 + r, tok_begin,
+                                        static_cast<size_t>(H) * DV, 3 * static_cast<size_t>(n),
+                                        static_cast<size_t>(h) * DV + j0 + j)
+                            : Elem<Tin>::load(v, (static_cast<size_t>(c0 + r) * H + h) * DV + j0 + j);
+            sV[r][j] = vv;
         }
         if (t < C) {
             float bt = 0.f;
@@ -255,72 +272,11 @@ chunk_fp32_kernel(ChunkArgs a)
     }
 }
 
-// Output norm as its own pass over fp32 o: one wave per (token, head) row,
-// o <- o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) over the d_v columns.
-template <int DV, typename Tg, typename Tout>
-__global__ void __launch_bounds__(256)
-out_norm_kernel(const float* __restrict__ x, const Tg* __restrict__ gate, const float* __restrict__ w, float eps,
-                Tout* __restrict__ y, long rows)
-{
-    constexpr int PER = DV / 64;
-    const long row = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    const int lane = threadIdx.x & 63;
-    float xv[PER], ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        xv[e] = x[row * DV + lane + 64 * e];
-        ss += xv[e] * xv[e];
-    }
-    const float rs = rsqrtf(wave_sum(ss) * (1.f / DV) + eps);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int j = lane + 64 * e;
-        const float gt = Elem<Tg>::load(gate, static_cast<size_t>(row) * DV + j);
-        Elem<Tout>::store(y, static_cast<size_t>(row) * DV + j, xv[e] * rs * (w ? w[j] : 1.f) / (1.f + __expf(-gt)));
-    }
-}
-
-template <int DV>
-hipError_t launch_out_norm(const ChunkArgs& a, const float* x, hipStream_t stream)
-{
-    const long rows = static_cast<long>(a.B) * a.T * a.H;
-    if (rows == 0) return hipSuccess;
-    const dim3 grid(static_cast<unsigned>((rows + 3) / 4)), block(256);
-    const float* w = a.norm_w;
-    if (a.in_bf16 && a.out_bf16)
-        out_norm_kernel<DV, uint16_t, uint16_t><<<grid, block, 0, stream>>>(
-            x, static_cast<const uint16_t*>(a.out_gate), w, a.norm_eps, static_cast<uint16_t*>(a.o), rows);
-    else if (a.in_bf16)
-        out_norm_kernel<DV, uint16_t, float><<<grid, block, 0, stream>>>(
-            x, static_cast<const uint16_t*>(a.out_gate), w, a.norm_eps, static_cast<float*>(a.o), rows);
-    else if (a.out_bf16)
-        out_norm_kernel<DV, float, uint16_t><<<grid, block, 0, stream>>>(
-            x, static_cast<const float*>(a.out_gate), w, a.norm_eps, static_cast<uint16_t*>(a.o), rows);
-    else
-        out_norm_kernel<DV, float, float><<<grid, block, 0, stream>>>(
-            x, static_cast<const float*>(a.out_gate), w, a.norm_eps, static_cast<float*>(a.o), rows);
-    return hipGetLastError();
-}
-
 template <int DK, int DV>
-hipError_t launch_dims(const ChunkArgs& a0, float* o_tmp, hipStream_t stream)
+hipError_t launch_dims(const ChunkArgs& a, hipStream_t stream)
 {
-    const int chains = (a0.cu_seqlens ? a0.num_seqs : a0.B) * a0.H;
+    const int chains = (a.cu_seqlens ? a.num_seqs : a.B) * a.H;
     const dim3 grid(chains * (DV / DVS)), block(256);
-    if (a0.out_norm) {
-        // the chunk kernel leaves fp32 o in o_tmp; the norm pass writes o
-        ChunkArgs a = a0;
-        a.o = o_tmp;
-        if (a.in_bf16)
-            chunk_fp32_kernel<DK, DV, uint16_t, float><<<grid, block, 0, stream>>>(a);
-        else
-            chunk_fp32_kernel<DK, DV, float, float><<<grid, block, 0, stream>>>(a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        return launch_out_norm<DV>(a0, o_tmp, stream);
-    }
-    const ChunkArgs& a = a0;
     if (a.in_bf16 && a.out_bf16)
         chunk_fp32_kernel<DK, DV, uint16_t, uint16_t><<<grid, block, 0, stream>>>(a);
     else if (a.in_bf16)
@@ -334,12 +290,12 @@ hipError_t launch_dims(const ChunkArgs& a0, float* o_tmp, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_chunk_fp32(const ChunkArgs& a, float* o_tmp, hipStream_t stream)
+hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t stream)
 {
-    if (a.dk == 128 && a.dv == 128) return launch_dims<128, 128>(a, o_tmp, stream);
-    if (a.dk == 128 && a.dv == 64) return launch_dims<128, 64>(a, o_tmp, stream);
-    if (a.dk == 64 && a.dv == 128) return launch_dims<64, 128>(a, o_tmp, stream);
-    return launch_dims<64, 64>(a, o_tmp, stream);
+    if (a.dk == 128 && a.dv == 128) return launch_dims<128, 128>(a, stream);
+    if (a.dk == 128 && a.dv == 64) return launch_dims<128, 64>(a, stream);
+    if (a.dk == 64 && a.dv == 128) return launch_dims<64, 128>(a, stream);
+    return launch_dims<64, 64>(a, stream);
 }
 
 }  // namespace kda

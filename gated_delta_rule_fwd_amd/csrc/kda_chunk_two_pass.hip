@@ -43,7 +43,9 @@
 //                                                 nearly cancel)
 //   K Gamma S, Q Gamma S  fp16 operand x fp16 hi/lo state
 //   A_qk U~             fp16 hi/lo x fp16
-//   K'^T U~             fp16 x fp16              (|K'| <= 1, U~ bounded)
+//   K'^T U~             fp16 x fp16 hi/lo        (|K'| <= 1; U~ split because
+//                                                 the state can be small next
+//                                                 to U~)
 #include "kda_kernels.h"
 #include "kda_mfma.h"
 
@@ -55,11 +57,6 @@ using namespace mfma;
 
 static_assert(sizeof(ChunkRecord) == kChunkRecordBytes, "ChunkRecord layout");
 
-#ifndef KDA_PLAIN_SCAN_WAVES
-#define KDA_PLAIN_SCAN_WAVES 4
-#endif
-// waves per pass-2 workgroup without the output norm (4: two workgroups per chain)
-constexpr int kPlainScanWaves = KDA_PLAIN_SCAN_WAVES;
 
 // ---------------------------------------------------------------------------
 // Pass 1: chunk-local operands
@@ -128,7 +125,9 @@ __device__ __forceinline__ float row_sign_scan16(float x)
 // into q^ and k^ of row r, which gives every pair factor its sigma_r sigma_s,
 // and the chunk-end sign sigma_L into gamma and K^ gamma/Gamma.  All the
 // exponential factors stay those of b = sum log|alpha|.
-template <bool SIGNED>
+constexpr int XS_LD = DK + 8;   // row stride (bf16) of the short convolution's staging
+
+template <bool SIGNED, bool CONV>
 __global__ void __launch_bounds__(NT, 2)
 chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __restrict__ slot_seq, int nslots)
 {
@@ -147,20 +146,23 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
     // q/k/g rows are adjacent in memory
     const int h = blockIdx.x % H, slot = blockIdx.x / H;
 
-    long c0, tok1;
+    long c0, tok0, tok1;
+    int seq;
     if (a.cu_seqlens) {
-        const int seq = slot_seq[slot];
+        seq = slot_seq[slot];
         if (seq < 0) return;
         int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
         b0 = min(max(b0, 0), a.T);
         b1 = min(max(b1, b0), a.T);
         c0 = b0 + static_cast<long>(slot - (seq + b0 / C)) * C;
+        tok0 = b0;
         tok1 = b1;
     } else {
         const int nck = (a.T + C - 1) / C;
-        const int seq = slot / nck;
+        seq = slot / nck;
         c0 = static_cast<long>(seq) * a.T + static_cast<long>(slot - seq * nck) * C;
-        tok1 = static_cast<long>(seq) * a.T + a.T;
+        tok0 = static_cast<long>(seq) * a.T;
+        tok1 = tok0 + a.T;
     }
     if (c0 >= tok1) return;
     const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
@@ -180,28 +182,13 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         const uint16_t* kr = static_cast<const uint16_t*>(a.k) + base * DK + 8 * g;
         uint4 rq[4], rk[4];
         float4 rgv[8];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            rq[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
-            rk[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
-        }
+        uint4 rz[4];
+        // the decay inputs and beta are requested first: with the short
+        // convolution their latency then overlaps the staging below
         if (a.gated) {
-            // g = -5 sigmoid(e^{A_h} (z + dt_bias)) from bf16 z
             const uint16_t* zr = static_cast<const uint16_t*>(a.z) + base * DK + 8 * g;
-            const float ea = __expf(a.A_log[h]);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const uint4 rz = *reinterpret_cast<const uint4*>(zr + 32 * kb);
-                float4 b0 = make_float4(0.f, 0.f, 0.f, 0.f), b1 = b0;
-                if (a.dt_bias) {
-                    b0 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g);
-                    b1 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g + 4);
-                }
-                rgv[2 * kb] = make_float4(gate_log_decay(bf_lo(rz.x), b0.x, ea), gate_log_decay(bf_hi(rz.x), b0.y, ea),
-                                          gate_log_decay(bf_lo(rz.y), b0.z, ea), gate_log_decay(bf_hi(rz.y), b0.w, ea));
-                rgv[2 * kb + 1] = make_float4(gate_log_decay(bf_lo(rz.z), b1.x, ea), gate_log_decay(bf_hi(rz.z), b1.y, ea),
-                                              gate_log_decay(bf_lo(rz.w), b1.z, ea), gate_log_decay(bf_hi(rz.w), b1.w, ea));
-            }
+            for (int kb = 0; kb < 4; ++kb) rz[kb] = *reinterpret_cast<const uint4*>(zr + 32 * kb);
         } else {
             const float* gr = a.g + base * DK + 8 * g;
 #pragma unroll
@@ -210,18 +197,118 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
                 rgv[2 * kb + 1] = *reinterpret_cast<const float4*>(gr + 32 * kb + 4);
             }
         }
-        const float braw = a.beta_logits ? beta_from_logit(a.beta[base]) : a.beta[base];
+        const float beta_in = a.beta[base];
+        if constexpr (CONV) {
+            // Short convolution of q and k ("Kimi K3 の KDA ..." section 1.2.1:
+            // per channel, the current token and the 3 before it, then SiLU).
+            // The chunk's raw rows with the 3 before it, and this head's taps,
+            // go to LDS (the space of the later phases); each lane then
+            // convolves its own row and channels in fp32.  Rows before the
+            // sequence start come from its conv state (or are zero); rows past
+            // its end repeat the last token (masked later, like the plain path).
+            // rows padded to XS_LD so the 16 lanes that read 16 consecutive rows
+            // of the same channels hit distinct LDS banks
+            uint16_t* xs = reinterpret_cast<uint16_t*>(&s.u);                        // [2][C + 3][XS_LD] raw
+            float* wsm = reinterpret_cast<float*>(xs + 2 * (C + 3) * XS_LD);         // [2][DK][4] taps
+            static_assert(2 * (C + 3) * XS_LD * 2 + 2 * DK * 4 * 4 <= sizeof(s.u) + sizeof(s.akk), "conv staging fits");
+            const uint16_t* src[2] = {static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k)};
+            const uint16_t* st[2] = {static_cast<const uint16_t*>(a.conv_init[0]),
+                                     static_cast<const uint16_t*>(a.conv_init[1])};
+            constexpr int PPR = DK / 8, PIECES = 2 * (C + 3) * PPR;
+            for (int i = t; i < PIECES; i += NT) {
+                const int x = i / ((C + 3) * PPR), rem = i % ((C + 3) * PPR), r = rem / PPR, part = rem % PPR;
+                const long tj = c0 - 3 + r;
+                uint4 val = make_uint4(0u, 0u, 0u, 0u);
+                if (tj >= tok0)
+                    val = *reinterpret_cast<const uint4*>(src[x] + (static_cast<size_t>(min(tj, tok1 - 1)) * H + h) * DK +
+                                                          8 * part);
+                else if (st[x])
+                    val = *reinterpret_cast<const uint4*>(
+                        st[x] + ((static_cast<size_t>(seq) * 3 + static_cast<size_t>(3 + tj - tok0)) * H + h) * DK +
+                        8 * part);
+                *reinterpret_cast<uint4*>(xs + (x * (C + 3) + r) * XS_LD + 8 * part) = val;
+            }
+            {
+                static_assert(NT == 2 * DK, "one thread per (tensor, channel)");
+                const int x = t / DK, c = t % DK;
+                *reinterpret_cast<float4*>(wsm + 4 * t) =
+                    *reinterpret_cast<const float4*>(a.conv_w[x] + 4 * (static_cast<size_t>(h) * DK + c));
+            }
+            __syncthreads();
+            // silu(conv) in fp32 from the staged rows row .. row + 3 (tokens
+            // tk - 3 .. tk) and taps; one group of 8 channels at a time keeps
+            // the operands of a single group live
+            auto conv_row = [&](int x, float (&dst)[32]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int ch = 32 * kb + 8 * g;
+                    uint4 raw[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        raw[j] = *reinterpret_cast<const uint4*>(xs + (x * (C + 3) + row + j) * XS_LD + ch);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float4 wt = *reinterpret_cast<const float4*>(wsm + 4 * (x * DK + ch + e));
+                        const float tw[4] = {wt.x, wt.y, wt.z, wt.w};
+                        float acc = 0.f;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t word = (e >> 1) == 0 ? raw[j].x : (e >> 1) == 1 ? raw[j].y
+                                                : (e >> 1) == 2 ? raw[j].z : raw[j].w;
+                            acc += tw[j] * ((e & 1) ? bf_hi(word) : bf_lo(word));
+                        }
+                        dst[8 * kb + e] = silu(acc);
+                    }
+                    // this group's results are produced before the next
+                    // group's LDS reads issue, which bounds the live operands
+                    __asm__ volatile("" : "+v"(dst[8 * kb + 0]), "+v"(dst[8 * kb + 1]), "+v"(dst[8 * kb + 2]),
+                                     "+v"(dst[8 * kb + 3]), "+v"(dst[8 * kb + 4]), "+v"(dst[8 * kb + 5]),
+                                     "+v"(dst[8 * kb + 6]), "+v"(dst[8 * kb + 7])::"memory");
+                }
+            };
+            conv_row(0, qv);
+            conv_row(1, kv);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                rq[kb] = *reinterpret_cast<const uint4*>(qr + 32 * kb);
+                rk[kb] = *reinterpret_cast<const uint4*>(kr + 32 * kb);
+            }
+        }
+        if (a.gated) {
+            // g = -5 sigmoid(e^{A_h} (z + dt_bias)) from bf16 z
+            const float ea = __expf(a.A_log[h]);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint4 z4 = rz[kb];
+                float4 b0 = make_float4(0.f, 0.f, 0.f, 0.f), b1 = b0;
+                if (a.dt_bias) {
+                    b0 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g);
+                    b1 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g + 4);
+                }
+                rgv[2 * kb] = make_float4(gate_log_decay(bf_lo(z4.x), b0.x, ea), gate_log_decay(bf_hi(z4.x), b0.y, ea),
+                                          gate_log_decay(bf_lo(z4.y), b0.z, ea), gate_log_decay(bf_hi(z4.y), b0.w, ea));
+                rgv[2 * kb + 1] = make_float4(gate_log_decay(bf_lo(z4.z), b1.x, ea), gate_log_decay(bf_hi(z4.z), b1.y, ea),
+                                              gate_log_decay(bf_lo(z4.w), b1.z, ea), gate_log_decay(bf_hi(z4.w), b1.w, ea));
+            }
+        }
+        const float braw = a.beta_logits ? beta_from_logit(beta_in) : beta_in;
         const float live = (row < L) ? 1.f : 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const uint32_t qw[4] = {rq[kb].x, rq[kb].y, rq[kb].z, rq[kb].w};
-            const uint32_t kw[4] = {rk[kb].x, rk[kb].y, rk[kb].z, rk[kb].w};
+            if constexpr (CONV) {
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                qv[8 * kb + 2 * e2] = bf_lo(qw[e2]);
-                qv[8 * kb + 2 * e2 + 1] = bf_hi(qw[e2]);
-                kv[8 * kb + 2 * e2] = bf_lo(kw[e2]) * live;
-                kv[8 * kb + 2 * e2 + 1] = bf_hi(kw[e2]) * live;
+                for (int e = 0; e < 8; ++e) kv[8 * kb + e] *= live;
+            } else {
+                const uint32_t qw[4] = {rq[kb].x, rq[kb].y, rq[kb].z, rq[kb].w};
+                const uint32_t kw[4] = {rk[kb].x, rk[kb].y, rk[kb].z, rk[kb].w};
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    qv[8 * kb + 2 * e2] = bf_lo(qw[e2]);
+                    qv[8 * kb + 2 * e2 + 1] = bf_hi(qw[e2]);
+                    kv[8 * kb + 2 * e2] = bf_lo(kw[e2]) * live;
+                    kv[8 * kb + 2 * e2 + 1] = bf_hi(kw[e2]) * live;
+                }
             }
             bv[8 * kb + 0] = rgv[2 * kb].x;
             bv[8 * kb + 1] = rgv[2 * kb].y;
@@ -635,56 +722,47 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 // Pass 2: the state recurrence over the records
 // ---------------------------------------------------------------------------
 
-// Pass-2 workgroups of NW waves own 16 * NW value columns each.
-template <int DVS>
+constexpr int DVS = 64;     // value columns per pass-2 workgroup: 4 waves x 16
+constexpr int NSLICE = DV / DVS;
+
+// V staging: bf16 as loaded, or fp32 when it is the short convolution's output
+template <bool CONV>
 struct alignas(16) ScanSmem {
-    ChunkRecord r;                   // this chunk's operands
-    __bf16 vs[C][DVS];               // V slice, plain [token][column]
+    ChunkRecord r;                                               // this chunk's operands
+    typename std::conditional<CONV, float, __bf16>::type vs[C][DVS];   // V slice [token][column]
     float obuf[2][C * DVS];          // output tile staging ([token][column], bf16 or fp32), two chunks
 };
 
 // output tile staging; bf16 is rounded to nearest even by the hardware conversion
-template <int DVS>
 __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const float*)
 {
     base[r * DVS + c] = x;
 }
-template <int DVS>
 __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const uint16_t*)
 {
     reinterpret_cast<uint16_t*>(base)[r * DVS + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(unsigned int bits16)
-{
-    return __uint_as_float(bits16 << 16);
-}
-
-// NW = 4: two workgroups per chain (64 columns each); NW = 8: one workgroup
-// per chain holding all 128 columns (two waves per SIMD), which the output
-// norm needs since it reduces over a whole row of o.
-template <typename Tout, int NW, bool NORM>
-__global__ void __launch_bounds__(64 * NW, 1)
+// The state update K'^T U~ takes U~ as fp16 hi + lo (two products) rather
+// than one fp16 rounding: with the keys the model produces (SiLU'd, sharing a
+// common direction) the state stays small next to what each chunk writes,
+// and U~'s single fp16 rounding alone costs ~3e-2 of RMS(S).
+template <typename Tout, bool CONV, bool SPLIT = true>
+__global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
 {
-    constexpr int NTS = 64 * NW;
-    constexpr int DVS = 16 * NW;
-    constexpr int NSLICE = DV / DVS;
-    static_assert(NSLICE == 1 || NSLICE == 2, "pass-2 slicing");
-    static_assert(!NORM || NSLICE == 1, "the output norm needs whole rows");
-    using Tstage = typename std::conditional<NORM, float, Tout>::type;
-    __shared__ ScanSmem<DVS> s;
+    __shared__ ScanSmem<CONV> s;
 
     const int t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l = t & 63, g = l >> 4, n = l & 15;
     const int H = a.H;
-    // Workgroup -> (chain, slice).  With two slices, both slices of a chain
-    // get ids that are equal mod 8, so they are dispatched to the same XCD
-    // and the second read of each record hits that XCD's L2.
+    // Workgroup -> (chain, slice).  Both slices of a chain get ids that are
+    // equal mod 8, so they are dispatched to the same XCD and the second read
+    // of each record hits that XCD's L2.
     const int bid = blockIdx.x;
-    const int slice = NSLICE == 1 ? 0 : (bid >> 3) & 1;
-    const int chain = NSLICE == 1 ? bid : (((bid >> 4) << 3) | (bid & 7));
+    const int slice = (bid >> 3) & (NSLICE - 1);
+    const int chain = ((bid >> 4) << 3) | (bid & 7);
     const int nchains = (a.cu_seqlens ? a.num_seqs : a.B) * H;
     if (chain >= nchains) return;
     const int j0 = slice * DVS;
@@ -724,42 +802,90 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     // current chunk is computed (issued in pieces between the compute steps
     // so the loads overlap them), then go to LDS between two barriers.
     constexpr int RV = static_cast<int>(sizeof(ChunkRecord) / 16);
-    constexpr int RFULL = RV / NTS;
-    constexpr int RTAIL = RV - RFULL * NTS;
+    constexpr int RFULL = RV / NT;
+    constexpr int RTAIL = RV - RFULL * NT;
     constexpr int PPR = DVS / 8;                   // 16-byte pieces per V row
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 P[RFULL + 1], PV[2];
+    // Short convolution of v ("Kimi K3 の KDA ..." section 1.2.1): the 4 raw
+    // rows under each output row travel in registers and are convolved (in
+    // fp32, staged in fp32) when they are committed to LDS; this thread's 8
+    // columns are the same for both of its rows.
+    u32x4 PVc[CONV ? 2 : 1][CONV ? 4 : 1];
+    float4 WV[CONV ? 8 : 1];
+    const uint16_t* __restrict__ vst = static_cast<const uint16_t*>(a.conv_init[2]);
+    if constexpr (CONV) {
+        const size_t chv = static_cast<size_t>(h) * DV + j0 + 8 * (t % PPR);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) WV[e] = *reinterpret_cast<const float4*>(a.conv_w[2] + 4 * (chv + e));
+    }
     // record pieces i in [i0, i1) of chunk j; piece RFULL is the partial one
     auto fetch = [&](int j, int i0, int i1) __attribute__((always_inline)) {
         const u32x4* src = reinterpret_cast<const u32x4*>(rc + j);
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
             if (i < RFULL)
-                P[i] = src[t + NTS * i];
+                P[i] = src[t + NT * i];
             else if (t < RTAIL)
-                P[i] = src[t + NTS * i];
+                P[i] = src[t + NT * i];
         }
     };
     auto fetch_v = [&](int j) __attribute__((always_inline)) {
         const long cb = tok0 + static_cast<long>(j) * C;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int idx = t + NTS * u, r = idx / PPR, part = idx % PPR;
+            const int idx = t + NT * u, r = idx / PPR, part = idx % PPR;
             // rows past the end read the last valid token: T' has zero
             // columns for them, so only finiteness matters
             const long tk = min(cb + r, tok1 - 1);
-            PV[u] = *reinterpret_cast<const u32x4*>(vp + (static_cast<size_t>(tk) * H + h) * DV + j0 + 8 * part);
+            if constexpr (CONV) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const long tj = tk - 3 + jj;
+                    if (tj >= tok0)
+                        PVc[u][jj] = *reinterpret_cast<const u32x4*>(vp + (static_cast<size_t>(tj) * H + h) * DV + j0 +
+                                                                     8 * part);
+                    else if (vst)
+                        PVc[u][jj] = *reinterpret_cast<const u32x4*>(
+                            vst + ((static_cast<size_t>(seq) * 3 + static_cast<size_t>(3 + tj - tok0)) * H + h) * DV +
+                            j0 + 8 * part);
+                    else
+                        PVc[u][jj] = u32x4{0u, 0u, 0u, 0u};
+                }
+            } else {
+                PV[u] = *reinterpret_cast<const u32x4*>(vp + (static_cast<size_t>(tk) * H + h) * DV + j0 + 8 * part);
+            }
         }
+    };
+    // silu(conv) of the 8 columns of fetched row u, written to LDS in fp32
+    auto commit_conv_v = [&](int u, float* dst) __attribute__((always_inline)) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float tw[4] = {WV[e].x, WV[e].y, WV[e].z, WV[e].w};
+            float acc = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint32_t word = PVc[u][jj][e >> 1];
+                acc += tw[jj] * ((e & 1) ? bf_hi(word) : bf_lo(word));
+            }
+            y[e] = silu(acc);
+        }
+        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(y[4], y[5], y[6], y[7]);
     };
     auto commit = [&]() __attribute__((always_inline)) {
         u32x4* dst = reinterpret_cast<u32x4*>(&s.r);
 #pragma unroll
-        for (int i = 0; i < RFULL; ++i) dst[t + NTS * i] = P[i];
-        if (t < RTAIL) dst[t + NTS * RFULL] = P[RFULL];
+        for (int i = 0; i < RFULL; ++i) dst[t + NT * i] = P[i];
+        if (t < RTAIL) dst[t + NT * RFULL] = P[RFULL];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int idx = t + NTS * u, r = idx / PPR, part = idx % PPR;
-            *reinterpret_cast<u32x4*>(&s.vs[r][8 * part]) = PV[u];
+            const int idx = t + NT * u, r = idx / PPR, part = idx % PPR;
+            if constexpr (CONV)
+                commit_conv_v(u, &s.vs[r][8 * part]);
+            else
+                *reinterpret_cast<u32x4*>(&s.vs[r][8 * part]) = PV[u];
         }
     };
 
@@ -777,82 +903,13 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         constexpr int PER_ROW = DVS / CH;
         const char* src = reinterpret_cast<const char*>(s.obuf[buf]);
 #pragma unroll
-        for (int pc = t; pc < C * PER_ROW; pc += NTS) {
+        for (int pc = t; pc < C * PER_ROW; pc += NT) {
             const int r = pc / PER_ROW, part = pc % PER_ROW;
             if (r < rows) {
                 const uint4 val = *reinterpret_cast<const uint4*>(src + (r * DVS + part * CH) * sizeof(Tout));
                 *reinterpret_cast<uint4*>(op + (static_cast<size_t>(cbase + r) * H + h) * DV + j0 + part * CH) = val;
             }
         }
-    };
-    // Output norm ("Kimi K3 の KDA ..." section 1.2.1, the gated RMSNorm after
-    // the kernel): o <- o / sqrt(mean_c o_c^2 + eps) * w_c * sigmoid(gate_c)
-    // over the d_v columns of one (token, head).  Thread t owns row t / 8 and
-    // columns 4 (t % 8 + 8 i) .. + 3, i < 4, so the 8 threads of a row read
-    // 128 contiguous bytes of the staged tile per step; the gate of chunk j
-    // is loaded during chunk j and used when its tile is stored.
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    const int nr = t >> 3, np = t & 7;
-    u32x2 G[4];
-    float4 WR[4];
-    if constexpr (NORM) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            WR[i] = a.norm_w ? *reinterpret_cast<const float4*>(a.norm_w + 4 * (np + 8 * i))
-                             : make_float4(1.f, 1.f, 1.f, 1.f);
-    }
-    auto fetch_gate = [&](long cbase) __attribute__((always_inline)) {
-        if constexpr (NORM) {
-            const long tk = min(cbase + nr, tok1 - 1);
-            const uint16_t* gp = static_cast<const uint16_t*>(a.out_gate) + (static_cast<size_t>(tk) * H + h) * DV;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) G[i] = *reinterpret_cast<const u32x2*>(gp + 4 * (np + 8 * i));
-        }
-    };
-    auto store_tile_norm = [&](int buf, long cbase, int rows) __attribute__((always_inline)) {
-        if constexpr (NORM) {
-            const float* src = s.obuf[buf] + nr * DVS;
-            float4 x[4];
-            float ss = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = *reinterpret_cast<const float4*>(src + 4 * (np + 8 * i));
-                ss += x[i].x * x[i].x + x[i].y * x[i].y + x[i].z * x[i].z + x[i].w * x[i].w;
-            }
-            ss += __shfl_xor(ss, 1, 64);
-            ss += __shfl_xor(ss, 2, 64);
-            ss += __shfl_xor(ss, 4, 64);
-            const float rs = rsqrtf(ss * (1.f / DV) + a.norm_eps);
-            if (nr < rows) {
-                Tout* dst = op + (static_cast<size_t>(cbase + nr) * H + h) * DV;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float gt[4] = {bf16_bits_to_f32(G[i].x & 0xffffu), bf16_bits_to_f32(G[i].x >> 16),
-                                         bf16_bits_to_f32(G[i].y & 0xffffu), bf16_bits_to_f32(G[i].y >> 16)};
-                    const float xv[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-                    const float wv[4] = {WR[i].x, WR[i].y, WR[i].z, WR[i].w};
-                    float y[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) y[e] = xv[e] * rs * wv[e] / (1.f + __expf(-gt[e]));
-                    if constexpr (sizeof(Tout) == 4) {
-                        *reinterpret_cast<float4*>(dst + 4 * (np + 8 * i)) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else {
-                        u32x2 pk;
-                        pk.x = static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[0]))) |
-                               (static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[1]))) << 16);
-                        pk.y = static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[2]))) |
-                               (static_cast<unsigned int>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(y[3]))) << 16);
-                        *reinterpret_cast<u32x2*>(dst + 4 * (np + 8 * i)) = pk;
-                    }
-                }
-            }
-        }
-    };
-    auto store_out = [&](int buf, long cbase, int rows) __attribute__((always_inline)) {
-        if constexpr (NORM)
-            store_tile_norm(buf, cbase, rows);
-        else
-            store_tile(buf, cbase, rows);
     };
     // operand fragments of the R step for token tiles 2mh, 2mh + 1
     auto load_r = [&](int mh, f16x8 (&fa)[2][4], float (&vv)[2][4]) __attribute__((always_inline)) {
@@ -912,8 +969,8 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                stage_out<DVS>(s.obuf[buf], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
-                               static_cast<const Tstage*>(nullptr));
+                stage_out(s.obuf[buf], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
+                          static_cast<const Tout*>(nullptr));
         }
     };
     // operand fragments of the state update for channel tiles 4half .. 4half + 3
@@ -927,8 +984,8 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         }
     };
     // S <- Diag(gamma) S + (K^ gamma/Gamma)^T U~ for channel tiles 4half .. 4half + 3
-    auto step_k = [&](int half, const f16x8 (&ka)[4][2], const float4 (&gm4)[4], const f16x8 (&ub)[2])
-        __attribute__((always_inline)) {
+    auto step_k = [&](int half, const f16x8 (&ka)[4][2], const float4 (&gm4)[4], const f16x8 (&ub)[2],
+                      const f16x8 (&ubl)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int m4 = 0; m4 < 4; ++m4) {
             const int mt = 4 * half + m4;
@@ -938,9 +995,12 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             sacc[mt][3] *= gm4[m4].w;
             sacc[mt] = mmh(ka[m4][0], ub[0], sacc[mt]);
             sacc[mt] = mmh(ka[m4][1], ub[1], sacc[mt]);
+            if constexpr (SPLIT) {
+                sacc[mt] = mmh(ka[m4][0], ubl[0], sacc[mt]);
+                sacc[mt] = mmh(ka[m4][1], ubl[1], sacc[mt]);
+            }
         }
     };
-
     // state as fp16 hi/lo B-frags (channel order of the accumulators)
     auto split_state = [&](f16x8 (&sh)[4], f16x8 (&sl)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -966,8 +1026,8 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     };
     // U~ = T' R with R as bf16 hi/lo B-frags (token order of the
     // accumulators); the result goes out as fp16 B-frags
-    auto step_t = [&](const bf16x8 (&th)[6], const bf16x8 (&tl)[6], f32x4 (&ut)[4], f16x8 (&ub)[2])
-        __attribute__((always_inline)) {
+    auto step_t = [&](const bf16x8 (&th)[6], const bf16x8 (&tl)[6], f32x4 (&ut)[4], f16x8 (&ub)[2],
+                      f16x8 (&ubl)[2]) __attribute__((always_inline)) {
         bf16x8 rbh[2], rbl[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -996,12 +1056,26 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                ub[kb][i] = static_cast<_Float16>(ut[2 * kb][i]);
-                ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
+                if constexpr (SPLIT) {
+                    _Float16 hi, lo;
+                    splith(ut[2 * kb][i], hi, lo);
+                    ub[kb][i] = hi;
+                    ubl[kb][i] = lo;
+                    splith(ut[2 * kb + 1][i], hi, lo);
+                    ub[kb][4 + i] = hi;
+                    ubl[kb][4 + i] = lo;
+                } else {
+                    ub[kb][i] = static_cast<_Float16>(ut[2 * kb][i]);
+                    ub[kb][4 + i] = static_cast<_Float16>(ut[2 * kb + 1][i]);
+                }
             }
         }
     };
 
+    // Each chunk is software-pipelined inside the wave: the LDS fragments of
+    // the next step are requested before the matrix products of the current
+    // one, so the LDS and the matrix cores work at the same time (one wave
+    // per SIMD: nothing else would hide the LDS latency).
     long prev_c0 = 0;
     int prev_L = 0;
     for (int j = 0; j < nch; ++j) {
@@ -1010,100 +1084,53 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         const bool more = j + 1 < nch;
         const int buf = j & 1;
 
-        if constexpr (NW == 4) {
-            // One wave per SIMD: each chunk is software-pipelined inside the
-            // wave (the LDS fragments of the next step are requested before
-            // the matrix products of the current one), since nothing else
-            // would hide the LDS latency.
-            f16x8 fa0[2][4], fa1[2][4];
-            float vv0[2][4], vv1[2][4];
-            load_r(0, fa0, vv0);
-            if (more) {
-                fetch_v(j + 1);
-                fetch(j + 1, 0, 5);
-            }
-            if (j > 0) store_out(buf ^ 1, prev_c0, prev_L);
-            f16x8 sh[4], sl[4];
-            split_state(sh, sl);
-            __builtin_amdgcn_sched_barrier(0);
-            load_r(1, fa1, vv1);
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 ut[4];
-            step_r(0, fa0, vv0, sh, sl, ut);
-            __builtin_amdgcn_sched_barrier(0);
-            bf16x8 th[6], tl[6];
-            load_t(th, tl);
-            if (more) fetch(j + 1, 5, 10);
-            __builtin_amdgcn_sched_barrier(0);
-            step_r(1, fa1, vv1, sh, sl, ut);
-            __builtin_amdgcn_sched_barrier(0);
-            f16x8 qa0[2][4], ah0[2][2], al0[2][2];
-            load_o(0, qa0, ah0, al0);
-            __builtin_amdgcn_sched_barrier(0);
-            f16x8 ub[2];
-            step_t(th, tl, ut, ub);
-            if (more) fetch(j + 1, 10, 15);
-            __builtin_amdgcn_sched_barrier(0);
-            f16x8 qa1[2][4], ah1[2][2], al1[2][2];
-            load_o(1, qa1, ah1, al1);
-            __builtin_amdgcn_sched_barrier(0);
-            step_o(0, buf, qa0, ah0, al0, sh, sl, ub);
-            __builtin_amdgcn_sched_barrier(0);
-            f16x8 ka0[4][2];
-            float4 gm0[4];
-            load_k(0, ka0, gm0);
-            if (more) fetch(j + 1, 15, RFULL + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            step_o(1, buf, qa1, ah1, al1, sh, sl, ub);
-            __builtin_amdgcn_sched_barrier(0);
-            f16x8 ka1[4][2];
-            float4 gm1[4];
-            load_k(1, ka1, gm1);
-            __builtin_amdgcn_sched_barrier(0);
-            step_k(0, ka0, gm0, ub);
-            step_k(1, ka1, gm1, ub);
-        } else {
-            // Two waves per SIMD hide each other's LDS latency: the steps run
-            // in order and reuse one set of fragment registers.
-            if (more) {
-                fetch_v(j + 1);
-                fetch(j + 1, 0, RFULL + 1);
-            }
-            if (j > 0) store_out(buf ^ 1, prev_c0, prev_L);
-            fetch_gate(c0);
-            f16x8 sh[4], sl[4];
-            split_state(sh, sl);
-            f32x4 ut[4];
-            {
-                f16x8 fa[2][4];
-                float vv[2][4];
-                load_r(0, fa, vv);
-                step_r(0, fa, vv, sh, sl, ut);
-                load_r(1, fa, vv);
-                step_r(1, fa, vv, sh, sl, ut);
-            }
-            f16x8 ub[2];
-            {
-                bf16x8 th[6], tl[6];
-                load_t(th, tl);
-                step_t(th, tl, ut, ub);
-            }
-            {
-                f16x8 qa[2][4], ah[2][2], al[2][2];
-                load_o(0, qa, ah, al);
-                step_o(0, buf, qa, ah, al, sh, sl, ub);
-                load_o(1, qa, ah, al);
-                step_o(1, buf, qa, ah, al, sh, sl, ub);
-            }
-            {
-                f16x8 ka[4][2];
-                float4 gm[4];
-                load_k(0, ka, gm);
-                step_k(0, ka, gm, ub);
-                load_k(1, ka, gm);
-                step_k(1, ka, gm, ub);
-            }
+        f16x8 fa0[2][4], fa1[2][4];
+        float vv0[2][4], vv1[2][4];
+        load_r(0, fa0, vv0);
+        if (more) {
+            fetch_v(j + 1);
+            fetch(j + 1, 0, 5);
         }
+        if (j > 0) store_tile(buf ^ 1, prev_c0, prev_L);
+        f16x8 sh[4], sl[4];
+        split_state(sh, sl);
+        __builtin_amdgcn_sched_barrier(0);
+        load_r(1, fa1, vv1);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 ut[4];
+        step_r(0, fa0, vv0, sh, sl, ut);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 th[6], tl[6];
+        load_t(th, tl);
+        if (more) fetch(j + 1, 5, 10);
+        __builtin_amdgcn_sched_barrier(0);
+        step_r(1, fa1, vv1, sh, sl, ut);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 qa0[2][4], ah0[2][2], al0[2][2];
+        load_o(0, qa0, ah0, al0);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 ub[2], ubl[2];
+        step_t(th, tl, ut, ub, ubl);
+        if (more) fetch(j + 1, 10, 15);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 qa1[2][4], ah1[2][2], al1[2][2];
+        load_o(1, qa1, ah1, al1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_o(0, buf, qa0, ah0, al0, sh, sl, ub);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 ka0[4][2];
+        float4 gm0[4];
+        load_k(0, ka0, gm0);
+        if (more) fetch(j + 1, 15, RFULL + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_o(1, buf, qa1, ah1, al1, sh, sl, ub);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8 ka1[4][2];
+        float4 gm1[4];
+        load_k(1, ka1, gm1);
+        __builtin_amdgcn_sched_barrier(0);
+        step_k(0, ka0, gm0, ub, ubl);
+        step_k(1, ka1, gm1, ub, ubl);
         __syncthreads();
         // every read of this chunk's record is done: the next one moves in
         if (more) commit();
@@ -1111,7 +1138,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         prev_L = L;
         __syncthreads();
     }
-    if (nch > 0) store_out((nch - 1) & 1, prev_c0, prev_L);
+    if (nch > 0) store_tile((nch - 1) & 1, prev_c0, prev_L);
 
     if (a.final_state) {
         const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
@@ -1153,35 +1180,30 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_
             slot_map_kernel<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(
                 a.cu_seqlens, a.num_seqs, a.T, static_cast<int>(slots), map);
         }
-        if (a.signed_alpha)
-            chunk_prep_kernel<true><<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map,
-                                                                                            static_cast<int>(slots));
+        const unsigned pg = static_cast<unsigned>(slots * a.H);
+        if (a.signed_alpha && a.conv)
+            chunk_prep_kernel<true, true><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
+        else if (a.signed_alpha)
+            chunk_prep_kernel<true, false><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
+        else if (a.conv)
+            chunk_prep_kernel<false, true><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
         else
-            chunk_prep_kernel<false><<<static_cast<unsigned>(slots * a.H), NT, 0, stream>>>(a, recs, map,
-                                                                                             static_cast<int>(slots));
+            chunk_prep_kernel<false, false><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
     }
     const int ns = static_cast<int>(slots);
-    if (a.out_norm) {
-        // one 8-wave workgroup per chain (whole rows of o for the norm)
-        const dim3 grid(chains), block(512);
+    // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
+    const int groups = (chains + 7) / 8;
+    const dim3 grid(groups * 8 * NSLICE), block(NT);
+    if (a.conv) {
         if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, 8, true><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<uint16_t, true><<<grid, block, 0, stream>>>(a, recs, ns);
         else
-            chunk_scan_kernel<float, 8, true><<<grid, block, 0, stream>>>(a, recs, ns);
-    } else if (kPlainScanWaves == 8) {
-        const dim3 grid(chains), block(512);
-        if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, 8, false><<<grid, block, 0, stream>>>(a, recs, ns);
-        else
-            chunk_scan_kernel<float, 8, false><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<float, true><<<grid, block, 0, stream>>>(a, recs, ns);
     } else {
-        // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
-        const int groups = (chains + 7) / 8;
-        const dim3 grid(groups * 16), block(256);
         if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, 4, false><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<uint16_t, false><<<grid, block, 0, stream>>>(a, recs, ns);
         else
-            chunk_scan_kernel<float, 4, false><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<float, false><<<grid, block, 0, stream>>>(a, recs, ns);
     }
     return hipGetLastError();
 }

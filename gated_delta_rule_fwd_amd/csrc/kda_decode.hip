@@ -8,6 +8,8 @@
 //   S  <- S~ + k^ u^T                               (erase + write, in place)
 //   o  = scale * (r + (k^ . q^) u)  == scale * S_new^T q^  (read after write)
 //   optional output norm: o <- o / sqrt(mean(o^2) + eps) * w * sigmoid(gate)
+//   optional short convolution: q, k, v = silu(causal width-4 conv) of the
+//   raw inputs with the 3 cached ones, the cache shifting by one token
 // ("Kimi K3 模型结构（2）", Q&A: decode runs this recurrent form one token at a
 // time.)
 //
@@ -21,6 +23,30 @@
 #include "kda_kernels.h"
 
 namespace kda {
+
+// One token of the short convolution for channel col of sequence n: the 3
+// cached inputs (rows 3n .. 3n + 2 of a [N, 3, width] state, oldest first;
+// zero without a state) and x; the state shifts by one, written by the same
+// thread that read it, so it may be updated in place.
+template <typename Tin>
+__device__ __forceinline__ float decode_conv(float x, const Tin* init, Tin* fin, const float* w, size_t row0,
+                                             size_t width, size_t col)
+{
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    if (init) {
+        c0 = Elem<Tin>::load(init, row0 * width + col);
+        c1 = Elem<Tin>::load(init, (row0 + 1) * width + col);
+        c2 = Elem<Tin>::load(init, (row0 + 2) * width + col);
+    }
+    const float4 wt = *reinterpret_cast<const float4*>(w + 4 * col);
+    const float y = silu(wt.x * c0 + wt.y * c1 + wt.z * c2 + wt.w * x);
+    if (fin) {
+        Elem<Tin>::store(fin, row0 * width + col, c1);
+        Elem<Tin>::store(fin, (row0 + 1) * width + col, c2);
+        Elem<Tin>::store(fin, (row0 + 2) * width + col, x);
+    }
+    return y;
+}
 
 template <int DK, int DV, typename Tin, typename Tout>
 __global__ void __launch_bounds__(256)
@@ -53,7 +79,7 @@ decode_step_kernel(DecodeArgs a)
 #pragma unroll
     for (int m = 0; m < RPT; ++m) s[m] = S4[(rg + RG * m) * CG + cg];
 
-    __shared__ float sq[DK], sk[DK], sa[DK];
+    __shared__ float sq[DK], sk[DK], sa[DK], sv[DV];
     __shared__ float red[2][4][DV];
     __shared__ float sdot;
 
@@ -65,6 +91,14 @@ decode_step_kernel(DecodeArgs a)
             const int i = lane + 64 * e;
             qv[e] = Elem<Tin>::load(q, static_cast<size_t>(c) * DK + i);
             kv[e] = Elem<Tin>::load(k, static_cast<size_t>(c) * DK + i);
+            if (a.conv) {   // silu(causal width-4 conv) with the cached inputs
+                const int n = c / a.H, h = c % a.H;
+                const size_t col = static_cast<size_t>(h) * DK + i, width = static_cast<size_t>(a.H) * DK;
+                qv[e] = decode_conv(qv[e], static_cast<const Tin*>(a.conv_init[0]), static_cast<Tin*>(a.conv_final[0]),
+                                    a.conv_w[0], 3 * static_cast<size_t>(n), width, col);
+                kv[e] = decode_conv(kv[e], static_cast<const Tin*>(a.conv_init[1]), static_cast<Tin*>(a.conv_final[1]),
+                                    a.conv_w[1], 3 * static_cast<size_t>(n), width, col);
+            }
             float gi;
             if (a.gated) {   // bounded decay map of the gated entry point
                 const int h = c % a.H;
@@ -93,6 +127,18 @@ decode_step_kernel(DecodeArgs a)
         }
         dot = wave_sum(dot);
         if (lane == 0) sdot = dot;
+#pragma unroll
+        for (int e = 0; e < DV / 64; ++e) {
+            const int j = lane + 64 * e;
+            float vj = Elem<Tin>::load(v, static_cast<size_t>(c) * DV + j);
+            if (a.conv) {
+                const int n = c / a.H, h = c % a.H;
+                vj = decode_conv(vj, static_cast<const Tin*>(a.conv_init[2]), static_cast<Tin*>(a.conv_final[2]),
+                                 a.conv_w[2], 3 * static_cast<size_t>(n), static_cast<size_t>(a.H) * DV,
+                                 static_cast<size_t>(h) * DV + j);
+            }
+            sv[j] = vj;
+        }
     }
     __syncthreads();
 
@@ -132,7 +178,7 @@ decode_step_kernel(DecodeArgs a)
         const int j = 4 * cg + e;
         const float pj = red[0][0][j] + red[0][1][j] + red[0][2][j] + red[0][3][j];
         const float rj = red[1][0][j] + red[1][1][j] + red[1][2][j] + red[1][3][j];
-        const float vj = Elem<Tin>::load(v, static_cast<size_t>(c) * DV + j);
+        const float vj = sv[j];
         u[e] = b * (vj - pj);
         ov[e] = scale * (rj + dot * u[e]);
     }

@@ -46,6 +46,35 @@ __device__ __forceinline__ float gate_log_decay(float z, float bias, float exp_a
 }
 __device__ __forceinline__ float beta_from_logit(float b) { return 1.f / (1.f + __expf(-b)); }
 
+// Short convolution prologue ("Kimi K3 の KDA ..." section 1.2.1: causal and
+// per channel over the current token and the 3 before it, then SiLU).  Taps
+// w[4c .. 4c+3] of channel c run oldest token first; inputs before a
+// sequence's first token come from its conv state (3 rows of `width`
+// channels per sequence, oldest first) or are zero.
+__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+
+template <typename Tin>
+__device__ __forceinline__ float conv_input(const Tin* x, const Tin* state, long tk, long tok0, size_t width,
+                                            size_t state_row0, size_t col)
+{
+    if (tk >= tok0) return Elem<Tin>::load(x, static_cast<size_t>(tk) * width + col);
+    if (!state) return 0.f;
+    return Elem<Tin>::load(state, (state_row0 + static_cast<size_t>(3 + tk - tok0)) * width + col);
+}
+
+// silu(conv) at token tk (>= tok0) of channel col; state_row0 = 3 * sequence.
+template <typename Tin>
+__device__ __forceinline__ float conv_silu(const Tin* x, const Tin* state, const float* w, long tk, long tok0,
+                                           size_t width, size_t state_row0, size_t col)
+{
+    const float4 wt = *reinterpret_cast<const float4*>(w + 4 * col);
+    float acc = wt.w * conv_input(x, state, tk, tok0, width, state_row0, col);
+    acc += wt.z * conv_input(x, state, tk - 1, tok0, width, state_row0, col);
+    acc += wt.y * conv_input(x, state, tk - 2, tok0, width, state_row0, col);
+    acc += wt.x * conv_input(x, state, tk - 3, tok0, width, state_row0, col);
+    return silu(acc);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);

@@ -36,6 +36,11 @@ struct ChunkArgs {
     const float* norm_w;
     float norm_eps;
     int out_norm;
+    // short convolution + SiLU on q, k, v (index 0, 1, 2): taps [H*d, 4]
+    // fp32 and conv states [N, 3, H*d] in in_dtype (nullable: zeros)
+    const float* conv_w[3];
+    const void* conv_init[3];
+    int conv;
 };
 
 // Inputs of one decode step; z/A_log/dt_bias replace g when gated.
@@ -61,13 +66,23 @@ struct DecodeArgs {
     const float* norm_w;
     float norm_eps;
     int out_norm;
+    // short convolution: taps, the conv states read ([N, 3, H*d], nullable:
+    // zeros) and where the shifted states go (nullable: not kept; may alias)
+    const float* conv_w[3];
+    const void* conv_init[3];
+    void* conv_final[3];
+    int conv;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
-// fp32 per-position-pair path: any supported head dims and dtypes.  With
-// a.out_norm it writes fp32 o to o_tmp ([tokens, H, d_v]) and then applies
-// the output norm in a second kernel that writes a.o.
-hipError_t launch_chunk_fp32(const ChunkArgs& a, float* o_tmp, hipStream_t stream);
+// fp32 per-position-pair path: any supported head dims and dtypes.
+hipError_t launch_chunk_fp32(const ChunkArgs& a, hipStream_t stream);
+
+// Output norm, one wave per (token, head) row of d_v: a.o <- x / sqrt(mean(x^2)
+// + a.norm_eps) * a.norm_w * sigmoid(a.out_gate) with x the fp32 output of the
+// forward pass (a.o itself when a.o is fp32).  The prefill paths run it after
+// the forward pass, since their workgroups hold only a slice of each row.
+hipError_t launch_out_norm(const ChunkArgs& a, const float* x, hipStream_t stream);
 
 // Matrix-core path: bf16 inputs, d_k = d_v = 128, g >= -5, in two passes.
 //   pass 1 (chunk-parallel): every (chunk, head) writes one ChunkRecord of
@@ -83,6 +98,12 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed);
 // int32 per slot naming its sequence or -1.
 size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed);
 hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream);
+
+// Conv states after a prefill: the last 3 raw inputs of every sequence for
+// q, k, v (rows from a.conv_init where a sequence is shorter than 3); each
+// thread reads all three source rows of its (sequence, channel) before
+// writing, so final may alias a.conv_init.
+hipError_t launch_conv_final(const ChunkArgs& a, void* const final_state[3], hipStream_t stream);
 
 // Device-side range checks for KDA_FLAG_VALIDATE; counts violations into
 // counters[0..2] (g, beta, cu_seqlens); the launcher zeroes them first with

@@ -88,10 +88,12 @@ typedef enum kda_dtype {
  * points. */
 #define KDA_FLAG_SIGNED_ALPHA 0x10u
 /* The call carries an output norm (kda_out_norm below).  Must be set exactly
- * when a norm is passed to kda_chunk_fwd_fused / kda_recurrent_step_fused;
- * it is part of the descriptor so that kda_chunk_fwd_workspace_bytes() can
- * size the fp32 path's temporary output. */
+ * when a norm is passed to kda_chunk_fwd_fused / kda_recurrent_step_fused.
+ * It is part of the descriptor so that kda_chunk_fwd_workspace_bytes() can
+ * size the fp32 staging of o that a prefill with a bf16 o needs: the norm
+ * runs as a second kernel there, and it must see o before it is rounded. */
 #define KDA_FLAG_OUT_NORM 0x20u
+
 
 typedef struct kda_chunk_desc {
     int B;              /* batch (must be 1 when cu_seqlens is given) */
@@ -109,9 +111,8 @@ typedef struct kda_chunk_desc {
 /* Bytes of device workspace the chunkwise entry points need for this
  * descriptor: the matrix-core path (bf16 inputs, d_k = d_v = 128, no
  * KDA_FLAG_FP32_PATH) keeps one 74,240-byte record per (64-token chunk,
- * head) there; the fp32 path needs none, except B*T*H*d_v fp32 values for
- * its temporary output under KDA_FLAG_OUT_NORM; KDA_FLAG_VALIDATE adds 256
- * bytes.  When num_seqs > 0 and B == 1 the figure covers both the dense and
+ * head) there; the fp32 path needs none; KDA_FLAG_OUT_NORM with a bf16 o adds
+ * B*T*H*d_v fp32 values; KDA_FLAG_VALIDATE adds 256 bytes.  When num_seqs > 0 and B == 1 the figure covers both the dense and
  * the packed (cu_seqlens) layout.  Returns 0 for a descriptor the entry
  * points reject and (size_t)-1 for a null descriptor. */
 KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
@@ -214,7 +215,7 @@ typedef struct kda_decay_gate {
 } kda_decay_gate;
 
 /*
- * Output norm fused at the store of o ("Kimi K3 の KDA ..." section 1.2.1:
+ * Output norm ("Kimi K3 の KDA ..." section 1.2.1:
  * after the kernel, the model applies a per-head RMSNorm over the head's
  * value dimension, a sigmoid on the output gate, and their elementwise
  * product).  Per token (and sequence) t, head h and value channel c, with o
@@ -228,6 +229,11 @@ typedef struct kda_decay_gate {
  *   weight  [d_v] fp32 per-channel gain shared by all heads, nullable
  *           (ones), 16-byte aligned
  *   eps     >= 0, added to the mean square (the pages give no value)
+ *
+ * The decode step applies it in the kernel that computes o.  The prefill
+ * paths split each row of o over workgroups, so there it runs as a second
+ * kernel over fp32 o: in place for an fp32 o, from the workspace (sized by
+ * KDA_FLAG_OUT_NORM) for a bf16 o.
  */
 typedef struct kda_out_norm {
     const void* gate;
@@ -236,22 +242,57 @@ typedef struct kda_out_norm {
 } kda_out_norm;
 
 /*
- * The forward pass with both of the model's adjacent steps fused: the
- * decay-gate prologue (when decay_gate is given; g must then be NULL) and the
- * output norm (when norm is given; KDA_FLAG_OUT_NORM must then be set in the
- * flags, and only then).  With decay_gate == NULL and norm == NULL this is
- * kda_chunk_fwd / kda_recurrent_step.  Every other argument, layout, flag,
- * workspace rule and error is that of those entry points; a norm with a
- * null gate or a negative or non-finite eps is KDA_ERR_INVALID_ARG, as is a
- * mismatch between norm and KDA_FLAG_OUT_NORM.  o must not alias the norm's
- * gate.
+ * Short convolution fused at the load of q, k and v ("Kimi K3 の KDA ..."
+ * section 1.2.1: three causal convolutions of width 4, each channel
+ * independent, over the current token and the 3 before it, followed by a
+ * SiLU; "GDN, KDA の整理", the conv cache of the previous 3 inputs).  With it
+ * q, k and v passed to the entry point are the raw projections, and the
+ * forward pass uses, per tensor x in (q, k, v), sequence token t and channel
+ * c of the H*d channels (c = h*d + i),
+ *
+ *   x'[t, c] = silu(sum_{j<4} weight[c][j] * x[t - 3 + j, c])
+ *
+ * with x[t'] for t' before the sequence's first token taken from row
+ * 3 + t' - first of init_state (zero when it is NULL).  On the matrix-core
+ * path x' is rounded to bf16 before use, as a bf16 module would hand it over.
+ *
+ *   weight[i]       [H*d, 4] fp32 (d = d_k for q, k; d_v for v), 16-byte
+ *                   aligned; taps of channel c at 4c .. 4c+3, oldest token
+ *                   first.  Required.
+ *   init_state[i]   [N, 3, H*d] in_dtype, 16-byte aligned: the 3 inputs that
+ *                   precede each sequence, oldest first; NULL = zeros.
+ *   final_state[i]  [N, 3, H*d] in_dtype, 16-byte aligned: receives each
+ *                   sequence's last 3 raw inputs (taken from init_state where
+ *                   the sequence is shorter than 3); NULL = not written.  May
+ *                   alias init_state[i] (it is written after every read).
+ *
+ * For the decode step N sequences advance by one token: init_state is the
+ * conv cache before the token and final_state receives it shifted by one.
+ */
+typedef struct kda_short_conv {
+    const float* weight[3];
+    const void* init_state[3];
+    void* final_state[3];
+} kda_short_conv;
+
+/*
+ * The forward pass with the model's adjacent steps: the short convolution
+ * of q, k, v (when conv is given), the decay-gate prologue (when decay_gate
+ * is given; g must then be NULL) and the output norm (when norm is given;
+ * KDA_FLAG_OUT_NORM must then be set in the flags, and only then).  With all
+ * three NULL this is kda_chunk_fwd / kda_recurrent_step.  Every other
+ * argument, layout, flag, workspace rule and error is that of those entry
+ * points; a norm with a null gate or a negative or non-finite eps is
+ * KDA_ERR_INVALID_ARG, as is a mismatch between norm and KDA_FLAG_OUT_NORM,
+ * a conv with a missing weight or a misaligned conv pointer.  o must not
+ * alias the norm's gate.
  */
 KDA_API kda_status kda_chunk_fwd_fused(const kda_chunk_desc* desc,
                          const void* q, const void* k, const void* v,
                          const float* g, const kda_decay_gate* decay_gate,
                          const float* beta,
                          const float* init_state, const int32_t* cu_seqlens,
-                         const kda_out_norm* norm,
+                         const kda_short_conv* conv, const kda_out_norm* norm,
                          void* o, float* final_state,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
@@ -260,7 +301,8 @@ KDA_API kda_status kda_recurrent_step_fused(int N, int H, int d_k, int d_v,
                               float scale, unsigned flags,
                               const void* q, const void* k, const void* v,
                               const float* g, const kda_decay_gate* decay_gate,
-                              const float* beta, const kda_out_norm* norm,
+                              const float* beta, const kda_short_conv* conv,
+                              const kda_out_norm* norm,
                               float* state, void* o, hipStream_t stream);
 
 /* Static description of a status code. */

@@ -31,7 +31,7 @@ import numpy as np
 
 BLOCK_T = 4096  # tokens per independently seeded block
 _TENSOR_ID = {"q": 1, "k": 2, "v": 3, "z": 4, "beta": 5, "s0": 6, "A": 7, "dt_bias": 8, "sign": 9,
-              "out_gate": 10, "norm_w": 11}
+              "out_gate": 10, "norm_w": 11, "conv_w": 12, "conv_s": 13}
 
 
 # ----------------------------------------------------------------------------
@@ -373,3 +373,25 @@ def make_out_gate(seed: int, shape, dtype: str = "bf16") -> np.ndarray:
 def norm_weight(seed: int, dv: int) -> np.ndarray:
     """The norm's per-channel gain [d_v] ~ U(0.5, 1.5), fp32."""
     return _rng(seed, "norm_w", 0).uniform(0.5, 1.5, size=dv).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Short-convolution inputs: per-channel taps and the 3-token conv state
+# ----------------------------------------------------------------------------
+def conv_weights(seed: int, H: int, dk: int, dv: int, std: float = 0.5):
+    """Taps of the q, k and v convolutions, [H*d, 4] fp32 each ~ N(0, std^2)
+    (oldest token first)."""
+    rng = _rng(seed, "conv_w", 0)
+    return tuple((rng.standard_normal((H * d, 4), dtype=np.float32) * np.float32(std)).astype(np.float32)
+                 for d in (dk, dk, dv))
+
+
+def conv_states(seed: int, N: int, H: int, dk: int, dv: int, dtype: str = "bf16"):
+    """Conv states of q, k and v, [N, 3, H*d] ~ N(0, 1) (the 3 previous raw
+    inputs of each sequence), bf16 bits or fp32."""
+    rng = _rng(seed, "conv_s", 0)
+    out = []
+    for d in (dk, dk, dv):
+        x = rng.standard_normal((N, 3, H * d), dtype=np.float32)
+        out.append(bf16_bits(x) if dtype == "bf16" else x)
+    return tuple(out)

@@ -23,6 +23,10 @@ Contents
   * ``forward_signed``: the same recurrence with the decay given as a signed
     alpha in [-1, 1] and beta in [0, 2] (Complex KDA, "[논문리뷰] Complex KDA
     ..." page).
+  * ``short_conv`` / ``conv_qkv`` / ``forward_conv`` / ``decode_conv``: the
+    causal width-4 depthwise convolution + SiLU that produces q, k, v from
+    their projections, with its 3-token conv state ("Kimi K3 の KDA ..."
+    section 1.2.1; "GDN, KDA の整理" on the conv cache), then the recurrence.
   * ``out_norm``: the gated RMSNorm that follows the kernel in the model,
     o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) per (token, head) row
     ("Kimi K3 の KDA ..." section 1.2.1, the output gate).
@@ -194,6 +198,95 @@ def decode_gated(state, q, k, v, z, A_log, dt_bias, beta_logits, *, scale=1.0, t
     logits [N,H], then decode_steps."""
     return decode_steps(state, q, k, v, gate_map(z, A_log, dt_bias), beta_from_logits(beta_logits),
                         scale=scale, threads=threads)
+
+
+# ----------------------------------------------------------------------------
+# Short convolution prologue
+# ----------------------------------------------------------------------------
+CONV_WIDTH = 4
+
+
+def silu(x):
+    """x sigmoid(x) in fp64."""
+    x = np.asarray(x, np.float64)
+    return x * sigmoid(x)
+
+
+def short_conv(x, w, init=None, cu_seqlens=None):
+    """Causal depthwise convolution of width 4 along the token axis, then SiLU
+    ("Kimi K3 の KDA ..." section 1.2.1: each channel is independent and mixes
+    the current token with the 3 before it; the SiLU follows).  Reading: tap j
+    of channel c multiplies the input 3 - j tokens back (w[:, 3] is the
+    current token), no bias; inputs before a sequence's first token come from
+    its conv state (the previous 3 inputs, oldest first; "GDN, KDA の整理",
+    section on the conv cache) or are zero.  Sequences never see each other.
+
+    x: [B, T, C]; w: [C, 4]; init: [N, 3, C] or None; cu_seqlens: [N+1] with
+    B = 1, or None (then N = B).  Returns (y fp64 [B, T, C], final [N, 3, C]):
+    the SiLU of the convolution, and each sequence's last 3 inputs (drawn from
+    init where the sequence is shorter than 3).  Tokens outside every packed
+    sequence get y = 0."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    B, T, C = x.shape
+    assert w.shape == (C, CONV_WIDTH)
+    if cu_seqlens is None:
+        segs = [(b, 0, T) for b in range(B)]
+    else:
+        assert B == 1
+        cu = np.asarray(cu_seqlens)
+        segs = [(0, int(cu[n]), int(cu[n + 1])) for n in range(len(cu) - 1)]
+    y = np.zeros_like(x)
+    final = np.empty((len(segs), CONV_WIDTH - 1, C))
+    for n, (b, t0, t1) in enumerate(segs):
+        prev = np.zeros((CONV_WIDTH - 1, C)) if init is None else np.asarray(init[n], np.float64)
+        xs = np.concatenate([prev, x[b, t0:t1]], axis=0)            # token t0 + i sits at row i + 3
+        L = t1 - t0
+        pre = np.zeros((L, C))
+        for j in range(CONV_WIDTH):
+            pre += w[:, j] * xs[j:j + L]                             # row i + j = token t0 + i - (3 - j)
+        y[b, t0:t1] = silu(pre)
+        final[n] = xs[L:L + CONV_WIDTH - 1]
+    return y, final
+
+
+def conv_qkv(q, k, v, weights, inits=None, cu_seqlens=None):
+    """short_conv on q, k [B,T,H,d_k] and v [B,T,H,d_v], each over its H*d
+    channels with its own weights ([H*d, 4]) and state ([N, 3, H*d] or None).
+    Returns ((q, k, v) fp64 in the input shapes, (final_q, final_k, final_v))."""
+    outs, finals = [], []
+    for i, x in enumerate((q, k, v)):
+        x = np.asarray(x, np.float64)
+        B, T, H, d = x.shape
+        y, f = short_conv(x.reshape(B, T, H * d), weights[i], None if inits is None else inits[i], cu_seqlens)
+        outs.append(y.reshape(B, T, H, d))
+        finals.append(f)
+    return tuple(outs), tuple(finals)
+
+
+def forward_conv(q, k, v, g, beta, weights, conv_inits=None, init_state=None, cu_seqlens=None, *,
+                 alpha_given=False, **kw):
+    """The recurrence on conv-SiLU'd q, k, v (the inputs the kernel sees in
+    the model once the short convolutions have run).  The convolved values
+    reach the C recurrence rounded once to fp32.  Returns (o, final_state,
+    conv finals)."""
+    (qc, kc, vc), finals = conv_qkv(q, k, v, weights, conv_inits, cu_seqlens)
+    o, sT = forward_arrays(qc, kc, vc, g, beta, init_state, cu_seqlens, alpha_given=alpha_given, **kw)
+    return o, sT, finals
+
+
+def decode_conv(caches, weights, q, k, v):
+    """One decode token per sequence through the three short convolutions:
+    q, k [N,H,d_k], v [N,H,d_v]; caches: 3 arrays [N, 3, H*d] (or None for
+    zeros).  Returns ((q, k, v) convolved, new caches)."""
+    outs, news = [], []
+    for i, x in enumerate((q, k, v)):
+        x = np.asarray(x, np.float64)
+        N, H, d = x.shape
+        y, f = short_conv(x.reshape(N, 1, H * d), weights[i], None if caches is None else caches[i])
+        outs.append(y.reshape(N, H, d))
+        news.append(f)
+    return tuple(outs), tuple(news)
 
 
 # ----------------------------------------------------------------------------

@@ -182,20 +182,29 @@ def test_gated_entry_points_reject_bad_arguments(lib):
 def test_workspace_for_the_output_norm(lib):
     size = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(**kw)))
     on = kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM
-    # matrix-core path: the norm is applied in the scan pass, no extra bytes
-    assert size(B=2, T=100, H=3, flags=on) == size(B=2, T=100, H=3)
-    # fp32 path: fp32 o for every (token, head) row as a temporary
+    # a bf16 o is staged in fp32 for the norm pass, after the records
+    assert size(B=2, T=100, H=3, flags=on) == size(B=2, T=100, H=3) + 2 * 100 * 3 * 128 * 4
     assert size(B=2, T=100, H=3, d_k=64, d_v=64, flags=on) == 2 * 100 * 3 * 64 * 4
-    assert size(B=1, T=10, H=1, in_dtype=0, flags=on | kda.FLAG_VALIDATE) == 256 + 10 * 128 * 4
+    # an fp32 o is normalised in place
+    assert size(B=2, T=100, H=3, out_dtype=0, flags=on) == size(B=2, T=100, H=3)
+    assert size(B=1, T=10, H=1, in_dtype=0, out_dtype=0, flags=on | kda.FLAG_VALIDATE) == 256
 
 
-def _call_fused(lib, d, g=FAKE + 0x300000, dg=None, norm=None, ws=FAKE, ws_bytes=1 << 40):
+def _call_fused(lib, d, g=FAKE + 0x300000, dg=None, norm=None, ws=FAKE, ws_bytes=1 << 40, conv=None):
     p = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(3)]
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return lib.kda_chunk_fwd_fused(ctypes.byref(d), p[0], p[1], p[2], vp(g), None if dg is None else ctypes.byref(dg),
                                    ctypes.c_void_p(FAKE + 0x400000), None, None,
+                                   None if conv is None else ctypes.byref(conv),
                                    None if norm is None else ctypes.byref(norm), ctypes.c_void_p(FAKE + 0x600000),
                                    None, vp(ws), ctypes.c_size_t(ws_bytes), None)
+
+
+def _conv(weights=(FAKE + 0xD00000, FAKE + 0xD10000, FAKE + 0xD20000), inits=(None,) * 3, finals=(None,) * 3):
+    sc = kda.ShortConv()
+    for i in range(3):
+        sc.weight[i], sc.init_state[i], sc.final_state[i] = weights[i], inits[i], finals[i]
+    return sc
 
 
 def test_fused_entry_points_reject_bad_arguments(lib):
@@ -215,13 +224,12 @@ def test_fused_entry_points_reject_bad_arguments(lib):
                        norm=good) == 1                                             # A_log required
     assert _call_fused(lib, _desc(flags=on), norm=good, ws=None, ws_bytes=0) == 3  # same workspace rule
     assert _call_fused(lib, _desc(flags=on | kda.FLAG_SIGNED_ALPHA), g=None, dg=dg, norm=good) == 2
-    # the plain and gated entry points take no norm
-    assert _call(lib, _desc(flags=on), ws=FAKE, ws_bytes=1 << 40) == 1
     P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(9)]
 
-    def step(flags=on, norm=good, g=P[3], dg=None, N=4):
+    def step(flags=on, norm=good, g=P[3], dg=None, N=4, conv=None):
         return lib.kda_recurrent_step_fused(N, 2, 128, 128, 1, 1, 1.0, flags, P[0], P[1], P[2], g,
                                             None if dg is None else ctypes.byref(dg), P[4],
+                                            None if conv is None else ctypes.byref(conv),
                                             None if norm is None else ctypes.byref(norm), P[5], P[6], None)
 
     assert step(norm=None) == 1
@@ -231,4 +239,14 @@ def test_fused_entry_points_reject_bad_arguments(lib):
     assert step(dg=dg) == 1
     assert step(flags=on | kda.FLAG_VALIDATE) == 2
     assert step(N=0) == 0
-    assert lib.kda_recurrent_step(4, 2, 128, 128, 1, 1, 1.0, on, *P[:7], None) == 1
+    assert _call(lib, _desc(flags=on), ws=FAKE, ws_bytes=1 << 40) == 1      # the plain entry points take no norm
+    # short convolution: every weight required, every pointer 16-byte aligned
+    plain = kda.FLAG_QK_L2NORM
+    assert _call_fused(lib, _desc(), conv=_conv(weights=(FAKE, None, FAKE))) == 1
+    assert _call_fused(lib, _desc(), conv=_conv(weights=(FAKE, FAKE + 4, FAKE))) == 1
+    assert _call_fused(lib, _desc(), conv=_conv(inits=(None, FAKE + 8, None))) == 1
+    assert _call_fused(lib, _desc(), conv=_conv(finals=(None, None, FAKE + 2))) == 1
+    assert _call_fused(lib, _desc(), conv=_conv(), ws=None, ws_bytes=0) == 3      # same workspace rule
+    assert step(flags=plain, norm=None, conv=_conv(weights=(None, FAKE, FAKE))) == 1
+    assert step(flags=plain, norm=None, conv=_conv(inits=(FAKE + 4, None, None))) == 1
+    assert step(flags=plain, norm=None, conv=_conv(), N=0) == 0

@@ -584,3 +584,110 @@ def test_out_norm_after_one_token_from_zero_state():
     sign = np.sign(float(beta[0]) * float(_unit(k[0]) @ _unit(q[0])))
     expect = sign * vv / np.sqrt(np.mean(vv * vv)) * w / (1.0 + np.exp(-gate))
     np.testing.assert_allclose(oracle.out_norm(o[0], gate, w, eps=0.0), expect, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Short convolution ("Kimi K3 の KDA ..." section 1.2.1: causal, per channel,
+# the current token and the 3 before it, then SiLU; "GDN, KDA の整理": the conv
+# cache holds the previous 3 inputs)
+# ---------------------------------------------------------------------------
+def _silu(x):
+    import math
+    return x / (1.0 + math.exp(-x))
+
+
+def test_short_conv_worked_by_hand():
+    # one channel, taps (1, 2, 3, 4) oldest first, an impulse at t = 0: the
+    # pre-activations walk the taps backwards, (4, 3, 2, 1, 0)
+    w = np.array([[1.0, 2.0, 3.0, 4.0]])
+    y, fin = oracle.short_conv(np.array([1.0, 0, 0, 0, 0])[None, :, None], w)
+    np.testing.assert_allclose(y[0, :, 0], [_silu(4.0), _silu(3.0), _silu(2.0), _silu(1.0), 0.0], rtol=1e-15)
+    assert np.all(fin == 0.0)
+    # with a conv state (5, 6, 7) and one input 1: 1*5 + 2*6 + 3*7 + 4*1 = 42,
+    # and the new state drops the oldest input
+    y, fin = oracle.short_conv(np.array([[[1.0]]]), w, init=np.array([[[5.0], [6.0], [7.0]]]))
+    np.testing.assert_allclose(y[0, 0, 0], _silu(42.0), rtol=1e-15)
+    np.testing.assert_array_equal(fin[0, :, 0], [6.0, 7.0, 1.0])
+
+
+def test_silu_closed_forms():
+    x = np.linspace(-20, 20, 81)
+    assert oracle.silu(0.0) == 0.0
+    np.testing.assert_allclose(oracle.silu(x) - oracle.silu(-x), x, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(oracle.silu(x), x / (1.0 + np.exp(-x)), rtol=1e-14, atol=1e-300)
+
+
+def test_short_conv_identity_and_shift_taps():
+    rng = np.random.default_rng(81)
+    x = rng.standard_normal((2, 9, 5))
+    init = rng.standard_normal((2, 3, 5))
+    ident = np.tile([0.0, 0.0, 0.0, 1.0], (5, 1))
+    y, fin = oracle.short_conv(x, ident, init)
+    np.testing.assert_allclose(y, oracle.silu(x), rtol=0, atol=0)
+    np.testing.assert_array_equal(fin, x[:, -3:])
+    shift = np.tile([1.0, 0.0, 0.0, 0.0], (5, 1))                    # 3 tokens back
+    y, _ = oracle.short_conv(x, shift, init)
+    np.testing.assert_allclose(y[:, 3:], oracle.silu(x[:, :-3]), rtol=0, atol=0)
+    np.testing.assert_allclose(y[:, :3], oracle.silu(init), rtol=0, atol=0)
+
+
+def test_short_conv_is_causal_with_a_window_of_four():
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal((1, 20, 3))
+    w = rng.standard_normal((3, 4))
+    y0, _ = oracle.short_conv(x, w)
+    x2 = x.copy()
+    x2[0, 9] += 1.0
+    y1, _ = oracle.short_conv(x2, w)
+    changed = np.any(y1 != y0, axis=(0, 2))
+    assert not changed[:9].any() and changed[9:13].all() and not changed[13:].any()
+
+
+def test_short_conv_state_carries_a_split_and_decode_steps():
+    rng = np.random.default_rng(83)
+    x = rng.standard_normal((1, 30, 6))
+    w = rng.standard_normal((6, 4))
+    init = rng.standard_normal((1, 3, 6))
+    y, fin = oracle.short_conv(x, w, init)
+    for cut in (1, 2, 3, 17):
+        ya, fa = oracle.short_conv(x[:, :cut], w, init)
+        yb, fb = oracle.short_conv(x[:, cut:], w, fa)
+        np.testing.assert_allclose(np.concatenate([ya, yb], axis=1), y, rtol=1e-15, atol=1e-15)
+        np.testing.assert_array_equal(fb, fin)
+    st = init
+    for t in range(30):                                             # one token per call
+        yt, st = oracle.short_conv(x[:, t:t + 1], w, st)
+        np.testing.assert_allclose(yt[0, 0], y[0, t], rtol=1e-15, atol=1e-15)
+    # a sequence shorter than the window keeps part of its incoming state
+    _, f2 = oracle.short_conv(x[:, :2], w, init)
+    np.testing.assert_array_equal(f2[0], np.concatenate([init[0, 2:], x[0, :2]]))
+
+
+def test_short_conv_packed_sequences_are_isolated():
+    rng = np.random.default_rng(84)
+    lens = [5, 0, 1, 12]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = rng.standard_normal((1, cu[-1], 4))
+    w = rng.standard_normal((4, 4))
+    init = rng.standard_normal((4, 3, 4))
+    y, fin = oracle.short_conv(x, w, init, cu)
+    for n in range(4):
+        yn, fn = oracle.short_conv(x[:, cu[n]:cu[n + 1]], w, init[n:n + 1])
+        np.testing.assert_array_equal(y[:, cu[n]:cu[n + 1]], yn)
+        np.testing.assert_array_equal(fin[n], fn[0])
+    np.testing.assert_array_equal(fin[1], init[1])                   # empty sequence: state passes through
+
+
+def test_conv_then_recurrence_first_token_closed_form():
+    # zero conv state and zero recurrent state: q, k, v become silu(w_3 x)
+    # and the first output is scale beta (k^ . q^) v_c
+    rng = np.random.default_rng(85)
+    d = 8
+    q, k, v, g, beta = _rand_chain(rng, 1, d, d)
+    ws = [rng.standard_normal((d, 4)) for _ in range(3)]
+    o, _, fin = oracle.forward_conv(q[None, :, None], k[None, :, None], v[None, :, None], g[None, :, None],
+                                    beta[None, :, None], ws, scale=0.5)
+    qc, kc, vc = (oracle.silu(ws[i][:, 3] * x[0].astype(np.float64)) for i, x in enumerate((q, k, v)))
+    expect = 0.5 * float(beta[0]) * float(_unit(kc) @ _unit(qc)) * vc
+    np.testing.assert_allclose(o[0, 0, 0], expect, rtol=1e-6, atol=1e-7)   # the conv output reaches fp32 once
+    np.testing.assert_array_equal(fin[0][0], np.concatenate([np.zeros((2, d)), q[None, 0].astype(np.float64)]))
