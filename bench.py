@@ -56,10 +56,17 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+# the sources each measured path is built from (kernels, their headers, the launch code)
+KERNEL_SOURCES = {
+    "chunk_fwd": ("kda_chunk_two_pass.hip", "kda_mfma.h", "kda_kernels.h", "kda_device.h", "kda_abi.hip"),
+    "decode": ("kda_decode.hip", "kda_kernels.h", "kda_device.h", "kda_abi.hip"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gated_delta_rule_fwd_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(KERNEL_SOURCES[kernel]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -74,7 +81,7 @@ def load_traffic(kernel: str):
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -255,7 +262,7 @@ def write_traffic(fetch_dir, write_dir):
         if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
             rd = v["FETCH_SIZE"] * scale["FETCH_SIZE"]
             wr = v["WRITE_SIZE"] * scale["WRITE_SIZE"]
-            out[key] = {"source_hash": kernel_source_hash(), "hbm_bytes_per_launch": rd + wr, "read_bytes": rd,
+            out[key] = {"source_hash": kernel_source_hash(key), "hbm_bytes_per_launch": rd + wr, "read_bytes": rd,
                         "write_bytes": wr, "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
@@ -443,7 +450,7 @@ def main():
         write_traffic(*args.traffic_from)
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch

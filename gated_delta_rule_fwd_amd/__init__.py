@@ -83,8 +83,7 @@ def load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
-        raise ImportError("libkda.so is not built (%s); run __graft_entry__.build() or "
-                          "python gated_delta_rule_fwd_amd/build.py" % _LIB_PATH)
+        raise ImportError("libkda.so is not built (%s); run python gated_delta_rule_fwd_amd/build.py" % _LIB_PATH)
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, F, U, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint, ctypes.c_size_t
     lib.kda_chunk_fwd.restype = I

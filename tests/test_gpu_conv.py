@@ -216,3 +216,43 @@ def test_prefill_then_decode_continues_the_sequence(kda):
         check("decode_after_prefill/t%d" % t, host64(ot), o_all[:, t], None, None, TOL_BF16, bf16_store=False)
     check_state("decode_after_prefill/final", host64(s), s_all, TOL_BF16)
     _check_conv_states("decode_after_prefill", cache, f_all)
+
+
+def test_layer_decode_step_conv_gate_and_norm(kda):
+    """The whole decode step of the layer in one call: short convolution with
+    its cache, decay-gate prologue, beta logits, the recurrence, output norm;
+    eight steps carrying both states."""
+    import torch
+    N, H, d, steps = 8, 4, 128, 8
+    S0 = kda_inputs.decode_initial_state(50, N, H, d, 0.02)
+    ws = kda_inputs.conv_weights(50, H, d, d)
+    cs = kda_inputs.conv_states(50, N, H, d, d)
+    A_log, dt_bias = kda_inputs.gate_params(50, H, d)
+    w = kda_inputs.norm_weight(50, d)
+    state, cache = dev(S0), tuple(dev(c) for c in cs)
+    s_ref, c_ref = S0.astype(np.float64), tuple(_f(c).astype(np.float64) for c in cs)
+    for step in range(steps):
+        x = kda_inputs.gated_decode_step(50, step, N, H, d)
+        gate = kda_inputs.make_out_gate(2000 + step, (N, H, d))
+        (qc, kc, vc), c_ref = oracle.decode_conv(c_ref, ws, _f(x.q), _f(x.k), _f(x.v))
+        o_ref, s_ref = oracle.decode_gated(s_ref, qc, kc, vc, _f(x.z), A_log, dt_bias, x.beta_logits)
+        y_ref = oracle.out_norm(o_ref, _f(gate).astype(np.float64), w, 1e-5)
+        o = kda.recurrent_step_gated(dev(x.q), dev(x.k), dev(x.v), dev(x.z), dev(A_log), dev(x.beta_logits), state,
+                                     dt_bias=dev(dt_bias), beta_logits=True, out_dtype=torch.float32,
+                                     out_gate=dev(gate), norm_weight=dev(w), norm_eps=1e-5,
+                                     conv_weights=tuple(dev(t) for t in ws), conv_state=cache)
+        torch.cuda.synchronize()
+        check("layer_decode/step%d" % step, host64(o), y_ref, None, None, TOL_BF16, bf16_store=False)
+        _check_conv_states("layer_decode/step%d" % step, cache, c_ref)
+    check_state("layer_decode/final", host64(state), s_ref, TOL_BF16)
+
+
+def test_conv_with_validate(kda):
+    import torch
+    inp = kda_inputs.make_prefill(51, 1, 0, 2, 128, 128, lengths=[100, 0, 37])
+    ws = kda_inputs.conv_weights(51, 2, 128, 128)
+    cs = kda_inputs.conv_states(51, 3, 2, 128, 128)
+    o_ref, s_ref, f_ref = _oracle(inp, ws, cs)
+    o, s, fin = _run_plain(kda, inp, ws, cs, torch.float32, validate=True)
+    check("conv_validate", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
+    _check_conv_states("conv_validate", fin, f_ref)
