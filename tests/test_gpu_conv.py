@@ -256,3 +256,36 @@ def test_conv_with_validate(kda):
     o, s, fin = _run_plain(kda, inp, ws, cs, torch.float32, validate=True)
     check("conv_validate", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
     _check_conv_states("conv_validate", fin, f_ref)
+
+
+def test_layer_core_full_size_sampled_heads(kda):
+    """The whole fused layer core at the long-prefill size (B=1, H=96,
+    T=65536; the bench's launch): short convolution, gate prologue, output
+    norm; the oracle runs on three sampled heads (the convolution, gate map
+    and norm act per head and channel, so a head's slice of every input
+    suffices)."""
+    import torch
+    H, d = 96, 128
+    inp = kda_inputs.make_gated_prefill(2, 1, 65536, H, d, d, s0_std=0.02)
+    ws = kda_inputs.conv_weights(2, H, d, d)
+    cs = kda_inputs.conv_states(2, 1, H, d, d)
+    gate = kda_inputs.make_out_gate(2, inp.v.shape)
+    w = kda_inputs.norm_weight(2, d)
+    finals = _empty_like_states(cs)
+    o, s = kda.chunk_fwd_gated(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.z), dev(inp.A_log), dev(inp.beta_logits),
+                               dev(inp.init_state), dt_bias=dev(inp.dt_bias), beta_logits=True,
+                               out_gate=dev(gate), norm_weight=dev(w), norm_eps=1e-5,
+                               conv_weights=tuple(dev(x) for x in ws), conv_init=tuple(dev(c) for c in cs),
+                               conv_final=finals)
+    torch.cuda.synchronize()
+    for h in (0, 51, 95):
+        hs, cols = slice(h, h + 1), slice(h * d, (h + 1) * d)
+        g = oracle.gate_map(inp.f32("z")[:, :, hs], inp.A_log[hs], inp.dt_bias[hs])
+        o_ref, s_ref, f_ref = oracle.forward_conv(
+            inp.f32("q")[:, :, hs], inp.f32("k")[:, :, hs], inp.f32("v")[:, :, hs], g,
+            oracle.beta_from_logits(inp.beta_logits[:, :, hs]), [x[cols] for x in ws],
+            [_f(c)[:, :, cols] for c in cs], inp.init_state[:, hs])
+        y_ref = oracle.out_norm(o_ref, _f(gate[:, :, hs]).astype(np.float64), w, 1e-5)
+        check("layer_core_64k/h%d" % h, host64(o[:, :, hs]), y_ref, host64(s[:, hs]), s_ref, TOL_BF16,
+              bf16_store=True)
+        _check_conv_states("layer_core_64k/h%d" % h, [f[:, :, cols] for f in finals], f_ref)
