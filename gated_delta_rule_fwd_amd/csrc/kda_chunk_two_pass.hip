@@ -922,27 +922,50 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             for (int i = 0; i < 4; ++i) vv[m2][i] = static_cast<float>(s.vs[16 * mt + 4 * g + i][16 * w + n]);
         }
     };
-    // R = V - (K^ Gamma) S for token tiles 2mh, 2mh + 1 (rows 16mt + 4g + i, column n of the strip)
-    auto step_r = [&](int mh, const f16x8 (&fa)[2][4], const float (&vv)[2][4], const f16x8 (&sh)[4],
-                      const f16x8 (&sl)[4], f32x4 (&ut)[4]) __attribute__((always_inline)) {
+    // Q^ Gamma fragments for token tiles 2mh, 2mh + 1
+    auto load_q = [&](int mh, f16x8 (&qa)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[2 * mh + m2][kb][l];
+    };
+    // R = V - (K^ Gamma) S and the first term of O, (Q^ Gamma) S, for token
+    // tiles 2mh, 2mh + 1: four independent accumulation chains share the
+    // state operand, so the matrix core has work while each chain waits on
+    // its previous product
+    auto step_rq = [&](int mh, const f16x8 (&fa)[2][4], const f16x8 (&qa)[2][4], const float (&vv)[2][4],
+                       const f16x8 (&sh)[4], const f16x8 (&sl)[4], f32x4 (&ut)[4], f32x4 (&oq)[4])
+        __attribute__((always_inline)) {
+        f32x4 ar[2], aq[2];
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2) {
-            f32x4 acc = {vv[m2][0], vv[m2][1], vv[m2][2], vv[m2][3]};
+            ar[m2] = f32x4{vv[m2][0], vv[m2][1], vv[m2][2], vv[m2][3]};
+            aq[m2] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                acc = mmh(fa[m2][kb], sh[kb], acc);
-                acc = mmh(fa[m2][kb], sl[kb], acc);
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                ar[m2] = mmh(fa[m2][kb], sh[kb], ar[m2]);
+                aq[m2] = mmh(qa[m2][kb], sh[kb], aq[m2]);
             }
-            ut[2 * mh + m2] = acc;
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                ar[m2] = mmh(fa[m2][kb], sl[kb], ar[m2]);
+                aq[m2] = mmh(qa[m2][kb], sl[kb], aq[m2]);
+            }
+        }
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            ut[2 * mh + m2] = ar[m2];
+            oq[2 * mh + m2] = aq[m2];
         }
     };
-    // operand fragments of the O step for token tiles 2half, 2half + 1
-    auto load_o = [&](int half, f16x8 (&qa)[2][4], f16x8 (&ah)[2][2], f16x8 (&al)[2][2]) __attribute__((always_inline)) {
+    // A_qk fragments for token tiles 2half, 2half + 1
+    auto load_a = [&](int half, f16x8 (&ah)[2][2], f16x8 (&al)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2) {
             const int mt = 2 * half + m2;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[mt][kb][l];
 #pragma unroll
             for (int kb = 0; kb <= half; ++kb) {
                 ah[m2][kb] = s.r.aqk[0][tri_block(mt, kb)][l];
@@ -951,17 +974,12 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         }
     };
     // O = (Q^ Gamma) S + A_qk U~ for token tiles 2half, 2half + 1, staged in LDS
-    auto step_o = [&](int half, int buf, const f16x8 (&qa)[2][4], const f16x8 (&ah)[2][2], const f16x8 (&al)[2][2],
-                      const f16x8 (&sh)[4], const f16x8 (&sl)[4], const f16x8 (&ub)[2]) __attribute__((always_inline)) {
+    auto step_oa = [&](int half, int buf, const f32x4 (&oq)[4], const f16x8 (&ah)[2][2], const f16x8 (&al)[2][2],
+                       const f16x8 (&ub)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2) {
             const int mt = 2 * half + m2;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                acc = mmh(qa[m2][kb], sh[kb], acc);
-                acc = mmh(qa[m2][kb], sl[kb], acc);
-            }
+            f32x4 acc = oq[mt];
 #pragma unroll
             for (int kb = 0; kb <= half; ++kb) {
                 acc = mmh(ah[m2][kb], ub[kb], acc);
@@ -1075,7 +1093,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     // Each chunk is software-pipelined inside the wave: the LDS fragments of
     // the next step are requested before the matrix products of the current
     // one, so the LDS and the matrix cores work at the same time (one wave
-    // per SIMD: nothing else would hide the LDS latency).
+    // per SIMD: nothing else would hide the LDS latency).  (Q^ Gamma) S rides
+    // along with R's dependent chains, and the O and state-update products
+    // are left to the scheduler to interleave.
     long prev_c0 = 0;
     int prev_L = 0;
     for (int j = 0; j < nch; ++j) {
@@ -1084,9 +1104,10 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         const bool more = j + 1 < nch;
         const int buf = j & 1;
 
-        f16x8 fa0[2][4], fa1[2][4];
+        f16x8 fa0[2][4], fa1[2][4], qa0[2][4], qa1[2][4];
         float vv0[2][4], vv1[2][4];
         load_r(0, fa0, vv0);
+        load_q(0, qa0);
         if (more) {
             fetch_v(j + 1);
             fetch(j + 1, 0, 5);
@@ -1096,40 +1117,36 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         split_state(sh, sl);
         __builtin_amdgcn_sched_barrier(0);
         load_r(1, fa1, vv1);
+        load_q(1, qa1);
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 ut[4];
-        step_r(0, fa0, vv0, sh, sl, ut);
+        f32x4 ut[4], oq[4];
+        step_rq(0, fa0, qa0, vv0, sh, sl, ut, oq);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 th[6], tl[6];
         load_t(th, tl);
         if (more) fetch(j + 1, 5, 10);
         __builtin_amdgcn_sched_barrier(0);
-        step_r(1, fa1, vv1, sh, sl, ut);
+        step_rq(1, fa1, qa1, vv1, sh, sl, ut, oq);
         __builtin_amdgcn_sched_barrier(0);
-        f16x8 qa0[2][4], ah0[2][2], al0[2][2];
-        load_o(0, qa0, ah0, al0);
+        f16x8 ah0[2][2], al0[2][2], ah1[2][2], al1[2][2];
+        load_a(0, ah0, al0);
+        load_a(1, ah1, al1);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ub[2], ubl[2];
         step_t(th, tl, ut, ub, ubl);
         if (more) fetch(j + 1, 10, 15);
         __builtin_amdgcn_sched_barrier(0);
-        f16x8 qa1[2][4], ah1[2][2], al1[2][2];
-        load_o(1, qa1, ah1, al1);
-        __builtin_amdgcn_sched_barrier(0);
-        step_o(0, buf, qa0, ah0, al0, sh, sl, ub);
-        __builtin_amdgcn_sched_barrier(0);
         f16x8 ka0[4][2];
         float4 gm0[4];
         load_k(0, ka0, gm0);
-        if (more) fetch(j + 1, 15, RFULL + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        step_o(1, buf, qa1, ah1, al1, sh, sl, ub);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ka1[4][2];
         float4 gm1[4];
         load_k(1, ka1, gm1);
-        __builtin_amdgcn_sched_barrier(0);
+        if (more) fetch(j + 1, 15, RFULL + 1);
+        step_oa(0, buf, oq, ah0, al0, ub);
         step_k(0, ka0, gm0, ub, ubl);
+        step_oa(1, buf, oq, ah1, al1, ub);
         step_k(1, ka1, gm1, ub, ubl);
         __syncthreads();
         // every read of this chunk's record is done: the next one moves in
