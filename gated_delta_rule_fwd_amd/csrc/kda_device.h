@@ -40,9 +40,14 @@ template <> struct Elem<uint16_t> {
 // in-kernel sigmoid of beta):
 //   g    = -5 sigmoid(e^{A_h} (z + dt_bias[h, c]))   in (-5, 0)
 //   beta = sigmoid(logit)
-// exp(-x) overflowing to +inf gives g = -0 and beta = 0, the right limits.
+// g is evaluated as -5 / (1 + 2^y) with y = -e^{A_h} log2(e) (z + dt_bias):
+// one multiply-add, one exp2 and one reciprocal (to 1 ulp) per element, the
+// factor -e^{A_h} log2(e) being the same for a whole head.  2^y overflowing
+// to +inf gives g = -0, and exp(-x) overflowing gives beta = 0: the right
+// limits.
 __device__ __forceinline__ float gate_log_decay(float z, float bias, float exp_a) {
-    return -5.f / (1.f + __expf(-exp_a * (z + bias)));
+    const float y = (z + bias) * (-exp_a * 1.44269504088896341f);
+    return -5.f * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(y));
 }
 __device__ __forceinline__ float beta_from_logit(float b) { return 1.f / (1.f + __expf(-b)); }
 
