@@ -56,7 +56,12 @@ __device__ __forceinline__ float beta_from_logit(float b) { return 1.f / (1.f + 
 // w[4c .. 4c+3] of channel c run oldest token first; inputs before a
 // sequence's first token come from its conv state (3 rows of `width`
 // channels per sequence, oldest first) or are zero.
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+// x / (1 + e^{-x}) as x times a reciprocal (to 1 ulp) of 1 + 2^{-x log2(e)}:
+// three instructions instead of a correctly rounded division; 2^{...}
+// overflowing to +inf gives -0, the limit.
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
 
 template <typename Tin>
 __device__ __forceinline__ float conv_input(const Tin* x, const Tin* state, long tk, long tok0, size_t width,
