@@ -183,12 +183,25 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         uint4 rq[4], rk[4];
         float4 rgv[8];
         uint4 rz[4];
+        float a_log = 0.f;
         // the decay inputs and beta are requested first: with the short
         // convolution their latency then overlaps the staging below
         if (a.gated) {
             const uint16_t* zr = static_cast<const uint16_t*>(a.z) + base * DK + 8 * g;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) rz[kb] = *reinterpret_cast<const uint4*>(zr + 32 * kb);
+            a_log = a.A_log[h];
+            // this lane's dt_bias channels, requested with z (rgv holds them
+            // until the map below replaces them by g)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                rgv[2 * kb] = make_float4(0.f, 0.f, 0.f, 0.f);
+                rgv[2 * kb + 1] = rgv[2 * kb];
+                if (a.dt_bias) {
+                    rgv[2 * kb] = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g);
+                    rgv[2 * kb + 1] = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g + 4);
+                }
+            }
         } else {
             const float* gr = a.g + base * DK + 8 * g;
 #pragma unroll
@@ -297,15 +310,11 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         }
         if (a.gated) {
             // g = -5 sigmoid(e^{A_h} (z + dt_bias)) from bf16 z
-            const float ea = __expf(a.A_log[h]);
+            const float ea = __expf(a_log);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const uint4 z4 = rz[kb];
-                float4 b0 = make_float4(0.f, 0.f, 0.f, 0.f), b1 = b0;
-                if (a.dt_bias) {
-                    b0 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g);
-                    b1 = *reinterpret_cast<const float4*>(a.dt_bias + h * DK + 32 * kb + 8 * g + 4);
-                }
+                const float4 b0 = rgv[2 * kb], b1 = rgv[2 * kb + 1];
                 rgv[2 * kb] = make_float4(gate_log_decay(bf_lo(z4.x), b0.x, ea), gate_log_decay(bf_hi(z4.x), b0.y, ea),
                                           gate_log_decay(bf_lo(z4.y), b0.z, ea), gate_log_decay(bf_hi(z4.y), b0.w, ea));
                 rgv[2 * kb + 1] = make_float4(gate_log_decay(bf_lo(z4.z), b1.x, ea), gate_log_decay(bf_hi(z4.z), b1.y, ea),

@@ -64,7 +64,6 @@ decode_step_kernel(DecodeArgs a)
     constexpr int CG = DV / 4;        // float4 column groups
     constexpr int RG = 256 / CG;      // row groups
     constexpr int RPT = DK / RG;      // rows per thread
-    constexpr int RG_PER_WAVE = 64 / CG;
     static_assert(RPT >= 1 && DK % RG == 0, "shape");
 
     const int c = blockIdx.x;         // chain = n * H + h
@@ -188,7 +187,6 @@ decode_step_kernel(DecodeArgs a)
         u[e] = b * (vj - pj);
         ov[e] = scale * (rj + dot * u[e]);
     }
-    (void)RG_PER_WAVE;
 
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
