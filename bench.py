@@ -220,11 +220,20 @@ def cpu_decode_baseline(n_sample=32):
     x = kda_inputs.decode_step(w["seed"], 0, n_sample, DEC_H, D)
     f = lambda a: kda_inputs.bf16_to_f32(a) if a.dtype == np.uint16 else a
     threads = os.cpu_count() or 1
+    q, k, v = f(x.q), f(x.k), f(x.v)
+    S1 = np.ascontiguousarray(S0[:4])
+    q1, k1, v1, g1, b1 = (np.ascontiguousarray(a[:4]) for a in (q, k, v, x.g, x.beta))
     t0 = time.perf_counter()
-    oracle.decode_steps(S0, f(x.q), f(x.k), f(x.v), x.g, x.beta, threads=threads)
+    oracle.decode_steps(S0, q, k, v, x.g, x.beta, threads=threads)
     dt = time.perf_counter() - t0
+    # one core: the first 4 sequences
+    t1 = time.perf_counter()
+    oracle.decode_steps(S1, q1, k1, v1, g1, b1, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"ms_per_step": dt * 1e3 * DEC_N / n_sample, "cores": threads, "kind": "oracle",
-            "sample": "%d of 256 sequences x 96 heads, one step, %.2f s; scaled to the full step" % (n_sample, dt)}
+            "sample": "%d of 256 sequences x 96 heads, one step, %.2f s; scaled to the full step" % (n_sample, dt),
+            "one_core_ms_per_step": dt1 * 1e3 * DEC_N / 4,
+            "one_core_sample": "4 of 256 sequences x 96 heads, one step, 1 thread, %.3f s; scaled to the full step" % dt1}
 
 
 def _counter_rows(d):
