@@ -74,8 +74,9 @@ struct alignas(16) PrepSmem {
                                      //   exp(ref_w), exp(ref_4 - ref_{w+1})
     float dl12[2][DK];               // exp(tot_1), exp(tot_2)
     float beta[C];
-    float tsg[4][DK];                // Complex KDA: sign of the decay product over each sub-tile
-    float psg[4][DK];                //   and over the sub-tiles before each one
+    uint32_t tsg[4][4];              // Complex KDA: sign bits of the decay product over each
+                                     //   sub-tile [sub-tile][lane group], bit 8kb + e <->
+                                     //   channel 32kb + 8g + e
 };
 
 // Packed sequences: slot -> sequence (or -1 for a slot no sequence uses).
@@ -108,16 +109,22 @@ __global__ void slot_map_kernel(const int32_t* __restrict__ cu, int num_seqs, in
 // into different LDS banks; the copy to the record undoes it.
 __device__ __forceinline__ int swz(int slot) { return slot ^ ((slot >> 3) & 7); }
 
-// Inclusive prefix product of +-1 signs over the 16 lanes of a DPP row
-// (lanes with no source keep the identity 1).
-__device__ __forceinline__ float row_sign_scan16(float x)
+// Inclusive prefix XOR over the 16 lanes of a DPP row (lanes with no source
+// read 0, the identity): 32 sign bits scanned at once.
+__device__ __forceinline__ uint32_t row_xor_scan16(uint32_t x)
 {
-    const int one = __float_as_int(1.f);
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x111, 0xf, 0xf, false));  // row_shr:1
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x112, 0xf, 0xf, false));  // row_shr:2
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x114, 0xf, 0xf, false));  // row_shr:4
-    x *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(x), 0x118, 0xf, 0xf, false));  // row_shr:8
-    return x;
+    const int v = static_cast<int>(x);
+    int r = v ^ __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    r ^= __builtin_amdgcn_update_dpp(0, r, 0x112, 0xf, 0xf, true);          // row_shr:2
+    r ^= __builtin_amdgcn_update_dpp(0, r, 0x114, 0xf, 0xf, true);          // row_shr:4
+    r ^= __builtin_amdgcn_update_dpp(0, r, 0x118, 0xf, 0xf, true);          // row_shr:8
+    return static_cast<uint32_t>(r);
+}
+
+// x with its sign flipped when bit i of mask is set (x * -1, exactly)
+__device__ __forceinline__ float flip_sign(float x, uint32_t mask, int i)
+{
+    return __uint_as_float(__float_as_uint(x) ^ (((mask >> i) & 1u) << 31));
 }
 
 // SIGNED: Complex KDA, g holds the signed decay alpha.  With sigma_r the sign
@@ -173,7 +180,7 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
     // token and are masked to the identity of the recurrence (k = g = beta = 0).
     const int row = 16 * w + n;
     float qv[32], kv[32], bv[32];
-    float sgn[SIGNED ? 32 : 1];
+    uint32_t neg = 0;                // Complex KDA: bit e set <-> alpha of element e is negative
     float beta_r;
     {
         const long tk = min(c0 + row, tok1 - 1);
@@ -349,13 +356,14 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             bv[8 * kb + 7] = rgv[2 * kb + 1].w;
         }
         if constexpr (SIGNED) {
-            // alpha -> (sign, log|alpha|); rows past the end act as alpha = 1
+            // alpha -> (sign bit, log|alpha|); rows past the end act as alpha = 1
 #pragma unroll
             for (int e = 0; e < 32; ++e) {
                 const float al = bv[e];
-                sgn[e] = (row < L && al < 0.f) ? -1.f : 1.f;
+                neg |= (al < 0.f ? 1u : 0u) << e;
                 bv[e] = (row < L) ? __logf(fabsf(al)) : 0.f;
             }
+            if (row >= L) neg = 0u;
         } else {
 #pragma unroll
             for (int e = 0; e < 32; ++e) bv[e] *= live;
@@ -393,14 +401,11 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             for (int e = 0; e < 8; ++e) s.tot[w][32 * kb + 8 * g + e] = bv[8 * kb + e];
     }
     if constexpr (SIGNED) {
-        // running sign inside the sub-tile, folded into q^ and k^ of this row
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const float sc = row_sign_scan16(sgn[e]);
-            qv[e] *= sc;
-            kv[e] *= sc;
-            if (n == 15) s.tsg[w][32 * (e >> 3) + 8 * g + (e & 7)] = sc;
-        }
+        // running sign inside the sub-tile: a prefix XOR of the 32 sign bits
+        // over the 16 rows (it is applied to q^ and k^ of this row with the
+        // sign of the sub-tiles before, in the loop below)
+        neg = row_xor_scan16(neg);
+        if (n == 15) s.tsg[w][g] = neg;
     }
     if (g == 0) s.beta[row] = beta_r;
     __syncthreads();
@@ -434,16 +439,15 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             rg->gam[c] = __expf(r4);
         }
         if constexpr (SIGNED) {
-            const float p1 = s.tsg[0][c], p2 = p1 * s.tsg[1][c], p3 = p2 * s.tsg[2][c], sL = p3 * s.tsg[3][c];
+            // sign of the decay product over the whole chunk, channel c
+            const int gc = (c >> 3) & 3, bc = ((c >> 5) << 3) | (c & 7);
+            const uint32_t sLb = ((s.tsg[0][gc] ^ s.tsg[1][gc] ^ s.tsg[2][gc] ^ s.tsg[3][gc]) >> bc) & 1u;
+            const float sL = sLb ? -1.f : 1.f;
             __syncthreads();   // every fac entry above is written before it is rescaled
             if (t < DK) {
-                s.psg[0][c] = 1.f;
-                s.psg[1][c] = p1;
                 s.fac[0][3][c] *= sL;
                 s.fac[1][3][c] *= sL;
             } else {
-                s.psg[2][c] = p2;
-                s.psg[3][c] = p3;
                 s.fac[2][3][c] *= sL;
                 s.fac[3][3][c] = sL;
                 rg->gam[c] *= sL;
@@ -458,6 +462,13 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
     // off-diagonal tiles share one A-operand, X^ E.
     // Complex KDA also keeps the low half of the A_kk operands: with |alpha|
     // near 1 nothing damps the rounding of single-bf16 A_kk over a long chain
+    // Complex KDA: the sign of this row's decay product per channel = the
+    // running sign inside sub-tile w XOR the sign over the sub-tiles before it
+    uint32_t sgnb = 0u;
+    if constexpr (SIGNED) {
+        sgnb = neg;
+        for (int v = 0; v < w; ++v) sgnb ^= s.tsg[v][g];
+    }
     bf16x8 kao[4], qoh[4], qol[4], kaol[SIGNED ? 4 : 1];
     f16x8 kq16[4];   // K^ gamma/Gamma of this row, channels 32kb + 8g + e
     f32x4 akd = {0.f, 0.f, 0.f, 0.f}, aqd = {0.f, 0.f, 0.f, 0.f};
@@ -469,8 +480,6 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         lds8(&s.fac[w][1][cb], dw);
         lds8(&s.fac[w][2][cb], er);
         lds8(&s.fac[w][3][cb], el);
-        float ps[8];
-        if constexpr (SIGNED) lds8(&s.psg[w][cb], ps);
         bf16x8 kfh, kfl, kad, kadl, qdh, qdl;
         float qgv[8], kgv[8];
 #pragma unroll
@@ -480,8 +489,8 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             const float f = __builtin_amdgcn_rcpf(d);  // exp(ref_{w+1} - b)
             const float E = d * dw[e];               // exp(b - ref_w)
             const float gm = E * er[e];              // exp(b)
-            const float kx = SIGNED ? kv[8 * kb + e] * ps[e] : kv[8 * kb + e];
-            const float qx = SIGNED ? qv[8 * kb + e] * ps[e] : qv[8 * kb + e];
+            const float kx = SIGNED ? flip_sign(kv[8 * kb + e], sgnb, 8 * kb + e) : kv[8 * kb + e];
+            const float qx = SIGNED ? flip_sign(qv[8 * kb + e], sgnb, 8 * kb + e) : qv[8 * kb + e];
             __bf16 hi, lo;
             split(kx * f, hi, lo);
             kfh[e] = hi;
