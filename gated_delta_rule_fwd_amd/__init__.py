@@ -277,7 +277,9 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
     if ws > 0 and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
-    wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if workspace is not None:
+        _need(workspace, "workspace")
+    wsb = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
     if on is not None or sc is not None:
         dg = None if gate is None else ctypes.byref(DecayGate(z.data_ptr(), A_log.data_ptr(),
                                                               None if dt_bias is None else dt_bias.data_ptr()))
