@@ -14,7 +14,8 @@
 //   S' = Diag(gamma) S + (K^ * gamma / Gamma)^T X
 //
 // The intra-chunk decay ratios are formed per position pair in log space, the
-// fp32 route that page 1 (section 1.2.1, on the lower-bounded decay) names as
+// fp32 route that "Kimi K3 の KDA ..." (section 1.2.1, on the lower-bounded decay)
+// names as
 // the costly one; it needs no bound on g.  The triangular system is solved by
 // forward substitution, i.e. the UT transform applied to the right-hand side.
 //

@@ -25,8 +25,8 @@
  *     the layouts given below; beta and cu_seqlens must be 4-byte aligned,
  *     every other tensor 16-byte aligned.  The caller owns every buffer;
  *     the library allocates nothing and keeps no state between calls other
- *     than a read-only cache of device properties.  Entry points are
- *     thread-safe.
+ *     than each calling thread's last HIP error code (kda_last_hip_error).
+ *     Entry points are thread-safe.
  *   - Work is enqueued on `stream` and runs asynchronously; there is no host
  *     synchronisation except under KDA_FLAG_VALIDATE.
  *   - Every argument is checked on the host before anything is launched, so a
@@ -64,8 +64,8 @@ typedef enum kda_dtype {
 } kda_dtype;
 
 /* q and k are L2-normalised over d_k inside the kernel (eps = 1e-6 under the
- * square root).  Mirrors the model's use_qk_l2norm_in_kernel switch (page 1,
- * section 1.2.1).  Without it q and k are used as given. */
+ * square root).  Mirrors the model's use_qk_l2norm_in_kernel switch ("Kimi K3
+ * の KDA ..." section 1.2.1).  Without it q and k are used as given. */
 #define KDA_FLAG_QK_L2NORM 0x1u
 /* Debug: before the forward pass, check on the device that every g is in
  * [-5, 0], every beta in [0, 1] and that cu_seqlens is monotone from 0 to T;
@@ -75,8 +75,8 @@ typedef enum kda_dtype {
 /* Use the fp32 (per-position-pair) arithmetic path even for bf16 inputs. */
 #define KDA_FLAG_FP32_PATH 0x4u
 /* beta holds write-strength logits; the kernel applies the sigmoid, as the
- * model does in-kernel (page 1, section 1.2.1: beta is a per-head fp32 scalar
- * passed through a sigmoid inside the kernel).  Accepted by every prefill and
+ * model does in-kernel ("Kimi K3 の KDA ..." section 1.2.1: beta is a per-head
+ * fp32 scalar passed through a sigmoid inside the kernel).  Accepted by every prefill and
  * decode entry point. */
 #define KDA_FLAG_BETA_LOGITS 0x8u
 /* Complex KDA ("[논문리뷰] Complex KDA ..." page: the gate range widened to

@@ -32,8 +32,8 @@ Contents
     ("Kimi K3 の KDA ..." section 1.2.1, the output gate).
   * ``product_form``: a second, independently written NumPy formulation that
     builds each transition matrix (I - beta k k^T) Diag(alpha) explicitly
-    (page 1, section 2.3.5: the state map is the ordered product of per-token
-    transitions).  Used for tiny brute-force checks.
+    ("Kimi K3 の KDA ..." section 2.3.5: the state map is the ordered product of
+    per-token transitions).  Used for tiny brute-force checks.
 
 Every function here is pinned by tests in tests/test_oracle_pins.py against
 identities the pages state and textbook linear algebra; see each test's

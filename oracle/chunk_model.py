@@ -29,8 +29,8 @@ the recurrence (the derivation is in the design notes) and the test
 
 The ratio Gamma_r / Gamma_s is formed per 16-token sub-tile pair with a
 reference point between s and r, so no factor leaves [e^-80, e^80] when
-g >= -5 (page 1 section 1.2.1 on the bounded decay; page 2 Q&A on the -5
-bound: 16 steps give at most e^80 < bf16 max).
+g >= -5 ("Kimi K3 の KDA ..." section 1.2.1 on the bounded decay; "Kimi K3 模型结构（2）" Q&A on
+the -5 bound: 16 steps give at most e^80 < bf16 max).
 """
 from __future__ import annotations
 

@@ -13,15 +13,15 @@
  *         per head inside the kernel)
  *     alpha = exp(g)                       (g is the natural-log decay per key
  *        channel: "GDN, KDA の整理", section "Kimi Delta Attention")
- *     S~ = Diag(alpha) S                   (decay first: page 1, section
- *        1.2.1, "decay -> erase -> write"; page 4 applies the decay before the
- *        gradient step, section "Online learning")
+ *     S~ = Diag(alpha) S                   (decay first: "Kimi K3 の KDA ..."
+ *        section 1.2.1, decay then erase then write; "GDN, KDA の整理"
+ *        applies the decay before the gradient step, section "Online learning")
  *     e  = v - S~^T k^                     (innovation: value minus the
  *        decayed state's prediction for k^)
  *     S  = S~ + beta k^ e^T                (erase + write, one gradient step
  *        of rate beta on 1/2 ||S^T k - v||^2)
- *     o_t = scale * S^T q^                 (read AFTER the write: page 1,
- *        section 1.2.1 notes each token reads S_t, not S_{t-1})
+ *     o_t = scale * S^T q^                 (read AFTER the write: "Kimi K3 の KDA ..."
+ *        section 1.2.1: each token reads S_t, not S_{t-1})
  *   final_state[n,h] = S
  *
  * Inputs are fp32 arrays (bf16 tensors widened exactly by the caller) and

@@ -136,7 +136,7 @@ def test_beta_zero_closed_form():
 
 
 # ---------------------------------------------------------------------------
-# P5 -- non-expansiveness (page 1 section 1.2.1: L2-normalised k keeps the
+# P5 -- non-expansiveness ("Kimi K3 の KDA ..." section 1.2.1: L2-normalised k keeps the
 # erase operator's spectral norm <= 1; Complex KDA review, key terms)
 # ---------------------------------------------------------------------------
 def test_non_expansive():
@@ -297,7 +297,7 @@ def test_order_sensitivity():
 
 # ---------------------------------------------------------------------------
 # P13 -- two formulations agree: innovation form (C) vs explicit product of
-# transition matrices (NumPy) -- page 1 section 1.2.1 (innovation) and
+# transition matrices (NumPy) -- "Kimi K3 の KDA ..." section 1.2.1 (innovation) and
 # "GDN, KDA の整理" section "Online learning" (gradient step on the decayed state)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("scale", [1.0, 0.125])
