@@ -121,3 +121,61 @@ def test_random_fused_prefill(kda, i):
         # the outgoing conv states are copies of raw inputs (or of the incoming states): exact
         for x, (got, ref) in enumerate(zip(finals, f_ref)):
             assert np.array_equal(host64(got), np.asarray(ref, np.float64)), "conv state %d" % x
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_fused_decode(kda, i):
+    """Four decode steps per case with the decay input, the short convolution
+    (cache advanced in place) and the output norm drawn per case, carrying
+    the fp32 state and the conv cache; the oracle carries them in fp64."""
+    import torch
+    r = np.random.default_rng(7000 + i)
+    N, H = int(r.integers(1, 7)), int(r.integers(1, 4))
+    d = int(r.choice([64, 128]))
+    dtype = "f32" if r.random() < 0.25 else "bf16"
+    mode = str(r.choice(["plain", "gated", "signed"]))
+    use_conv, use_norm = bool(r.random() < 0.6), bool(r.random() < 0.6)
+    seed = 8000 + i
+    print("case", i, dict(N=N, H=H, d=d, dtype=dtype, mode=mode, conv=use_conv, norm=use_norm), flush=True)
+    S0 = kda_inputs.decode_initial_state(seed, N, H, d, 0.02)
+    state, s_ref = dev(S0), S0.astype(np.float64)
+    ws = kda_inputs.conv_weights(seed, H, d, d) if use_conv else None
+    cache = c_ref = None
+    if use_conv:
+        cs = kda_inputs.conv_states(seed, N, H, d, d, dtype=dtype)
+        cache, c_ref = tuple(dev(c) for c in cs), tuple(_f(c).astype(np.float64) for c in cs)
+    A_log, dt_bias = kda_inputs.gate_params(seed, H, d)
+    w = kda_inputs.norm_weight(seed, d) if use_norm else None
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    for step in range(4):
+        if mode == "gated":
+            x = kda_inputs.gated_decode_step(seed, step, N, H, d, dtype=dtype)
+        elif mode == "signed":
+            x = kda_inputs.signed_decode_step(seed, step, N, H, d, dtype=dtype)
+        else:
+            x = kda_inputs.decode_step(seed, step, N, H, d, dtype=dtype)
+        q, k, v = _f(x.q), _f(x.k), _f(x.v)
+        if use_conv:
+            (q, k, v), c_ref = oracle.decode_conv(c_ref, ws, q, k, v)
+        if mode == "gated":
+            o_ref, s_ref = oracle.decode_gated(s_ref, q, k, v, _f(x.z), A_log, dt_bias, x.beta_logits)
+        else:
+            o_ref, s_ref = oracle.decode_steps(s_ref, q, k, v, x.g, x.beta, alpha_given=(mode == "signed"))
+        kw = dict(out_dtype=torch.float32)
+        if use_conv:
+            kw.update(conv_weights=tuple(dev(t) for t in ws), conv_state=cache)
+        if use_norm:
+            gate = kda_inputs.make_out_gate(seed + 100 + step, (N, H, d), dtype=dtype)
+            o_ref = oracle.out_norm(o_ref, _f(gate).astype(np.float64), w, EPS)
+            kw.update(out_gate=dev(gate), norm_weight=dev(w), norm_eps=EPS)
+        if mode == "gated":
+            o = kda.recurrent_step_gated(dev(x.q), dev(x.k), dev(x.v), dev(x.z), dev(A_log), dev(x.beta_logits),
+                                         state, dt_bias=dev(dt_bias), beta_logits=True, **kw)
+        else:
+            o = kda.recurrent_step(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), state,
+                                   signed_alpha=(mode == "signed"), **kw)
+        torch.cuda.synchronize()
+        check("fdecode%d/step%d" % (i, step), host64(o), o_ref, host64(state), s_ref, tol, bf16_store=False)
+        if use_conv:
+            for x_, (got, ref) in enumerate(zip(cache, c_ref)):
+                assert np.array_equal(host64(got), np.asarray(ref, np.float64)), "conv cache %d" % x_
