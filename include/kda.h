@@ -28,7 +28,9 @@
  *     than each calling thread's last HIP error code (kda_last_hip_error).
  *     Entry points are thread-safe.
  *   - Work is enqueued on `stream` and runs asynchronously; there is no host
- *     synchronisation except under KDA_FLAG_VALIDATE.
+ *     synchronisation except under KDA_FLAG_VALIDATE.  Without that flag a
+ *     call only launches kernels (no memset, copy or allocation), so it may
+ *     be captured into a HIP graph and replayed.
  *   - Every argument is checked on the host before anything is launched, so a
  *     call that returns an error other than KDA_ERR_HIP / KDA_ERR_RANGE has had
  *     no side effect.
