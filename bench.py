@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--cpu-sample-heads", type=int, default=96)
     p.add_argument("--cpu-sample-tokens", type=int, default=65536)
     p.add_argument("--no-extra", action="store_true", help="skip the mid/varlen prefill timings and the copy kernel")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the headline: a context-length sweep T = 2K..64K at H=16, d=128 (bf16), "
+                        "one JSON line with ms and tokens/s per length")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of this bench "
                         "(FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
@@ -161,6 +164,40 @@ def time_decode(kda, torch, kda_inputs, norm=False):
     if not norm:
         line["roofline"]["traffic"] = load_traffic("decode")
     return line
+
+
+def context_sweep(kda, torch, kda_inputs, heads=16, lengths=(2048, 4096, 8192, 16384, 32768, 65536), reps=10):
+    """Prefill time per call over context lengths at 16 heads, d = 128 (the
+    head count and dims of the throughput comparison on the Complex KDA
+    review page; the chunkwise page compares kernels over 2K..64K tokens).
+    Synthetic bf16 inputs drawn like the long-prefill workload."""
+    rows = []
+    for T_ in lengths:
+        inp = kda_inputs.make_prefill(20 + T_ // 2048, 1, T_, heads, D, D, gate="k3", s0_std=0.02)
+        d = {k: _dev(torch, getattr(inp, k)) for k in ("q", "k", "v", "g", "beta", "init_state")}
+        o = torch.empty((1, T_, heads, D), dtype=torch.bfloat16, device="cuda")
+        sT = torch.empty((1, heads, D, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kda.workspace_bytes(1, T_, heads, D, D), dtype=torch.uint8, device="cuda")
+        call = lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["init_state"], o=o,
+                                     final_state=sT, workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        stream = torch.cuda.current_stream()
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        med = float(np.median(ts))
+        gbs = (BYTES_PER_TOKEN_HEAD * T_ * heads + 2 * STATE_BYTES * heads) / (med * 1e-3) / 1e9
+        rows.append({"T": T_, "ms_median": med, "tokens_per_s": T_ / (med * 1e-3), "algorithmic_gbs": gbs})
+        del d, o, sT, ws
+    return {"sweep": "prefill B=1 H=%d d_k=d_v=128 bf16, synthetic; median of %d calls" % (heads, reps),
+            "rows": rows}
 
 
 def cpu_baseline(inp_full, heads, tokens):
@@ -471,6 +508,9 @@ def main():
         sys.exit(1)
     kda.load()
     torch.manual_seed(0)
+    if args.sweep:
+        print(json.dumps(context_sweep(kda, torch, kda_inputs)))
+        return
 
     inp = kda_inputs.workload("long_bf16")
     to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
