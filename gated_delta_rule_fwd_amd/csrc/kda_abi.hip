@@ -19,6 +19,9 @@ constexpr unsigned kKnownFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_VALIDATE | KDA_FL
                                  KDA_FLAG_SIGNED_ALPHA | KDA_FLAG_OUT_NORM;
 constexpr unsigned kDecodeFlags = KDA_FLAG_QK_L2NORM | KDA_FLAG_BETA_LOGITS | KDA_FLAG_SIGNED_ALPHA | KDA_FLAG_OUT_NORM;
 constexpr size_t kValidateBytes = 256;
+constexpr long long kMaxTokenHeads = 1LL << 31;      // B*T*H of a prefill call
+constexpr long long kMaxPrefillChains = 1LL << 22;   // N*H of a prefill call
+constexpr long long kMaxDecodeChains = (1LL << 24) - 1;
 
 kda_status hip_fail(hipError_t e)
 {
@@ -101,6 +104,7 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d)
 {
     if (!d) return static_cast<size_t>(-1);
     if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->num_seqs < 0) return 0;   // rejected by kda_chunk_fwd
+    if (static_cast<long long>(d->B) * d->T * d->H > kMaxTokenHeads) return 0;
     // the descriptor does not say whether cu_seqlens will be passed: cover both
     const size_t dense = workspace_need(d, false);
     const size_t packed = (d->B == 1 && d->num_seqs > 0) ? workspace_need(d, true) : 0;
@@ -132,8 +136,10 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     if (cu_seqlens && (d->B != 1 || d->num_seqs < 0)) return KDA_ERR_INVALID_ARG;
     const long long N = cu_seqlens ? d->num_seqs : d->B;
     const long long tokens = static_cast<long long>(d->B) * d->T;
-    if (tokens * d->H * (d->d_k > d->d_v ? d->d_k : d->d_v) >= (1LL << 40)) return KDA_ERR_INVALID_ARG;
-    if (N * d->H > (1LL << 30)) return KDA_ERR_INVALID_ARG;
+    // size limits: one grid dimension takes at most 2^32 work items (the
+    // sequential passes launch 512 per chain; the chunk-parallel pass, 256 per
+    // (chunk, head), is checked below)
+    if (tokens * d->H > kMaxTokenHeads || N * d->H > kMaxPrefillChains) return KDA_ERR_INVALID_ARG;
     const void* decay = gate ? gate->z : static_cast<const void*>(g);
     if (tokens > 0 && (!q || !k || !v || !decay || !beta || !o)) return KDA_ERR_INVALID_ARG;
     if (gate && tokens > 0 && !gate->A_log) return KDA_ERR_INVALID_ARG;
@@ -150,7 +156,7 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
     if (uses_two_pass(d) && kda::chunk_record_slots(d->B, d->T, d->num_seqs, cu_seqlens != nullptr) * d->H >= (1LL << 24))
-        return KDA_ERR_INVALID_ARG;   // more (chunk, head) workgroups than one launch takes
+        return KDA_ERR_INVALID_ARG;   // more (chunk, head) workgroups than one launch takes (about 2^30 token-heads)
 
     kda::ChunkArgs a{};
     a.B = d->B;
@@ -237,7 +243,7 @@ kda_status recurrent_step_impl(int N, int H, int d_k, int d_v, kda_dtype in_dtyp
     if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return KDA_ERR_UNSUPPORTED;
     if (!head_dim_ok(d_k) || !head_dim_ok(d_v)) return KDA_ERR_UNSUPPORTED;
     if (N < 0 || H <= 0) return KDA_ERR_INVALID_ARG;
-    if (static_cast<long long>(N) * H > (1LL << 31) - 1) return KDA_ERR_INVALID_ARG;
+    if (static_cast<long long>(N) * H > kMaxDecodeChains) return KDA_ERR_INVALID_ARG;   // one 256-thread group per chain
     if (!out_norm_ok(norm, flags, o)) return KDA_ERR_INVALID_ARG;
     if (!conv_ok(conv)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;

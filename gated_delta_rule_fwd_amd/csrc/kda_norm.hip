@@ -44,28 +44,35 @@ __global__ void __launch_bounds__(256)
 out_norm_kernel(const float* x, To* o, const Tg* __restrict__ gate, const float* __restrict__ w, float eps, long rows)
 {
     constexpr int LPR = DV / 4;                 // lanes per row
-    constexpr int RPB = 256 / LPR;              // rows per block
-    const long row = static_cast<long>(blockIdx.x) * RPB + threadIdx.x / LPR;
+    constexpr int RPB = 256 / LPR;              // rows per block and pass
     const int c = 4 * (threadIdx.x % LPR);
-    const bool live = row < rows;
-    const size_t base = static_cast<size_t>(live ? row : 0) * DV + c;
-    const float4 v = live ? *reinterpret_cast<const float4*>(x + base) : make_float4(0.f, 0.f, 0.f, 0.f);
-    float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
-    if (!live) return;
-    const float rs = rsqrtf(ss * (1.f / DV) + eps);
-    const float4 gt = Quad<Tg>::load(gate + base);
     const float4 wt = w ? *reinterpret_cast<const float4*>(w + c) : make_float4(1.f, 1.f, 1.f, 1.f);
-    Quad<To>::store(o + base, make_float4(v.x * rs * wt.x / (1.f + __expf(-gt.x)), v.y * rs * wt.y / (1.f + __expf(-gt.y)),
-                                          v.z * rs * wt.z / (1.f + __expf(-gt.z)), v.w * rs * wt.w / (1.f + __expf(-gt.w))));
+    // grid-stride over row blocks: the grid is capped, so any row count fits one launch
+    for (long row0 = static_cast<long>(blockIdx.x) * RPB; row0 < rows; row0 += static_cast<long>(gridDim.x) * RPB) {
+        const long row = row0 + threadIdx.x / LPR;
+        const bool live = row < rows;
+        const size_t base = static_cast<size_t>(live ? row : 0) * DV + c;
+        const float4 v = live ? *reinterpret_cast<const float4*>(x + base) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+        for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        if (live) {
+            const float rs = rsqrtf(ss * (1.f / DV) + eps);
+            const float4 gt = Quad<Tg>::load(gate + base);
+            Quad<To>::store(o + base,
+                            make_float4(v.x * rs * wt.x / (1.f + __expf(-gt.x)), v.y * rs * wt.y / (1.f + __expf(-gt.y)),
+                                        v.z * rs * wt.z / (1.f + __expf(-gt.z)), v.w * rs * wt.w / (1.f + __expf(-gt.w))));
+        }
+    }
 }
 
 template <int DV>
 hipError_t launch_dv(const ChunkArgs& a, const float* x, long rows, hipStream_t stream)
 {
     constexpr long RPB = 256 / (DV / 4);
-    const dim3 grid(static_cast<unsigned>((rows + RPB - 1) / RPB)), block(256);
+    constexpr long kMaxBlocks = 1L << 20;
+    const long blocks = (rows + RPB - 1) / RPB;
+    const dim3 grid(static_cast<unsigned>(blocks < kMaxBlocks ? blocks : kMaxBlocks)), block(256);
     if (a.in_bf16 && a.out_bf16)
         out_norm_kernel<DV, uint16_t, uint16_t><<<grid, block, 0, stream>>>(
             x, static_cast<uint16_t*>(a.o), static_cast<const uint16_t*>(a.out_gate), a.norm_w, a.norm_eps, rows);

@@ -52,7 +52,8 @@ extern "C" {
 
 typedef enum kda_status {
     KDA_OK = 0,
-    KDA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misaligned pointer, bad layout */
+    KDA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misaligned pointer, bad layout,
+                                 size above the limits below */
     KDA_ERR_UNSUPPORTED = 2,  /* head dims other than 64/128, unknown dtype or flag */
     KDA_ERR_WORKSPACE = 3,    /* workspace smaller than kda_chunk_fwd_workspace_bytes() */
     KDA_ERR_RANGE = 4,        /* only with KDA_FLAG_VALIDATE: g outside [-5, 0], beta outside
@@ -96,6 +97,14 @@ typedef enum kda_dtype {
  * runs as a second kernel there, and it must see o before it is rounded. */
 #define KDA_FLAG_OUT_NORM 0x20u
 
+
+/* Size limits (a larger call returns KDA_ERR_INVALID_ARG before any launch):
+ * prefill B*T*H <= 2^31 token-heads, N*H <= 2^22 chains, and on the
+ * matrix-core path fewer than 2^24 (64-token chunk, head) pairs; decode N*H
+ * <= 2^24 - 1 chains.  They come from the 2^32 work items one grid dimension
+ * takes; every device index is 64-bit.  On one 288 GB device memory runs out
+ * first (a matrix-core prefill needs about 2.7 KB per token-head with its
+ * workspace). */
 
 typedef struct kda_chunk_desc {
     int B;              /* batch (must be 1 when cu_seqlens is given) */

@@ -95,6 +95,22 @@ def test_chunk_fwd_rejects_bad_arguments(lib):
     assert _call(lib, _desc()) == 3                            # matrix-core path needs its record workspace
 
 
+def test_size_limits(lib):
+    # prefill: B*T*H <= 2^31 token-heads and N*H <= 2^22 chains (fp32 path: no workspace needed)
+    f32 = dict(in_dtype=0, out_dtype=0)
+    assert _call(lib, _desc(B=1, T=2 ** 29, H=5, **f32)) == 1
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(B=1, T=2 ** 29, H=5))) == 0
+    assert _call(lib, _desc(B=4096, T=1, H=1025, **f32)) == 1
+    # matrix-core path: fewer than 2^24 (chunk, head) workgroups in the chunk-parallel pass
+    d = _desc(B=1, T=2 ** 30, H=1)
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    assert need == 2 ** 24 * RECORD
+    assert _call(lib, d, ws=FAKE, ws_bytes=need) == 1
+    # decode: N*H <= 2^24 - 1 chains
+    P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(7)]
+    assert lib.kda_recurrent_step(2 ** 12, 2 ** 12, 128, 128, 1, 1, 1.0, kda.FLAG_QK_L2NORM, *P, None) == 1
+
+
 RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
 
 
