@@ -301,8 +301,14 @@ def write_traffic(fetch_dir, write_dir):
         scale[ctr] = COPY_BYTES / max(copy)   # the largest copy is the bench's calibration copy
         for key, names in groups.items():
             vals = [float(r["Counter_Value"]) * 1024 for r in rows if any(n in r["Kernel_Name"] for n in names)]
-            # one call = one dispatch of each kernel of the group
-            ncalls = max(1, min(sum(1 for r in rows if n in r["Kernel_Name"]) for n in names))
+            if key == "chunk_fwd":
+                # a staged call dispatches each kernel once per stage: count
+                # calls by pass-1 workgroups, B * ceil(T/64) * H per call
+                wgs = sum(int(r["Grid_Size"]) // int(r["Workgroup_Size"]) for r in rows
+                          if "chunk_prep_kernel" in r["Kernel_Name"])
+                ncalls = max(1, round(wgs / (B * ((T + 63) // 64) * H)))
+            else:
+                ncalls = max(1, sum(1 for r in rows if names[0] in r["Kernel_Name"]))
             per.setdefault(key, {})[ctr] = sum(vals) / ncalls
     for key, v in per.items():
         if "FETCH_SIZE" in v and "WRITE_SIZE" in v:

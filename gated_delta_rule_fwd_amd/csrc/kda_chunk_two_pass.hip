@@ -151,7 +151,8 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
     const int H = a.H;
     // consecutive workgroups take consecutive heads of one chunk: their
     // q/k/g rows are adjacent in memory
-    const int h = blockIdx.x % H, slot = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    int slot = blockIdx.x / H;
 
     long c0, tok0, tok1;
     int seq;
@@ -165,9 +166,12 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         tok0 = b0;
         tok1 = b1;
     } else {
+        // this launch covers chunks chunk_lo .. chunk_lo + chunk_cnt - 1 of every sequence
         const int nck = (a.T + C - 1) / C;
-        seq = slot / nck;
-        c0 = static_cast<long>(seq) * a.T + static_cast<long>(slot - seq * nck) * C;
+        seq = slot / a.chunk_cnt;
+        const int j = a.chunk_lo + (slot - seq * a.chunk_cnt);
+        slot = seq * nck + j;
+        c0 = static_cast<long>(seq) * a.T + static_cast<long>(j) * C;
         tok0 = static_cast<long>(seq) * a.T;
         tok1 = tok0 + a.T;
     }
@@ -821,6 +825,11 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         slot0 = seq * ((a.T + C - 1) / C);
     }
     const int nch = static_cast<int>((tok1 - tok0 + C - 1) / C);
+    // this launch runs chunks jb .. je - 1 of the chain, from init_state (the
+    // chain's initial state, or the state a launch over the chunks before
+    // left) to final_state
+    const int jb = min(a.chunk_lo, nch);
+    const int je = static_cast<int>(min(static_cast<long>(nch), static_cast<long>(a.chunk_lo) + a.chunk_cnt));
     const ChunkRecord* __restrict__ rc = recs + static_cast<size_t>(h) * nslots + slot0;
     const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
     Tout* __restrict__ op = static_cast<Tout*>(a.o);
@@ -927,9 +936,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         }
     };
 
-    if (nch > 0) {
-        fetch(0, 0, RFULL + 1);
-        fetch_v(0);
+    if (je > jb) {
+        fetch(jb, 0, RFULL + 1);
+        fetch_v(jb);
         commit();
     }
     __syncthreads();
@@ -1136,10 +1145,10 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     // are left to the scheduler to interleave.
     long prev_c0 = 0;
     int prev_L = 0;
-    for (int j = 0; j < nch; ++j) {
+    for (int j = jb; j < je; ++j) {
         const long c0 = tok0 + static_cast<long>(j) * C;
         const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
-        const bool more = j + 1 < nch;
+        const bool more = j + 1 < je;
         const int buf = j & 1;
 
         f16x8 fa0[2][4], fa1[2][4], qa0[2][4], qa1[2][4];
@@ -1150,7 +1159,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             fetch_v(j + 1);
             fetch(j + 1, 0, 5);
         }
-        if (j > 0) store_tile(buf ^ 1, prev_c0, prev_L);
+        if (j > jb) store_tile(buf ^ 1, prev_c0, prev_L);
         f16x8 sh[4], sl[4];
         split_state(sh, sl);
         __builtin_amdgcn_sched_barrier(0);
@@ -1193,7 +1202,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         prev_L = L;
         __syncthreads();
     }
-    if (nch > 0) store_tile((nch - 1) & 1, prev_c0, prev_L);
+    if (je > jb) store_tile((je - 1) & 1, prev_c0, prev_L);
 
     if (a.final_state) {
         const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
@@ -1217,50 +1226,209 @@ size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed)
 {
     const long long slots = chunk_record_slots(B, T, num_seqs, packed);
     size_t bytes = static_cast<size_t>(slots) * H * kChunkRecordBytes;
-    if (packed) bytes += (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256;
+    if (packed)
+        bytes += (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256;
+    else
+        bytes += static_cast<size_t>(B) * H * DK * DV * sizeof(float);
     return bytes;
 }
 
-hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream)
+namespace {
+
+// A short idle gap on the pass-1 stream: the sequential pass of the stage
+// that becomes ready together with the next pass-1 launch then takes its CUs
+// first (its workgroups need a whole CU each, which the small pass-1
+// workgroups would otherwise keep refilling).  About 20 us; always ends.
+__global__ void stage_gap_kernel(int naps)
 {
-    const int chains = (a.cu_seqlens ? a.num_seqs : a.B) * a.H;
-    if (chains == 0) return hipSuccess;
-    const long long slots = chunk_record_slots(a.B, a.T, a.num_seqs, a.cu_seqlens != nullptr);
-    ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
-    if (slots > 0) {
-        int* map = nullptr;
-        if (a.cu_seqlens) {
-            map = reinterpret_cast<int*>(static_cast<char*>(workspace) +
-                                         static_cast<size_t>(slots) * a.H * kChunkRecordBytes);
-            slot_map_kernel<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(
-                a.cu_seqlens, a.num_seqs, a.T, static_cast<int>(slots), map);
-        }
-        const unsigned pg = static_cast<unsigned>(slots * a.H);
-        if (a.signed_alpha && a.conv)
-            chunk_prep_kernel<true, true><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
-        else if (a.signed_alpha)
-            chunk_prep_kernel<true, false><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
-        else if (a.conv)
-            chunk_prep_kernel<false, true><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
-        else
-            chunk_prep_kernel<false, false><<<pg, NT, 0, stream>>>(a, recs, map, static_cast<int>(slots));
+    for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+constexpr int kMaxStages = 6;
+constexpr int kMinStageChunks = 16;
+constexpr int kMaxDevices = 16;
+
+// Chunk ranges of the overlapped schedule: bounds[0] = 0 < ... < bounds[n] =
+// nck; returns n (1 = no overlap).  Stage s+1's pass 1 runs on the CUs that
+// stage s's pass 2 leaves idle and should take no longer than it, so stage
+// sizes follow n_{s+1} = n_s / rho with rho = (pass-1 time of one chunk of
+// every chain on the idle CUs) / (pass-2 time of one chunk).  The unit costs
+// are measured on the 64K-token, 96-head prefill: ~6.0 us of one CU per
+// (chunk, head) for pass 1 on CUs it has to itself, ~3.4 us per chunk for
+// pass 2 while pass 1 runs beside it.
+int plan_stages(int nck, int chains, int cus, int* bounds)
+{
+    bounds[0] = 0;
+    bounds[1] = nck;
+    const int wg2 = 16 * ((chains + 7) / 8);       // pass-2 workgroups, one CU each
+    const int idle = cus - wg2;
+    // below 256 chunks the extra launches and the gap cost more than the
+    // overlap gains (4096-token prefills at 24 and 32 heads: +5 %)
+    if (nck < 256 || idle < 32) return 1;
+    const double rho = chains * 6.0 / idle / 3.4;
+    const double grow = 1.0 / rho;
+    double sum = 0.0, term = 1.0;
+    for (int k = 0; k < kMaxStages; ++k, term *= grow) sum += term;
+    int n = 0, done = 0;
+    double size = static_cast<double>(nck) / sum;
+    while (done < nck) {
+        int take = static_cast<int>(size + 0.5);
+        if (take < kMinStageChunks) take = kMinStageChunks;
+        const int left = nck - done;
+        if (take > left || left - take < kMinStageChunks || n + 1 == kMaxStages) take = left;
+        done += take;
+        bounds[++n] = done;
+        size = take * grow;
     }
-    const int ns = static_cast<int>(slots);
+    return n;
+}
+
+// Per calling thread and device: the second stream and the events of the
+// overlapped schedule, created on first use and kept until the process ends.
+struct OverlapStreams {
+    bool ready = false;
+    hipStream_t side = nullptr;
+    hipEvent_t p1[kMaxStages] = {};   // pass 1 of stage s done (recorded on the caller's stream)
+    hipEvent_t p2[kMaxStages] = {};   // pass 2 of stage s done (recorded on the side stream)
+};
+thread_local OverlapStreams t_overlap[kMaxDevices];
+
+OverlapStreams* overlap_streams(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    OverlapStreams& o = t_overlap[dev];
+    if (o.ready) return &o;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    bool ok = hipStreamCreateWithFlags(&o.side, hipStreamNonBlocking) == hipSuccess;
+    for (int s = 0; ok && s < kMaxStages; ++s)
+        ok = hipEventCreateWithFlags(&o.p1[s], hipEventDisableTiming) == hipSuccess &&
+             hipEventCreateWithFlags(&o.p2[s], hipEventDisableTiming) == hipSuccess;
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (!ok) return nullptr;   // what was created stays allocated; the serial order is used
+    o.ready = true;
+    return &o;
+}
+
+template <bool SIGNED, bool CONV>
+void launch_prep(const ChunkArgs& a, ChunkRecord* recs, const int* map, int slots, unsigned groups,
+                 hipStream_t stream)
+{
+    chunk_prep_kernel<SIGNED, CONV><<<groups, NT, 0, stream>>>(a, recs, map, slots);
+}
+
+void prep(const ChunkArgs& a, ChunkRecord* recs, const int* map, int slots, unsigned groups, hipStream_t stream)
+{
+    if (a.signed_alpha && a.conv)
+        launch_prep<true, true>(a, recs, map, slots, groups, stream);
+    else if (a.signed_alpha)
+        launch_prep<true, false>(a, recs, map, slots, groups, stream);
+    else if (a.conv)
+        launch_prep<false, true>(a, recs, map, slots, groups, stream);
+    else
+        launch_prep<false, false>(a, recs, map, slots, groups, stream);
+}
+
+void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, hipStream_t stream)
+{
     // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
     const int groups = (chains + 7) / 8;
     const dim3 grid(groups * 8 * NSLICE), block(NT);
     if (a.conv) {
         if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, true><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<uint16_t, true><<<grid, block, 0, stream>>>(a, recs, slots);
         else
-            chunk_scan_kernel<float, true><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<float, true><<<grid, block, 0, stream>>>(a, recs, slots);
     } else {
         if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, false><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<uint16_t, false><<<grid, block, 0, stream>>>(a, recs, slots);
         else
-            chunk_scan_kernel<float, false><<<grid, block, 0, stream>>>(a, recs, ns);
+            chunk_scan_kernel<float, false><<<grid, block, 0, stream>>>(a, recs, slots);
     }
-    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStream_t stream)
+{
+    const bool packed = args.cu_seqlens != nullptr;
+    const int chains = (packed ? args.num_seqs : args.B) * args.H;
+    if (chains == 0) return hipSuccess;
+    const long long slots = chunk_record_slots(args.B, args.T, args.num_seqs, packed);
+    const int ns = static_cast<int>(slots);
+    ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
+    char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
+    const int nck = packed ? 0 : (args.T + C - 1) / C;
+
+    // the overlapped schedule for a dense batch, when it pays and the stream is not being captured
+    int bounds[kMaxStages + 1];
+    int stages = 1;
+    OverlapStreams* ov = nullptr;
+    if (!packed) {
+        int dev = 0, cus = 0;
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone &&
+            hipStreamGetDevice(stream, &dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            stages = plan_stages(nck, chains, cus, bounds);
+        if (stages > 1) ov = overlap_streams(dev);
+        if (!ov) stages = 1;
+    }
+
+    ChunkArgs a = args;
+    if (stages == 1) {
+        int* map = nullptr;
+        if (slots > 0) {
+            if (packed) {
+                map = reinterpret_cast<int*>(after);
+                slot_map_kernel<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(
+                    a.cu_seqlens, a.num_seqs, a.T, ns, map);
+            }
+            a.chunk_lo = 0;
+            a.chunk_cnt = packed ? ns : nck;
+            prep(a, recs, map, ns, static_cast<unsigned>(slots * a.H), stream);
+        }
+        a.chunk_lo = 0;
+        a.chunk_cnt = packed ? ns : nck;
+        scan(a, recs, ns, chains, stream);
+        return hipGetLastError();
+    }
+
+    // stage s covers chunks bounds[s] .. bounds[s+1] - 1 of every sequence;
+    // the state between stages goes through the workspace
+    float* carried = reinterpret_cast<float*>(after);
+    auto stage_args = [&](int s) {
+        ChunkArgs b = args;
+        b.chunk_lo = bounds[s];
+        b.chunk_cnt = bounds[s + 1] - bounds[s];
+        b.init_state = s == 0 ? args.init_state : carried;
+        b.final_state = s + 1 == stages ? args.final_state : carried;
+        return b;
+    };
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t r) { if (e == hipSuccess && r != hipSuccess) e = r; return e == hipSuccess; };
+    prep(stage_args(0), recs, nullptr, ns, static_cast<unsigned>(args.B * bounds[1] * args.H), stream);
+    ok(hipGetLastError());
+    ok(hipEventRecord(ov->p1[0], stream));
+    for (int s = 0; s < stages && e == hipSuccess; ++s) {
+        if (!ok(hipStreamWaitEvent(ov->side, ov->p1[s], 0))) break;
+        scan(stage_args(s), recs, ns, chains, ov->side);
+        ok(hipGetLastError());
+        ok(hipEventRecord(ov->p2[s], ov->side));
+        if (s + 1 < stages && e == hipSuccess) {
+            // pass 1 of stage s+1 starts with pass 2 of stage s, behind a short gap
+            if (s >= 1) ok(hipStreamWaitEvent(stream, ov->p2[s - 1], 0));
+            stage_gap_kernel<<<1, 64, 0, stream>>>(6);
+            const ChunkArgs b = stage_args(s + 1);
+            prep(b, recs, nullptr, ns, static_cast<unsigned>(args.B * b.chunk_cnt * args.H), stream);
+            ok(hipGetLastError());
+            ok(hipEventRecord(ov->p1[s + 1], stream));
+        }
+    }
+    // join: later work on the caller's stream sees every stage
+    if (e == hipSuccess) ok(hipStreamWaitEvent(stream, ov->p2[stages - 1], 0));
+    return e;
 }
 
 }  // namespace kda

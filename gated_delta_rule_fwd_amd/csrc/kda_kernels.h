@@ -41,6 +41,9 @@ struct ChunkArgs {
     const float* conv_w[3];
     const void* conv_init[3];
     int conv;
+    // matrix-core path: the chunks each launch covers in every chain
+    // (chunk_lo .. chunk_lo + chunk_cnt - 1; set by launch_chunk_two_pass)
+    int chunk_lo, chunk_cnt;
 };
 
 // Inputs of one decode step; z/A_log/dt_bias replace g when gated.
@@ -94,9 +97,16 @@ hipError_t launch_out_norm(const ChunkArgs& a, const float* x, hipStream_t strea
 // ceil(len/64) never reaches the next sequence's first slot).
 constexpr size_t kChunkRecordBytes = 74240;
 long long chunk_record_slots(int B, int T, int num_seqs, bool packed);
-// workspace: records (h * slots + slot), then (packed sequences only) one
-// int32 per slot naming its sequence or -1.
+// workspace: records (h * slots + slot), then one int32 per slot naming its
+// sequence or -1 (packed sequences) or the fp32 state of every chain
+// [B*H, 128, 128] carried between the overlapped launches (dense batch).
 size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed);
+// A dense batch whose sequential pass leaves CUs idle runs in stages: pass 1
+// of stage s+1 on the idle CUs while pass 2 of stage s runs, pass 2 on a
+// second stream of the calling thread, joined to `stream` before returning.
+// Otherwise (packed sequences, short chains, many chains, or a stream under
+// graph capture) pass 1 then pass 2 on `stream`.  Both orders give the same
+// bits.
 hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream);
 
 // Conv states after a prefill: the last 3 raw inputs of every sequence for

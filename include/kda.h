@@ -24,13 +24,20 @@
  *   - All tensor pointers are DEVICE pointers, row-major and contiguous in
  *     the layouts given below; beta and cu_seqlens must be 4-byte aligned,
  *     every other tensor 16-byte aligned.  The caller owns every buffer;
- *     the library allocates nothing and keeps no state between calls other
- *     than each calling thread's last HIP error code (kda_last_hip_error).
- *     Entry points are thread-safe.
+ *     the library allocates no device memory.  Between calls it keeps each
+ *     calling thread's last HIP error code (kda_last_hip_error) and, per
+ *     calling thread and device, one HIP stream and twelve events (created
+ *     on first use, kept until the process ends) with which a long dense
+ *     prefill overlaps its two kernels (kda_chunk_fwd below).  Entry points
+ *     are thread-safe.
  *   - Work is enqueued on `stream` and runs asynchronously; there is no host
- *     synchronisation except under KDA_FLAG_VALIDATE.  Without that flag a
- *     call only launches kernels (no memset, copy or allocation), so it may
- *     be captured into a HIP graph and replayed.
+ *     synchronisation except under KDA_FLAG_VALIDATE.  Work a call puts on
+ *     its second stream is joined back to `stream` (an event wait) before
+ *     the call returns, so later work on `stream` sees every output.
+ *     Without KDA_FLAG_VALIDATE a call only launches kernels and records or
+ *     waits on events (no memset, copy or allocation), so it may be captured
+ *     into a HIP graph and replayed; under capture the prefill does not use
+ *     the second stream.
  *   - Every argument is checked on the host before anything is launched, so a
  *     call that returns an error other than KDA_ERR_HIP / KDA_ERR_RANGE has had
  *     no side effect.
@@ -122,7 +129,10 @@ typedef struct kda_chunk_desc {
 /* Bytes of device workspace the chunkwise entry points need for this
  * descriptor: the matrix-core path (bf16 inputs, d_k = d_v = 128, no
  * KDA_FLAG_FP32_PATH) keeps one 74,240-byte record per (64-token chunk,
- * head) there; the fp32 path needs none; KDA_FLAG_OUT_NORM with a bf16 o adds
+ * head) there, plus, for a dense batch, the fp32 state of every (b, h) chain
+ * (64 KB each) carried between the overlapped stages, or, for packed
+ * sequences, one int32 per chunk slot; the fp32 path needs none;
+ * KDA_FLAG_OUT_NORM with a bf16 o adds
  * B*T*H*d_v fp32 values; KDA_FLAG_VALIDATE adds 256 bytes.  When num_seqs > 0 and B == 1 the figure covers both the dense and
  * the packed (cu_seqlens) layout.  Returns 0 for a descriptor the entry
  * points reject and (size_t)-1 for a null descriptor. */
@@ -133,6 +143,13 @@ KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
  * chunkwise algorithm and on which form each phase uses).  Chunks of 64
  * tokens restart at every sequence start; the last chunk of a sequence may be
  * partial; a zero-length sequence passes its initial state through unchanged.
+ *
+ * The matrix-core path runs a chunk-parallel kernel and then a sequential
+ * one.  For a dense batch of at least 256 chunks per sequence whose
+ * sequential kernel leaves CUs idle, the chunks are split into up to six
+ * stages and the chunk-parallel kernel of stage s+1 runs on the idle CUs
+ * while the sequential kernel of stage s runs on a second stream; the
+ * outputs are bit-identical to the unstaged order.
  *
  *   q, k        [B, T, H, d_k]  in_dtype
  *   v           [B, T, H, d_v]  in_dtype

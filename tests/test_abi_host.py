@@ -104,7 +104,7 @@ def test_size_limits(lib):
     # matrix-core path: fewer than 2^24 (chunk, head) workgroups in the chunk-parallel pass
     d = _desc(B=1, T=2 ** 30, H=1)
     need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
-    assert need == 2 ** 24 * RECORD
+    assert need == 2 ** 24 * RECORD + STATE
     assert _call(lib, d, ws=FAKE, ws_bytes=need) == 1
     # decode: N*H <= 2^24 - 1 chains
     P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(7)]
@@ -112,6 +112,7 @@ def test_size_limits(lib):
 
 
 RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
+STATE = 128 * 128 * 4   # fp32 state of one chain, carried between the stages of a dense batch
 
 
 def test_workspace_sizes(lib):
@@ -120,18 +121,18 @@ def test_workspace_sizes(lib):
     assert size(in_dtype=0) == 0
     assert size(d_k=64, d_v=64) == 0
     assert size(flags=kda.FLAG_QK_L2NORM | kda.FLAG_FP32_PATH) == 0
-    # dense batch: B * ceil(T / 64) chunk records per head
-    assert size(B=3, T=130, H=5) == 3 * 3 * 5 * RECORD
+    # dense batch: B * ceil(T / 64) chunk records per head, then the state of every chain
+    assert size(B=3, T=130, H=5) == 3 * 3 * 5 * RECORD + 3 * 5 * STATE
     # packed sequences: num_seqs + T // 64 slots per head plus one int32 per slot (256-byte rounded);
     # the descriptor does not say which layout is coming, so the larger need is reported
     slots = 7 + 1000 // 64
-    assert size(B=1, T=1000, H=4, num_seqs=7) == max(slots * 4 * RECORD + 256, 16 * 4 * RECORD)
+    assert size(B=1, T=1000, H=4, num_seqs=7) == max(slots * 4 * RECORD + 256, 16 * 4 * RECORD + 4 * STATE)
     assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 50 * 2 * RECORD + 256 + 3 * 2 * RECORD
     # validation counters come first
-    assert size(B=2, T=64, H=1, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * RECORD
+    assert size(B=2, T=64, H=1, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * RECORD + 2 * STATE
     # a misaligned workspace is refused before anything runs
     d = _desc(B=1, T=64, H=1)
-    assert _call(lib, d, ws=FAKE + 8, ws_bytes=RECORD) == 1
+    assert _call(lib, d, ws=FAKE + 8, ws_bytes=RECORD + STATE) == 1
 
 
 def test_chunk_fwd_empty_batch_is_a_no_op(lib):
