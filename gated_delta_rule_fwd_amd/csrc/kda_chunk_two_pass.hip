@@ -1248,12 +1248,20 @@ constexpr int kMaxStages = 6;
 constexpr int kMinStageChunks = 16;
 constexpr int kMaxDevices = 16;
 
+// With less pass-1 work than ~8K (chunk, chain) pairs the extra launches and
+// the gaps cost more than the overlap gains (+5 % on 4096-token prefills at
+// 24 and 32 heads, +2 % at 16K tokens and 16 heads).
+bool stages_may_pay(int nck, int chains)
+{
+    return nck >= 256 && static_cast<long>(nck) * chains >= 8192;
+}
+
 // Chunk ranges of the overlapped schedule: bounds[0] = 0 < ... < bounds[n] =
 // nck; returns n (1 = no overlap).  Stage s+1's pass 1 runs on the CUs that
 // stage s's pass 2 leaves idle and should take no longer than it, so stage
 // sizes follow n_{s+1} = n_s / rho with rho = (pass-1 time of one chunk of
 // every chain on the idle CUs) / (pass-2 time of one chunk).  The unit costs
-// are measured on the 64K-token, 96-head prefill: ~6.0 us of one CU per
+// are measured on the 64K-token, 96-head prefill: ~6.3 us of one CU per
 // (chunk, head) for pass 1 on CUs it has to itself, ~3.4 us per chunk for
 // pass 2 while pass 1 runs beside it.
 int plan_stages(int nck, int chains, int cus, int* bounds)
@@ -1262,10 +1270,8 @@ int plan_stages(int nck, int chains, int cus, int* bounds)
     bounds[1] = nck;
     const int wg2 = 16 * ((chains + 7) / 8);       // pass-2 workgroups, one CU each
     const int idle = cus - wg2;
-    // below 256 chunks the extra launches and the gap cost more than the
-    // overlap gains (4096-token prefills at 24 and 32 heads: +5 %)
-    if (nck < 256 || idle < 32) return 1;
-    const double rho = chains * 6.0 / idle / 3.4;
+    if (!stages_may_pay(nck, chains) || idle < 32) return 1;
+    const double rho = chains * 6.3 / idle / 3.4;
     const double grow = 1.0 / rho;
     double sum = 0.0, term = 1.0;
     for (int k = 0; k < kMaxStages; ++k, term *= grow) sum += term;
@@ -1365,7 +1371,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     int bounds[kMaxStages + 1];
     int stages = 1;
     OverlapStreams* ov = nullptr;
-    if (!packed) {
+    if (!packed && stages_may_pay(nck, chains)) {
         int dev = 0, cus = 0;
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone &&
