@@ -1278,7 +1278,7 @@ int plan_stages(int nck, int chains, int cus, int* bounds)
     int n = 0, done = 0;
     double size = static_cast<double>(nck) / sum;
     while (done < nck) {
-        int take = static_cast<int>(size + 0.5);
+        int take = static_cast<int>((size < nck ? size : nck) + 0.5);
         if (take < kMinStageChunks) take = kMinStageChunks;
         const int left = nck - done;
         if (take > left || left - take < kMinStageChunks || n + 1 == kMaxStages) take = left;
