@@ -1,7 +1,8 @@
 """Parity past 2^31 elements per tensor: at T = 65536 and H = 320 the bf16 q,
 k, v and o hold 2.7e9 elements (byte offsets up to 5.4e9) and the fp32 g
 byte offsets reach 1.07e10, so any 32-bit index arithmetic in the kernels
-would read or write the wrong rows.  The decode state at N = 512, H = 320
+would read or write the wrong rows.  A 64-head prefill of 270,000 tokens
+does the same through the staged order, and the decode state at N = 512, H = 320
 holds 2.7e9 fp32 values likewise.
 
 The inputs are four seeded chains tiled over the heads (head h carries chain
@@ -80,6 +81,36 @@ def test_prefill_past_2_31_elements(kda):
         for j, h in enumerate(heads):
             c = h % CHAINS
             check("large_prefill/h%d" % h, o_h[:, :, j], o_ref[:, :, c], s_h[:, j], s_ref[:, c], TOL_BF16,
+                  bf16_store=True)
+
+
+def test_staged_prefill_past_2_31_elements(kda):
+    """A dense prefill that runs in stages (64 heads leave CUs idle during the
+    sequential pass) at T = 270,000 tokens: 2.2e9 elements per bf16 tensor and
+    4,219 chunks per chain.  Every head against its representative bit for
+    bit, the four representatives against the oracle on the first and last
+    65,536 tokens and on the final state."""
+    import torch
+    T, H, d = 270_000, 64, 128
+    assert T * H * d > 2 ** 31
+    print("large staged prefill T=%d H=%d" % (T, H), flush=True)
+    base = kda_inputs.make_prefill(93, 1, T, CHAINS, d, d, dtype="bf16", s0_std=0.02)
+    o_ref, s_ref = oracle.forward(base)
+    q, k, v = (_tile(_dev(getattr(base, n)), 2, H) for n in ("q", "k", "v"))
+    g = _tile(_dev(base.g), 2, H)
+    beta = _tile(_dev(base.beta), 2, H)
+    s0 = _tile(_dev(base.init_state), 1, H)
+    o, s = kda.chunk_fwd(q, k, v, g, beta, s0)
+    torch.cuda.synchronize()
+    del q, k, v, g, beta
+    assert _same_as_representatives(o, 2, H), "o of a head differs from its chain's representative"
+    assert _same_as_representatives(s, 1, H), "final state of a head differs from its chain's representative"
+    W = 65536
+    for h in range(CHAINS):
+        s_h = host64(s[:, h])
+        for t0 in (0, T - W):
+            o_h = host64(o[:, t0:t0 + W, h])
+            check("large_staged/h%d/t%d" % (h, t0), o_h, o_ref[:, t0:t0 + W, h], s_h, s_ref[:, h], TOL_BF16,
                   bf16_store=True)
 
 
