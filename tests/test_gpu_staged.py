@@ -47,7 +47,10 @@ def _run_both(kda, fwd, args, kw, B, T):
     return (o1, s1), (o2.reshape(o1.shape), s2)
 
 
-@pytest.mark.parametrize("B,T,H", [(1, 16384, 4), (2, 17000, 3)])
+# Every shape here is above the staging threshold: at least 256 chunks per
+# sequence, at least 8K (chunk, chain) pairs, and few enough chains (B*H <= 112)
+# to leave CUs idle during the sequential pass.
+@pytest.mark.parametrize("B,T,H", [(1, 16384, 32), (2, 17000, 16)])
 def test_staged_equals_unstaged_plain(kda, B, T, H):
     import torch
     inp = kda_inputs.make_prefill(80 + B, B, T, H, 128, 128, s0_std=0.02)
@@ -59,7 +62,7 @@ def test_staged_equals_unstaged_plain(kda, B, T, H):
 def test_staged_equals_unstaged_gated_conv_norm(kda):
     """The whole layer core: gate prologue, short convolution, output norm."""
     import torch
-    B, T, H = 1, 16500, 3
+    B, T, H = 1, 16500, 32
     gin = kda_inputs.make_gated_prefill(83, B, T, H, 128, 128, s0_std=0.02)
     ws = kda_inputs.conv_weights(83, H, 128, 128)
     gate = dev(kda_inputs.make_out_gate(83, (B, T, H, 128)))
@@ -83,7 +86,7 @@ def test_staged_equals_unstaged_gated_conv_norm(kda):
 
 def test_staged_equals_unstaged_signed(kda):
     import torch
-    B, T, H = 1, 16384, 2
+    B, T, H = 1, 16384, 32
     inp = kda_inputs.make_signed_prefill(84, B, T, H, 128, 128, s0_std=0.02)
     args = [dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state)]
     (o1, s1), (o2, s2) = _run_both(kda, kda.chunk_fwd, args, dict(signed_alpha=True), B, T)
@@ -93,7 +96,7 @@ def test_staged_equals_unstaged_signed(kda):
 def test_staged_against_oracle(kda):
     """A staged call with a ragged last chunk against the fp64 oracle."""
     import torch
-    B, T, H = 1, 16400, 2
+    B, T, H = 1, 16400, 32
     inp = kda_inputs.make_prefill(85, B, T, H, 128, 128, s0_std=0.02)
     o, s = kda.chunk_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state),
                          out_dtype=torch.float32)
@@ -106,7 +109,7 @@ def test_staged_call_in_a_graph_and_on_two_threads(kda):
     """Captured (unstaged inside the graph) and replayed, and run from two
     host threads on streams of their own: both equal the eager staged call."""
     import torch
-    B, T, H = 1, 16384, 4
+    B, T, H = 1, 16384, 32
     inps = [kda_inputs.make_prefill(86 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
     devs = [[dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(x.init_state)] for x in inps]
     bufs = []
@@ -156,3 +159,23 @@ def test_staged_call_in_a_graph_and_on_two_threads(kda):
     assert not errors, errors
     for i in range(2):
         assert torch.equal(bufs[i]["o"], refs[i][0]) and torch.equal(bufs[i]["s"], refs[i][1]), "thread %d" % i
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_random_staged_against_oracle(kda, i):
+    """Seeded random dense batches long enough to run in stages (ragged last
+    chunk, one or two sequences, few heads, each gate distribution) against
+    the fp64 oracle on every head."""
+    import numpy as np
+    import torch
+    r = np.random.default_rng(9000 + i)
+    B = int(r.integers(1, 3))
+    T = int(r.integers(16384, 24000))
+    H = int(r.integers(32, 49)) // B          # 32..48 chains: staged
+    gate = str(r.choice(["k3", "slow", "sigmoid"]))
+    print("case", i, dict(B=B, T=T, H=H, gate=gate), flush=True)
+    inp = kda_inputs.make_prefill(9100 + i, B, T, H, 128, 128, gate=gate, s0_std=0.02)
+    o, s = kda.chunk_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.forward(inp)
+    check("random_staged%d" % i, host64(o), o_ref, host64(s), s_ref, 2e-2, bf16_store=True)
