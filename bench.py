@@ -61,7 +61,8 @@ def parse():
 
 # the sources each measured path is built from (kernels, their headers, the launch code)
 KERNEL_SOURCES = {
-    "chunk_fwd": ("kda_chunk_two_pass.hip", "kda_mfma.h", "kda_kernels.h", "kda_device.h", "kda_abi.hip"),
+    "chunk_fwd": ("kda_chunk_two_pass.hip", "kda_stage_plan.h", "kda_mfma.h", "kda_kernels.h", "kda_device.h",
+                  "kda_abi.hip"),
     "decode": ("kda_decode.hip", "kda_kernels.h", "kda_device.h", "kda_abi.hip"),
 }
 

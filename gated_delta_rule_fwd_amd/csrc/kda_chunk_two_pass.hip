@@ -48,6 +48,7 @@
 //                                                 to U~)
 #include "kda_kernels.h"
 #include "kda_mfma.h"
+#include "kda_stage_plan.h"
 
 namespace kda {
 
@@ -1244,50 +1245,7 @@ __global__ void stage_gap_kernel(int naps)
     for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
-constexpr int kMaxStages = 6;
-constexpr int kMinStageChunks = 16;
 constexpr int kMaxDevices = 16;
-
-// With less pass-1 work than ~8K (chunk, chain) pairs the extra launches and
-// the gaps cost more than the overlap gains (+5 % on 4096-token prefills at
-// 24 and 32 heads, +2 % at 16K tokens and 16 heads).
-bool stages_may_pay(int nck, int chains)
-{
-    return nck >= 256 && static_cast<long>(nck) * chains >= 8192;
-}
-
-// Chunk ranges of the overlapped schedule: bounds[0] = 0 < ... < bounds[n] =
-// nck; returns n (1 = no overlap).  Stage s+1's pass 1 runs on the CUs that
-// stage s's pass 2 leaves idle and should take no longer than it, so stage
-// sizes follow n_{s+1} = n_s / rho with rho = (pass-1 time of one chunk of
-// every chain on the idle CUs) / (pass-2 time of one chunk).  The unit costs
-// are measured on the 64K-token, 96-head prefill: ~6.3 us of one CU per
-// (chunk, head) for pass 1 on CUs it has to itself, ~3.4 us per chunk for
-// pass 2 while pass 1 runs beside it.
-int plan_stages(int nck, int chains, int cus, int* bounds)
-{
-    bounds[0] = 0;
-    bounds[1] = nck;
-    const int wg2 = 16 * ((chains + 7) / 8);       // pass-2 workgroups, one CU each
-    const int idle = cus - wg2;
-    if (!stages_may_pay(nck, chains) || idle < 32) return 1;
-    const double rho = chains * 6.3 / idle / 3.4;
-    const double grow = 1.0 / rho;
-    double sum = 0.0, term = 1.0;
-    for (int k = 0; k < kMaxStages; ++k, term *= grow) sum += term;
-    int n = 0, done = 0;
-    double size = static_cast<double>(nck) / sum;
-    while (done < nck) {
-        int take = static_cast<int>((size < nck ? size : nck) + 0.5);
-        if (take < kMinStageChunks) take = kMinStageChunks;
-        const int left = nck - done;
-        if (take > left || left - take < kMinStageChunks || n + 1 == kMaxStages) take = left;
-        done += take;
-        bounds[++n] = done;
-        size = take * grow;
-    }
-    return n;
-}
 
 // Per calling thread and device: the second stream and the events of the
 // overlapped schedule, created on first use and kept until the process ends.
