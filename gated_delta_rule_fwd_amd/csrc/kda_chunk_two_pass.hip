@@ -1257,6 +1257,11 @@ struct OverlapStreams {
 };
 thread_local OverlapStreams t_overlap[kMaxDevices];
 
+OverlapStreams* existing_overlap_streams(int dev)
+{
+    return dev >= 0 && dev < kMaxDevices && t_overlap[dev].ready ? &t_overlap[dev] : nullptr;
+}
+
 OverlapStreams* overlap_streams(int dev)
 {
     if (dev < 0 || dev >= kMaxDevices) return nullptr;
@@ -1331,12 +1336,15 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     OverlapStreams* ov = nullptr;
     if (!packed && stages_may_pay(nck, chains)) {
         int dev = 0, cus = 0;
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone &&
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusInvalidated;
+        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusInvalidated &&
             hipStreamGetDevice(stream, &dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
             stages = plan_stages(nck, chains, cus, bounds);
-        if (stages > 1) ov = overlap_streams(dev);
+        // under graph capture only a second stream that already exists is used
+        // (the capture then records the fork and the join); streams and events
+        // are not created inside a capture
+        if (stages > 1) ov = cap == hipStreamCaptureStatusNone ? overlap_streams(dev) : existing_overlap_streams(dev);
         if (!ov) stages = 1;
     }
 

@@ -36,8 +36,10 @@
  *     the call returns, so later work on `stream` sees every output.
  *     Without KDA_FLAG_VALIDATE a call only launches kernels and records or
  *     waits on events (no memset, copy or allocation), so it may be captured
- *     into a HIP graph and replayed; under capture the prefill does not use
- *     the second stream.
+ *     into a HIP graph and replayed.  Under capture the prefill uses its
+ *     second stream only if the calling thread has created it already (by an
+ *     earlier staged call); the graph then records the fork and the join.
+ *     Otherwise the captured work takes the unstaged order.
  *   - Every argument is checked on the host before anything is launched, so a
  *     call that returns an error other than KDA_ERR_HIP / KDA_ERR_RANGE has had
  *     no side effect.

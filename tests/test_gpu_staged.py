@@ -106,8 +106,11 @@ def test_staged_against_oracle(kda):
 
 
 def test_staged_call_in_a_graph_and_on_two_threads(kda):
-    """Captured (unstaged inside the graph) and replayed, and run from two
-    host threads on streams of their own: both equal the eager staged call."""
+    """Captured and replayed (staged inside the graph: the calling thread's
+    second stream exists from the eager calls, so the capture records the fork
+    and the join), captured on a fresh thread (no second stream yet: the graph
+    holds the unstaged order), and run from two host threads on streams of
+    their own: all equal the eager staged call bit for bit."""
     import torch
     B, T, H = 1, 16384, 32
     inps = [kda_inputs.make_prefill(86 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
@@ -135,11 +138,35 @@ def test_staged_call_in_a_graph_and_on_two_threads(kda):
         torch.cuda.synchronize()
         assert torch.equal(bufs[0]["o"], refs[0][0]) and torch.equal(bufs[0]["s"], refs[0][1]), "replay %d" % rep
 
+    # a capture on a thread that has made no staged call yet
+    errors = []
+
+    def capture_fresh():
+        try:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                kda.chunk_fwd(*devs[1], o=bufs[1]["o"], final_state=bufs[1]["s"], workspace=bufs[1]["ws"])
+            torch.cuda.synchronize()
+            for _ in range(2):
+                bufs[1]["o"].zero_()
+                bufs[1]["s"].zero_()
+                torch.cuda.synchronize()
+                g2.replay()
+                torch.cuda.synchronize()
+                if not (torch.equal(bufs[1]["o"], refs[1][0]) and torch.equal(bufs[1]["s"], refs[1][1])):
+                    errors.append("fresh-thread graph replay differs")
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    t = threading.Thread(target=capture_fresh)
+    t.start()
+    t.join()
+    assert not errors, errors
+
     for b in bufs:
         b["o"].zero_()
         b["s"].zero_()
     torch.cuda.synchronize()
-    errors = []
 
     def worker(i):
         try:
