@@ -1274,8 +1274,18 @@ OverlapStreams* overlap_streams(int dev)
     for (int s = 0; ok && s < kMaxStages; ++s)
         ok = hipEventCreateWithFlags(&o.p1[s], hipEventDisableTiming) == hipSuccess &&
              hipEventCreateWithFlags(&o.p2[s], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        // give back what was created; the call takes the unstaged order
+        for (int s = 0; s < kMaxStages; ++s) {
+            if (o.p1[s]) (void)hipEventDestroy(o.p1[s]);
+            if (o.p2[s]) (void)hipEventDestroy(o.p2[s]);
+            o.p1[s] = o.p2[s] = nullptr;
+        }
+        if (o.side) (void)hipStreamDestroy(o.side);
+        o.side = nullptr;
+    }
     if (cur != dev) (void)hipSetDevice(cur);
-    if (!ok) return nullptr;   // what was created stays allocated; the serial order is used
+    if (!ok) return nullptr;
     o.ready = true;
     return &o;
 }
@@ -1330,7 +1340,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
     const int nck = packed ? 0 : (args.T + C - 1) / C;
 
-    // the overlapped schedule for a dense batch, when it pays and the stream is not being captured
+    // the overlapped schedule for a dense batch, when it pays
     int bounds[kMaxStages + 1];
     int stages = 1;
     OverlapStreams* ov = nullptr;
@@ -1380,6 +1390,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     };
     hipError_t e = hipSuccess;
     auto ok = [&](hipError_t r) { if (e == hipSuccess && r != hipSuccess) e = r; return e == hipSuccess; };
+    int joined = -1;   // last stage whose pass-2 completion event is recorded
     prep(stage_args(0), recs, nullptr, ns, static_cast<unsigned>(args.B * bounds[1] * args.H), stream);
     ok(hipGetLastError());
     ok(hipEventRecord(ov->p1[0], stream));
@@ -1387,7 +1398,9 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
         if (!ok(hipStreamWaitEvent(ov->side, ov->p1[s], 0))) break;
         scan(stage_args(s), recs, ns, chains, ov->side);
         ok(hipGetLastError());
-        ok(hipEventRecord(ov->p2[s], ov->side));
+        const hipError_t rec = hipEventRecord(ov->p2[s], ov->side);
+        if (rec == hipSuccess) joined = s;
+        ok(rec);
         if (s + 1 < stages && e == hipSuccess) {
             // pass 1 of stage s+1 starts with pass 2 of stage s, behind a short gap
             if (s >= 1) ok(hipStreamWaitEvent(stream, ov->p2[s - 1], 0));
@@ -1398,8 +1411,13 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
             ok(hipEventRecord(ov->p1[s + 1], stream));
         }
     }
-    // join: later work on the caller's stream sees every stage
-    if (e == hipSuccess) ok(hipStreamWaitEvent(stream, ov->p2[stages - 1], 0));
+    // join: later work on the caller's stream sees every stage; after an
+    // error too, so that nothing on the second stream escapes the caller's
+    // stream order
+    if (joined >= 0) {
+        const hipError_t r = hipStreamWaitEvent(stream, ov->p2[joined], 0);
+        if (e == hipSuccess) e = r;
+    }
     return e;
 }
 
