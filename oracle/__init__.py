@@ -37,7 +37,11 @@ Contents
 
 Every function here is pinned by tests in tests/test_oracle_pins.py against
 identities the pages state and textbook linear algebra; see each test's
-docstring for the passage it follows.
+docstring for the passage it follows.  The one-token helpers (decode_steps,
+decode_gated, decode_conv) and the per-head channel layout of conv_qkv are
+pinned by the per-token hand-off of the affine maps ("Kimi K3 の KDA ..."
+sections 2.3.4.2 and 2.3.4.5) with several sequences and heads, against
+per-chain computations written out separately.
 """
 from __future__ import annotations
 

@@ -691,3 +691,128 @@ def test_conv_then_recurrence_first_token_closed_form():
     expect = 0.5 * float(beta[0]) * float(_unit(kc) @ _unit(qc)) * vc
     np.testing.assert_allclose(o[0, 0, 0], expect, rtol=1e-6, atol=1e-7)   # the conv output reaches fp32 once
     np.testing.assert_array_equal(fin[0][0], np.concatenate([np.zeros((2, d)), q[None, 0].astype(np.float64)]))
+
+
+# ---------------------------------------------------------------------------
+# Decode helpers: one token per call carries the state, so iterating them is
+# the whole-sequence run split at every token ("Kimi K3 の KDA ..." sections
+# 2.3.4.2 and 2.3.4.5: composing the per-segment affine maps in order gives
+# the map of the concatenation; a segment may be a single token).  Each pin
+# uses N >= 2 sequences and H >= 2 heads with distinct states and inputs, so
+# a reshape that mixes the sequence, head or token axes changes the result,
+# and each compares against a per-chain computation written out separately.
+# ---------------------------------------------------------------------------
+def _dec_inputs(rng, T, N, H, dk, dv):
+    q = rng.standard_normal((T, N, H, dk)).astype(np.float32)
+    k = rng.standard_normal((T, N, H, dk)).astype(np.float32)
+    v = rng.standard_normal((T, N, H, dv)).astype(np.float32)
+    g = rng.uniform(-5.0, 0.0, (T, N, H, dk)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (T, N, H)).astype(np.float32)
+    S0 = rng.standard_normal((N, H, dk, dv))
+    return q, k, v, g, beta, S0
+
+
+def test_decode_steps_iterated_is_the_sequence_run():
+    rng = np.random.default_rng(91)
+    T, N, H, dk, dv = 7, 3, 2, 4, 5
+    q, k, v, g, beta, S0 = _dec_inputs(rng, T, N, H, dk, dv)
+    st = S0.copy()
+    o_steps = np.empty((T, N, H, dv))
+    for t in range(T):
+        o_steps[t], st = oracle.decode_steps(st, q[t], k[t], v[t], g[t], beta[t], scale=0.75)
+    # the same tokens as N sequences of T tokens in one call
+    o_seq, s_seq = oracle.forward_arrays(q.transpose(1, 0, 2, 3), k.transpose(1, 0, 2, 3), v.transpose(1, 0, 2, 3),
+                                         g.transpose(1, 0, 2, 3), beta.transpose(1, 0, 2), S0, scale=0.75)
+    np.testing.assert_allclose(o_steps.transpose(1, 0, 2, 3), o_seq, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st, s_seq, rtol=1e-12, atol=1e-12)
+    # and chain by chain through the explicit transition products
+    for n in range(N):
+        for h in range(H):
+            o_ref, s_ref = oracle.product_form(q[:, n, h], k[:, n, h], v[:, n, h], g[:, n, h], beta[:, n, h],
+                                               S0[n, h], scale=0.75)
+            np.testing.assert_allclose(o_steps[:, n, h], o_ref, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(st[n, h], s_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_decode_gated_is_the_map_then_the_step():
+    rng = np.random.default_rng(92)
+    T, N, H, dk, dv = 4, 2, 3, 4, 3
+    q, k, v, _, _, S0 = _dec_inputs(rng, T, N, H, dk, dv)
+    z = rng.standard_normal((T, N, H, dk))
+    bl = rng.standard_normal((T, N, H))
+    A_log = np.array([-0.7, 0.2, 0.9])              # distinct per head
+    dt_bias = rng.standard_normal((H, dk))           # distinct per (head, channel)
+    st = S0.copy()
+    outs = []
+    for t in range(T):
+        o, st = oracle.decode_gated(st, q[t], k[t], v[t], z[t], A_log, dt_bias, bl[t])
+        outs.append(o)
+    # per chain, with the bounded map and the sigmoid evaluated element by
+    # element: g = -5 / (1 + exp(-e^A (z + bias))), beta = 1 / (1 + exp(-b))
+    for n in range(N):
+        for h in range(H):
+            gg = np.array([[-5.0 / (1.0 + np.exp(-np.exp(A_log[h]) * (z[t, n, h, c] + dt_bias[h, c])))
+                            for c in range(dk)] for t in range(T)])
+            bb = np.array([1.0 / (1.0 + np.exp(-bl[t, n, h])) for t in range(T)])
+            # the recurrence reads g and beta rounded once to fp32
+            o_ref, s_ref = oracle.product_form(q[:, n, h], k[:, n, h], v[:, n, h], gg.astype(np.float32),
+                                               bb.astype(np.float32), S0[n, h])
+            np.testing.assert_allclose(np.array([o[n, h] for o in outs]), o_ref, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(st[n, h], s_ref, rtol=1e-10, atol=1e-12)
+
+
+def _conv_by_hand(x, w, prev):
+    """Causal width-4 convolution + SiLU of one channel written as a loop:
+    y_t = silu(sum_j w[j] x_{t-3+j}), with x_{-3..-1} = prev."""
+    xs = list(prev) + list(x)
+    y = []
+    for t in range(len(x)):
+        a = sum(w[j] * xs[t + j] for j in range(4))
+        y.append(a / (1.0 + np.exp(-a)))
+    return np.array(y), np.array(xs[len(x):len(x) + 3])
+
+
+def test_decode_conv_iterated_is_the_sequence_convolution():
+    rng = np.random.default_rng(93)
+    T, N, H, dk, dv = 6, 3, 2, 3, 2
+    xs = [rng.standard_normal((T, N, H, d)) for d in (dk, dk, dv)]
+    ws = [rng.standard_normal((H * d, 4)) for d in (dk, dk, dv)]
+    caches = [rng.standard_normal((N, 3, H * d)) for d in (dk, dk, dv)]
+    st = [c.copy() for c in caches]
+    outs = []
+    for t in range(T):
+        y, st = oracle.decode_conv(st, ws, xs[0][t], xs[1][t], xs[2][t])
+        outs.append(y)
+    for i, d in enumerate((dk, dk, dv)):
+        # whole sequences through short_conv: [N, T, H*d], one state per sequence
+        seq = xs[i].transpose(1, 0, 2, 3).reshape(N, T, H * d)
+        for n in range(N):
+            y_seq, f_seq = oracle.short_conv(seq[n:n + 1], ws[i], caches[i][n:n + 1])
+            y_dec = np.stack([outs[t][i][n].reshape(H * d) for t in range(T)])
+            np.testing.assert_allclose(y_dec, y_seq[0], rtol=1e-13, atol=1e-13)
+            np.testing.assert_array_equal(st[i][n], f_seq[0])
+            for h in range(H):                         # channel h*d + c is (head h, channel c)
+                for c in range(d):
+                    yh, fh = _conv_by_hand(xs[i][:, n, h, c], ws[i][h * d + c], caches[i][n, :, h * d + c])
+                    np.testing.assert_allclose(y_dec[:, h * d + c], yh, rtol=1e-13, atol=1e-13)
+                    np.testing.assert_array_equal(st[i][n, :, h * d + c], fh)
+
+
+def test_conv_qkv_convolves_each_head_slice_with_its_taps():
+    rng = np.random.default_rng(94)
+    B, T, H, dk, dv = 2, 9, 3, 4, 2
+    xs = [rng.standard_normal((B, T, H, d)) for d in (dk, dk, dv)]
+    ws = [rng.standard_normal((H * d, 4)) for d in (dk, dk, dv)]
+    inits = [rng.standard_normal((B, 3, H * d)) for d in (dk, dk, dv)]
+    (yq, yk, yv), finals = oracle.conv_qkv(xs[0], xs[1], xs[2], ws, inits)
+    for i, (y, d) in enumerate(zip((yq, yk, yv), (dk, dk, dv))):
+        for h in range(H):
+            sl = slice(h * d, (h + 1) * d)
+            ys, fs = oracle.short_conv(xs[i][:, :, h], ws[i][sl], inits[i][:, :, sl])
+            np.testing.assert_array_equal(y[:, :, h], ys)
+            np.testing.assert_array_equal(finals[i][:, :, sl], fs)
+            for b in range(B):
+                for c in range(d):
+                    yh, fh = _conv_by_hand(xs[i][b, :, h, c], ws[i][h * d + c], inits[i][b, :, h * d + c])
+                    np.testing.assert_allclose(y[b, :, h, c], yh, rtol=1e-13, atol=1e-13)
+                    np.testing.assert_array_equal(finals[i][b, :, h * d + c], fh)
