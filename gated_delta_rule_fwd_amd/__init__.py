@@ -21,13 +21,22 @@ prefill calls take ``conv_init=`` / ``conv_final=`` (three [N, 3, H*d]
 tensors each, entries may be None), the decode calls ``conv_state=`` (updated
 in place).  Such calls go through kda_chunk_fwd_fused /
 kda_recurrent_step_fused.
+
+A long dense prefill overlaps its two kernels on the stream of a caller-owned
+``Context`` (kda_context_create / kda_context_destroy).  By default the
+prefill calls use one Context per host thread and device, made on first use
+outside a graph capture and released with the thread; ``context=None`` runs
+the kernels one after the other on the call's stream.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import threading
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_gated", "recurrent_step_gated", "workspace_bytes", "lib_path",
+           "Context", "default_context",
            "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS",
            "FLAG_SIGNED_ALPHA", "FLAG_OUT_NORM", "STATUS"]
 
@@ -54,7 +63,8 @@ class KDAError(RuntimeError):
 class ChunkDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("d_k", ctypes.c_int),
                 ("d_v", ctypes.c_int), ("num_seqs", ctypes.c_int), ("in_dtype", ctypes.c_int),
-                ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float), ("flags", ctypes.c_uint)]
+                ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float), ("flags", ctypes.c_uint),
+                ("context", ctypes.c_void_p)]
 
 
 class DecayGate(ctypes.Structure):
@@ -108,8 +118,80 @@ def load():
     lib.kda_last_hip_error.argtypes = []
     lib.kda_version.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
+    lib.kda_context_create.restype = I
+    lib.kda_context_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.kda_context_destroy.restype = I
+    lib.kda_context_destroy.argtypes = [P]
     _lib = lib
     return lib
+
+
+_exiting = False
+
+
+@atexit.register
+def _mark_exit():
+    global _exiting
+    _exiting = True
+
+
+class Context:
+    """A kda_context: the second HIP stream and the events with which a long
+    dense prefill overlaps its two kernels, on the device that is current
+    (or ``device``) when it is made.  Serves one call at a time; release it
+    with close() (or by dropping it)."""
+
+    def __init__(self, device=None):
+        torch = _torch()
+        lib = load()
+        h = ctypes.c_void_p()
+        with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+            self.device = torch.cuda.current_device()
+            _check(lib.kda_context_create(ctypes.byref(h)))
+        self._h = h.value
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("context is closed")
+        return self._h
+
+    def close(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h is not None and not _exiting:
+            _check(load().kda_context_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+_tls = threading.local()
+
+
+def default_context(device=None):
+    """This thread's Context for ``device`` (default: the current device),
+    made on first use; None while the current stream is capturing a graph and
+    none exists yet (no stream or event is made inside a capture)."""
+    torch = _torch()
+    if isinstance(device, torch.device):
+        device = device.index
+    dev = torch.cuda.current_device() if device is None else int(device)
+    ctxs = getattr(_tls, "contexts", None)
+    if ctxs is None:
+        ctxs = _tls.contexts = {}
+    c = ctxs.get(dev)
+    if c is None and not torch.cuda.is_current_stream_capturing():
+        c = ctxs[dev] = Context(dev)
+    return c
 
 
 def _check(status: int):
@@ -159,8 +241,9 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
-def _desc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, scale, flags) -> ChunkDesc:
-    return ChunkDesc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, float(scale), flags)
+def _desc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, scale, flags, context=None) -> ChunkDesc:
+    return ChunkDesc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, float(scale), flags,
+                     None if context is None else context.handle)
 
 
 def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True, scale=1.0, flags=FLAG_QK_L2NORM):
@@ -172,7 +255,8 @@ def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True,
 def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
               normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False,
               signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
-              conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None):
+              conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None,
+              context="default"):
     """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
     beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
     [N+1] device tensor or None (then N = B).  With signed_alpha (Complex KDA)
@@ -181,22 +265,26 @@ def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=N
     ([d_v] fp32 or None) and norm_eps.  conv_weights ([H*d,4] fp32 for q, k,
     v) fuses the short convolution: q, k, v are then the raw projections,
     conv_init / conv_final the [N,3,H*d] conv states read / written.
+    context: a Context, None (no overlap of the two kernels) or "default"
+    (this thread's Context for the device).  o, final_state and the
+    workspace, when not given, are allocated on ``stream``.
     Returns (o, final_state)."""
     return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
                   validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha,
-                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final))
+                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context)
 
 
 def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *, dt_bias=None, out_dtype=None,
                     scale=1.0, normalize=True, output_final_state=True, validate=False, fp32_path=False,
                     beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
-                    conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None):
+                    conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None,
+                    context="default"):
     """As chunk_fwd, with g = -5 sigmoid(exp(A_log[h]) (z + dt_bias[h, c]))
     computed in the kernel: z [B,T,H,d_k] in q's dtype, A_log [H] fp32,
     dt_bias [H,d_k] fp32 or None."""
     return _chunk(q, k, v, None, (z, A_log, dt_bias), beta, init_state, cu_seqlens, out_dtype, scale, normalize,
                   output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, stream, False,
-                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final))
+                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context)
 
 
 def _norm_args(norm, o_shape, in_dtype, dv):
@@ -236,9 +324,20 @@ def _conv_args(conv, N, H, dk, dv, dtype):
 
 def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
            validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False, norm=None,
-           conv=None):
+           conv=None, context="default"):
     torch = _torch()
     lib = load()
+    if stream is not None and stream != torch.cuda.current_stream(q.device):
+        # the buffers this call allocates belong to `stream`: the caching
+        # allocator then reuses them only behind that stream's work
+        with torch.cuda.stream(stream):
+            return _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize,
+                          output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, None,
+                          signed_alpha, norm, conv, context)
+    if isinstance(context, str):
+        if context != "default":
+            raise ValueError("context must be a Context, None or 'default'")
+        context = default_context(q.device)
     _need(q, "q")
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -272,8 +371,10 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_VALIDATE if validate else 0) | \
         (FLAG_FP32_PATH if fp32_path else 0) | (FLAG_BETA_LOGITS if beta_logits else 0) | \
         (FLAG_SIGNED_ALPHA if signed_alpha else 0) | (FLAG_OUT_NORM if on is not None else 0)
+    if context is not None and context.device != q.device.index:
+        raise ValueError("context belongs to device %d, tensors to %s" % (context.device, q.device))
     d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(out_dtype),
-              scale, flags)
+              scale, flags, context)
     ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
     if ws > 0 and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
@@ -324,6 +425,10 @@ def _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logit
           norm=None, conv=None):
     torch = _torch()
     lib = load()
+    if stream is not None and stream != torch.cuda.current_stream(q.device):
+        with torch.cuda.stream(stream):   # o, when allocated here, belongs to `stream`
+            return _step(q, k, v, g, gate, beta, state, out_dtype, scale, normalize, beta_logits, o, None,
+                         signed_alpha, norm, conv)
     _need(q, "q")
     N, H, dk = q.shape
     dv = v.shape[-1]

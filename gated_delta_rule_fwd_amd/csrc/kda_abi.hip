@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <new>
+
 #include "../../include/kda.h"
 #include "kda_kernels.h"
 
@@ -36,6 +38,50 @@ extern "C" {
 const char* kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
 
 int kda_last_hip_error(void) { return g_last_hip_error; }
+
+kda_status kda_context_create(kda_context* out)
+{
+    if (!out) return KDA_ERR_INVALID_ARG;
+    *out = nullptr;
+    kda_context_s* c = new (std::nothrow) kda_context_s{};
+    if (!c) return hip_fail(hipErrorOutOfMemory);
+    hipError_t e = hipGetDevice(&c->device);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking);   // default priority
+    for (int s = 0; e == hipSuccess && s < kda::kMaxStages; ++s) {
+        e = hipEventCreateWithFlags(&c->p1[s], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&c->p2[s], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) {
+        // give back what was made
+        for (int s = 0; s < kda::kMaxStages; ++s) {
+            if (c->p1[s]) (void)hipEventDestroy(c->p1[s]);
+            if (c->p2[s]) (void)hipEventDestroy(c->p2[s]);
+        }
+        if (c->side) (void)hipStreamDestroy(c->side);
+        delete c;
+        return hip_fail(e);
+    }
+    *out = c;
+    return KDA_OK;
+}
+
+kda_status kda_context_destroy(kda_context c)
+{
+    if (!c) return KDA_OK;
+    hipError_t first = hipSuccess;
+    auto keep = [&](hipError_t r) { if (first == hipSuccess) first = r; };
+    int cur = -1;
+    keep(hipGetDevice(&cur));
+    const bool switched = cur >= 0 && cur != c->device && hipSetDevice(c->device) == hipSuccess;
+    for (int s = 0; s < kda::kMaxStages; ++s) {
+        keep(hipEventDestroy(c->p1[s]));
+        keep(hipEventDestroy(c->p2[s]));
+    }
+    keep(hipStreamDestroy(c->side));
+    if (switched) keep(hipSetDevice(cur));
+    delete c;
+    return first == hipSuccess ? KDA_OK : hip_fail(first);
+}
 
 const char* kda_status_str(kda_status s)
 {
@@ -220,7 +266,7 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
         if (a.out_bf16) fw.o = static_cast<char*>(workspace) + off + recs;
     }
     if (uses_two_pass(d))
-        e = kda::launch_chunk_two_pass(fw, static_cast<char*>(workspace) + off, stream);
+        e = kda::launch_chunk_two_pass(fw, static_cast<char*>(workspace) + off, stream, d->context);
     else
         e = kda::launch_chunk_fp32(fw, stream);
     if (e == hipSuccess && norm) e = kda::launch_out_norm(a, static_cast<const float*>(fw.o), stream);

@@ -1245,49 +1245,22 @@ __global__ void stage_gap_kernel(int naps)
     for (int i = 0; i < naps; ++i) __builtin_amdgcn_s_sleep(127);
 }
 
-constexpr int kMaxDevices = 16;
-
-// Per calling thread and device: the second stream and the events of the
-// overlapped schedule, created on first use and kept until the process ends.
-struct OverlapStreams {
-    bool ready = false;
-    hipStream_t side = nullptr;
-    hipEvent_t p1[kMaxStages] = {};   // pass 1 of stage s done (recorded on the caller's stream)
-    hipEvent_t p2[kMaxStages] = {};   // pass 2 of stage s done (recorded on the side stream)
-};
-thread_local OverlapStreams t_overlap[kMaxDevices];
-
-OverlapStreams* existing_overlap_streams(int dev)
+// Whether the staged order may use the context's stream for a call on
+// `stream`: same device, and the context's stream is not part of a graph
+// capture other than the one `stream` belongs to (a stream that joined a
+// capture stays in it until the capture ends; work of an eager call, or of
+// another capture, must not land there).  Under capture the fork and the
+// join are recorded into the caller's graph.
+bool context_usable(kda_context_s* ctx, hipStream_t stream, int dev)
 {
-    return dev >= 0 && dev < kMaxDevices && t_overlap[dev].ready ? &t_overlap[dev] : nullptr;
-}
-
-OverlapStreams* overlap_streams(int dev)
-{
-    if (dev < 0 || dev >= kMaxDevices) return nullptr;
-    OverlapStreams& o = t_overlap[dev];
-    if (o.ready) return &o;
-    int cur = 0;
-    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
-    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
-    bool ok = hipStreamCreateWithFlags(&o.side, hipStreamNonBlocking) == hipSuccess;
-    for (int s = 0; ok && s < kMaxStages; ++s)
-        ok = hipEventCreateWithFlags(&o.p1[s], hipEventDisableTiming) == hipSuccess &&
-             hipEventCreateWithFlags(&o.p2[s], hipEventDisableTiming) == hipSuccess;
-    if (!ok) {
-        // give back what was created; the call takes the unstaged order
-        for (int s = 0; s < kMaxStages; ++s) {
-            if (o.p1[s]) (void)hipEventDestroy(o.p1[s]);
-            if (o.p2[s]) (void)hipEventDestroy(o.p2[s]);
-            o.p1[s] = o.p2[s] = nullptr;
-        }
-        if (o.side) (void)hipStreamDestroy(o.side);
-        o.side = nullptr;
-    }
-    if (cur != dev) (void)hipSetDevice(cur);
-    if (!ok) return nullptr;
-    o.ready = true;
-    return &o;
+    if (!ctx || ctx->device != dev) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone, ss = hipStreamCaptureStatusNone;
+    unsigned long long cid = 0, sid = 0;
+    if (hipStreamGetCaptureInfo(stream, &cs, &cid) != hipSuccess) return false;
+    if (hipStreamGetCaptureInfo(ctx->side, &ss, &sid) != hipSuccess) return false;
+    if (cs == hipStreamCaptureStatusInvalidated || ss == hipStreamCaptureStatusInvalidated) return false;
+    if (ss == hipStreamCaptureStatusNone) return true;
+    return cs == hipStreamCaptureStatusActive && cid == sid;
 }
 
 template <bool SIGNED, bool CONV>
@@ -1329,7 +1302,7 @@ void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, hi
 
 }  // namespace
 
-hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStream_t stream)
+hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStream_t stream, kda_context_s* ctx)
 {
     const bool packed = args.cu_seqlens != nullptr;
     const int chains = (packed ? args.num_seqs : args.B) * args.H;
@@ -1340,22 +1313,20 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
     const int nck = packed ? 0 : (args.T + C - 1) / C;
 
-    // the overlapped schedule for a dense batch, when it pays
+    // the overlapped schedule for a dense batch, when it pays and the
+    // caller's context can carry it
     int bounds[kMaxStages + 1];
     int stages = 1;
-    OverlapStreams* ov = nullptr;
-    if (!packed && stages_may_pay(nck, chains)) {
+    bool capturing = false;
+    if (!packed && ctx && stages_may_pay(nck, chains)) {
         int dev = 0, cus = 0;
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusInvalidated;
-        if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusInvalidated &&
-            hipStreamGetDevice(stream, &dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamGetDevice(stream, &dev) == hipSuccess && context_usable(ctx, stream, dev) &&
+            hipStreamIsCapturing(stream, &cap) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
             stages = plan_stages(nck, chains, cus, bounds);
-        // under graph capture only a second stream that already exists is used
-        // (the capture then records the fork and the join); streams and events
-        // are not created inside a capture
-        if (stages > 1) ov = cap == hipStreamCaptureStatusNone ? overlap_streams(dev) : existing_overlap_streams(dev);
-        if (!ov) stages = 1;
+            capturing = cap != hipStreamCaptureStatusNone;
+        }
     }
 
     ChunkArgs a = args;
@@ -1390,34 +1361,34 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     };
     hipError_t e = hipSuccess;
     auto ok = [&](hipError_t r) { if (e == hipSuccess && r != hipSuccess) e = r; return e == hipSuccess; };
-    int joined = -1;   // last stage whose pass-2 completion event is recorded
+    int launched = -1;   // last stage whose pass 2 is enqueued on the context's stream
+    int recorded = -1;   // last stage whose pass-2 completion event is recorded behind it
     prep(stage_args(0), recs, nullptr, ns, static_cast<unsigned>(args.B * bounds[1] * args.H), stream);
     ok(hipGetLastError());
-    ok(hipEventRecord(ov->p1[0], stream));
+    ok(hipEventRecord(ctx->p1[0], stream));
     for (int s = 0; s < stages && e == hipSuccess; ++s) {
-        if (!ok(hipStreamWaitEvent(ov->side, ov->p1[s], 0))) break;
-        scan(stage_args(s), recs, ns, chains, ov->side);
-        ok(hipGetLastError());
-        const hipError_t rec = hipEventRecord(ov->p2[s], ov->side);
-        if (rec == hipSuccess) joined = s;
-        ok(rec);
+        if (!ok(hipStreamWaitEvent(ctx->side, ctx->p1[s], 0))) break;
+        scan(stage_args(s), recs, ns, chains, ctx->side);
+        const hipError_t lr = hipGetLastError();
+        if (lr == hipSuccess) launched = s;
+        if (!ok(lr)) break;
+        if (ok(hipEventRecord(ctx->p2[s], ctx->side))) recorded = s;
         if (s + 1 < stages && e == hipSuccess) {
             // pass 1 of stage s+1 starts with pass 2 of stage s, behind a short gap
-            if (s >= 1) ok(hipStreamWaitEvent(stream, ov->p2[s - 1], 0));
+            if (s >= 1) ok(hipStreamWaitEvent(stream, ctx->p2[s - 1], 0));
             stage_gap_kernel<<<1, 64, 0, stream>>>(6);
             const ChunkArgs b = stage_args(s + 1);
             prep(b, recs, nullptr, ns, static_cast<unsigned>(args.B * b.chunk_cnt * args.H), stream);
             ok(hipGetLastError());
-            ok(hipEventRecord(ov->p1[s + 1], stream));
+            ok(hipEventRecord(ctx->p1[s + 1], stream));
         }
     }
-    // join: later work on the caller's stream sees every stage; after an
+    // join: later work on the caller's stream sees every stage, after an
     // error too, so that nothing on the second stream escapes the caller's
     // stream order
-    if (joined >= 0) {
-        const hipError_t r = hipStreamWaitEvent(stream, ov->p2[joined], 0);
-        if (e == hipSuccess) e = r;
-    }
+    const StageJoin jn = plan_join(launched, recorded, capturing);
+    if (jn.wait_stage >= 0) ok(hipStreamWaitEvent(stream, ctx->p2[jn.wait_stage], 0));
+    if (jn.sync_side) ok(hipStreamSynchronize(ctx->side));
     return e;
 }
 

@@ -4,6 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_stage_plan.h"
+
+// The objects behind a kda_context (include/kda.h): made by
+// kda_context_create, released by kda_context_destroy, owned by the caller.
+struct kda_context_s {
+    int device;                          // device the stream and events belong to
+    hipStream_t side;                    // second stream of the staged prefill (default priority)
+    hipEvent_t p1[kda::kMaxStages];      // chunk-parallel kernel of stage s done (calling stream)
+    hipEvent_t p2[kda::kMaxStages];      // sequential kernel of stage s done (second stream)
+};
+
 namespace kda {
 
 // Problem description shared by the chunkwise launchers.
@@ -101,13 +112,14 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed);
 // sequence or -1 (packed sequences) or the fp32 state of every chain
 // [B*H, 128, 128] carried between the overlapped launches (dense batch).
 size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed);
-// A dense batch whose sequential pass leaves CUs idle runs in stages: pass 1
-// of stage s+1 on the idle CUs while pass 2 of stage s runs, pass 2 on a
-// second stream of the calling thread, joined to `stream` before returning.
-// Otherwise (packed sequences, short chains, many chains, or a stream under
-// graph capture) pass 1 then pass 2 on `stream`.  Both orders give the same
+// With a context (nullable), a dense batch whose sequential pass leaves CUs
+// idle runs in stages: pass 1 of stage s+1 on the idle CUs while pass 2 of
+// stage s runs, pass 2 on the context's stream, joined to `stream` before
+// returning.  Otherwise (no context, a context of another device or one whose
+// stream belongs to another graph capture, packed sequences, short chains,
+// many chains) pass 1 then pass 2 on `stream`.  Both orders give the same
 // bits.
-hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream);
+hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream, kda_context_s* ctx);
 
 // Conv states after a prefill: the last 3 raw inputs of every sequence for
 // q, k, v (rows from a.conv_init where a sequence is shorter than 3); each

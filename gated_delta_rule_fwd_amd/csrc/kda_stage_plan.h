@@ -52,4 +52,28 @@ inline int plan_stages(int nck, int chains, int cus, int* bounds)
     return n;
 }
 
+// Joining the second stream back to the calling stream at the end of a
+// staged call.  `launched` is the last stage whose sequential kernel was
+// enqueued on the second stream (-1: none), `recorded` the last stage whose
+// completion event was recorded right behind it (recorded <= launched).
+// When every launched stage has its event, the calling stream waits on the
+// last one.  When the event after the last launched stage could not be
+// recorded, no event covers that stage: the calling stream still waits on
+// the last recorded one, and the second stream is drained on the host
+// (outside a graph capture; inside one the capture fails with the error
+// anyway), so no kernel of the call outlives it unordered.
+struct StageJoin {
+    int wait_stage;    // stage whose event the calling stream waits on, -1: none
+    bool sync_side;    // synchronise the second stream on the host
+};
+
+inline StageJoin plan_join(int launched, int recorded, bool capturing)
+{
+    StageJoin j{-1, false};
+    if (launched < 0) return j;
+    j.wait_stage = recorded;
+    if (recorded < launched && !capturing) j.sync_side = true;
+    return j;
+}
+
 }  // namespace kda

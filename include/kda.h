@@ -24,22 +24,22 @@
  *   - All tensor pointers are DEVICE pointers, row-major and contiguous in
  *     the layouts given below; beta and cu_seqlens must be 4-byte aligned,
  *     every other tensor 16-byte aligned.  The caller owns every buffer;
- *     the library allocates no device memory.  Between calls it keeps each
- *     calling thread's last HIP error code (kda_last_hip_error) and, per
- *     calling thread and device, one HIP stream and twelve events (created
- *     on first use, kept until the process ends) with which a long dense
- *     prefill overlaps its two kernels (kda_chunk_fwd below).  Entry points
- *     are thread-safe.
+ *     the library allocates no device memory.  HIP streams and events are
+ *     created only by kda_context_create (and released by
+ *     kda_context_destroy); the caller owns the context and passes it in
+ *     the prefill descriptor.  The only state the library keeps between
+ *     calls is each calling thread's last HIP error code
+ *     (kda_last_hip_error).  Entry points are thread-safe; one context
+ *     serves one call at a time (use one per thread).
  *   - Work is enqueued on `stream` and runs asynchronously; there is no host
- *     synchronisation except under KDA_FLAG_VALIDATE.  Work a call puts on
- *     its second stream is joined back to `stream` (an event wait) before
- *     the call returns, so later work on `stream` sees every output.
- *     Without KDA_FLAG_VALIDATE a call only launches kernels and records or
- *     waits on events (no memset, copy or allocation), so it may be captured
- *     into a HIP graph and replayed.  Under capture the prefill uses its
- *     second stream only if the calling thread has created it already (by an
- *     earlier staged call); the graph then records the fork and the join.
- *     Otherwise the captured work takes the unstaged order.
+ *     synchronisation except under KDA_FLAG_VALIDATE (and after a failed
+ *     event record, see kda_chunk_fwd).  Work a call puts on the context's
+ *     stream is joined back to `stream` (an event wait) before the call
+ *     returns, so later work on `stream` sees every output.  Without
+ *     KDA_FLAG_VALIDATE a call only launches kernels and records or waits
+ *     on events (no memset, copy or allocation), so it may be captured into
+ *     a HIP graph and replayed; a staged prefill's fork to the context's
+ *     stream and its join are then recorded into the graph.
  *   - Every argument is checked on the host before anything is launched, so a
  *     call that returns an error other than KDA_ERR_HIP / KDA_ERR_RANGE has had
  *     no side effect.
@@ -115,6 +115,24 @@ typedef enum kda_dtype {
  * first (a matrix-core prefill needs about 2.7 KB per token-head with its
  * workspace). */
 
+/*
+ * Caller-owned objects with which a long dense prefill overlaps its two
+ * kernels: one HIP stream (non-blocking, default priority) and twelve events
+ * (timing disabled) on the device that was current when it was created.
+ * Nothing else in the library creates a stream or an event.
+ */
+typedef struct kda_context_s* kda_context;
+
+/* Creates a context on the calling thread's current device.  Returns
+ * KDA_ERR_INVALID_ARG for a null `ctx`, KDA_ERR_HIP when the runtime fails
+ * (then nothing is left allocated and *ctx is NULL). */
+KDA_API kda_status kda_context_create(kda_context* ctx);
+
+/* Releases a context (NULL is a no-op).  No call that uses it may still be
+ * running on the host; work it enqueued may still be pending on the device
+ * (HIP releases the stream and events once it completes). */
+KDA_API kda_status kda_context_destroy(kda_context ctx);
+
 typedef struct kda_chunk_desc {
     int B;              /* batch (must be 1 when cu_seqlens is given) */
     int T;              /* tokens per batch row, or total packed tokens when varlen */
@@ -126,6 +144,9 @@ typedef struct kda_chunk_desc {
     kda_dtype out_dtype; /* dtype of o */
     float scale;        /* output scale (1.0 = the pages' form) */
     unsigned flags;     /* KDA_FLAG_* */
+    kda_context context; /* nullable: a context lets a long dense prefill overlap its
+                            two kernels on the context's stream (kda_chunk_fwd); NULL
+                            runs them one after the other on `stream` */
 } kda_chunk_desc;
 
 /* Bytes of device workspace the chunkwise entry points need for this
@@ -147,11 +168,16 @@ KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
  * partial; a zero-length sequence passes its initial state through unchanged.
  *
  * The matrix-core path runs a chunk-parallel kernel and then a sequential
- * one.  For a dense batch of at least 256 chunks per sequence whose
- * sequential kernel leaves CUs idle, the chunks are split into up to six
- * stages and the chunk-parallel kernel of stage s+1 runs on the idle CUs
- * while the sequential kernel of stage s runs on a second stream; the
- * outputs are bit-identical to the unstaged order.
+ * one.  When desc->context is given and usable (created on the device of
+ * `stream`, its stream not part of a graph capture other than the one
+ * `stream` belongs to), a dense batch of at least 256 chunks per sequence
+ * whose sequential kernel leaves CUs idle is split into up to six stages:
+ * the chunk-parallel kernel of stage s+1 runs on the idle CUs while the
+ * sequential kernel of stage s runs on the context's stream.  The outputs
+ * are bit-identical to the unstaged order.  If an event cannot be recorded
+ * after a stage was enqueued on the context's stream, that stream is
+ * synchronised on the host before the error returns (outside a capture), so
+ * no kernel of the call outlives it unordered.
  *
  *   q, k        [B, T, H, d_k]  in_dtype
  *   v           [B, T, H, d_v]  in_dtype

@@ -30,7 +30,8 @@ def lib():
 def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
                                   "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step", "kda_recurrent_step_gated",
-                                  "kda_recurrent_step_fused", "kda_status_str", "kda_last_hip_error", "kda_version"])
+                                  "kda_recurrent_step_fused", "kda_status_str", "kda_last_hip_error", "kda_version",
+                                  "kda_context_create", "kda_context_destroy"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -48,6 +49,44 @@ def test_status_strings(lib):
     assert b"ok" == lib.kda_status_str(0)
     assert lib.kda_version().startswith(b"kda-mi355x")
     assert lib.kda_last_hip_error() == 0
+
+
+def test_context_arguments(lib):
+    assert lib.kda_context_create(None) == 1                   # nowhere to put the handle
+    assert lib.kda_context_destroy(None) == 0                  # releasing nothing is a no-op
+
+
+LAYOUT_DRIVER = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "kda.h"
+int main(void)
+{
+    printf("%zu %zu %zu %zu %zu\n", sizeof(kda_chunk_desc), offsetof(kda_chunk_desc, scale),
+           offsetof(kda_chunk_desc, flags), offsetof(kda_chunk_desc, context), sizeof(kda_out_norm));
+    return 0;
+}
+"""
+
+
+def test_descriptor_layout_matches_the_header(tmp_path):
+    """The binding's ctypes structures have the C layout of include/kda.h
+    (compiled here with the host C compiler)."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("no host C compiler or HIP headers")
+    src, exe = tmp_path / "layout.c", tmp_path / "layout"
+    src.write_text(LAYOUT_DRIVER)
+    subprocess.run([cc, "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROOT, "include"),
+                    "-I/opt/rocm/include", str(src), "-o", str(exe)], check=True, capture_output=True)
+    size, off_scale, off_flags, off_ctx, norm_size = map(int, subprocess.run([str(exe)], capture_output=True,
+                                                                             text=True, check=True).stdout.split())
+    assert size == ctypes.sizeof(kda.ChunkDesc)
+    assert off_scale == kda.ChunkDesc.scale.offset
+    assert off_flags == kda.ChunkDesc.flags.offset
+    assert off_ctx == kda.ChunkDesc.context.offset
+    assert norm_size == ctypes.sizeof(kda.OutNorm)
 
 
 def _desc(**kw):

@@ -65,15 +65,22 @@ def test_mid_bf16_fp32_path(kda):
 
 
 def test_long_bf16_sampled_heads(kda):
-    """Full-size launch (B=1, H=96, T=65536), oracle on three sampled heads."""
+    """Full-size launch (B=1, H=96, T=65536), oracle on three sampled heads;
+    bf16 o (graded with the half-ulp allowance) and fp32 o from the same
+    kernel (only the store differs) at the literal 2e-2 RMS(o) bound."""
     import torch
     inp = kda_inputs.workload("long_bf16")
-    o, s = _run(kda, inp, out_dtype=torch.bfloat16)
-    for h in (0, 47, 95):
-        heads = slice(h, h + 1)
-        o_ref, s_ref = oracle.forward(inp, heads)
-        check("long_bf16/h%d" % h, host64(o[:, :, heads]), o_ref, host64(s[:, heads]), s_ref, TOL_BF16,
-              bf16_store=True)
+    heads = (0, 47, 95)
+    refs = {h: oracle.forward(inp, slice(h, h + 1)) for h in heads}
+    for odt, bf16_store in ((torch.bfloat16, True), (torch.float32, False)):
+        o, s = _run(kda, inp, out_dtype=odt)
+        for h in heads:
+            hs = slice(h, h + 1)
+            o_ref, s_ref = refs[h]
+            check("long_bf16/%s/h%d" % (str(odt).split(".")[-1], h), host64(o[:, :, hs]), o_ref, host64(s[:, hs]),
+                  s_ref, TOL_BF16, bf16_store=bf16_store)
+        del o, s
+        torch.cuda.empty_cache()
 
 
 def test_varlen_bf16_sampled_heads(kda):
@@ -82,27 +89,31 @@ def test_varlen_bf16_sampled_heads(kda):
     _parity(kda, inp, "varlen_bf16", TOL_BF16, heads=slice(5, 8))
 
 
-def test_decode_128_steps(kda):
-    """N=256, H=96, d=128, 128 in-place steps; every step's o and the final
-    states checked on the first 6 sequences (all heads)."""
+@pytest.mark.parametrize("out_bf16", [True, False], ids=["o_bf16", "o_fp32"])
+def test_decode_128_steps(kda, out_bf16):
+    """N=256, H=96, d=128, 128 in-place steps: o at every step and the final
+    states, on sequences spread over the batch (0, 1, 127, 255; all heads).
+    bf16 o is graded with the half-ulp allowance; fp32 o (same kernel, only
+    the store differs) at the literal 2e-2 RMS(o) bound."""
     import torch
     w = kda_inputs.DECODE_WORKLOAD
     N, H, d, steps, seed = w["N"], w["H"], w["d"], w["steps"], w["seed"]
     S0 = kda_inputs.decode_initial_state(seed, N, H, d, w["s0_std"])
     state = dev(S0)
-    ns = 6
-    s_ref = S0[:ns].astype(np.float64)
-    worst = 0.0
+    sel = [0, 1, 127, 255]
+    idx = torch.tensor(sel, device="cuda")
+    s_ref = S0[sel].astype(np.float64)
+    odt = torch.bfloat16 if out_bf16 else torch.float32
+    name = "decode/%s" % ("o_bf16" if out_bf16 else "o_fp32")
     for step in range(steps):
         x = kda_inputs.decode_step(seed, step, N, H, d)
-        o = kda.recurrent_step(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), state)
-        o_ref, s_ref = oracle.decode_steps(s_ref, kda_inputs.bf16_to_f32(x.q[:ns]), kda_inputs.bf16_to_f32(x.k[:ns]),
-                                           kda_inputs.bf16_to_f32(x.v[:ns]), x.g[:ns], x.beta[:ns])
-        if step % 16 == 0 or step == steps - 1:
-            rec = check("decode/step%d" % step, host64(o[:ns]), o_ref, None, None, TOL_BF16, bf16_store=True)
-            worst = max(worst, rec["o_err"])
+        o = kda.recurrent_step(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), state, out_dtype=odt)
+        o_ref, s_ref = oracle.decode_steps(s_ref, kda_inputs.bf16_to_f32(x.q[sel]), kda_inputs.bf16_to_f32(x.k[sel]),
+                                           kda_inputs.bf16_to_f32(x.v[sel]), x.g[sel], x.beta[sel])
+        check("%s/step%d" % (name, step), host64(o.index_select(0, idx)), o_ref, None, None, TOL_BF16,
+              bf16_store=out_bf16)
     torch.cuda.synchronize()
-    check_state("decode/final_state", host64(state[:ns]), s_ref, TOL_BF16)
+    check_state("%s/final_state" % name, host64(state.index_select(0, idx)), s_ref, TOL_BF16)
 
 
 # ---------------------------------------------------------------------------

@@ -106,11 +106,12 @@ def test_staged_against_oracle(kda):
 
 
 def test_staged_call_in_a_graph_and_on_two_threads(kda):
-    """Captured and replayed (staged inside the graph: the calling thread's
-    second stream exists from the eager calls, so the capture records the fork
-    and the join), captured on a fresh thread (no second stream yet: the graph
-    holds the unstaged order), and run from two host threads on streams of
-    their own: all equal the eager staged call bit for bit."""
+    """Captured and replayed (staged inside the graph: the thread's default
+    context exists from the eager calls, so the capture records the fork and
+    the join), captured on a fresh thread (no context yet, and none is made
+    inside a capture: the graph holds the unstaged order), and run from two
+    host threads on streams and contexts of their own: all equal the eager
+    staged call bit for bit."""
     import torch
     B, T, H = 1, 16384, 32
     inps = [kda_inputs.make_prefill(86 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
@@ -206,3 +207,53 @@ def test_random_staged_against_oracle(kda, i):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.forward(inp)
     check("random_staged%d" % i, host64(o), o_ref, host64(s), s_ref, 2e-2, bf16_store=True)
+
+
+def test_context_ownership(kda):
+    """The staged order needs a caller-owned context: an explicit Context and
+    context=None (one kernel after the other on the call's stream) give the
+    same bits; while the context's stream is part of an open graph capture,
+    an eager call on another stream with the same context takes the unstaged
+    order on its own stream (nothing of it enters the graph), and both the
+    eager result and every replay of the graph equal the reference."""
+    import torch
+    B, T, H = 1, 16384, 32
+    inps = [kda_inputs.make_prefill(88 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
+    devs = [[dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(x.init_state)] for x in inps]
+    ws = kda.workspace_bytes(B, T, H, 128, 128)
+    bufs = [dict(o=torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda"),
+                 s=torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda"),
+                 ws=torch.empty(ws, dtype=torch.uint8, device="cuda")) for _ in range(2)]
+    with kda.Context() as ctx:
+        refs = []
+        for i in range(2):
+            kda.chunk_fwd(*devs[i], o=bufs[i]["o"], final_state=bufs[i]["s"], workspace=bufs[i]["ws"], context=None)
+            torch.cuda.synchronize()
+            refs.append((bufs[i]["o"].clone(), bufs[i]["s"].clone()))
+            bufs[i]["o"].zero_()
+            kda.chunk_fwd(*devs[i], o=bufs[i]["o"], final_state=bufs[i]["s"], workspace=bufs[i]["ws"], context=ctx)
+            torch.cuda.synchronize()
+            assert torch.equal(bufs[i]["o"], refs[i][0]) and torch.equal(bufs[i]["s"], refs[i][1]), "explicit %d" % i
+        for b in bufs:
+            b["o"].zero_()
+            b["s"].zero_()
+        torch.cuda.synchronize()
+        other = torch.cuda.Stream()   # default priority
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+            kda.chunk_fwd(*devs[0], o=bufs[0]["o"], final_state=bufs[0]["s"], workspace=bufs[0]["ws"], context=ctx)
+            with torch.cuda.stream(other):
+                kda.chunk_fwd(*devs[1], o=bufs[1]["o"], final_state=bufs[1]["s"], workspace=bufs[1]["ws"],
+                              context=ctx)
+        other.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs[1]["o"], refs[1][0]) and torch.equal(bufs[1]["s"], refs[1][1]), "eager beside capture"
+        assert not bufs[0]["o"].any(), "captured work ran eagerly"
+        for rep in range(2):
+            bufs[1]["o"].zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(bufs[0]["o"], refs[0][0]) and torch.equal(bufs[0]["s"], refs[0][1]), "replay %d" % rep
+            assert not bufs[1]["o"].any(), "the eager call entered the graph"
+        del graph

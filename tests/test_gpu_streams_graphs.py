@@ -73,6 +73,38 @@ def test_side_stream_matches_default_stream(kda):
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+def test_stream_argument_without_a_stream_context(kda):
+    """stream= names a side stream while the current stream stays the
+    default one: the buffers the call allocates (o, the final state and the
+    record workspace) belong to the side stream, and the results equal the
+    default-stream ones bit for bit (a staged prefill and a decode step)."""
+    import torch
+    inp = kda_inputs.make_prefill(75, 1, 16384, 32, 128, 128, s0_std=0.02)
+    d = inputs_to_device(inp)
+    args = [d[k] for k in ("q", "k", "v", "g", "beta", "init_state")]
+    o1, s1 = kda.chunk_fwd(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):   # freed buffers of one call are reused by the next only behind the side stream
+        o2, s2 = kda.chunk_fwd(*args, stream=side)
+    side.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+    N, H, D = 4, 3, 128
+    S0 = dev(kda_inputs.decode_initial_state(76, N, H, D))
+    x = kda_inputs.decode_step(76, 0, N, H, D)
+    xa = [dev(a) for a in (x.q, x.k, x.v, x.g, x.beta)]
+    st1 = S0.clone()
+    o1 = kda.recurrent_step(*xa, st1)
+    torch.cuda.synchronize()
+    st2 = S0.clone()
+    side.wait_stream(torch.cuda.current_stream())
+    o2 = kda.recurrent_step(*xa, st2, stream=side)
+    side.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+
+
 def test_decode_steps_in_a_graph(kda):
     """Eight decode steps captured once, replayed three times from a reset
     state with eager work in between; every replay equals the eager run."""

@@ -86,3 +86,44 @@ def test_stage_sizes_follow_the_cost_ratio(plan):
     assert all(a >= b for a, b in zip(s, s[1:-1])), s
     assert all(a <= b for a, b in zip(g, g[1:])), g
     assert s[0] > 512 and g[0] == 16
+
+
+JOIN_DRIVER = r"""
+#include "kda_stage_plan.h"
+#include <cstdio>
+int main()
+{
+    int launched, recorded, capturing;
+    while (std::scanf("%d %d %d", &launched, &recorded, &capturing) == 3) {
+        const kda::StageJoin j = kda::plan_join(launched, recorded, capturing != 0);
+        std::printf("%d %d\n", j.wait_stage, j.sync_side ? 1 : 0);
+    }
+    return 0;
+}
+"""
+
+
+def test_join_after_failures(tmp_path):
+    """The join at the end of a staged call: the calling stream waits on the
+    last recorded pass-2 event; when a stage was enqueued on the second stream
+    but its event failed to record, the second stream is drained on the host
+    (outside a capture) so nothing of the call outlives it unordered."""
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if not cxx:
+        pytest.skip("no host C++ compiler")
+    src, exe = tmp_path / "join.cpp", tmp_path / "join"
+    src.write_text(JOIN_DRIVER)
+    subprocess.run([cxx, "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
+    cases = [
+        (-1, -1, 0, (-1, 0)),   # nothing reached the second stream
+        (-1, -1, 1, (-1, 0)),
+        (3, 3, 0, (3, 0)),      # every stage recorded: wait on the last
+        (3, 3, 1, (3, 0)),
+        (0, -1, 0, (-1, 1)),    # stage 0 enqueued, its event failed: drain
+        (2, 1, 0, (1, 1)),      # stage 2's event failed: wait on stage 1 and drain
+        (2, 1, 1, (1, 0)),      # under capture: no host synchronisation
+    ]
+    text = "".join("%d %d %d\n" % c[:3] for c in cases)
+    out = subprocess.run([str(exe)], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
+    for c, line in zip(cases, out):
+        assert tuple(int(x) for x in line.split()) == c[3], (c, line)
