@@ -36,7 +36,7 @@ import os
 import threading
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_gated", "recurrent_step_gated", "workspace_bytes", "lib_path",
-           "Context", "default_context",
+           "Context", "default_context", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS",
            "FLAG_SIGNED_ALPHA", "FLAG_OUT_NORM", "STATUS"]
 
@@ -51,7 +51,8 @@ FLAG_SIGNED_ALPHA = 0x10
 FLAG_OUT_NORM = 0x20
 KDA_F32, KDA_BF16 = 0, 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
-          4: "KDA_ERR_RANGE", 5: "KDA_ERR_HIP"}
+          4: "KDA_ERR_RANGE", 5: "KDA_ERR_HIP", 6: "KDA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KDAError(RuntimeError):
@@ -118,6 +119,8 @@ def load():
     lib.kda_last_hip_error.argtypes = []
     lib.kda_version.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
+    lib.kda_chunk_fwd_noalloc.restype = I
+    lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 9 + [P]
     lib.kda_context_create.restype = I
     lib.kda_context_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     lib.kda_context_destroy.restype = I
@@ -272,6 +275,45 @@ def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=N
     return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
                   validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha,
                   (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context)
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, o, final_state=None, scale=1.0,
+                      normalize=True, fp32_path=False, beta_logits=False, signed_alpha=False, stream=None,
+                      context=None):
+    """kda_chunk_fwd_noalloc: chunk_fwd for callers that cannot allocate.
+    Nothing is allocated here or in the library: the caller passes o (and
+    final_state, if wanted); the kernels' scratch is the library's fixed
+    per-device area of NOALLOC_SCRATCH_BYTES (KDAError KDA_ERR_SCRATCH when a
+    call needs more).  Calls that overlap on one GPU race on that area.
+    Returns (o, final_state)."""
+    torch = _torch()
+    lib = load()
+    _need(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(k, "k", q.dtype, q.shape)
+    _need(v, "v", q.dtype, (B, T, H, dv))
+    _need(g, "g", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    if init_state is not None:
+        _need(init_state, "init_state", torch.float32, (N, H, dk, dv))
+    _need(o, "o", None, (B, T, H, dv))
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    if context is not None and context.device != q.device.index:
+        raise ValueError("context belongs to device %d, tensors to %s" % (context.device, q.device))
+    flags = (FLAG_QK_L2NORM if normalize else 0) | (FLAG_FP32_PATH if fp32_path else 0) | \
+        (FLAG_BETA_LOGITS if beta_logits else 0) | (FLAG_SIGNED_ALPHA if signed_alpha else 0)
+    d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(o.dtype),
+              scale, flags, context)
+    _check(lib.kda_chunk_fwd_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(init_state), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
+                                     _stream(stream)))
+    return o, final_state
 
 
 def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *, dt_bias=None, out_dtype=None,

@@ -3,14 +3,49 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <new>
 
 #include "../../include/kda.h"
 #include "kda_kernels.h"
 
+// Device scratch of kda_chunk_fwd_noalloc: one copy per GPU, held until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is a stand-in, not a device address): it uses the address that
+// hipGetSymbolAddress returns for the device, kept in g_scratch below.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Per device: the address of `scratch` there, looked up once with that
+// device current (or the error of the lookup).
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch[kMaxScratchDevices];
+hipError_t g_scratch_err[kMaxScratchDevices];
+
+hipError_t scratch_on(int dev, void** out)
+{
+    *out = nullptr;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void* p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur >= 0 && cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        g_scratch[dev] = e == hipSuccess ? p : nullptr;
+        g_scratch_err[dev] = e;
+    });
+    *out = g_scratch[dev];
+    return g_scratch_err[dev];
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -92,6 +127,7 @@ const char* kda_status_str(kda_status s)
     case KDA_ERR_WORKSPACE: return "workspace too small";
     case KDA_ERR_RANGE: return "input out of range (g outside [-5,0], beta outside [0,1] or bad cu_seqlens)";
     case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_SCRATCH: return "call needs more device scratch than the fixed no-allocation area";
     }
     return "unknown status";
 }
@@ -349,6 +385,23 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
 {
     return chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, nullptr, nullptr, o, final_state,
                           workspace, ws_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* init_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state, hipStream_t stream)
+{
+    if (!d) return KDA_ERR_INVALID_ARG;
+    if (d->flags & KDA_FLAG_VALIDATE) return KDA_ERR_UNSUPPORTED;
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e);
+    void* ws = nullptr;
+    e = scratch_on(dev, &ws);
+    if (e != hipSuccess) return hip_fail(e);
+    const kda_status st = chunk_fwd_impl(d, q, k, v, g, nullptr, beta, init_state, cu_seqlens, nullptr, nullptr, o,
+                                         final_state, ws, KDA_NOALLOC_SCRATCH_BYTES, stream);
+    return st == KDA_ERR_WORKSPACE ? KDA_ERR_SCRATCH : st;
 }
 
 kda_status kda_chunk_fwd_gated(const kda_chunk_desc* d, const void* q, const void* k, const void* v, const void* z,

@@ -67,7 +67,9 @@ typedef enum kda_status {
     KDA_ERR_WORKSPACE = 3,    /* workspace smaller than kda_chunk_fwd_workspace_bytes() */
     KDA_ERR_RANGE = 4,        /* only with KDA_FLAG_VALIDATE: g outside [-5, 0], beta outside
                                  [0, 1], or cu_seqlens not a monotone partition of [0, T] */
-    KDA_ERR_HIP = 5           /* a HIP launch/runtime error; see kda_last_hip_error() */
+    KDA_ERR_HIP = 5,          /* a HIP launch/runtime error; see kda_last_hip_error() */
+    KDA_ERR_SCRATCH = 6       /* kda_chunk_fwd_noalloc only: the call needs more device scratch
+                                 than its fixed area of KDA_NOALLOC_SCRATCH_BYTES */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -360,6 +362,30 @@ KDA_API kda_status kda_recurrent_step_fused(int N, int H, int d_k, int d_v,
                               const float* beta, const kda_short_conv* conv,
                               const kda_out_norm* norm,
                               float* state, void* o, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, layouts, flags and errors are those of kda_chunk_fwd, without
+ * the workspace: the scratch the kernels need (kda_chunk_fwd_workspace_bytes
+ * of the descriptor) lives in a fixed device array of KDA_NOALLOC_SCRATCH_BYTES
+ * that the library defines; each GPU it runs on holds one copy until the
+ * process ends.  Its address is looked up once per device, on the first call
+ * that runs there.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); a call that needs more scratch than the array holds
+ * returns KDA_ERR_SCRATCH before any launch, and KDA_FLAG_VALIDATE (which
+ * reads its counters back to the host) is KDA_ERR_UNSUPPORTED.  Every call
+ * on one GPU uses that GPU's array and leaves its contents behind: calls
+ * that overlap on one GPU (on different streams, or from different threads,
+ * without ordering between them) race on it and give undefined results.
+ * Nothing in the array needs to start at zero.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+KDA_API kda_status kda_chunk_fwd_noalloc(const kda_chunk_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* init_state, const int32_t* cu_seqlens,
+                         void* o, float* final_state, hipStream_t stream);
 
 /* Static description of a status code. */
 KDA_API const char* kda_status_str(kda_status status);

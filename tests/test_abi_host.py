@@ -31,7 +31,7 @@ def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
                                   "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step", "kda_recurrent_step_gated",
                                   "kda_recurrent_step_fused", "kda_status_str", "kda_last_hip_error", "kda_version",
-                                  "kda_context_create", "kda_context_destroy"])
+                                  "kda_context_create", "kda_context_destroy", "kda_chunk_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -44,11 +44,20 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
-        assert lib.kda_status_str(code)
+    for code in range(7):
+        assert lib.kda_status_str(code) and lib.kda_status_str(code) != b"unknown status"
     assert b"ok" == lib.kda_status_str(0)
     assert lib.kda_version().startswith(b"kda-mi355x")
     assert lib.kda_last_hip_error() == 0
+
+
+def test_noalloc_host_checks(lib):
+    # rejected on the host before any device is touched: no descriptor, the
+    # validate flag (it reads counters back to the host)
+    P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(9)]
+    assert lib.kda_chunk_fwd_noalloc(None, *P, None) == 1
+    d = _desc(flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE)
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(d), *P, None) == 2
 
 
 def test_context_arguments(lib):
