@@ -141,19 +141,23 @@ bool uses_two_pass(const kda_chunk_desc* d)
     return d->in_dtype == KDA_BF16 && d->d_k == 128 && d->d_v == 128 && !(d->flags & KDA_FLAG_FP32_PATH);
 }
 
-// fp32 staging of o for the norm pass (a bf16 o with KDA_FLAG_OUT_NORM)
+// fp32 staging of o for the separate norm pass of the fp32 path (a bf16 o
+// with KDA_FLAG_OUT_NORM); the matrix-core path normalises o in its
+// sequential kernel instead
 size_t norm_staging_bytes(const kda_chunk_desc* d)
 {
-    if (!(d->flags & KDA_FLAG_OUT_NORM) || d->out_dtype != KDA_BF16) return 0;
+    if (!(d->flags & KDA_FLAG_OUT_NORM) || d->out_dtype != KDA_BF16 || uses_two_pass(d)) return 0;
     return static_cast<size_t>(d->B) * d->T * d->H * d->d_v * sizeof(float);
 }
 
 // Workspace of one call: validation counters, the records (matrix-core
-// path), then the norm staging.
+// path, with the norm's row-sum words), then the norm staging (fp32 path).
 size_t workspace_need(const kda_chunk_desc* d, bool packed)
 {
     size_t bytes = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
-    if (uses_two_pass(d)) bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed);
+    if (uses_two_pass(d))
+        bytes += kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed,
+                                               (d->flags & KDA_FLAG_OUT_NORM) != 0);
     return bytes + norm_staging_bytes(d);
 }
 
@@ -290,22 +294,21 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     }
 
     const size_t off = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
-    const size_t recs = uses_two_pass(d) ? kda::two_pass_workspace_bytes(d->B, d->T, d->H, d->num_seqs,
-                                                                          cu_seqlens != nullptr)
-                                         : 0;
-    // with a norm, the forward pass writes fp32 o (to the staging area when
-    // o is bf16), then the norm pass writes o
-    kda::ChunkArgs fw = a;
-    if (norm) {
-        fw.out_norm = 0;
-        fw.out_bf16 = false;
-        if (a.out_bf16) fw.o = static_cast<char*>(workspace) + off + recs;
-    }
-    if (uses_two_pass(d))
-        e = kda::launch_chunk_two_pass(fw, static_cast<char*>(workspace) + off, stream, d->context);
-    else
+    if (uses_two_pass(d)) {
+        // the sequential kernel applies the output norm as it stores o
+        e = kda::launch_chunk_two_pass(a, static_cast<char*>(workspace) + off, stream, d->context);
+    } else {
+        // with a norm, the fp32 path writes fp32 o (to the staging area when
+        // o is bf16), then the norm pass writes o
+        kda::ChunkArgs fw = a;
+        if (norm) {
+            fw.out_norm = 0;
+            fw.out_bf16 = false;
+            if (a.out_bf16) fw.o = static_cast<char*>(workspace) + off;
+        }
         e = kda::launch_chunk_fp32(fw, stream);
-    if (e == hipSuccess && norm) e = kda::launch_out_norm(a, static_cast<const float*>(fw.o), stream);
+        if (e == hipSuccess && norm) e = kda::launch_out_norm(a, static_cast<const float*>(fw.o), stream);
+    }
     if (e != hipSuccess) return hip_fail(e);
     if (conv) {
         // after every kernel that reads the incoming conv state

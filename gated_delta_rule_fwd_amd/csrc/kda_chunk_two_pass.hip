@@ -768,13 +768,44 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 constexpr int DVS = 64;     // value columns per pass-2 workgroup: 4 waves x 16
 constexpr int NSLICE = DV / DVS;
 
+// Row stride (floats) of the fp32 output staging of the output norm: padded
+// so that the 16 rows one wave instruction touches fall into distinct banks.
+constexpr int OSTRIDE_NORM = DVS + 4;
+
 // V staging: bf16 as loaded, or fp32 when it is the short convolution's output
-template <bool CONV>
+template <bool CONV, bool NORM>
 struct alignas(16) ScanSmem {
     ChunkRecord r;                                               // this chunk's operands
     typename std::conditional<CONV, float, __bf16>::type vs[C][DVS];   // V slice [token][column]
-    float obuf[2][C * DVS];          // output tile staging ([token][column], bf16 or fp32), two chunks
+    // output tile staging ([token][column], bf16 or fp32), two chunks; with
+    // the output norm fp32 and three chunks (a tile waits one chunk for the
+    // other slice's row sums before it is normalised and stored)
+    float obuf[NORM ? 3 : 2][C * (NORM ? OSTRIDE_NORM : DVS)];
+    float nw[NORM ? DVS : 4];        // output norm: gain of this slice's columns
 };
+
+// Output norm across the two value slices of a chain: per chunk, each slice
+// publishes its 64 per-row sums of o^2 (taken from the unrounded fp32 o) as
+// 64-bit words (chunk index + 1) << 32 | float bits, written and read with
+// device-scope atomics, so a word is either the value of the expected chunk
+// or recognisably stale; no other memory ordering is needed.  Four words per
+// row and slice cycle with the chunk index.  A reader polls with a bounded
+// number of retries (the other slice runs the same chunk sequence and
+// publishes before it waits, so the bound is never reached unless that
+// workgroup cannot run; it keeps the kernel finite in any case).
+constexpr int kNormSlotsPerRow = 4;
+constexpr int kNormSpinLimit = 1 << 20;
+__host__ __device__ constexpr size_t norm_slot_words(long long chains)
+{
+    return static_cast<size_t>(chains) * NSLICE * kNormSlotsPerRow * C;
+}
+
+__global__ void zero_words_kernel(unsigned long long* __restrict__ p, size_t n)
+{
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = 0ull;
+}
 
 // output tile staging; bf16 is rounded to nearest even by the hardware conversion
 __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const float*)
@@ -785,16 +816,22 @@ __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, co
 {
     reinterpret_cast<uint16_t*>(base)[r * DVS + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
+// fp32 staging of the output norm (padded rows)
+struct NormStage {};
+__device__ __forceinline__ void stage_out(float* base, int r, int c, float x, const NormStage*)
+{
+    base[r * OSTRIDE_NORM + c] = x;
+}
 
 // The state update K'^T U~ takes U~ as fp16 hi + lo (two products) rather
 // than one fp16 rounding: with the keys the model produces (SiLU'd, sharing a
 // common direction) the state stays small next to what each chunk writes,
 // and U~'s single fp16 rounding alone costs ~3e-2 of RMS(S).
-template <typename Tout, bool CONV, bool SPLIT = true>
+template <typename Tout, bool CONV, bool NORM, bool SPLIT = true>
 __global__ void __launch_bounds__(NT, 1)
-chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
+chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots, unsigned long long* norm_slots)
 {
-    __shared__ ScanSmem<CONV> s;
+    __shared__ ScanSmem<CONV, NORM> s;
 
     const int t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -937,6 +974,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         }
     };
 
+    if constexpr (NORM) {
+        if (t < DVS) s.nw[t] = a.norm_w ? a.norm_w[j0 + t] : 1.f;
+    }
     if (je > jb) {
         fetch(jb, 0, RFULL + 1);
         fetch_v(jb);
@@ -959,6 +999,90 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             }
         }
     };
+    // ---- output norm ("Kimi K3 の KDA ..." section 1.2.1: RMSNorm over the
+    // head's d_v values, then the sigmoid gate): thread t handles row t/4 of a
+    // staged fp32 tile and 16 of its 64 columns; the 4 threads of a row are
+    // adjacent lanes.  publish: this slice's sum of o^2 per row of chunk m,
+    // kept in a register and written to the row's word for the other slice.
+    // finish: the other slice's sum for chunk m (polled), then
+    // o = x / sqrt(mean(x^2) + eps) * w * sigmoid(gate) stored once.
+    const int nrow = t >> 2, nq = t & 3;
+    unsigned long long* __restrict__ my_words =
+        NORM ? norm_slots + static_cast<size_t>(chain * NSLICE + slice) * kNormSlotsPerRow * C + nrow : nullptr;
+    const unsigned long long* __restrict__ other_words =
+        NORM ? norm_slots + static_cast<size_t>(chain * NSLICE + (slice ^ 1)) * kNormSlotsPerRow * C + nrow : nullptr;
+    const uint16_t* __restrict__ gp = static_cast<const uint16_t*>(a.out_gate);
+    auto row_sum = [&](int b) __attribute__((always_inline)) {
+        const float* src = s.obuf[b] + nrow * OSTRIDE_NORM + 16 * nq;
+        float ps = 0.f;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4 x = *reinterpret_cast<const float4*>(src + 4 * e4);
+            ps += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        }
+        ps += __shfl_xor(ps, 1, 64);
+        ps += __shfl_xor(ps, 2, 64);
+        return ps;
+    };
+    auto publish = [&](int m, int b, bool live) __attribute__((always_inline)) {
+        const float ps = row_sum(b);
+        if (live && nq == 0)
+            __hip_atomic_store(my_words + (m & (kNormSlotsPerRow - 1)) * C,
+                               (static_cast<unsigned long long>(m + 1) << 32) | __float_as_uint(ps), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        return ps;
+    };
+    auto poll = [&](int m) __attribute__((always_inline)) {
+        return __hip_atomic_load(other_words + (m & (kNormSlotsPerRow - 1)) * C, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto load_gate = [&](long cbase, int rows, uint4 (&gt)[2]) __attribute__((always_inline)) {
+        const long tk = cbase + min(nrow, max(rows - 1, 0));
+        const uint16_t* src = gp + (static_cast<size_t>(tk) * H + h) * DV + j0 + 16 * nq;
+        gt[0] = *reinterpret_cast<const uint4*>(src);
+        gt[1] = *reinterpret_cast<const uint4*>(src + 8);
+    };
+    // (live = false: nothing is waited for or stored; the loop calls these
+    // unconditionally so that no branch around a load leaves the register
+    // bookkeeping of later waits uncertain)
+    auto finish = [&](int m, int b, long cbase, int rows, float own, unsigned long long word, const uint4 (&gt)[2],
+                      bool live) __attribute__((always_inline)) {
+        for (int it = 0;
+             live && static_cast<unsigned>(word >> 32) != static_cast<unsigned>(m + 1) && it < kNormSpinLimit; ++it) {
+            __builtin_amdgcn_s_sleep(1);
+            word = poll(m);
+        }
+        const float inv = rsqrtf((own + __uint_as_float(static_cast<unsigned>(word))) * (1.f / DV) + a.norm_eps);
+        const float* src = s.obuf[b] + nrow * OSTRIDE_NORM + 16 * nq;
+        float y[16];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4 x = *reinterpret_cast<const float4*>(src + 4 * e4);
+            const float4 wt = *reinterpret_cast<const float4*>(&s.nw[16 * nq + 4 * e4]);
+            const uint4 g4 = gt[e4 >> 1];
+            const uint32_t w0 = (e4 & 1) ? g4.z : g4.x, w1 = (e4 & 1) ? g4.w : g4.y;
+            y[4 * e4 + 0] = x.x * inv * wt.x * sigmoid_fast(bf_lo(w0));
+            y[4 * e4 + 1] = x.y * inv * wt.y * sigmoid_fast(bf_hi(w0));
+            y[4 * e4 + 2] = x.z * inv * wt.z * sigmoid_fast(bf_lo(w1));
+            y[4 * e4 + 3] = x.w * inv * wt.w * sigmoid_fast(bf_hi(w1));
+        }
+        if (live && nrow < rows) {
+            Tout* dst = op + (static_cast<size_t>(cbase + nrow) * H + h) * DV + j0 + 16 * nq;
+            if constexpr (std::is_same<Tout, float>::value) {
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4)
+                    *reinterpret_cast<float4*>(dst + 4 * e4) =
+                        make_float4(y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]);
+            } else {
+#pragma unroll
+                for (int h8 = 0; h8 < 2; ++h8)
+                    *reinterpret_cast<uint4*>(dst + 8 * h8) =
+                        make_uint4(pack_bf16x2(y[8 * h8], y[8 * h8 + 1]), pack_bf16x2(y[8 * h8 + 2], y[8 * h8 + 3]),
+                                   pack_bf16x2(y[8 * h8 + 4], y[8 * h8 + 5]), pack_bf16x2(y[8 * h8 + 6], y[8 * h8 + 7]));
+            }
+        }
+    };
+
     // operand fragments of the R step for token tiles 2mh, 2mh + 1
     auto load_r = [&](int mh, f16x8 (&fa)[2][4], float (&vv)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -1036,7 +1160,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 stage_out(s.obuf[buf], 16 * mt + 4 * g + i, 16 * w + n, a.scale * acc[i],
-                          static_cast<const Tout*>(nullptr));
+                          static_cast<const typename std::conditional<NORM, NormStage, Tout>::type*>(nullptr));
         }
     };
     // operand fragments of the state update for channel tiles 4half .. 4half + 3
@@ -1144,14 +1268,28 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
     // per SIMD: nothing else would hide the LDS latency).  (Q^ Gamma) S rides
     // along with R's dependent chains, and the O and state-update products
     // are left to the scheduler to interleave.
-    long prev_c0 = 0;
-    int prev_L = 0;
+    long prev_c0 = 0, prev2_c0 = 0;
+    int prev_L = 0, prev2_L = 0;
+    int cur = 0;                          // output norm: obuf buffer of chunk j, (j - jb) mod 3
+    float own1 = 0.f, own2 = 0.f;         // output norm: this slice's row sums of chunks j-1, j-2
+    // output norm: the other slice's row sum and the gate rows of chunk j-2,
+    // requested during the previous iteration (with its record prefetch, so
+    // the wait at its commit covers them and nothing waits on them here)
+    unsigned long long word2 = 0ull;
+    uint4 gate2[2] = {};
     for (int j = jb; j < je; ++j) {
         const long c0 = tok0 + static_cast<long>(j) * C;
         const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
         const bool more = j + 1 < je;
-        const int buf = j & 1;
+        const int buf = NORM ? cur : (j & 1);
 
+        if constexpr (NORM) {
+            // first, before this iteration issues any load: chunk j-2 is
+            // normalised and stored, chunk j-1's row sums go out (in this
+            // order: the other slice reads a word before it can be reused)
+            finish(j - 2, cur == 2 ? 0 : cur + 1, prev2_c0, prev2_L, own2, word2, gate2, j >= jb + 2);
+            own1 = publish(j - 1, cur == 0 ? 2 : cur - 1, j > jb);
+        }
         f16x8 fa0[2][4], fa1[2][4], qa0[2][4], qa1[2][4];
         float vv0[2][4], vv1[2][4];
         load_r(0, fa0, vv0);
@@ -1160,7 +1298,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
             fetch_v(j + 1);
             fetch(j + 1, 0, 5);
         }
-        if (j > jb) store_tile(buf ^ 1, prev_c0, prev_L);
+        if constexpr (!NORM) {
+            if (j > jb) store_tile(buf ^ 1, prev_c0, prev_L);
+        }
         f16x8 sh[4], sl[4];
         split_state(sh, sl);
         __builtin_amdgcn_sched_barrier(0);
@@ -1173,6 +1313,13 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         bf16x8 th[6], tl[6];
         load_t(th, tl);
         if (more) fetch(j + 1, 5, 10);
+        if constexpr (NORM) {
+            // the other slice published chunk j-1's sums at the start of its
+            // iteration j; they and chunk j-1's gate rows are used at the start
+            // of the next iteration
+            word2 = poll(j - 1);
+            load_gate(prev_c0, prev_L, gate2);
+        }
         __builtin_amdgcn_sched_barrier(0);
         step_rq(1, fa1, qa1, vv1, sh, sl, ut, oq);
         __builtin_amdgcn_sched_barrier(0);
@@ -1199,11 +1346,30 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots)
         __syncthreads();
         // every read of this chunk's record is done: the next one moves in
         if (more) commit();
+        prev2_c0 = prev_c0;
+        prev2_L = prev_L;
         prev_c0 = c0;
         prev_L = L;
+        own2 = own1;
+        cur = cur == 2 ? 0 : cur + 1;
         __syncthreads();
     }
-    if (je > jb) store_tile((je - 1) & 1, prev_c0, prev_L);
+    if constexpr (NORM) {
+        // the last two chunks: je - 2 (its sums went out and the other
+        // slice's were requested in the last iteration), then je - 1
+        const int n_run = je - jb;
+        if (n_run >= 2)
+            finish(je - 2, cur == 0 ? 1 : (cur == 1 ? 2 : 0), prev2_c0, prev2_L, own2, word2, gate2, true);
+        if (n_run >= 1) {
+            const int b = cur == 0 ? 2 : cur - 1;
+            const float own = publish(je - 1, b, true);
+            uint4 gt[2];
+            load_gate(prev_c0, prev_L, gt);
+            finish(je - 1, b, prev_c0, prev_L, own, poll(je - 1), gt, true);
+        }
+    } else {
+        if (je > jb) store_tile((je - 1) & 1, prev_c0, prev_L);
+    }
 
     if (a.final_state) {
         const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
@@ -1223,14 +1389,18 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed)
     return static_cast<long long>(B) * ((T + C - 1) / C);
 }
 
-size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed)
+// The packed slot map or the carried state, after the records.
+static size_t two_pass_middle_bytes(int B, int H, long long slots, bool packed)
+{
+    if (packed) return (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256;
+    return static_cast<size_t>(B) * H * DK * DV * sizeof(float);
+}
+
+size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm)
 {
     const long long slots = chunk_record_slots(B, T, num_seqs, packed);
-    size_t bytes = static_cast<size_t>(slots) * H * kChunkRecordBytes;
-    if (packed)
-        bytes += (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256;
-    else
-        bytes += static_cast<size_t>(B) * H * DK * DV * sizeof(float);
+    size_t bytes = static_cast<size_t>(slots) * H * kChunkRecordBytes + two_pass_middle_bytes(B, H, slots, packed);
+    if (norm) bytes += norm_slot_words(static_cast<long long>(packed ? num_seqs : B) * H) * sizeof(unsigned long long);
     return bytes;
 }
 
@@ -1282,21 +1452,32 @@ void prep(const ChunkArgs& a, ChunkRecord* recs, const int* map, int slots, unsi
         launch_prep<false, false>(a, recs, map, slots, groups, stream);
 }
 
-void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, hipStream_t stream)
+template <typename Tout, bool CONV>
+void launch_scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, unsigned long long* norm_slots, dim3 grid,
+                 hipStream_t stream)
+{
+    if (a.out_norm)
+        chunk_scan_kernel<Tout, CONV, true><<<grid, NT, 0, stream>>>(a, recs, slots, norm_slots);
+    else
+        chunk_scan_kernel<Tout, CONV, false><<<grid, NT, 0, stream>>>(a, recs, slots, nullptr);
+}
+
+void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, unsigned long long* norm_slots,
+          hipStream_t stream)
 {
     // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
     const int groups = (chains + 7) / 8;
-    const dim3 grid(groups * 8 * NSLICE), block(NT);
+    const dim3 grid(groups * 8 * NSLICE);
     if (a.conv) {
         if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, true><<<grid, block, 0, stream>>>(a, recs, slots);
+            launch_scan<uint16_t, true>(a, recs, slots, norm_slots, grid, stream);
         else
-            chunk_scan_kernel<float, true><<<grid, block, 0, stream>>>(a, recs, slots);
+            launch_scan<float, true>(a, recs, slots, norm_slots, grid, stream);
     } else {
         if (a.out_bf16)
-            chunk_scan_kernel<uint16_t, false><<<grid, block, 0, stream>>>(a, recs, slots);
+            launch_scan<uint16_t, false>(a, recs, slots, norm_slots, grid, stream);
         else
-            chunk_scan_kernel<float, false><<<grid, block, 0, stream>>>(a, recs, slots);
+            launch_scan<float, false>(a, recs, slots, norm_slots, grid, stream);
     }
 }
 
@@ -1312,6 +1493,15 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
     const int nck = packed ? 0 : (args.T + C - 1) / C;
+    // output norm: the row-sum words the two value slices of a chain exchange,
+    // zeroed by a kernel (no memset node) before any pass 2 of this call
+    unsigned long long* norm_slots = nullptr;
+    if (args.out_norm) {
+        norm_slots = reinterpret_cast<unsigned long long*>(after + two_pass_middle_bytes(args.B, args.H, slots, packed));
+        const size_t words = norm_slot_words(chains);
+        const size_t blocks = (words + 255) / 256;
+        zero_words_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(norm_slots, words);
+    }
 
     // the overlapped schedule for a dense batch, when it pays and the
     // caller's context can carry it
@@ -1344,7 +1534,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
         }
         a.chunk_lo = 0;
         a.chunk_cnt = packed ? ns : nck;
-        scan(a, recs, ns, chains, stream);
+        scan(a, recs, ns, chains, norm_slots, stream);
         return hipGetLastError();
     }
 
@@ -1368,7 +1558,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     ok(hipEventRecord(ctx->p1[0], stream));
     for (int s = 0; s < stages && e == hipSuccess; ++s) {
         if (!ok(hipStreamWaitEvent(ctx->side, ctx->p1[s], 0))) break;
-        scan(stage_args(s), recs, ns, chains, ctx->side);
+        scan(stage_args(s), recs, ns, chains, norm_slots, ctx->side);
         const hipError_t lr = hipGetLastError();
         if (lr == hipSuccess) launched = s;
         if (!ok(lr)) break;

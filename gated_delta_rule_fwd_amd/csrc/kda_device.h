@@ -50,6 +50,11 @@ __device__ __forceinline__ float gate_log_decay(float z, float bias, float exp_a
     return -5.f * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(y));
 }
 __device__ __forceinline__ float beta_from_logit(float b) { return 1.f / (1.f + __expf(-b)); }
+// sigmoid(x) as a reciprocal (to 1 ulp) of 1 + 2^{-x log2(e)}: three
+// instructions; 2^{...} overflowing to +inf gives 0, the limit
+__device__ __forceinline__ float sigmoid_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x * -1.44269504088896341f));
+}
 
 // Short convolution prologue ("Kimi K3 の KDA ..." section 1.2.1: causal and
 // per channel over the current token and the 3 before it, then SiLU).  Taps

@@ -111,7 +111,10 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed);
 // workspace: records (h * slots + slot), then one int32 per slot naming its
 // sequence or -1 (packed sequences) or the fp32 state of every chain
 // [B*H, 128, 128] carried between the overlapped launches (dense batch).
-size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed);
+// With the output norm (`norm`), the pass-2 workgroups of the two value
+// slices of a chain exchange per-row sums of o^2 through 2 KB per chain after
+// that, and o is normalised as it is stored.
+size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm);
 // With a context (nullable), a dense batch whose sequential pass leaves CUs
 // idle runs in stages: pass 1 of stage s+1 on the idle CUs while pass 2 of
 // stage s runs, pass 2 on the context's stream, joined to `stream` before

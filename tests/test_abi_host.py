@@ -247,11 +247,17 @@ def test_gated_entry_points_reject_bad_arguments(lib):
 def test_workspace_for_the_output_norm(lib):
     size = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(**kw)))
     on = kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM
-    # a bf16 o is staged in fp32 for the norm pass, after the records
-    assert size(B=2, T=100, H=3, flags=on) == size(B=2, T=100, H=3) + 2 * 100 * 3 * 128 * 4
+    # matrix-core path: the two value slices of each chain exchange per-row
+    # sums of o^2 through 2 x 4 x 64 words of 8 bytes per chain, after the
+    # records; o itself is normalised as it is stored (bf16 or fp32)
+    words = 2 * 4 * 64 * 8
+    assert size(B=2, T=100, H=3, flags=on) == size(B=2, T=100, H=3) + 2 * 3 * words
+    assert size(B=2, T=100, H=3, out_dtype=0, flags=on) == size(B=2, T=100, H=3) + 2 * 3 * words
+    assert size(B=1, T=1000, H=2, num_seqs=5, flags=on) == size(B=1, T=1000, H=2, num_seqs=5) + 5 * 2 * words
+    # fp32 path: a bf16 o is staged in fp32 for the norm pass; an fp32 o is
+    # normalised in place
     assert size(B=2, T=100, H=3, d_k=64, d_v=64, flags=on) == 2 * 100 * 3 * 64 * 4
-    # an fp32 o is normalised in place
-    assert size(B=2, T=100, H=3, out_dtype=0, flags=on) == size(B=2, T=100, H=3)
+    assert size(B=2, T=100, H=3, d_k=64, d_v=64, out_dtype=0, flags=on) == 0
     assert size(B=1, T=10, H=1, in_dtype=0, out_dtype=0, flags=on | kda.FLAG_VALIDATE) == 256
 
 

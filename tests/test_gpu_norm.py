@@ -1,8 +1,10 @@
 """GPU parity of the fused output norm (o <- o / sqrt(mean(o^2) + eps) * w *
-sigmoid(gate) per (token, head) row, applied at the store of o) against the
-fp64 oracle's recurrence followed by its out_norm.  Every kernel family that
-can carry the norm is covered: the matrix-core prefill (8-wave scan pass), the
-exact fp32 prefill (separate norm pass) and the decode step.  Marked ``gpu``."""
+sigmoid(gate) per (token, head) row) against the fp64 oracle's recurrence
+followed by its out_norm.  Every kernel family that can carry the norm is
+covered: the matrix-core prefill (the sequential kernel normalises o as it
+stores it, its two value-slice workgroups exchanging per-row sums of o^2),
+the exact fp32 prefill (separate norm pass over fp32 o) and the decode step
+(norm in the lanes that hold o).  Marked ``gpu``."""
 import numpy as np
 import pytest
 
@@ -42,8 +44,9 @@ def _plain(kda, inp, gate, w, out_dtype, **kw):
 
 @pytest.mark.parametrize("use_w", [True, False])
 def test_norm_matrix_core_prefill(kda, use_w):
-    """bf16, d=128: the 8-wave scan pass with the norm at the tile store;
-    ragged T, both output dtypes, with and without the gain."""
+    """bf16, d=128: the sequential kernel with the norm at the store of o
+    (row sums exchanged between the two value slices); ragged T, both output
+    dtypes, with and without the gain."""
     import torch
     inp = kda_inputs.make_prefill(31, 1, 1000, 8, 128, 128, s0_std=0.02)
     gate = kda_inputs.make_out_gate(31, inp.v.shape)
@@ -158,3 +161,45 @@ def test_norm_decode_steps(kda, dtype, d, gated):
         check("norm_decode_%s_g%d/step%d" % (dtype, gated, step), host64(o),
               oracle.out_norm(o_ref, _f64(gate), w, EPS), None, None, tol, bf16_store=False)
     check_state("norm_decode_%s_g%d/final" % (dtype, gated), host64(state), s_ref, tol)
+
+
+@pytest.mark.parametrize("odt_name", ["bfloat16", "float32"])
+def test_norm_matrix_core_short_sequences(kda, odt_name):
+    """The matrix-core norm finishes each chunk one chunk after its row sums
+    are exchanged and flushes the last two at the end: packed sequences of
+    one, two, three and more chunks (and empty ones), both output dtypes."""
+    import torch
+    odt = getattr(torch, odt_name)
+    lens = [1, 64, 65, 128, 0, 129, 192, 193, 300, 17]
+    inp = kda_inputs.make_prefill(41, 1, 0, 3, 128, 128, s0_std=0.02, lengths=lens)
+    gate = kda_inputs.make_out_gate(41, inp.v.shape)
+    w = kda_inputs.norm_weight(41, 128)
+    o_ref, s_ref = oracle.forward(inp)
+    y_ref = oracle.out_norm(o_ref, _f64(gate), w, EPS)
+    o, s = _plain(kda, inp, gate, w, odt)
+    check("norm_short/%s" % odt_name, host64(o), y_ref, host64(s), s_ref, TOL_BF16, bf16_store=(odt == torch.bfloat16))
+
+
+def test_norm_matrix_core_workspace_reuse(kda):
+    """Two calls with different inputs in one workspace: the second equals the
+    same call in a fresh workspace bit for bit (the row-sum words the value
+    slices exchange are cleared at the start of every call, so words a
+    previous call left behind cannot pass for the current chunk's)."""
+    import torch
+    B, T, H = 1, 700, 4
+    ins = [kda_inputs.make_prefill(42 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
+    gates = [dev(kda_inputs.make_out_gate(42 + i, (B, T, H, 128))) for i in range(2)]
+    ws = torch.empty(kda.workspace_bytes(B, T, H, 128, 128, flags=kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM),
+                     dtype=torch.uint8, device="cuda")
+    outs = []
+    for i in (0, 1):
+        x = ins[i]
+        o, s = kda.chunk_fwd(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(x.init_state),
+                             out_gate=gates[i], norm_eps=EPS, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((o, s))
+    x = ins[1]
+    o2, s2 = kda.chunk_fwd(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(x.init_state),
+                           out_gate=gates[1], norm_eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[1][0], o2) and torch.equal(outs[1][1], s2)
