@@ -446,7 +446,7 @@ def time_gated(kda, torch, kda_inputs, reps=20, warm=5, norm=False, conv=False):
     torch.cuda.empty_cache()
     if conv:
         return _line("long prefill B=1 H=96 T=65536 d=128, the fused layer core: short convolution + SiLU of raw bf16 "
-                     "q, k, v with conv states in and out, decay-gate prologue, output norm pass (seed 2)",
+                     "q, k, v with conv states in and out, decay-gate prologue, output norm (seed 2)",
                      ts, BYTES_PER_TOKEN_HEAD_LAYER * B * T * H + 2 * STATE_BYTES * B * H + 4 * D +
                      2 * 3 * 3 * H * D * 2 + 3 * 4 * 4 * H * D)
     if norm:
