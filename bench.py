@@ -56,7 +56,21 @@ def parse():
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of this bench "
                         "(FETCH_SIZE, then WRITE_SIZE) and exit; needs no GPU")
+    p.add_argument("--workload", choices=sorted(WORKLOAD_LINES),
+                   help="instead of the headline: time only this workload (for per-workload profiler runs) "
+                        "and print its line")
+    p.add_argument("--oracle-table", action="store_true",
+                   help="instead of the headline: time the fp64 oracle on bounded samples of the five workloads, "
+                        "on all host cores and on one core; needs no GPU")
+    p.add_argument("--mfma-from", metavar="DIR",
+                   help="summarise a rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and "
+                        "GRBM_GUI_ACTIVE (MFMA-busy fraction per kernel) and exit; needs no GPU")
     return p.parse_args()
+
+
+# --workload names -> the bench line they time
+WORKLOAD_LINES = {"tiny": "tiny_f32", "mid": "mid_bf16", "long": "long_bf16", "varlen": "varlen_bf16",
+                  "decode": "decode"}
 
 
 # the sources each measured path is built from (kernels, their headers, the launch code)
@@ -361,10 +375,12 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
         ins.append(d)
     tokens, H = inp.B * inp.T, inp.H
     n_seq = (inp.cu_seqlens.shape[0] - 1) if inp.cu_seqlens is not None else inp.B
-    o = torch.empty((inp.B, inp.T, H, inp.dv), dtype=torch.bfloat16, device="cuda")
+    f32 = inp.dtype == "f32"
+    o = torch.empty((inp.B, inp.T, H, inp.dv), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
     sT = torch.empty((n_seq, H, inp.dk, inp.dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kda.workspace_bytes(inp.B, inp.T, H, inp.dk, inp.dv, num_seqs=n_seq if d["cu"] is not None else 0),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, kda.workspace_bytes(inp.B, inp.T, H, inp.dk, inp.dv,
+                                                num_seqs=n_seq if d["cu"] is not None else 0, in_bf16=not f32,
+                                                out_bf16=not f32)), dtype=torch.uint8, device="cuda")
     call = lambda d: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["cu"], o=o,
                                    final_state=sT, workspace=ws)
     for i in range(warm):
@@ -379,7 +395,10 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
         e1.synchronize()
         ts.append(e0.elapsed_time(e1))
     ms = float(np.median(ts))
-    algo = BYTES_PER_TOKEN_HEAD * tokens * H + 2 * STATE_BYTES * n_seq * H
+    if f32:   # fp32 q, k, v, o (4 bytes each per channel), fp32 g, beta; d_k, d_v of the workload
+        algo = (4 * (2 * inp.dk + 2 * inp.dv) + 4 * inp.dk + 4) * tokens * H + 2 * 4 * inp.dk * inp.dv * n_seq * H
+    else:
+        algo = BYTES_PER_TOKEN_HEAD * tokens * H + 2 * STATE_BYTES * n_seq * H
     del ins, o, sT, ws
     torch.cuda.empty_cache()
     return {"tokens": tokens, "heads": H, "sequences": n_seq, "input_sets": sets, "ms_median": ms,
@@ -497,10 +516,94 @@ def time_signed(kda, torch, kda_inputs, reps=20, warm=5):
                  "beta in (0, 2) (seed 2)", ts, BYTES_PER_TOKEN_HEAD * B * T * H + 2 * STATE_BYTES * B * H)
 
 
+def oracle_table():
+    """The fp64 oracle (test infrastructure, untuned) timed on bounded samples
+    of the five workloads, on all host cores (OpenMP over chains) and on one
+    core, each scaled to the workload's unit.  CPU only."""
+    import oracle
+    import kda_inputs
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+    def sub(inp, tokens, heads):
+        return kda_inputs.PrefillInputs(
+            B=1, T=tokens, H=heads, dk=inp.dk, dv=inp.dv, dtype=inp.dtype,
+            q=np.ascontiguousarray(inp.q[:, :tokens, :heads]), k=np.ascontiguousarray(inp.k[:, :tokens, :heads]),
+            v=np.ascontiguousarray(inp.v[:, :tokens, :heads]), g=np.ascontiguousarray(inp.g[:, :tokens, :heads]),
+            beta=np.ascontiguousarray(inp.beta[:, :tokens, :heads]),
+            init_state=None if inp.init_state is None else np.ascontiguousarray(inp.init_state[:1, :heads]),
+            cu_seqlens=None)
+
+    def run(inp, threads):
+        t0 = time.perf_counter()
+        oracle.forward(inp, threads=threads)
+        return time.perf_counter() - t0
+
+    rows = {}
+    for name, key, heads_all, heads_one, tokens_one in (("tiny", "tiny_f32", 2, 1, 256), ("mid", "mid_bf16", 32, 1, 4096),
+                                                        ("long", "long_bf16", 96, 1, 16384)):
+        inp = kda_inputs.workload(key) if name != "long" else kda_inputs.workload(key, T=16384)
+        T_all = inp.T
+        dt = run(inp, min(cores, heads_all))
+        dt1 = run(sub(inp, tokens_one, heads_one), 1)
+        T_full = kda_inputs.WORKLOADS[key]["T"]
+        rows[name] = {"tokens_per_s_all_cores": T_all * heads_all / dt / kda_inputs.WORKLOADS[key]["H"],
+                      "sample_all_cores": "%d tokens x %d heads, %d threads, %.2f s" % (T_all, heads_all,
+                                                                                         min(cores, heads_all), dt),
+                      "tokens_per_s_one_core": tokens_one * heads_one / dt1 / kda_inputs.WORKLOADS[key]["H"],
+                      "sample_one_core": "%d tokens x %d head, 1 thread, %.2f s" % (tokens_one, heads_one, dt1),
+                      "full_workload_tokens": T_full}
+    # varlen: every sequence, the first 8 of 32 heads on all cores; the first
+    # 4096 tokens of sequence 0, one head, on one core
+    vin = kda_inputs.workload("varlen_bf16")
+    hs = slice(0, 8)
+    t0 = time.perf_counter()
+    oracle.forward(vin, hs, threads=min(cores, 8 * len(vin.cu_seqlens)))
+    dt = time.perf_counter() - t0
+    dt1 = run(sub(vin, 4096, 1), 1)
+    tot = int(vin.cu_seqlens[-1])
+    rows["varlen"] = {"tokens_per_s_all_cores": tot * 8 / dt / vin.H,
+                      "sample_all_cores": "all %d tokens x 8 of 32 heads, %.2f s" % (tot, dt),
+                      "tokens_per_s_one_core": 4096 / dt1 / vin.H,
+                      "sample_one_core": "first 4096 tokens of sequence 0, 1 head, 1 thread, %.2f s" % dt1}
+    dec = cpu_decode_baseline()
+    rows["decode"] = {"ms_per_step_all_cores": dec["ms_per_step"], "sample_all_cores": dec["sample"],
+                      "ms_per_step_one_core": dec["one_core_ms_per_step"], "sample_one_core": dec["one_core_sample"]}
+    return {"oracle_table": rows, "cores": cores, "host": host_info(),
+            "note": "fp64 token recurrence (C, OpenMP over chains); tokens/s scaled to the workload's head count"}
+
+
+def mfma_summary(d):
+    """MFMA-busy per kernel from one rocprofv3 --pmc run: SQ_VALU_MFMA_BUSY_CYCLES
+    over (GRBM_GUI_ACTIVE / 8 XCDs) x 256 CUs x 4 SIMDs, summed over the
+    dispatches of each kernel name."""
+    import collections
+    rows = _counter_rows(d)
+    acc = collections.defaultdict(lambda: collections.Counter())
+    for r in rows:
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        acc[name][r["Counter_Name"]] += float(r["Counter_Value"])
+        acc[name]["_dispatch:" + r.get("Dispatch_Id", "")] = 1
+    out = {}
+    for name, c in acc.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or not c.get("GRBM_GUI_ACTIVE"):
+            continue
+        cycles = c["GRBM_GUI_ACTIVE"] / 8.0
+        out[name] = {"dispatches": sum(1 for k in c if k.startswith("_dispatch:")),
+                     "mfma_busy_frac": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * 256 * 4),
+                     "sq_busy_cycles": c.get("SQ_BUSY_CYCLES"), "gpu_cycles_per_xcd": cycles}
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
 def main():
     args = parse()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
+        return
+    if args.mfma_from:
+        mfma_summary(args.mfma_from)
+        return
+    if args.oracle_table:
+        print(json.dumps(oracle_table()), flush=True)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -517,6 +620,16 @@ def main():
     torch.manual_seed(0)
     if args.sweep:
         print(json.dumps(context_sweep(kda, torch, kda_inputs)))
+        return
+    if args.workload:
+        name = WORKLOAD_LINES[args.workload]
+        if name == "decode":
+            line = time_decode(kda, torch, kda_inputs)
+        else:
+            sets = 2 if name == "mid_bf16" else 1
+            line = dict(workload=name, **time_workload(kda, torch, kda_inputs, name, sets=sets, reps=args.steps,
+                                                       warm=args.warmup))
+        print(json.dumps({"workload_line": args.workload, **line}), flush=True)
         return
 
     inp = kda_inputs.workload("long_bf16")
@@ -558,6 +671,8 @@ def main():
         if not args.no_extra:
             out["decode_out_norm"] = time_decode(kda, torch, kda_inputs, norm=True)
     if not args.no_extra:
+        out["prefill_tiny"] = dict(workload="B=1 H=2 T=256 d=64 fp32 (exact fp32 path), seed 0",
+                                   **time_workload(kda, torch, kda_inputs, "tiny_f32", sets=1))
         out["prefill_mid"] = dict(workload="B=1 H=32 T=4096 d=128 bf16, seed 1; two input sets rotated",
                                   **time_workload(kda, torch, kda_inputs, "mid_bf16", sets=2))
         out["prefill_varlen"] = dict(workload="16 packed sequences, lengths U[512,16384] from seed 3, H=32 d=128 bf16",
