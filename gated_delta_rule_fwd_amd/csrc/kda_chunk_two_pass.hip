@@ -842,9 +842,12 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // of each record hits that XCD's L2.
     const int bid = blockIdx.x;
     const int slice = (bid >> 3) & (NSLICE - 1);
-    const int chain = ((bid >> 4) << 3) | (bid & 7);
+    // unit of work: a chain, or with the segmented pass a (chain, unit) pair
+    const int vc = ((bid >> 4) << 3) | (bid & 7);
     const int nchains = (a.cu_seqlens ? a.num_seqs : a.B) * H;
-    if (chain >= nchains) return;
+    const int units = a.seg_phase == 1 ? seg_units_a(a.seg_count) : (a.seg_phase == 2 ? seg_units_c(a.seg_count) : 1);
+    if (vc >= nchains * units) return;
+    const int chain = vc / units, unit = vc - chain * units;
     const int j0 = slice * DVS;
     const int seq = chain / H, h = chain % H;
 
@@ -866,8 +869,41 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // this launch runs chunks jb .. je - 1 of the chain, from init_state (the
     // chain's initial state, or the state a launch over the chunks before
     // left) to final_state
-    const int jb = min(a.chunk_lo, nch);
-    const int je = static_cast<int>(min(static_cast<long>(nch), static_cast<long>(a.chunk_lo) + a.chunk_cnt));
+    int jb = min(a.chunk_lo, nch);
+    int je = static_cast<int>(min(static_cast<long>(nch), static_cast<long>(a.chunk_lo) + a.chunk_cnt));
+    // per unit: where the state comes from and goes, whether o is written,
+    // whether the values are taken as zero (the transition of a segment)
+    const float* sinit = a.init_state ? a.init_state + static_cast<size_t>(chain) * DK * DV : nullptr;
+    float* sfinal = a.final_state ? a.final_state + static_cast<size_t>(chain) * DK * DV : nullptr;
+    bool identity = false, zero_v = false, with_out = true;
+    if (a.seg_phase) {
+        const int P = a.seg_count;
+        float* blocks = a.seg_states + static_cast<size_t>(chain) * seg_state_blocks(P) * DK * DV;
+        auto block = [&](int k) { return blocks + static_cast<size_t>(k) * DK * DV; };
+        int sg;
+        if (a.seg_phase == 1) {
+            sg = (unit + 1) >> 1;
+            if (unit == 0) {
+                sfinal = block(0);
+            } else {
+                with_out = false;
+                if (unit & 1) {
+                    sinit = nullptr;
+                    sfinal = block(seg_block_b(P, sg));
+                } else {
+                    sinit = nullptr;
+                    identity = zero_v = true;
+                    sfinal = block(seg_block_m(P, sg));
+                }
+            }
+        } else {
+            sg = unit + 1;
+            sinit = block(seg_block_in(P, sg));
+            if (sg + 1 < P) sfinal = nullptr;
+        }
+        jb = min(sg * a.seg_len, nch);
+        je = min(jb + a.seg_len, nch);
+    }
     const ChunkRecord* __restrict__ rc = recs + static_cast<size_t>(h) * nslots + slot0;
     const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
     Tout* __restrict__ op = static_cast<Tout*>(a.o);
@@ -875,12 +911,15 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // ---- state strip: channels 16*mt + 4*g + i, column j0 + 16*w + n
     f32x4 sacc[8];
     {
-        const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
+        const size_t sbase = j0 + 16 * w + n;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sacc[mt][i] = a.init_state ? a.init_state[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int ch = 16 * mt + 4 * g + i;
+                sacc[mt][i] = sinit ? sinit[sbase + static_cast<size_t>(ch) * DV]
+                                    : ((identity && ch == static_cast<int>(sbase)) ? 1.f : 0.f);
+            }
     }
 
     // The next chunk's record and V slice travel in registers while the
@@ -917,6 +956,18 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     };
     auto fetch_v = [&](int j) __attribute__((always_inline)) {
         const long cb = tok0 + static_cast<long>(j) * C;
+        if (zero_v) {   // the transition of a segment: values taken as zero (a zero conv input gives silu(0) = 0)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if constexpr (CONV) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) PVc[u][jj] = u32x4{0u, 0u, 0u, 0u};
+                } else {
+                    PV[u] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int idx = t + NT * u, r = idx / PPR, part = idx % PPR;
@@ -1008,9 +1059,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // o = x / sqrt(mean(x^2) + eps) * w * sigmoid(gate) stored once.
     const int nrow = t >> 2, nq = t & 3;
     unsigned long long* __restrict__ my_words =
-        NORM ? norm_slots + static_cast<size_t>(chain * NSLICE + slice) * kNormSlotsPerRow * C + nrow : nullptr;
+        NORM ? norm_slots + static_cast<size_t>(vc * NSLICE + slice) * kNormSlotsPerRow * C + nrow : nullptr;
     const unsigned long long* __restrict__ other_words =
-        NORM ? norm_slots + static_cast<size_t>(chain * NSLICE + (slice ^ 1)) * kNormSlotsPerRow * C + nrow : nullptr;
+        NORM ? norm_slots + static_cast<size_t>(vc * NSLICE + (slice ^ 1)) * kNormSlotsPerRow * C + nrow : nullptr;
     const uint16_t* __restrict__ gp = static_cast<const uint16_t*>(a.out_gate);
     auto row_sum = [&](int b) __attribute__((always_inline)) {
         const float* src = s.obuf[b] + nrow * OSTRIDE_NORM + 16 * nq;
@@ -1287,8 +1338,8 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             // first, before this iteration issues any load: chunk j-2 is
             // normalised and stored, chunk j-1's row sums go out (in this
             // order: the other slice reads a word before it can be reused)
-            finish(j - 2, cur == 2 ? 0 : cur + 1, prev2_c0, prev2_L, own2, word2, gate2, j >= jb + 2);
-            own1 = publish(j - 1, cur == 0 ? 2 : cur - 1, j > jb);
+            finish(j - 2, cur == 2 ? 0 : cur + 1, prev2_c0, prev2_L, own2, word2, gate2, with_out && j >= jb + 2);
+            own1 = publish(j - 1, cur == 0 ? 2 : cur - 1, with_out && j > jb);
         }
         f16x8 fa0[2][4], fa1[2][4], qa0[2][4], qa1[2][4];
         float vv0[2][4], vv1[2][4];
@@ -1299,7 +1350,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             fetch(j + 1, 0, 5);
         }
         if constexpr (!NORM) {
-            if (j > jb) store_tile(buf ^ 1, prev_c0, prev_L);
+            if (with_out && j > jb) store_tile(buf ^ 1, prev_c0, prev_L);
         }
         f16x8 sh[4], sl[4];
         split_state(sh, sl);
@@ -1357,7 +1408,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     if constexpr (NORM) {
         // the last two chunks: je - 2 (its sums went out and the other
         // slice's were requested in the last iteration), then je - 1
-        const int n_run = je - jb;
+        const int n_run = with_out ? je - jb : 0;
         if (n_run >= 2)
             finish(je - 2, cur == 0 ? 1 : (cur == 1 ? 2 : 0), prev2_c0, prev2_L, own2, word2, gate2, true);
         if (n_run >= 1) {
@@ -1368,17 +1419,93 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             finish(je - 1, b, prev_c0, prev_L, own, poll(je - 1), gt, true);
         }
     } else {
-        if (je > jb) store_tile((je - 1) & 1, prev_c0, prev_L);
+        if (with_out && je > jb) store_tile((je - 1) & 1, prev_c0, prev_L);
     }
 
-    if (a.final_state) {
-        const size_t sbase = static_cast<size_t>(chain) * DK * DV + j0 + 16 * w + n;
+    if (sfinal) {
+        const size_t sbase = j0 + 16 * w + n;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a.final_state[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] = sacc[mt][i];
+                sfinal[sbase + static_cast<size_t>(16 * mt + 4 * g + i) * DV] = sacc[mt][i];
     }
+}
+
+// Phase B of the segmented sequential pass: every segment's initial state,
+// in order, from the segments' summaries: S_1 = the state after segment 0,
+// S_{s+1} = M_s S_s + B_s ("Kimi K3 の KDA ..." section 2.3.4.1: (A2, b2)
+// after (A1, b1) is (A2 A1, A2 b1 + b2)).  One workgroup per (chain,
+// 16-column strip of the state): the columns are independent affine systems
+// (section 2.3.2).  fp32 throughout; M_s is d_k x d_k, held like a state.
+__global__ void __launch_bounds__(256) seg_combine_kernel(float* __restrict__ seg_states, int P, int nchains)
+{
+    static_assert(DK == DV, "M_s is stored in a state-shaped block");
+    constexpr int SW = 16;                       // columns per workgroup
+    const int chain = blockIdx.x / (DV / SW), c0 = SW * (blockIdx.x % (DV / SW));
+    if (chain >= nchains) return;
+    float* blocks = seg_states + static_cast<size_t>(chain) * seg_state_blocks(P) * DK * DV;
+    auto block = [&](int k) { return blocks + static_cast<size_t>(k) * DK * DV; };
+    __shared__ float sx[DK][SW];
+    const int t = threadIdx.x;
+    for (int e = t; e < DK * SW; e += 256) {
+        const int r = e / SW, c = e % SW;
+        const float x = block(0)[static_cast<size_t>(r) * DV + c0 + c];
+        sx[r][c] = x;
+        block(seg_block_in(P, 1))[static_cast<size_t>(r) * DV + c0 + c] = x;
+    }
+    __syncthreads();
+    const int r = t >> 1, cb = 8 * (t & 1);      // row r, columns cb .. cb + 7 of the strip
+    for (int sg = 1; sg + 1 < P; ++sg) {
+        const float* M = block(seg_block_m(P, sg)) + static_cast<size_t>(r) * DV;
+        const float* Bs = block(seg_block_b(P, sg)) + static_cast<size_t>(r) * DV + c0 + cb;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = Bs[e];
+        for (int k4 = 0; k4 < DK; k4 += 4) {
+            const float4 m = *reinterpret_cast<const float4*>(M + k4);
+            const float mk[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += mk[u] * sx[k4 + u][cb + e];
+        }
+        __syncthreads();
+        float* out = block(seg_block_in(P, sg + 1)) + static_cast<size_t>(r) * DV + c0 + cb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sx[r][cb + e] = acc[e];
+            out[e] = acc[e];
+        }
+        __syncthreads();
+    }
+}
+
+// Workspace of the matrix-core path: the records, then the packed slot map
+// or the state carried between stages (dense), then the output norm's
+// row-sum words, then the segment states (dense batches that may take the
+// segmented pass).  The sizes cover the largest plan the call can take.
+struct TwoPassLayout {
+    size_t norm_off, seg_off, total;
+};
+
+TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bool norm)
+{
+    const long long slots = chunk_record_slots(B, T, num_seqs, packed);
+    const long long chains = static_cast<long long>(packed ? num_seqs : B) * H;
+    const int nck = packed ? 0 : (T + C - 1) / C;
+    const bool may_segment = !packed && plan_segments(nck, static_cast<int>(chains), 1 << 20) > 1;
+    TwoPassLayout L;
+    L.norm_off = static_cast<size_t>(slots) * H * kChunkRecordBytes;
+    L.norm_off += packed ? (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256
+                         : static_cast<size_t>(B) * H * DK * DV * sizeof(float);
+    const long long units = may_segment ? seg_units_a(kMaxSegments) : 1;
+    L.seg_off = L.norm_off + (norm ? norm_slot_words(chains * units) * sizeof(unsigned long long) : 0);
+    L.seg_off = (L.seg_off + 255) / 256 * 256;
+    L.total = L.seg_off + (may_segment ? static_cast<size_t>(chains) * seg_state_blocks(kMaxSegments) * DK * DV *
+                                             sizeof(float)
+                                       : 0);
+    return L;
 }
 
 }  // namespace
@@ -1389,19 +1516,9 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed)
     return static_cast<long long>(B) * ((T + C - 1) / C);
 }
 
-// The packed slot map or the carried state, after the records.
-static size_t two_pass_middle_bytes(int B, int H, long long slots, bool packed)
-{
-    if (packed) return (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256;
-    return static_cast<size_t>(B) * H * DK * DV * sizeof(float);
-}
-
 size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm)
 {
-    const long long slots = chunk_record_slots(B, T, num_seqs, packed);
-    size_t bytes = static_cast<size_t>(slots) * H * kChunkRecordBytes + two_pass_middle_bytes(B, H, slots, packed);
-    if (norm) bytes += norm_slot_words(static_cast<long long>(packed ? num_seqs : B) * H) * sizeof(unsigned long long);
-    return bytes;
+    return two_pass_layout(B, T, H, num_seqs, packed, norm).total;
 }
 
 namespace {
@@ -1493,14 +1610,46 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
     const int nck = packed ? 0 : (args.T + C - 1) / C;
-    // output norm: the row-sum words the two value slices of a chain exchange,
-    // zeroed by a kernel (no memset node) before any pass 2 of this call
+    const TwoPassLayout lay = two_pass_layout(args.B, args.T, args.H, args.num_seqs, packed, args.out_norm != 0);
+
+    // the segmented order for a dense batch with few chains
+    int nseg = 1;
+    if (!packed && plan_segments(nck, chains, 1 << 20) > 1) {
+        int dev = 0, cus = 0;
+        if (hipStreamGetDevice(stream, &dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            nseg = plan_segments(nck, chains, cus);
+    }
+    const long long units = nseg > 1 ? seg_units_a(nseg) : 1;
+
+    // output norm: the row-sum words the two value slices of a chain (or of a
+    // segment unit) exchange, zeroed by a kernel (no memset node) before any
+    // pass 2 of this call
     unsigned long long* norm_slots = nullptr;
     if (args.out_norm) {
-        norm_slots = reinterpret_cast<unsigned long long*>(after + two_pass_middle_bytes(args.B, args.H, slots, packed));
-        const size_t words = norm_slot_words(chains);
+        norm_slots = reinterpret_cast<unsigned long long*>(static_cast<char*>(workspace) + lay.norm_off);
+        const size_t words = norm_slot_words(chains * units);
         const size_t blocks = (words + 255) / 256;
         zero_words_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(norm_slots, words);
+    }
+
+    if (nseg > 1) {
+        // pass 1 over every chunk, then phase A (segment 0 and the middle
+        // segments' summaries), phase B (the initial states of segments
+        // 1 .. P-1), phase C (those segments with outputs), all on `stream`
+        ChunkArgs b = args;
+        b.chunk_lo = 0;
+        b.chunk_cnt = nck;
+        prep(b, recs, nullptr, ns, static_cast<unsigned>(slots * args.H), stream);
+        b.seg_count = nseg;
+        b.seg_len = (nck + nseg - 1) / nseg;
+        b.seg_states = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.seg_off);
+        b.seg_phase = 1;
+        scan(b, recs, ns, chains * seg_units_a(nseg), norm_slots, stream);
+        seg_combine_kernel<<<static_cast<unsigned>(chains * (DV / 16)), 256, 0, stream>>>(b.seg_states, nseg, chains);
+        b.seg_phase = 2;
+        scan(b, recs, ns, chains * seg_units_c(nseg), norm_slots, stream);
+        return hipGetLastError();
     }
 
     // the overlapped schedule for a dense batch, when it pays and the

@@ -55,7 +55,26 @@ struct ChunkArgs {
     // matrix-core path: the chunks each launch covers in every chain
     // (chunk_lo .. chunk_lo + chunk_cnt - 1; set by launch_chunk_two_pass)
     int chunk_lo, chunk_cnt;
+    // segmented sequential pass (plan_segments in kda_stage_plan.h): 0 = off;
+    // 1 = phase A, 2P - 3 units per chain: (chain, 0) = segment 0 with
+    // outputs, (chain, 2s - 1) / (chain, 2s) = segment s (1 .. P-2) from zero
+    // with the values / from the identity with zero values, no outputs; 2 =
+    // phase C, P - 1 units: (chain, s - 1) = segment s from its initial state
+    // with outputs.  seg_states holds per chain seg_state_blocks(seg_count)
+    // blocks of d_k x d_v fp32 (see there).
+    int seg_phase, seg_count, seg_len;
+    float* seg_states;
 };
+
+// Blocks of a chain's segment states: 0 = state after segment 0, 1 .. P-2 =
+// B_s, P-1 .. 2P-4 = M_s (s = 1 .. P-2), 2P-3 .. 3P-5 = initial state of
+// segment s = 1 .. P-1.
+constexpr int seg_state_blocks(int P) { return 3 * P - 4; }
+constexpr int seg_block_b(int P, int s) { return s; }
+constexpr int seg_block_m(int P, int s) { return P - 2 + s; }
+constexpr int seg_block_in(int P, int s) { return 2 * P - 4 + s; }
+constexpr int seg_units_a(int P) { return 2 * P - 3; }
+constexpr int seg_units_c(int P) { return P - 1; }
 
 // Inputs of one decode step; z/A_log/dt_bias replace g when gated.
 struct DecodeArgs {

@@ -52,6 +52,33 @@ inline int plan_stages(int nck, int chains, int cus, int* bounds)
     return n;
 }
 
+// Segmented sequential pass ("Kimi K3 の KDA ..." sections 2.3.4.2-2.3.4.5:
+// the map of a sequence is the composition of the affine maps of its
+// segments, S -> M S + B, so segments can be summarised apart and combined in
+// order).  For a dense batch with few chains the sequential pass occupies few
+// CUs; splitting every chain into P segments runs (A) segment 0 as usual and
+// every middle segment 1 .. P-2 twice in parallel -- from a zero state with
+// the values (its B) and from the identity with zero values (its M) -- then
+// (B) chains the segments' initial states S_{s+1} = M_s S_s + B_s, then (C)
+// reruns segments 1 .. P-1 from their initial states with outputs: about 2
+// segment lengths of sequential chunks instead of P.  Phase A needs
+// 2 * chains * (2P - 3) workgroups of one CU each, so
+// P = floor((cus / (2 chains) + 3) / 2), capped by kMaxSegments and by
+// segments of at least kMinSegChunks.  Returns P, or 1 when fewer than 3
+// segments fit (2 segments take as long as the plain pass).
+constexpr int kMaxSegments = 8;
+constexpr int kMinSegChunks = 32;
+constexpr int kMaxSegChains = 42;   // 3 segments of more chains never fit 256 CUs
+
+inline int plan_segments(int nck, int chains, int cus)
+{
+    if (chains <= 0 || chains > kMaxSegChains || nck < 3 * kMinSegChunks) return 1;
+    int p = (cus / (2 * chains) + 3) / 2;
+    if (p > kMaxSegments) p = kMaxSegments;
+    if (p > nck / kMinSegChunks) p = nck / kMinSegChunks;
+    return p >= 3 ? p : 1;
+}
+
 // Joining the second stream back to the calling stream at the end of a
 // staged call.  `launched` is the last stage whose sequential kernel was
 // enqueued on the second stream (-1: none), `recorded` the last stage whose

@@ -152,7 +152,7 @@ def test_size_limits(lib):
     # matrix-core path: fewer than 2^24 (chunk, head) workgroups in the chunk-parallel pass
     d = _desc(B=1, T=2 ** 30, H=1)
     need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
-    assert need == 2 ** 24 * RECORD + STATE
+    assert need == 2 ** 24 * RECORD + STATE + SEG_BLOCKS * STATE
     assert _call(lib, d, ws=FAKE, ws_bytes=need) == 1
     # decode: N*H <= 2^24 - 1 chains
     P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(7)]
@@ -161,6 +161,11 @@ def test_size_limits(lib):
 
 RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
 STATE = 128 * 128 * 4   # fp32 state of one chain, carried between the stages of a dense batch
+# a dense batch of at most 42 chains and at least 96 chunks per sequence may
+# take the segmented sequential pass: 3 * 8 - 4 state-sized blocks per chain
+# (segment 0's end state, B_s and M_s of the middle segments, the initial
+# states of segments 1 .. 7), 256-byte aligned after the rest
+SEG_BLOCKS = 3 * 8 - 4
 
 
 def test_workspace_sizes(lib):
@@ -176,6 +181,11 @@ def test_workspace_sizes(lib):
     slots = 7 + 1000 // 64
     assert size(B=1, T=1000, H=4, num_seqs=7) == max(slots * 4 * RECORD + 256, 16 * 4 * RECORD + 4 * STATE)
     assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 50 * 2 * RECORD + 256 + 3 * 2 * RECORD
+    # segment states: chains <= 42 and ceil(T / 64) >= 96 (dense only)
+    assert size(B=1, T=96 * 64, H=42) == 96 * 42 * RECORD + 42 * STATE + 42 * SEG_BLOCKS * STATE
+    assert size(B=1, T=96 * 64, H=43) == 96 * 43 * RECORD + 43 * STATE
+    assert size(B=1, T=95 * 64, H=2) == 95 * 2 * RECORD + 2 * STATE
+    assert size(B=2, T=6100, H=3) == 2 * 96 * 3 * RECORD + 6 * STATE + 6 * SEG_BLOCKS * STATE
     # validation counters come first
     assert size(B=2, T=64, H=1, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * RECORD + 2 * STATE
     # a misaligned workspace is refused before anything runs
@@ -254,6 +264,9 @@ def test_workspace_for_the_output_norm(lib):
     assert size(B=2, T=100, H=3, flags=on) == size(B=2, T=100, H=3) + 2 * 3 * words
     assert size(B=2, T=100, H=3, out_dtype=0, flags=on) == size(B=2, T=100, H=3) + 2 * 3 * words
     assert size(B=1, T=1000, H=2, num_seqs=5, flags=on) == size(B=1, T=1000, H=2, num_seqs=5) + 5 * 2 * words
+    # a batch that may take the segmented pass: words for each of the up to
+    # 2 * 8 - 3 segment units of phase A per chain, then the segment states
+    assert size(B=1, T=96 * 64, H=2, flags=on) == 96 * 2 * RECORD + 2 * STATE + 2 * 13 * words + 2 * SEG_BLOCKS * STATE
     # fp32 path: a bf16 o is staged in fp32 for the norm pass; an fp32 o is
     # normalised in place
     assert size(B=2, T=100, H=3, d_k=64, d_v=64, flags=on) == 2 * 100 * 3 * 64 * 4

@@ -1,0 +1,113 @@
+"""GPU parity of the segmented sequential pass: a dense batch with few chains
+and many chunks splits every chain into P segments, summarises the middle
+segments as affine maps S -> M S + B, chains the segments' initial states and
+reruns the segments with outputs ("Kimi K3 の KDA ..." sections 2.3.4.2-
+2.3.4.5).  The shapes here make the library take that order on a 256-CU
+MI355X (3 to 8 segments; the plan itself is checked on the CPU in
+test_stage_plan.py); o and the final state are compared with the fp64 oracle
+at the same tolerances as the plain order.  Marked ``gpu``."""
+import numpy as np
+import pytest
+
+import kda_inputs
+import oracle
+from gpu_util import check, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+EPS = 1e-5
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_fwd_amd as m
+    m.load()
+    if torch.cuda.get_device_properties(0).multi_processor_count < 256:
+        pytest.skip("segment counts below are those of a 256-CU device")
+    return m
+
+
+def _f(a):
+    return kda_inputs.bf16_to_f32(a) if a.dtype == np.uint16 else a
+
+
+def _run(kda, inp, odt, **kw):
+    import torch
+    o, s = kda.chunk_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state),
+                         dev(inp.cu_seqlens), out_dtype=odt, **kw)
+    torch.cuda.synchronize()
+    return o, s
+
+
+@pytest.mark.parametrize("shape", [(1, 8192 + 37, 2), (2, 16384, 4), (1, 6144 + 5, 1)],
+                         ids=["P4_ragged", "P8", "P3_one_chain"])
+def test_segments_plain(kda, shape):
+    """4 segments over 129 chunks (the last one partial), 8 segments over 256
+    chunks of 8 chains, 3 segments of one chain; nonzero initial state, both
+    output dtypes."""
+    import torch
+    B, T, H = shape
+    inp = kda_inputs.make_prefill(51, B, T, H, 128, 128, s0_std=0.02)
+    o_ref, s_ref = oracle.forward(inp)
+    for odt in (torch.bfloat16, torch.float32):
+        o, s = _run(kda, inp, odt)
+        check("seg_%dx%dx%d/%s" % (B, T, H, str(odt).split(".")[-1]), host64(o), o_ref, host64(s), s_ref,
+              TOL_BF16, bf16_store=(odt == torch.bfloat16))
+
+
+def test_segments_zero_initial_state_and_no_final_state(kda):
+    import torch
+    inp = kda_inputs.make_prefill(52, 1, 8192, 2, 128, 128)
+    o_ref, s_ref = oracle.forward(inp)
+    o, s = _run(kda, inp, torch.float32)
+    check("seg_s0_zero", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
+    o2, s2 = _run(kda, inp, torch.float32, output_final_state=False)
+    assert s2 is None
+    assert torch.equal(o2, o)
+
+
+def test_segments_signed(kda):
+    """Complex KDA: signed decays inside the segment maps."""
+    import torch
+    inp = kda_inputs.make_signed_prefill(53, 1, 8192 + 100, 2, 128, 128, s0_std=0.02)
+    o_ref, s_ref = oracle.forward_signed(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.g, inp.beta,
+                                         inp.init_state, inp.cu_seqlens)
+    o, s = _run(kda, inp, torch.bfloat16, signed_alpha=True)
+    check("seg_signed", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=True)
+
+
+def test_segments_conv_and_norm(kda):
+    """Short convolution (the value rows of a segment's first chunk reach back
+    into the previous segment) and the output norm (row-sum words per
+    segment unit) together."""
+    import torch
+    B, T, H = 1, 6144 + 70, 2
+    inp = kda_inputs.make_prefill(54, B, T, H, 128, 128, s0_std=0.02)
+    ws = kda_inputs.conv_weights(54, H, 128, 128)
+    cs = kda_inputs.conv_states(54, B, H, 128, 128)
+    gate = kda_inputs.make_out_gate(54, inp.v.shape)
+    w = kda_inputs.norm_weight(54, 128)
+    o_ref, s_ref, _ = oracle.forward_conv(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.g, inp.beta, ws,
+                                          tuple(_f(c) for c in cs), inp.init_state, inp.cu_seqlens)
+    y_ref = oracle.out_norm(o_ref, _f(gate).astype(np.float64), w, EPS)
+    for odt in (torch.bfloat16, torch.float32):
+        o, s = _run(kda, inp, odt, conv_weights=tuple(dev(x) for x in ws), conv_init=tuple(dev(c) for c in cs),
+                    out_gate=dev(gate), norm_weight=dev(w), norm_eps=EPS)
+        check("seg_conv_norm/%s" % str(odt).split(".")[-1], host64(o), y_ref, host64(s), s_ref, TOL_BF16,
+              bf16_store=(odt == torch.bfloat16))
+
+
+def test_segments_long_sampled_heads(kda):
+    """64K tokens x 16 heads (5 segments of about 205 chunks), oracle on two
+    sampled heads."""
+    import torch
+    inp = kda_inputs.workload("long_bf16", H=16)
+    o, s = _run(kda, inp, torch.bfloat16)
+    for h in (0, 15):
+        hs = slice(h, h + 1)
+        o_ref, s_ref = oracle.forward(inp, hs)
+        check("seg_long16/h%d" % h, host64(o[:, :, hs]), o_ref, host64(s[:, hs]), s_ref, TOL_BF16, bf16_store=True)
