@@ -67,7 +67,7 @@ inline int plan_stages(int nck, int chains, int cus, int* bounds)
 // segments of at least kMinSegChunks.  Returns P, or 1 when fewer than 3
 // segments fit (2 segments take as long as the plain pass).
 constexpr int kMaxSegments = 8;
-constexpr int kMinSegChunks = 32;
+constexpr int kMinSegChunks = 16;
 constexpr int kMaxSegChains = 42;   // 3 segments of more chains never fit 256 CUs
 
 inline int plan_segments(int nck, int chains, int cus)

@@ -161,7 +161,7 @@ def test_size_limits(lib):
 
 RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
 STATE = 128 * 128 * 4   # fp32 state of one chain, carried between the stages of a dense batch
-# a dense batch of at most 42 chains and at least 96 chunks per sequence may
+# a dense batch of at most 42 chains and at least 48 chunks per sequence may
 # take the segmented sequential pass: 3 * 8 - 4 state-sized blocks per chain
 # (segment 0's end state, B_s and M_s of the middle segments, the initial
 # states of segments 1 .. 7), 256-byte aligned after the rest
@@ -180,11 +180,14 @@ def test_workspace_sizes(lib):
     # the descriptor does not say which layout is coming, so the larger need is reported
     slots = 7 + 1000 // 64
     assert size(B=1, T=1000, H=4, num_seqs=7) == max(slots * 4 * RECORD + 256, 16 * 4 * RECORD + 4 * STATE)
-    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 50 * 2 * RECORD + 256 + 3 * 2 * RECORD
-    # segment states: chains <= 42 and ceil(T / 64) >= 96 (dense only)
+    assert size(B=1, T=64 * 40, H=2, num_seqs=3) == 40 * 2 * RECORD + 256 + 3 * 2 * RECORD
+    # here the dense reading (50 chunks of 2 chains) may take the segmented pass and needs more
+    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 50 * 2 * RECORD + 2 * STATE + 2 * SEG_BLOCKS * STATE
+    # segment states: chains <= 42 and ceil(T / 64) >= 48 (dense only)
     assert size(B=1, T=96 * 64, H=42) == 96 * 42 * RECORD + 42 * STATE + 42 * SEG_BLOCKS * STATE
     assert size(B=1, T=96 * 64, H=43) == 96 * 43 * RECORD + 43 * STATE
-    assert size(B=1, T=95 * 64, H=2) == 95 * 2 * RECORD + 2 * STATE
+    assert size(B=1, T=47 * 64, H=2) == 47 * 2 * RECORD + 2 * STATE
+    assert size(B=1, T=47 * 64 + 1, H=2) == 48 * 2 * RECORD + 2 * STATE + 2 * SEG_BLOCKS * STATE
     assert size(B=2, T=6100, H=3) == 2 * 96 * 3 * RECORD + 6 * STATE + 6 * SEG_BLOCKS * STATE
     # validation counters come first
     assert size(B=2, T=64, H=1, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * RECORD + 2 * STATE

@@ -43,12 +43,13 @@ def _run(kda, inp, odt, **kw):
     return o, s
 
 
-@pytest.mark.parametrize("shape", [(1, 8192 + 37, 2), (2, 16384, 4), (1, 6144 + 5, 1)],
-                         ids=["P4_ragged", "P8", "P3_one_chain"])
+@pytest.mark.parametrize("shape", [(1, 8192 + 37, 2), (2, 16384, 4), (1, 6144 + 5, 1), (1, 4096 + 100, 16),
+                                   (1, 3072 + 5, 32)],
+                         ids=["P8_ragged", "P8_B2", "P6_one_chain", "P4_16_chains", "P3_32_chains"])
 def test_segments_plain(kda, shape):
-    """4 segments over 129 chunks (the last one partial), 8 segments over 256
-    chunks of 8 chains, 3 segments of one chain; nonzero initial state, both
-    output dtypes."""
+    """8 segments over 129 chunks (the last one partial) and over 256 chunks
+    of 8 chains, 6 segments of one chain, 4 segments of 16 chains, 3 of 32
+    chains; nonzero initial state, both output dtypes."""
     import torch
     B, T, H = shape
     inp = kda_inputs.make_prefill(51, B, T, H, 128, 128, s0_std=0.02)
@@ -111,3 +112,49 @@ def test_segments_long_sampled_heads(kda):
         hs = slice(h, h + 1)
         o_ref, s_ref = oracle.forward(inp, hs)
         check("seg_long16/h%d" % h, host64(o[:, :, hs]), o_ref, host64(s[:, hs]), s_ref, TOL_BF16, bf16_store=True)
+
+
+def test_segments_in_a_graph(kda):
+    """A segmented call (with the output norm, so the row-sum words are
+    cleared by the fill kernel inside the graph) captured with its buffers;
+    replays after the inputs are overwritten eagerly reproduce the eager
+    results bit for bit, and the eager results equal those of context=None
+    (the segmented order does not use the context)."""
+    import torch
+    B, T, H = 1, 4096 + 33, 8
+    inps = [kda_inputs.make_prefill(55 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
+    gate = dev(kda_inputs.make_out_gate(55, (B, T, H, 128)))
+    bufs = {k: dev(getattr(inps[0], k)).clone() for k in ("q", "k", "v", "g", "beta", "init_state")}
+    o = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(B, T, H, 128, 128, flags=kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM),
+                     dtype=torch.uint8, device="cuda")
+
+    def call(context="default"):
+        kda.chunk_fwd(bufs["q"], bufs["k"], bufs["v"], bufs["g"], bufs["beta"], bufs["init_state"], out_gate=gate,
+                      norm_eps=EPS, o=o, final_state=st, workspace=ws, context=context)
+
+    refs = []
+    for inp in inps:
+        for k in bufs:
+            bufs[k].copy_(dev(getattr(inp, k)))
+        call()
+        torch.cuda.synchronize()
+        refs.append((o.clone(), st.clone()))
+        call(None)
+        torch.cuda.synchronize()
+        assert torch.equal(o, refs[-1][0]) and torch.equal(st, refs[-1][1])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        i = rep % 2
+        for k in bufs:
+            bufs[k].copy_(dev(getattr(inps[i], k)))
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, refs[i][0]), "replay %d: o" % rep
+        assert torch.equal(st, refs[i][1]), "replay %d: final state" % rep

@@ -49,8 +49,9 @@ def _run_both(kda, fwd, args, kw, B, T):
 
 # Every shape here is above the staging threshold: at least 256 chunks per
 # sequence, at least 8K (chunk, chain) pairs, and few enough chains (B*H <= 112)
-# to leave CUs idle during the sequential pass.
-@pytest.mark.parametrize("B,T,H", [(1, 16384, 32), (2, 17000, 16)])
+# to leave CUs idle during the sequential pass; more than 42 chains, below
+# which a dense batch takes the segmented sequential pass instead.
+@pytest.mark.parametrize("B,T,H", [(1, 16384, 48), (2, 17000, 24)])
 def test_staged_equals_unstaged_plain(kda, B, T, H):
     import torch
     inp = kda_inputs.make_prefill(80 + B, B, T, H, 128, 128, s0_std=0.02)
@@ -62,7 +63,7 @@ def test_staged_equals_unstaged_plain(kda, B, T, H):
 def test_staged_equals_unstaged_gated_conv_norm(kda):
     """The whole layer core: gate prologue, short convolution, output norm."""
     import torch
-    B, T, H = 1, 16500, 32
+    B, T, H = 1, 16500, 48
     gin = kda_inputs.make_gated_prefill(83, B, T, H, 128, 128, s0_std=0.02)
     ws = kda_inputs.conv_weights(83, H, 128, 128)
     gate = dev(kda_inputs.make_out_gate(83, (B, T, H, 128)))
@@ -86,7 +87,7 @@ def test_staged_equals_unstaged_gated_conv_norm(kda):
 
 def test_staged_equals_unstaged_signed(kda):
     import torch
-    B, T, H = 1, 16384, 32
+    B, T, H = 1, 16384, 48
     inp = kda_inputs.make_signed_prefill(84, B, T, H, 128, 128, s0_std=0.02)
     args = [dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state)]
     (o1, s1), (o2, s2) = _run_both(kda, kda.chunk_fwd, args, dict(signed_alpha=True), B, T)
@@ -96,7 +97,7 @@ def test_staged_equals_unstaged_signed(kda):
 def test_staged_against_oracle(kda):
     """A staged call with a ragged last chunk against the fp64 oracle."""
     import torch
-    B, T, H = 1, 16400, 32
+    B, T, H = 1, 16400, 48
     inp = kda_inputs.make_prefill(85, B, T, H, 128, 128, s0_std=0.02)
     o, s = kda.chunk_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state),
                          out_dtype=torch.float32)
@@ -113,7 +114,7 @@ def test_staged_call_in_a_graph_and_on_two_threads(kda):
     host threads on streams and contexts of their own: all equal the eager
     staged call bit for bit."""
     import torch
-    B, T, H = 1, 16384, 32
+    B, T, H = 1, 16384, 48
     inps = [kda_inputs.make_prefill(86 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
     devs = [[dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(x.init_state)] for x in inps]
     bufs = []
@@ -199,7 +200,7 @@ def test_random_staged_against_oracle(kda, i):
     r = np.random.default_rng(9000 + i)
     B = int(r.integers(1, 3))
     T = int(r.integers(16384, 24000))
-    H = int(r.integers(32, 49)) // B          # 32..48 chains: staged
+    H = int(r.integers(44, 65)) // B          # 44..64 chains: staged
     gate = str(r.choice(["k3", "slow", "sigmoid"]))
     print("case", i, dict(B=B, T=T, H=H, gate=gate), flush=True)
     inp = kda_inputs.make_prefill(9100 + i, B, T, H, 128, 128, gate=gate, s0_std=0.02)
@@ -217,7 +218,7 @@ def test_context_ownership(kda):
     order on its own stream (nothing of it enters the graph), and both the
     eager result and every replay of the graph equal the reference."""
     import torch
-    B, T, H = 1, 16384, 32
+    B, T, H = 1, 16384, 48
     inps = [kda_inputs.make_prefill(88 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
     devs = [[dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(x.init_state)] for x in inps]
     ws = kda.workspace_bytes(B, T, H, 128, 128)

@@ -79,7 +79,7 @@ def test_stream_argument_without_a_stream_context(kda):
     record workspace) belong to the side stream, and the results equal the
     default-stream ones bit for bit (a staged prefill and a decode step)."""
     import torch
-    inp = kda_inputs.make_prefill(75, 1, 16384, 32, 128, 128, s0_std=0.02)
+    inp = kda_inputs.make_prefill(75, 1, 16384, 48, 128, 128, s0_std=0.02)
     d = inputs_to_device(inp)
     args = [d[k] for k in ("q", "k", "v", "g", "beta", "init_state")]
     o1, s1 = kda.chunk_fwd(*args)

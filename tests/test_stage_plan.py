@@ -155,7 +155,7 @@ def test_segment_plan(tmp_path):
     src, exe = tmp_path / "seg.cpp", tmp_path / "seg"
     src.write_text(SEG_DRIVER)
     subprocess.run([cxx, "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
-    cases = [(nck, chains, cus) for nck in (1, 64, 95, 96, 100, 160, 200, 1024, 4096)
+    cases = [(nck, chains, cus) for nck in (1, 47, 48, 64, 95, 96, 100, 160, 200, 1024, 4096)
              for chains in (1, 2, 8, 16, 24, 32, 42, 43, 96) for cus in (80, 256, 304)]
     text = "".join("%d %d %d\n" % c for c in cases)
     out = subprocess.run([str(exe)], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
@@ -173,4 +173,4 @@ def test_segment_plan(tmp_path):
             assert not fits(p + 1, nck, chains, cus), (nck, chains, cus, p)
     got = dict(zip(cases, (int(x) for x in out[1:])))
     assert got[(1024, 16, 256)] == 5
-    assert got[(1024, 96, 256)] == 1 and got[(64, 1, 256)] == 1
+    assert got[(1024, 96, 256)] == 1 and got[(47, 1, 256)] == 1 and got[(64, 32, 256)] == 3
