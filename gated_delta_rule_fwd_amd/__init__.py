@@ -36,7 +36,7 @@ import os
 import threading
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_gated", "recurrent_step_gated", "workspace_bytes", "lib_path",
-           "Context", "default_context", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "Context", "default_context", "chunk_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "min_workspace_bytes",
            "load", "KDAError", "FLAG_QK_L2NORM", "FLAG_VALIDATE", "FLAG_FP32_PATH", "FLAG_BETA_LOGITS",
            "FLAG_SIGNED_ALPHA", "FLAG_OUT_NORM", "STATUS"]
 
@@ -101,6 +101,8 @@ def load():
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 9 + [P, S, P]
     lib.kda_chunk_fwd_workspace_bytes.restype = S
     lib.kda_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+    lib.kda_chunk_fwd_min_workspace_bytes.restype = S
+    lib.kda_chunk_fwd_min_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
     lib.kda_recurrent_step.restype = I
     lib.kda_recurrent_step.argtypes = [I, I, I, I, I, I, F, U] + [P] * 7 + [P]
     lib.kda_chunk_fwd_gated.restype = I
@@ -250,16 +252,26 @@ def _desc(B, T, H, dk, dv, num_seqs, in_dt, out_dt, scale, flags, context=None) 
 
 
 def workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True, scale=1.0, flags=FLAG_QK_L2NORM):
+    """kda_chunk_fwd_workspace_bytes: the workspace of the fastest order."""
     d = _desc(B, T, H, dk, dv, num_seqs, KDA_BF16 if in_bf16 else KDA_F32, KDA_BF16 if out_bf16 else KDA_F32,
               scale, flags)
     return int(load().kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
+
+
+def min_workspace_bytes(B, T, H, dk, dv, *, num_seqs=0, in_bf16=True, out_bf16=True, scale=1.0,
+                        flags=FLAG_QK_L2NORM):
+    """kda_chunk_fwd_min_workspace_bytes: the least workspace a call accepts
+    (the windowed order; independent of T on the matrix-core path)."""
+    d = _desc(B, T, H, dk, dv, num_seqs, KDA_BF16 if in_bf16 else KDA_F32, KDA_BF16 if out_bf16 else KDA_F32,
+              scale, flags)
+    return int(load().kda_chunk_fwd_min_workspace_bytes(ctypes.byref(d)))
 
 
 def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=None, scale=1.0,
               normalize=True, output_final_state=True, validate=False, fp32_path=False, beta_logits=False,
               signed_alpha=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
               conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None,
-              context="default"):
+              context="default", workspace_limit=None):
     """Chunkwise KDA forward (prefill).  q, k, g: [B,T,H,d_k]; v: [B,T,H,d_v];
     beta: [B,T,H]; init_state: [N,H,d_k,d_v] fp32 or None; cu_seqlens: int32
     [N+1] device tensor or None (then N = B).  With signed_alpha (Complex KDA)
@@ -270,11 +282,13 @@ def chunk_fwd(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, out_dtype=N
     conv_init / conv_final the [N,3,H*d] conv states read / written.
     context: a Context, None (no overlap of the two kernels) or "default"
     (this thread's Context for the device).  o, final_state and the
-    workspace, when not given, are allocated on ``stream``.
+    workspace, when not given, are allocated on ``stream``; the workspace
+    at most workspace_limit bytes when that is given (but never below
+    min_workspace_bytes: the windowed order, bit-identical and slower).
     Returns (o, final_state)."""
     return _chunk(q, k, v, g, None, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
                   validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha,
-                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context)
+                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context, workspace_limit)
 
 
 def chunk_fwd_noalloc(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, o, final_state=None, scale=1.0,
@@ -283,8 +297,9 @@ def chunk_fwd_noalloc(q, k, v, g, beta, init_state=None, cu_seqlens=None, *, o, 
     """kda_chunk_fwd_noalloc: chunk_fwd for callers that cannot allocate.
     Nothing is allocated here or in the library: the caller passes o (and
     final_state, if wanted); the kernels' scratch is the library's fixed
-    per-device area of NOALLOC_SCRATCH_BYTES (KDAError KDA_ERR_SCRATCH when a
-    call needs more).  Calls that overlap on one GPU race on that area.
+    per-device area of NOALLOC_SCRATCH_BYTES (a call needing more runs in the
+    windowed order; KDAError KDA_ERR_SCRATCH when even min_workspace_bytes
+    exceeds it).  Calls that overlap on one GPU race on that area.
     Returns (o, final_state)."""
     torch = _torch()
     lib = load()
@@ -320,13 +335,13 @@ def chunk_fwd_gated(q, k, v, z, A_log, beta, init_state=None, cu_seqlens=None, *
                     scale=1.0, normalize=True, output_final_state=True, validate=False, fp32_path=False,
                     beta_logits=False, out_gate=None, norm_weight=None, norm_eps=1e-5, conv_weights=None,
                     conv_init=None, conv_final=None, o=None, final_state=None, workspace=None, stream=None,
-                    context="default"):
+                    context="default", workspace_limit=None):
     """As chunk_fwd, with g = -5 sigmoid(exp(A_log[h]) (z + dt_bias[h, c]))
     computed in the kernel: z [B,T,H,d_k] in q's dtype, A_log [H] fp32,
     dt_bias [H,d_k] fp32 or None."""
     return _chunk(q, k, v, None, (z, A_log, dt_bias), beta, init_state, cu_seqlens, out_dtype, scale, normalize,
                   output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, stream, False,
-                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context)
+                  (out_gate, norm_weight, norm_eps), (conv_weights, conv_init, conv_final), context, workspace_limit)
 
 
 def _norm_args(norm, o_shape, in_dtype, dv):
@@ -366,7 +381,7 @@ def _conv_args(conv, N, H, dk, dv, dtype):
 
 def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize, output_final_state,
            validate, fp32_path, beta_logits, o, final_state, workspace, stream, signed_alpha=False, norm=None,
-           conv=None, context="default"):
+           conv=None, context="default", workspace_limit=None):
     torch = _torch()
     lib = load()
     if stream is not None and stream != torch.cuda.current_stream(q.device):
@@ -375,7 +390,7 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
         with torch.cuda.stream(stream):
             return _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, normalize,
                           output_final_state, validate, fp32_path, beta_logits, o, final_state, workspace, None,
-                          signed_alpha, norm, conv, context)
+                          signed_alpha, norm, conv, context, workspace_limit)
     if isinstance(context, str):
         if context != "default":
             raise ValueError("context must be a Context, None or 'default'")
@@ -418,6 +433,8 @@ def _chunk(q, k, v, g, gate, beta, init_state, cu_seqlens, out_dtype, scale, nor
     d = _desc(B, T, H, dk, dv, N if cu_seqlens is not None else 0, _dtype_code(q.dtype), _dtype_code(out_dtype),
               scale, flags, context)
     ws = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
+    if workspace_limit is not None and ws > workspace_limit:
+        ws = max(int(lib.kda_chunk_fwd_min_workspace_bytes(ctypes.byref(d))), int(workspace_limit))
     if ws > 0 and workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     if workspace is not None:

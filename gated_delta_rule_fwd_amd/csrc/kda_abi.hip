@@ -161,6 +161,29 @@ size_t workspace_need(const kda_chunk_desc* d, bool packed)
     return bytes + norm_staging_bytes(d);
 }
 
+// The least workspace of one call: as workspace_need, with the matrix-core
+// path's records for one chunk of every sequence (the windowed order).
+size_t workspace_min(const kda_chunk_desc* d, bool packed)
+{
+    size_t bytes = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
+    if (uses_two_pass(d))
+        bytes += kda::two_pass_min_workspace_bytes(d->B, d->T, d->H, d->num_seqs, packed,
+                                                   (d->flags & KDA_FLAG_OUT_NORM) != 0);
+    return bytes + norm_staging_bytes(d);
+}
+
+// Both queries: the descriptor does not say whether cu_seqlens will be
+// passed, so the larger of the dense and the packed figure is reported.
+size_t workspace_query(const kda_chunk_desc* d, size_t (*need)(const kda_chunk_desc*, bool))
+{
+    if (!d) return static_cast<size_t>(-1);
+    if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->num_seqs < 0) return 0;   // rejected by kda_chunk_fwd
+    if (static_cast<long long>(d->B) * d->T * d->H > kMaxTokenHeads) return 0;
+    const size_t dense = need(d, false);
+    const size_t packed = (d->B == 1 && d->num_seqs > 0) ? need(d, true) : 0;
+    return dense > packed ? dense : packed;
+}
+
 // Conv pointers: every weight present, everything 16-byte aligned.
 bool conv_ok(const kda_short_conv* conv)
 {
@@ -188,13 +211,12 @@ bool out_norm_ok(const kda_out_norm* norm, unsigned flags, const void* o)
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d)
 {
-    if (!d) return static_cast<size_t>(-1);
-    if (d->B <= 0 || d->T < 0 || d->H <= 0 || d->num_seqs < 0) return 0;   // rejected by kda_chunk_fwd
-    if (static_cast<long long>(d->B) * d->T * d->H > kMaxTokenHeads) return 0;
-    // the descriptor does not say whether cu_seqlens will be passed: cover both
-    const size_t dense = workspace_need(d, false);
-    const size_t packed = (d->B == 1 && d->num_seqs > 0) ? workspace_need(d, true) : 0;
-    return dense > packed ? dense : packed;
+    return workspace_query(d, workspace_need);
+}
+
+size_t kda_chunk_fwd_min_workspace_bytes(const kda_chunk_desc* d)
+{
+    return workspace_query(d, workspace_min);
 }
 
 }  // extern "C"
@@ -237,12 +259,10 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
         if (p && !aligned16(p)) return KDA_ERR_INVALID_ARG;
     if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_INVALID_ARG;
     if (gate && gate->A_log && !aligned4(gate->A_log)) return KDA_ERR_INVALID_ARG;
-    const size_t need = workspace_need(d, cu_seqlens != nullptr);
+    const size_t need = workspace_min(d, cu_seqlens != nullptr);
     if (ws_bytes < need || (need > 0 && !workspace)) return KDA_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return KDA_ERR_INVALID_ARG;
     if (N == 0) return KDA_OK;
-    if (uses_two_pass(d) && kda::chunk_record_slots(d->B, d->T, d->num_seqs, cu_seqlens != nullptr) * d->H >= (1LL << 24))
-        return KDA_ERR_INVALID_ARG;   // more (chunk, head) workgroups than one launch takes (about 2^30 token-heads)
 
     kda::ChunkArgs a{};
     a.B = d->B;
@@ -296,7 +316,7 @@ kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k,
     const size_t off = (d->flags & KDA_FLAG_VALIDATE) ? kValidateBytes : 0;
     if (uses_two_pass(d)) {
         // the sequential kernel applies the output norm as it stores o
-        e = kda::launch_chunk_two_pass(a, static_cast<char*>(workspace) + off, stream, d->context);
+        e = kda::launch_chunk_two_pass(a, static_cast<char*>(workspace) + off, ws_bytes - off, stream, d->context);
     } else {
         // with a norm, the fp32 path writes fp32 o (to the staging area when
         // o is bf16), then the norm pass writes o

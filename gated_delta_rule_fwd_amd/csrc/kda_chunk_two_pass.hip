@@ -157,7 +157,7 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
 
     long c0, tok0, tok1;
     int seq;
-    if (a.cu_seqlens) {
+    if (a.cu_seqlens && a.rec_stride == 0) {
         seq = slot_seq[slot];
         if (seq < 0) return;
         int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
@@ -167,14 +167,22 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         tok0 = b0;
         tok1 = b1;
     } else {
-        // this launch covers chunks chunk_lo .. chunk_lo + chunk_cnt - 1 of every sequence
-        const int nck = (a.T + C - 1) / C;
+        // this launch covers chunks chunk_lo .. chunk_lo + chunk_cnt - 1 of
+        // every sequence; the record goes to slot seq * rec_stride + (j - rec_base)
         seq = slot / a.chunk_cnt;
         const int j = a.chunk_lo + (slot - seq * a.chunk_cnt);
-        slot = seq * nck + j;
-        c0 = static_cast<long>(seq) * a.T + static_cast<long>(j) * C;
-        tok0 = static_cast<long>(seq) * a.T;
-        tok1 = tok0 + a.T;
+        slot = seq * a.rec_stride + (j - a.rec_base);
+        if (a.cu_seqlens) {
+            int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
+            b0 = min(max(b0, 0), a.T);
+            b1 = min(max(b1, b0), a.T);
+            tok0 = b0;
+            tok1 = b1;
+        } else {
+            tok0 = static_cast<long>(seq) * a.T;
+            tok1 = tok0 + a.T;
+        }
+        c0 = tok0 + static_cast<long>(j) * C;
     }
     if (c0 >= tok1) return;
     const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
@@ -852,7 +860,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     const int seq = chain / H, h = chain % H;
 
     long tok0, tok1;
-    int slot0;
+    int slot0, rbase = 0;   // the record of chunk j is slot slot0 + j - rbase
     if (a.cu_seqlens) {
         int b0 = a.cu_seqlens[seq], b1 = a.cu_seqlens[seq + 1];
         b0 = min(max(b0, 0), a.T);
@@ -863,7 +871,10 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     } else {
         tok0 = static_cast<long>(seq) * a.T;
         tok1 = tok0 + a.T;
-        slot0 = seq * ((a.T + C - 1) / C);
+    }
+    if (!a.cu_seqlens || a.rec_stride > 0) {
+        slot0 = seq * a.rec_stride;
+        rbase = a.rec_base;
     }
     const int nch = static_cast<int>((tok1 - tok0 + C - 1) / C);
     // this launch runs chunks jb .. je - 1 of the chain, from init_state (the
@@ -901,8 +912,10 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             sinit = block(seg_block_in(P, sg));
             if (sg + 1 < P) sfinal = nullptr;
         }
-        jb = min(sg * a.seg_len, nch);
-        je = min(jb + a.seg_len, nch);
+        // segments of the launch's chunk range (the whole chain, or a window)
+        const int end = je;
+        jb = min(jb + sg * a.seg_len, end);
+        je = min(jb + a.seg_len, end);
     }
     const ChunkRecord* __restrict__ rc = recs + static_cast<size_t>(h) * nslots + slot0;
     const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
@@ -945,7 +958,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     }
     // record pieces i in [i0, i1) of chunk j; piece RFULL is the partial one
     auto fetch = [&](int j, int i0, int i1) __attribute__((always_inline)) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(rc + j);
+        const u32x4* src = reinterpret_cast<const u32x4*>(rc + (j - rbase));
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
             if (i < RFULL)
@@ -1454,21 +1467,29 @@ __global__ void __launch_bounds__(256) seg_combine_kernel(float* __restrict__ se
         sx[r][c] = x;
         block(seg_block_in(P, 1))[static_cast<size_t>(r) * DV + c0 + c] = x;
     }
-    __syncthreads();
-    const int r = t >> 1, cb = 8 * (t & 1);      // row r, columns cb .. cb + 7 of the strip
-    for (int sg = 1; sg + 1 < P; ++sg) {
-        const float* M = block(seg_block_m(P, sg)) + static_cast<size_t>(r) * DV;
-        const float* Bs = block(seg_block_b(P, sg)) + static_cast<size_t>(r) * DV + c0 + cb;
-        float acc[8];
+    // thread: row r of the strip, columns cb .. cb + 7; its row of M_s and
+    // its 8 values of B_s are loaded one segment ahead (two register sets)
+    const int r = t >> 1, cb = 8 * (t & 1);
+    float4 mA[DK / 4], mB[DK / 4], bA[2], bB[2];
+    auto load = [&](int sg, float4 (&m)[DK / 4], float4 (&b)[2]) __attribute__((always_inline)) {
+        const float4* M = reinterpret_cast<const float4*>(block(seg_block_m(P, sg)) + static_cast<size_t>(r) * DV);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = Bs[e];
-        for (int k4 = 0; k4 < DK; k4 += 4) {
-            const float4 m = *reinterpret_cast<const float4*>(M + k4);
-            const float mk[4] = {m.x, m.y, m.z, m.w};
+        for (int k4 = 0; k4 < DK / 4; ++k4) m[k4] = M[k4];
+        const float4* Bs =
+            reinterpret_cast<const float4*>(block(seg_block_b(P, sg)) + static_cast<size_t>(r) * DV + c0 + cb);
+        b[0] = Bs[0];
+        b[1] = Bs[1];
+    };
+    // S_{sg+1} = M_sg S_sg + B_sg for this thread's 8 values
+    auto step = [&](int sg, const float4 (&m)[DK / 4], const float4 (&b)[2]) __attribute__((always_inline)) {
+        float acc[8] = {b[0].x, b[0].y, b[0].z, b[0].w, b[1].x, b[1].y, b[1].z, b[1].w};
+#pragma unroll
+        for (int k4 = 0; k4 < DK / 4; ++k4) {
+            const float mk[4] = {m[k4].x, m[k4].y, m[k4].z, m[k4].w};
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += mk[u] * sx[k4 + u][cb + e];
+                for (int e = 0; e < 8; ++e) acc[e] += mk[u] * sx[4 * k4 + u][cb + e];
         }
         __syncthreads();
         float* out = block(seg_block_in(P, sg + 1)) + static_cast<size_t>(r) * DV + c0 + cb;
@@ -1478,6 +1499,16 @@ __global__ void __launch_bounds__(256) seg_combine_kernel(float* __restrict__ se
             out[e] = acc[e];
         }
         __syncthreads();
+    };
+    if (P > 2) load(1, mA, bA);
+    __syncthreads();
+    for (int sg = 1; sg + 1 < P; sg += 2) {
+        if (sg + 2 < P) load(sg + 1, mB, bB);
+        step(sg, mA, bA);
+        if (sg + 2 < P) {
+            if (sg + 3 < P) load(sg + 2, mA, bA);
+            step(sg + 1, mB, bB);
+        }
     }
 }
 
@@ -1508,6 +1539,43 @@ TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bo
     return L;
 }
 
+// Workspace of the windowed order: a ring of records for `window` chunks of
+// every sequence, the state carried between windows, the output norm's
+// row-sum words.
+// With `seg`, room for the segmented order inside each window: row-sum words
+// for its segment units and the segment states.
+struct WindowLayout {
+    size_t carry_off, norm_off, seg_off, total;
+};
+
+WindowLayout window_layout(int B, int H, int num_seqs, bool packed, bool norm, long long window, bool seg = false)
+{
+    const long long chains = static_cast<long long>(packed ? num_seqs : B) * H;
+    WindowLayout L;
+    L.carry_off = static_cast<size_t>(window) * chains * kChunkRecordBytes;
+    L.norm_off = L.carry_off + static_cast<size_t>(chains) * DK * DV * sizeof(float);
+    const long long units = seg ? seg_units_a(kMaxSegments) : 1;
+    L.seg_off = L.norm_off + (norm ? norm_slot_words(chains * units) * sizeof(unsigned long long) : 0);
+    L.seg_off = (L.seg_off + 255) / 256 * 256;
+    L.total = L.seg_off + (seg ? static_cast<size_t>(chains) * seg_state_blocks(kMaxSegments) * DK * DV *
+                                     sizeof(float)
+                               : 0);
+    return L;
+}
+
+// Largest window (chunks of every sequence per launch) that fits `bytes`,
+// at most `nck` and below 2^24 pass-1 workgroups per launch; 0: none fits.
+long long window_chunks(int B, int H, int num_seqs, bool packed, bool norm, int nck, size_t bytes, bool seg = false)
+{
+    const long long chains = static_cast<long long>(packed ? num_seqs : B) * H;
+    const size_t fixed = window_layout(B, H, num_seqs, packed, norm, 0, seg).total;
+    if (chains <= 0 || bytes < fixed) return 0;
+    long long w = static_cast<long long>((bytes - fixed) / (static_cast<size_t>(chains) * kChunkRecordBytes));
+    if (w > nck) w = nck;
+    const long long cap = ((1LL << 24) - 1) / chains;
+    return w < cap ? w : cap;
+}
+
 }  // namespace
 
 long long chunk_record_slots(int B, int T, int num_seqs, bool packed)
@@ -1519,6 +1587,13 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed)
 size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm)
 {
     return two_pass_layout(B, T, H, num_seqs, packed, norm).total;
+}
+
+size_t two_pass_min_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm)
+{
+    const size_t one = window_layout(B, H, num_seqs, packed, norm, T > 0 ? 1 : 0).total;
+    const size_t full = two_pass_workspace_bytes(B, T, H, num_seqs, packed, norm);
+    return one < full ? one : full;
 }
 
 namespace {
@@ -1598,28 +1673,112 @@ void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, un
     }
 }
 
+// The segmented order over the chunk range b.chunk_lo .. + b.chunk_cnt of
+// every chain, whose records are in place: phase A (segment 0 from
+// b.init_state with outputs, the middle segments' summaries), phase B (the
+// initial states of segments 1 .. P-1), phase C (those segments with
+// outputs; the last one ends in b.final_state), all on `stream`.
+void run_segments(ChunkArgs b, const ChunkRecord* recs, int slots, int chains, int nseg, float* seg_states,
+                  unsigned long long* norm_slots, hipStream_t stream)
+{
+    b.seg_count = nseg;
+    b.seg_len = (b.chunk_cnt + nseg - 1) / nseg;
+    b.seg_states = seg_states;
+    b.seg_phase = 1;
+    scan(b, recs, slots, chains * seg_units_a(nseg), norm_slots, stream);
+    seg_combine_kernel<<<static_cast<unsigned>(chains * (DV / 16)), 256, 0, stream>>>(seg_states, nseg, chains);
+    b.seg_phase = 2;
+    scan(b, recs, slots, chains * seg_units_c(nseg), norm_slots, stream);
+}
+
+// Segments for a dense range of `nck` chunks per chain on the device of `stream`.
+int segments_for(int nck, int chains, hipStream_t stream)
+{
+    if (plan_segments(nck, chains, 1 << 20) <= 1) return 1;
+    int dev = 0, cus = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 1;
+    return plan_segments(nck, chains, cus);
+}
+
+// The windowed order, for a workspace below the full record area: windows of
+// `w` chunks of every sequence, one after the other on `stream` -- pass 1
+// writes the window's records into a ring of w chunks per sequence, pass 2
+// runs the window's chunks from the state the previous window left (the
+// chain's initial state for the first, a 64 KB-per-chain area in between,
+// the final state after the last).  The state goes through memory in fp32,
+// so the result is bit-identical to the unwindowed two-pass order; memory
+// use is independent of T.
+hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_bytes, hipStream_t stream)
+{
+    const bool packed = args.cu_seqlens != nullptr;
+    const int nseq = packed ? args.num_seqs : args.B;
+    const int chains = nseq * args.H;
+    const int nck = (args.T + C - 1) / C;   // chunks of the longest possible sequence
+    const bool norm = args.out_norm != 0;
+    // a dense batch of few chains keeps the segmented order inside windows
+    // that hold enough chunks for it (and the segment area next to them)
+    long long w = 0;
+    bool seg = false;
+    if (!packed) {
+        w = window_chunks(args.B, args.H, args.num_seqs, packed, norm, nck, ws_bytes, true);
+        seg = w > 0 && segments_for(static_cast<int>(w), chains, stream) > 1;
+    }
+    if (!seg) w = window_chunks(args.B, args.H, args.num_seqs, packed, norm, nck, ws_bytes);
+    if (w < 1) return hipErrorInvalidValue;   // below two_pass_min_workspace_bytes
+    const WindowLayout lay = window_layout(args.B, args.H, args.num_seqs, packed, norm, w, seg);
+    char* base = static_cast<char*>(workspace);
+    ChunkRecord* recs = reinterpret_cast<ChunkRecord*>(base);
+    float* carried = reinterpret_cast<float*>(base + lay.carry_off);
+    float* seg_states = seg ? reinterpret_cast<float*>(base + lay.seg_off) : nullptr;
+    const int ring = static_cast<int>(nseq * w);   // record slots per head
+    unsigned long long* norm_slots = nullptr;
+    if (norm) {
+        norm_slots = reinterpret_cast<unsigned long long*>(base + lay.norm_off);
+        const size_t words = norm_slot_words(static_cast<long long>(chains) * (seg ? seg_units_a(kMaxSegments) : 1));
+        const size_t blocks = (words + 255) / 256;
+        zero_words_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(norm_slots, words);
+    }
+    for (int lo = 0; lo < nck; lo += static_cast<int>(w)) {
+        ChunkArgs b = args;
+        b.chunk_lo = lo;
+        b.chunk_cnt = static_cast<int>(nck - lo < w ? nck - lo : w);
+        b.rec_base = lo;
+        b.rec_stride = static_cast<int>(w);
+        b.init_state = lo == 0 ? args.init_state : carried;
+        b.final_state = lo + b.chunk_cnt >= nck ? args.final_state : carried;
+        prep(b, recs, nullptr, ring, static_cast<unsigned>(nseq * b.chunk_cnt * args.H), stream);
+        const int nseg = seg ? segments_for(b.chunk_cnt, chains, stream) : 1;
+        if (nseg > 1)
+            run_segments(b, recs, ring, chains, nseg, seg_states, norm_slots, stream);
+        else
+            scan(b, recs, ring, chains, norm_slots, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
-hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStream_t stream, kda_context_s* ctx)
+hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t ws_bytes, hipStream_t stream,
+                                 kda_context_s* ctx)
 {
     const bool packed = args.cu_seqlens != nullptr;
     const int chains = (packed ? args.num_seqs : args.B) * args.H;
     if (chains == 0) return hipSuccess;
     const long long slots = chunk_record_slots(args.B, args.T, args.num_seqs, packed);
+    const TwoPassLayout lay = two_pass_layout(args.B, args.T, args.H, args.num_seqs, packed, args.out_norm != 0);
+    if (args.T > 0 && (ws_bytes < lay.total || slots * args.H >= (1LL << 24)))
+        return launch_windowed(args, workspace, ws_bytes, stream);
     const int ns = static_cast<int>(slots);
     ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
     const int nck = packed ? 0 : (args.T + C - 1) / C;
-    const TwoPassLayout lay = two_pass_layout(args.B, args.T, args.H, args.num_seqs, packed, args.out_norm != 0);
 
     // the segmented order for a dense batch with few chains
-    int nseg = 1;
-    if (!packed && plan_segments(nck, chains, 1 << 20) > 1) {
-        int dev = 0, cus = 0;
-        if (hipStreamGetDevice(stream, &dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-            nseg = plan_segments(nck, chains, cus);
-    }
+    const int nseg = packed ? 1 : segments_for(nck, chains, stream);
     const long long units = nseg > 1 ? seg_units_a(nseg) : 1;
 
     // output norm: the row-sum words the two value slices of a chain (or of a
@@ -1640,15 +1799,11 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
         ChunkArgs b = args;
         b.chunk_lo = 0;
         b.chunk_cnt = nck;
+        b.rec_stride = nck;
+        b.rec_base = 0;
         prep(b, recs, nullptr, ns, static_cast<unsigned>(slots * args.H), stream);
-        b.seg_count = nseg;
-        b.seg_len = (nck + nseg - 1) / nseg;
-        b.seg_states = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.seg_off);
-        b.seg_phase = 1;
-        scan(b, recs, ns, chains * seg_units_a(nseg), norm_slots, stream);
-        seg_combine_kernel<<<static_cast<unsigned>(chains * (DV / 16)), 256, 0, stream>>>(b.seg_states, nseg, chains);
-        b.seg_phase = 2;
-        scan(b, recs, ns, chains * seg_units_c(nseg), norm_slots, stream);
+        run_segments(b, recs, ns, chains, nseg,
+                     reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.seg_off), norm_slots, stream);
         return hipGetLastError();
     }
 
@@ -1669,6 +1824,10 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     }
 
     ChunkArgs a = args;
+    if (!packed) {
+        a.rec_stride = nck;
+        a.rec_base = 0;
+    }
     if (stages == 1) {
         int* map = nullptr;
         if (slots > 0) {
@@ -1691,7 +1850,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, hipStre
     // the state between stages goes through the workspace
     float* carried = reinterpret_cast<float*>(after);
     auto stage_args = [&](int s) {
-        ChunkArgs b = args;
+        ChunkArgs b = a;
         b.chunk_lo = bounds[s];
         b.chunk_cnt = bounds[s + 1] - bounds[s];
         b.init_state = s == 0 ? args.init_state : carried;

@@ -55,6 +55,11 @@ struct ChunkArgs {
     // matrix-core path: the chunks each launch covers in every chain
     // (chunk_lo .. chunk_lo + chunk_cnt - 1; set by launch_chunk_two_pass)
     int chunk_lo, chunk_cnt;
+    // record of chunk j of sequence n: slot n * rec_stride + (j - rec_base)
+    // (dense batches always; packed sequences when rec_stride > 0, the
+    // windowed order); packed sequences with rec_stride == 0 start at slot
+    // n + cu_seqlens[n]/64 and pass 1 finds its sequence in the slot map
+    int rec_stride, rec_base;
     // segmented sequential pass (plan_segments in kda_stage_plan.h): 0 = off;
     // 1 = phase A, 2P - 3 units per chain: (chain, 0) = segment 0 with
     // outputs, (chain, 2s - 1) / (chain, 2s) = segment s (1 .. P-2) from zero
@@ -134,14 +139,24 @@ long long chunk_record_slots(int B, int T, int num_seqs, bool packed);
 // slices of a chain exchange per-row sums of o^2 through 2 KB per chain after
 // that, and o is normalised as it is stored.
 size_t two_pass_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm);
+// The least workspace the path runs with: records for one chunk of every
+// sequence, the carried state and the norm's words (the windowed order;
+// independent of T).  Any size from this up works: below
+// two_pass_workspace_bytes() the chunks go in windows as large as fit.
+size_t two_pass_min_workspace_bytes(int B, int T, int H, int num_seqs, bool packed, bool norm);
 // With a context (nullable), a dense batch whose sequential pass leaves CUs
 // idle runs in stages: pass 1 of stage s+1 on the idle CUs while pass 2 of
 // stage s runs, pass 2 on the context's stream, joined to `stream` before
-// returning.  Otherwise (no context, a context of another device or one whose
-// stream belongs to another graph capture, packed sequences, short chains,
-// many chains) pass 1 then pass 2 on `stream`.  Both orders give the same
-// bits.
-hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, hipStream_t stream, kda_context_s* ctx);
+// returning.  A dense batch of at most 42 chains with at least 48 chunks per
+// sequence takes the segmented order instead (plan_segments).  Otherwise (no
+// context, a context of another device or one whose stream belongs to
+// another graph capture, packed sequences, short chains, many chains) pass 1
+// then pass 2 on `stream`.  With ws_bytes below two_pass_workspace_bytes()
+// (or more (chunk, head) records than one launch takes) the windowed order
+// runs instead, on `stream`.  The staged, windowed and plain orders give the
+// same bits; the segmented order differs from them by rounding.
+hipError_t launch_chunk_two_pass(const ChunkArgs& a, void* workspace, size_t ws_bytes, hipStream_t stream,
+                                 kda_context_s* ctx);
 
 // Conv states after a prefill: the last 3 raw inputs of every sequence for
 // q, k, v (rows from a.conv_init where a sequence is shorter than 3); each

@@ -64,12 +64,13 @@ typedef enum kda_status {
     KDA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, misaligned pointer, bad layout,
                                  size above the limits below */
     KDA_ERR_UNSUPPORTED = 2,  /* head dims other than 64/128, unknown dtype or flag */
-    KDA_ERR_WORKSPACE = 3,    /* workspace smaller than kda_chunk_fwd_workspace_bytes() */
+    KDA_ERR_WORKSPACE = 3,    /* workspace smaller than kda_chunk_fwd_min_workspace_bytes() */
     KDA_ERR_RANGE = 4,        /* only with KDA_FLAG_VALIDATE: g outside [-5, 0], beta outside
                                  [0, 1], or cu_seqlens not a monotone partition of [0, T] */
     KDA_ERR_HIP = 5,          /* a HIP launch/runtime error; see kda_last_hip_error() */
     KDA_ERR_SCRATCH = 6       /* kda_chunk_fwd_noalloc only: the call needs more device scratch
-                                 than its fixed area of KDA_NOALLOC_SCRATCH_BYTES */
+                                 than its fixed area of KDA_NOALLOC_SCRATCH_BYTES, even in
+                                 the windowed order */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -104,18 +105,20 @@ typedef enum kda_dtype {
 /* The call carries an output norm (kda_out_norm below).  Must be set exactly
  * when a norm is passed to kda_chunk_fwd_fused / kda_recurrent_step_fused.
  * It is part of the descriptor so that kda_chunk_fwd_workspace_bytes() can
- * size the fp32 staging of o that a prefill with a bf16 o needs: the norm
- * runs as a second kernel there, and it must see o before it is rounded. */
+ * size what the norm needs: on the matrix-core path 8 bytes per (row of a
+ * 64-token chunk, value slice, slot) for the row sums the two value slices
+ * of a chain exchange; on the fp32 path with a bf16 o the fp32 staging of o,
+ * since the norm runs as a second kernel there and must see o before it is
+ * rounded. */
 #define KDA_FLAG_OUT_NORM 0x20u
 
 
 /* Size limits (a larger call returns KDA_ERR_INVALID_ARG before any launch):
- * prefill B*T*H <= 2^31 token-heads, N*H <= 2^22 chains, and on the
- * matrix-core path fewer than 2^24 (64-token chunk, head) pairs; decode N*H
+ * prefill B*T*H <= 2^31 token-heads and N*H <= 2^22 chains; decode N*H
  * <= 2^24 - 1 chains.  They come from the 2^32 work items one grid dimension
- * takes; every device index is 64-bit.  On one 288 GB device memory runs out
- * first (a matrix-core prefill needs about 2.7 KB per token-head with its
- * workspace). */
+ * takes; every device index is 64-bit.  A matrix-core prefill with 2^24 or
+ * more (64-token chunk, head) pairs runs in the windowed order (see
+ * kda_chunk_fwd_min_workspace_bytes), whatever its workspace. */
 
 /*
  * Caller-owned objects with which a long dense prefill overlaps its two
@@ -151,17 +154,34 @@ typedef struct kda_chunk_desc {
                             runs them one after the other on `stream` */
 } kda_chunk_desc;
 
-/* Bytes of device workspace the chunkwise entry points need for this
- * descriptor: the matrix-core path (bf16 inputs, d_k = d_v = 128, no
- * KDA_FLAG_FP32_PATH) keeps one 74,240-byte record per (64-token chunk,
- * head) there, plus, for a dense batch, the fp32 state of every (b, h) chain
- * (64 KB each) carried between the overlapped stages, or, for packed
- * sequences, one int32 per chunk slot; the fp32 path needs none;
- * KDA_FLAG_OUT_NORM with a bf16 o adds
- * B*T*H*d_v fp32 values; KDA_FLAG_VALIDATE adds 256 bytes.  When num_seqs > 0 and B == 1 the figure covers both the dense and
- * the packed (cu_seqlens) layout.  Returns 0 for a descriptor the entry
- * points reject and (size_t)-1 for a null descriptor. */
+/* Bytes of device workspace with which the chunkwise entry points run this
+ * descriptor in their fastest order.  The matrix-core path (bf16 inputs,
+ * d_k = d_v = 128, no KDA_FLAG_FP32_PATH) keeps one 74,240-byte record per
+ * (64-token chunk, head) there, plus, for a dense batch, the fp32 state of
+ * every (b, h) chain (64 KB each) carried between launches, or, for packed
+ * sequences, one int32 per chunk slot (256-byte rounded); KDA_FLAG_OUT_NORM
+ * adds 4 KB per chain of row-sum words; a dense batch of at most 42 chains
+ * and at least 48 chunks per sequence, which may take the segmented order,
+ * adds 20 state-sized blocks (1.25 MB) per chain and row-sum words for 13
+ * segment units per chain.  The fp32 path needs none, except with
+ * KDA_FLAG_OUT_NORM and a bf16 o: B*T*H*d_v fp32 values.  KDA_FLAG_VALIDATE
+ * adds 256 bytes in front.  When num_seqs > 0 and B == 1 the figure covers
+ * both the dense and the packed (cu_seqlens) layout.  Returns 0 for a
+ * descriptor the entry points reject and (size_t)-1 for a null
+ * descriptor. */
 KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
+
+/* The least workspace the chunkwise entry points accept for this descriptor
+ * (constant-memory long context).  On the matrix-core path: records for one
+ * 64-token chunk of every sequence, the carried states and the norm's words,
+ * whatever T is.  A workspace from this size up to
+ * kda_chunk_fwd_workspace_bytes() runs the windowed order: windows of as
+ * many chunks of every sequence as the records of the workspace hold, pass 1
+ * then pass 2 per window on `stream`, the state carried between windows in
+ * fp32 ("Kimi K3 模型结构（2）", Q&A on the chunkwise algorithm: one state
+ * per chain, updated once per chunk), bit-identical to the unwindowed
+ * two-pass order.  Same return convention as kda_chunk_fwd_workspace_bytes. */
+KDA_API size_t kda_chunk_fwd_min_workspace_bytes(const kda_chunk_desc* desc);
 
 /*
  * Chunkwise forward for training/prefill ("Kimi K3 模型结构（2）", Q&A on the
@@ -170,16 +190,29 @@ KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
  * partial; a zero-length sequence passes its initial state through unchanged.
  *
  * The matrix-core path runs a chunk-parallel kernel and then a sequential
- * one.  When desc->context is given and usable (created on the device of
- * `stream`, its stream not part of a graph capture other than the one
- * `stream` belongs to), a dense batch of at least 256 chunks per sequence
- * whose sequential kernel leaves CUs idle is split into up to six stages:
- * the chunk-parallel kernel of stage s+1 runs on the idle CUs while the
- * sequential kernel of stage s runs on the context's stream.  The outputs
- * are bit-identical to the unstaged order.  If an event cannot be recorded
- * after a stage was enqueued on the context's stream, that stream is
- * synchronised on the host before the error returns (outside a capture), so
- * no kernel of the call outlives it unordered.
+ * one, in one of four orders, picked on the host from the shapes, the
+ * workspace size and the context:
+ *  - segmented: a dense batch of at most 42 (b, h) chains and at least 48
+ *    chunks per sequence, with the full workspace.  Each chain is cut into
+ *    P segments (3 <= P <= 8, as many as the device's CUs hold); the middle
+ *    segments are summarised as affine maps S -> M S + B and combined
+ *    ("Kimi K3 の KDA ..." sections 2.3.4.2-2.3.4.5), then the later
+ *    segments run again from their true initial states.  All on `stream`;
+ *    the results differ from the other orders by rounding only.
+ *  - staged: when desc->context is given and usable (created on the device
+ *    of `stream`, its stream not part of a graph capture other than the one
+ *    `stream` belongs to), a dense batch of more chains, at least 256 chunks
+ *    per sequence, whose sequential kernel leaves CUs idle, is split into up
+ *    to six stages: the chunk-parallel kernel of stage s+1 runs on the idle
+ *    CUs while the sequential kernel of stage s runs on the context's
+ *    stream.  If an event cannot be recorded after a stage was enqueued on
+ *    the context's stream, that stream is synchronised on the host before
+ *    the error returns (outside a capture), so no kernel of the call
+ *    outlives it unordered.
+ *  - windowed: a workspace below kda_chunk_fwd_workspace_bytes() (see
+ *    kda_chunk_fwd_min_workspace_bytes), on `stream`.
+ *  - plain: otherwise, the two kernels one after the other on `stream`.
+ * The staged, windowed and plain orders give bit-identical results.
  *
  *   q, k        [B, T, H, d_k]  in_dtype
  *   v           [B, T, H, d_v]  in_dtype
@@ -196,7 +229,9 @@ KDA_API size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
  *   o           [B, T, H, d_v]  out_dtype, fully overwritten; must not alias
  *               any input
  *   final_state [N, H, d_k, d_v] fp32, nullable
- *   workspace   device buffer of ws_bytes >= kda_chunk_fwd_workspace_bytes()
+ *   workspace   device buffer of ws_bytes >= kda_chunk_fwd_min_workspace_bytes()
+ *               (the fastest order needs kda_chunk_fwd_workspace_bytes());
+ *               16-byte aligned; its contents need not be initialised
  */
 KDA_API kda_status kda_chunk_fwd(const kda_chunk_desc* desc,
                          const void* q, const void* k, const void* v,
@@ -367,13 +402,14 @@ KDA_API kda_status kda_recurrent_step_fused(int N, int H, int d_k, int d_v,
  * kda_chunk_fwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation).
  * Arguments, layouts, flags and errors are those of kda_chunk_fwd, without
- * the workspace: the scratch the kernels need (kda_chunk_fwd_workspace_bytes
- * of the descriptor) lives in a fixed device array of KDA_NOALLOC_SCRATCH_BYTES
- * that the library defines; each GPU it runs on holds one copy until the
- * process ends.  Its address is looked up once per device, on the first call
- * that runs there.  The call allocates nothing (no hipMalloc, no allocating
- * library routine); a call that needs more scratch than the array holds
- * returns KDA_ERR_SCRATCH before any launch, and KDA_FLAG_VALIDATE (which
+ * the workspace: the scratch the kernels need lives in a fixed device array
+ * of KDA_NOALLOC_SCRATCH_BYTES that the library defines; each GPU it runs on
+ * holds one copy until the process ends.  Its address is looked up once per
+ * device, on the first call that runs there.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine).  A call whose
+ * kda_chunk_fwd_workspace_bytes exceeds the array runs in the windowed order
+ * within it; one whose kda_chunk_fwd_min_workspace_bytes exceeds it returns
+ * KDA_ERR_SCRATCH before any launch, and KDA_FLAG_VALIDATE (which
  * reads its counters back to the host) is KDA_ERR_UNSUPPORTED.  Every call
  * on one GPU uses that GPU's array and leaves its contents behind: calls
  * that overlap on one GPU (on different streams, or from different threads,

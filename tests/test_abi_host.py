@@ -31,7 +31,8 @@ def test_header_declares_expected_entry_points():
     assert _declared() == sorted(["kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_fused",
                                   "kda_chunk_fwd_workspace_bytes", "kda_recurrent_step", "kda_recurrent_step_gated",
                                   "kda_recurrent_step_fused", "kda_status_str", "kda_last_hip_error", "kda_version",
-                                  "kda_context_create", "kda_context_destroy", "kda_chunk_fwd_noalloc"])
+                                  "kda_context_create", "kda_context_destroy", "kda_chunk_fwd_noalloc",
+                                  "kda_chunk_fwd_min_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -149,11 +150,12 @@ def test_size_limits(lib):
     assert _call(lib, _desc(B=1, T=2 ** 29, H=5, **f32)) == 1
     assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(B=1, T=2 ** 29, H=5))) == 0
     assert _call(lib, _desc(B=4096, T=1, H=1025, **f32)) == 1
-    # matrix-core path: fewer than 2^24 (chunk, head) workgroups in the chunk-parallel pass
+    # matrix-core path: 2^24 or more (chunk, head) records run in windows,
+    # so such a call is not refused and its least workspace stays small
     d = _desc(B=1, T=2 ** 30, H=1)
-    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
-    assert need == 2 ** 24 * RECORD + STATE + SEG_BLOCKS * STATE
-    assert _call(lib, d, ws=FAKE, ws_bytes=need) == 1
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)) == 2 ** 24 * RECORD + STATE + SEG_BLOCKS * STATE
+    assert lib.kda_chunk_fwd_min_workspace_bytes(ctypes.byref(d)) == RECORD + STATE
+    assert _call(lib, d, ws=FAKE, ws_bytes=RECORD + STATE - 16) == 3
     # decode: N*H <= 2^24 - 1 chains
     P = [ctypes.c_void_p(FAKE + 0x100000 * i) for i in range(7)]
     assert lib.kda_recurrent_step(2 ** 12, 2 ** 12, 128, 128, 1, 1, 1.0, kda.FLAG_QK_L2NORM, *P, None) == 1
@@ -194,6 +196,34 @@ def test_workspace_sizes(lib):
     # a misaligned workspace is refused before anything runs
     d = _desc(B=1, T=64, H=1)
     assert _call(lib, d, ws=FAKE + 8, ws_bytes=RECORD + STATE) == 1
+
+
+def test_min_workspace_sizes(lib):
+    """The least workspace: records for one chunk of every sequence, the
+    carried states, the norm's words; never above the full figure; the
+    same for every T on the matrix-core path."""
+    mn = lambda **kw: lib.kda_chunk_fwd_min_workspace_bytes(ctypes.byref(_desc(**kw)))
+    full = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(**kw)))
+    assert lib.kda_chunk_fwd_min_workspace_bytes(None) == 2 ** 64 - 1
+    assert mn(B=3, T=130, H=5) == 3 * 5 * RECORD + 15 * STATE
+    for T in (1000, 10 ** 5, 10 ** 7):
+        assert mn(B=2, T=T, H=4) == 2 * 4 * (RECORD + STATE)
+    assert mn(B=2, T=10 ** 5, H=4, flags=kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM) == 2 * 4 * (RECORD + STATE + 4096)
+    assert mn(B=2, T=10 ** 5, H=4, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * 4 * (RECORD + STATE)
+    # one chunk per sequence: nothing to window
+    assert mn(B=3, T=64, H=5) == full(B=3, T=64, H=5)
+    assert mn(B=3, T=0, H=5) == full(B=3, T=0, H=5)
+    # packed: one chunk of each of the num_seqs sequences and their carried states;
+    # the larger of the dense and the packed reading is reported
+    assert mn(B=1, T=100000, H=4, num_seqs=7) == 7 * 4 * (RECORD + STATE)
+    # fp32 path: nothing, or the fp32 staging of o for the norm (not windowed)
+    assert mn(B=2, T=100, H=3, d_k=64, d_v=64) == 0
+    assert mn(B=2, T=100, H=3, d_k=64, d_v=64, flags=kda.FLAG_QK_L2NORM | kda.FLAG_OUT_NORM) == 2 * 100 * 3 * 64 * 4
+    for kw in (dict(B=3, T=130, H=5), dict(B=1, T=5000, H=2), dict(B=1, T=1000, H=4, num_seqs=7)):
+        assert mn(**kw) <= full(**kw)
+    # below the least size the call is refused before anything runs
+    d = _desc(B=2, T=10 ** 5, H=4)
+    assert _call(lib, d, ws=FAKE, ws_bytes=2 * 4 * (RECORD + STATE) - 16) == 3
 
 
 def test_chunk_fwd_empty_batch_is_a_no_op(lib):

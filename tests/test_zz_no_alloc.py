@@ -1,8 +1,9 @@
 """kda_chunk_fwd_noalloc through the C ABI: two calls in a row (the second
 smaller, on the scratch the first left behind) each equal kda_chunk_fwd on
-the same inputs bit for bit, against the fp64 oracle too; a call that needs
-more scratch than the fixed area is refused before any launch.  Named to be
-collected last.  Marked ``gpu``."""
+the same inputs bit for bit, against the fp64 oracle too; a call whose full
+workspace exceeds the fixed area runs in the windowed order there and still
+equals kda_chunk_fwd bit for bit; a call whose least workspace exceeds it is
+refused before any launch.  Named to be collected last.  Marked ``gpu``."""
 import numpy as np
 import pytest
 
@@ -50,10 +51,20 @@ def test_noalloc_matches_chunk_fwd_on_two_calls(kda):
         check("noalloc/" + name, host64(o), ro, host64(s), rs, 2e-2, bf16_store=True)
 
 
-def test_noalloc_refuses_a_call_beyond_the_scratch(kda):
+def test_noalloc_windowed_beyond_the_scratch(kda):
     import torch
     B, T, H = 1, 4096, 64                                                               # 4096 records: 304 MB
     assert kda.workspace_bytes(B, T, H, 128, 128) > kda.NOALLOC_SCRATCH_BYTES
+    assert kda.min_workspace_bytes(B, T, H, 128, 128) <= kda.NOALLOC_SCRATCH_BYTES
+    inp = kda_inputs.make_prefill(63, B, T, H, 128, 128, s0_std=0.02)
+    (o_ref, s_ref), (o, s) = _both(kda, inp)
+    assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
+
+
+def test_noalloc_refuses_a_call_beyond_the_scratch(kda):
+    import torch
+    B, T, H = 1, 64, 512                                # one chunk of 512 chains: 71.6 MB at least
+    assert kda.min_workspace_bytes(B, T, H, 128, 128) > kda.NOALLOC_SCRATCH_BYTES
     q = torch.zeros((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
     g = torch.zeros((B, T, H, 128), dtype=torch.float32, device="cuda")
     beta = torch.zeros((B, T, H), dtype=torch.float32, device="cuda")
