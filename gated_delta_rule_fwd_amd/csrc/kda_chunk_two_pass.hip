@@ -1702,6 +1702,82 @@ int segments_for(int nck, int chains, hipStream_t stream)
     return plan_segments(nck, chains, cus);
 }
 
+// The overlapped order over stages s = 0 .. n-1 (chunks lo(s) .. lo(s+1)-1
+// of every sequence, records at recs_of(s) + h * slots + slot, slots
+// addressed with a.rec_stride / a.rec_base as set here or by the caller):
+// pass 1 on `stream`, pass 2 on the context's stream, pass 1 of stage s+1
+// after pass 2 of stage s-1 (so a ring of two record areas suffices) and
+// behind a short gap, so that pass 2 of stage s takes its CUs first.  The
+// calling stream joins the context's stream before this returns.  Events
+// are reused modulo kMaxStages: each wait is enqueued before its event is
+// recorded again.
+template <typename Lo, typename RecsOf>
+hipError_t run_stages(const ChunkArgs& a, int stages, Lo lo, RecsOf recs_of, int slots, float* carried,
+                      unsigned long long* norm_slots, kda_context_s* ctx, hipStream_t stream, bool capturing,
+                      bool ring = false)
+{
+    const int chains = a.B * a.H;
+    auto stage_args = [&](int k) {
+        ChunkArgs b = a;
+        b.chunk_lo = lo(k);
+        b.chunk_cnt = lo(k + 1) - lo(k);
+        if (ring) b.rec_base = b.chunk_lo;
+        b.init_state = k == 0 ? a.init_state : carried;
+        b.final_state = k + 1 == stages ? a.final_state : carried;
+        return b;
+    };
+    auto ev1 = [&](int k) { return ctx->p1[k % kMaxStages]; };
+    auto ev2 = [&](int k) { return ctx->p2[k % kMaxStages]; };
+    hipError_t e = hipSuccess;
+    auto ok = [&](hipError_t r) { if (e == hipSuccess && r != hipSuccess) e = r; return e == hipSuccess; };
+    int launched = -1;   // last stage whose pass 2 is enqueued on the context's stream
+    int recorded = -1;   // last stage whose pass-2 completion event is recorded behind it
+    {
+        const ChunkArgs b = stage_args(0);
+        prep(b, recs_of(0), nullptr, slots, static_cast<unsigned>(a.B * b.chunk_cnt * a.H), stream);
+    }
+    ok(hipGetLastError());
+    ok(hipEventRecord(ev1(0), stream));
+    for (int k = 0; k < stages && e == hipSuccess; ++k) {
+        if (!ok(hipStreamWaitEvent(ctx->side, ev1(k), 0))) break;
+        scan(stage_args(k), recs_of(k), slots, chains, norm_slots, ctx->side);
+        const hipError_t lr = hipGetLastError();
+        if (lr == hipSuccess) launched = k;
+        if (!ok(lr)) break;
+        if (ok(hipEventRecord(ev2(k), ctx->side))) recorded = k;
+        if (k + 1 < stages && e == hipSuccess) {
+            // pass 1 of stage k+1 starts with pass 2 of stage k, behind a short gap
+            if (k >= 1) ok(hipStreamWaitEvent(stream, ev2(k - 1), 0));
+            stage_gap_kernel<<<1, 64, 0, stream>>>(6);
+            const ChunkArgs b = stage_args(k + 1);
+            prep(b, recs_of(k + 1), nullptr, slots, static_cast<unsigned>(a.B * b.chunk_cnt * a.H), stream);
+            ok(hipGetLastError());
+            ok(hipEventRecord(ev1(k + 1), stream));
+        }
+    }
+    // join: later work on the caller's stream sees every stage, after an
+    // error too, so that nothing on the second stream escapes the caller's
+    // stream order
+    const StageJoin jn = plan_join(launched, recorded, capturing);
+    if (jn.wait_stage >= 0) ok(hipStreamWaitEvent(stream, ev2(jn.wait_stage), 0));
+    if (jn.sync_side) ok(hipStreamSynchronize(ctx->side));
+    return e;
+}
+
+// Whether a dense batch may overlap its two passes on the context's stream,
+// and whether `stream` is being captured.
+bool overlap_usable(kda_context_s* ctx, hipStream_t stream, int* cus, bool* capturing)
+{
+    int dev = 0;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (!ctx || hipStreamGetDevice(stream, &dev) != hipSuccess || !context_usable(ctx, stream, dev) ||
+        hipStreamIsCapturing(stream, &cap) != hipSuccess ||
+        hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    *capturing = cap != hipStreamCaptureStatusNone;
+    return true;
+}
+
 // The windowed order, for a workspace below the full record area: windows of
 // `w` chunks of every sequence, one after the other on `stream` -- pass 1
 // writes the window's records into a ring of w chunks per sequence, pass 2
@@ -1710,7 +1786,8 @@ int segments_for(int nck, int chains, hipStream_t stream)
 // the final state after the last).  The state goes through memory in fp32,
 // so the result is bit-identical to the unwindowed two-pass order; memory
 // use is independent of T.
-hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_bytes, hipStream_t stream)
+hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_bytes, hipStream_t stream,
+                           kda_context_s* ctx)
 {
     const bool packed = args.cu_seqlens != nullptr;
     const int nseq = packed ? args.num_seqs : args.B;
@@ -1739,6 +1816,22 @@ hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_byt
         const size_t words = norm_slot_words(static_cast<long long>(chains) * (seg ? seg_units_a(kMaxSegments) : 1));
         const size_t blocks = (words + 255) / 256;
         zero_words_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(norm_slots, words);
+    }
+    // a dense batch whose sequential pass leaves CUs idle overlaps the two
+    // passes as the staged order does, with the ring split in two halves
+    // (stage k in half k mod 2)
+    int cus = 0;
+    bool capturing = false;
+    const int half = static_cast<int>(w / 2);
+    if (!packed && !seg && half >= kMinRingHalf && stages_may_pay(nck, chains) &&
+        overlap_usable(ctx, stream, &cus, &capturing) && cus - 16 * ((chains + 7) / 8) >= 32) {
+        ChunkArgs a = args;
+        a.rec_stride = half;
+        const size_t per_half = static_cast<size_t>(args.H) * nseq * half;   // records
+        const int stages = (nck + half - 1) / half;
+        return run_stages(a, stages, [&](int k) { return k * half < nck ? k * half : nck; },
+                          [&](int k) { return recs + (k & 1) * per_half; }, nseq * half, carried, norm_slots, ctx,
+                          stream, capturing, true);
     }
     for (int lo = 0; lo < nck; lo += static_cast<int>(w)) {
         ChunkArgs b = args;
@@ -1771,7 +1864,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
     const long long slots = chunk_record_slots(args.B, args.T, args.num_seqs, packed);
     const TwoPassLayout lay = two_pass_layout(args.B, args.T, args.H, args.num_seqs, packed, args.out_norm != 0);
     if (args.T > 0 && (ws_bytes < lay.total || slots * args.H >= (1LL << 24)))
-        return launch_windowed(args, workspace, ws_bytes, stream);
+        return launch_windowed(args, workspace, ws_bytes, stream, ctx);
     const int ns = static_cast<int>(slots);
     ChunkRecord* recs = static_cast<ChunkRecord*>(workspace);
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
@@ -1812,16 +1905,9 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
     int bounds[kMaxStages + 1];
     int stages = 1;
     bool capturing = false;
-    if (!packed && ctx && stages_may_pay(nck, chains)) {
-        int dev = 0, cus = 0;
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamGetDevice(stream, &dev) == hipSuccess && context_usable(ctx, stream, dev) &&
-            hipStreamIsCapturing(stream, &cap) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-            stages = plan_stages(nck, chains, cus, bounds);
-            capturing = cap != hipStreamCaptureStatusNone;
-        }
-    }
+    int cus = 0;
+    if (!packed && stages_may_pay(nck, chains) && overlap_usable(ctx, stream, &cus, &capturing))
+        stages = plan_stages(nck, chains, cus, bounds);
 
     ChunkArgs a = args;
     if (!packed) {
@@ -1846,48 +1932,12 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
         return hipGetLastError();
     }
 
-    // stage s covers chunks bounds[s] .. bounds[s+1] - 1 of every sequence;
-    // the state between stages goes through the workspace
+    // stage s covers chunks bounds[s] .. bounds[s+1] - 1 of every sequence,
+    // records in their absolute slots; the state between stages goes
+    // through the workspace
     float* carried = reinterpret_cast<float*>(after);
-    auto stage_args = [&](int s) {
-        ChunkArgs b = a;
-        b.chunk_lo = bounds[s];
-        b.chunk_cnt = bounds[s + 1] - bounds[s];
-        b.init_state = s == 0 ? args.init_state : carried;
-        b.final_state = s + 1 == stages ? args.final_state : carried;
-        return b;
-    };
-    hipError_t e = hipSuccess;
-    auto ok = [&](hipError_t r) { if (e == hipSuccess && r != hipSuccess) e = r; return e == hipSuccess; };
-    int launched = -1;   // last stage whose pass 2 is enqueued on the context's stream
-    int recorded = -1;   // last stage whose pass-2 completion event is recorded behind it
-    prep(stage_args(0), recs, nullptr, ns, static_cast<unsigned>(args.B * bounds[1] * args.H), stream);
-    ok(hipGetLastError());
-    ok(hipEventRecord(ctx->p1[0], stream));
-    for (int s = 0; s < stages && e == hipSuccess; ++s) {
-        if (!ok(hipStreamWaitEvent(ctx->side, ctx->p1[s], 0))) break;
-        scan(stage_args(s), recs, ns, chains, norm_slots, ctx->side);
-        const hipError_t lr = hipGetLastError();
-        if (lr == hipSuccess) launched = s;
-        if (!ok(lr)) break;
-        if (ok(hipEventRecord(ctx->p2[s], ctx->side))) recorded = s;
-        if (s + 1 < stages && e == hipSuccess) {
-            // pass 1 of stage s+1 starts with pass 2 of stage s, behind a short gap
-            if (s >= 1) ok(hipStreamWaitEvent(stream, ctx->p2[s - 1], 0));
-            stage_gap_kernel<<<1, 64, 0, stream>>>(6);
-            const ChunkArgs b = stage_args(s + 1);
-            prep(b, recs, nullptr, ns, static_cast<unsigned>(args.B * b.chunk_cnt * args.H), stream);
-            ok(hipGetLastError());
-            ok(hipEventRecord(ctx->p1[s + 1], stream));
-        }
-    }
-    // join: later work on the caller's stream sees every stage, after an
-    // error too, so that nothing on the second stream escapes the caller's
-    // stream order
-    const StageJoin jn = plan_join(launched, recorded, capturing);
-    if (jn.wait_stage >= 0) ok(hipStreamWaitEvent(stream, ctx->p2[jn.wait_stage], 0));
-    if (jn.sync_side) ok(hipStreamSynchronize(ctx->side));
-    return e;
+    return run_stages(a, stages, [&](int k) { return bounds[k]; }, [&](int) { return recs; }, ns, carried,
+                      norm_slots, ctx, stream, capturing);
 }
 
 }  // namespace kda

@@ -10,6 +10,11 @@ namespace kda {
 
 constexpr int kMaxStages = 6;
 constexpr int kMinStageChunks = 16;
+// The overlapped windowed order needs ring halves of at least this many
+// chunks: with smaller stages the gaps and events cost more than the overlap
+// gains (the 64K-token, 96-head prefill in a 0.25 GB workspace, halves of 18
+// chunks: 7.33 ms overlapped against 7.03 ms one window after the other).
+constexpr int kMinRingHalf = 32;
 
 // With less pass-1 work than ~8K (chunk, chain) pairs the extra launches and
 // the gaps cost more than the overlap gains (+5 % on 4096-token prefills at

@@ -217,3 +217,49 @@ def test_windowed_in_a_graph(kda):
         torch.cuda.synchronize()
         assert torch.equal(o, refs[i][0]), "replay %d: o" % rep
         assert torch.equal(st, refs[i][1]), "replay %d: final state" % rep
+
+
+def test_windowed_overlap_orders_and_graph(kda):
+    """48 chains, 258 chunks per sequence, a ring of 80 chunks: with the
+    context the windows overlap their passes (two ring halves of 40 chunks,
+    7 stages), without it they run one after the other; both equal the full
+    workspace's staged call bit for bit, and so does every replay of the
+    overlapped call captured in a graph."""
+    import torch
+    B, T, H = 1, 16384 + 100, 48
+    inps = [kda_inputs.make_prefill(70 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
+    bufs = {k: dev(getattr(inps[0], k)).clone() for k in ("q", "k", "v", "g", "beta", "init_state")}
+    o = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(_ws(B, H, 80), dtype=torch.uint8, device="cuda")
+
+    def call(context="default", workspace=ws):
+        kda.chunk_fwd(bufs["q"], bufs["k"], bufs["v"], bufs["g"], bufs["beta"], bufs["init_state"], o=o,
+                      final_state=st, workspace=workspace, context=context)
+
+    refs = []
+    for inp in inps:
+        for k in bufs:
+            bufs[k].copy_(dev(getattr(inp, k)))
+        call(workspace=None)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), st.clone()))
+        for ctx in ("default", None):
+            o.zero_()
+            call(ctx)
+            torch.cuda.synchronize()
+            assert torch.equal(o, refs[-1][0]) and torch.equal(st, refs[-1][1]), ctx
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        i = rep % 2
+        for k in bufs:
+            bufs[k].copy_(dev(getattr(inps[i], k)))
+        o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, refs[i][0]), "replay %d: o" % rep
+        assert torch.equal(st, refs[i][1]), "replay %d: final state" % rep
