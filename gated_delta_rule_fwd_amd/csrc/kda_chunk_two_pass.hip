@@ -835,7 +835,7 @@ __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, co
 // than one fp16 rounding: with the keys the model produces (SiLU'd, sharing a
 // common direction) the state stays small next to what each chunk writes,
 // and U~'s single fp16 rounding alone costs ~3e-2 of RMS(S).
-template <typename Tout, bool CONV, bool NORM, bool SPLIT = true>
+template <typename Tout, bool CONV, bool NORM, bool SPLIT = true, bool OUT = true>
 __global__ void __launch_bounds__(NT, 1)
 chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots, unsigned long long* norm_slots)
 {
@@ -886,7 +886,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // whether the values are taken as zero (the transition of a segment)
     const float* sinit = a.init_state ? a.init_state + static_cast<size_t>(chain) * DK * DV : nullptr;
     float* sfinal = a.final_state ? a.final_state + static_cast<size_t>(chain) * DK * DV : nullptr;
-    bool identity = false, zero_v = false, with_out = true;
+    // (OUT = false: the summary launch of the segmented order, no outputs)
+    constexpr bool with_out = OUT;
+    bool identity = false, zero_v = false;
     if (a.seg_phase) {
         const int P = a.seg_count;
         float* blocks = a.seg_states + static_cast<size_t>(chain) * seg_state_blocks(P) * DK * DV;
@@ -896,20 +898,17 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             sg = (unit + 1) >> 1;
             if (unit == 0) {
                 sfinal = block(0);
+            } else if (unit & 1) {
+                sinit = nullptr;
+                sfinal = block(seg_block_b(P, sg));
             } else {
-                with_out = false;
-                if (unit & 1) {
-                    sinit = nullptr;
-                    sfinal = block(seg_block_b(P, sg));
-                } else {
-                    sinit = nullptr;
-                    identity = zero_v = true;
-                    sfinal = block(seg_block_m(P, sg));
-                }
+                sinit = nullptr;
+                identity = zero_v = true;
+                sfinal = block(seg_block_m(P, sg));
             }
         } else {
-            sg = unit + 1;
-            sinit = block(seg_block_in(P, sg));
+            sg = unit;
+            if (sg > 0) sinit = block(seg_block_in(P, sg));
             if (sg + 1 < P) sfinal = nullptr;
         }
         // segments of the launch's chunk range (the whole chain, or a window)
@@ -1183,12 +1182,12 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2) {
                 ar[m2] = mmh(fa[m2][kb], sh[kb], ar[m2]);
-                aq[m2] = mmh(qa[m2][kb], sh[kb], aq[m2]);
+                if constexpr (OUT) aq[m2] = mmh(qa[m2][kb], sh[kb], aq[m2]);
             }
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2) {
                 ar[m2] = mmh(fa[m2][kb], sl[kb], ar[m2]);
-                aq[m2] = mmh(qa[m2][kb], sl[kb], aq[m2]);
+                if constexpr (OUT) aq[m2] = mmh(qa[m2][kb], sl[kb], aq[m2]);
             }
         }
 #pragma unroll
@@ -1357,7 +1356,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         f16x8 fa0[2][4], fa1[2][4], qa0[2][4], qa1[2][4];
         float vv0[2][4], vv1[2][4];
         load_r(0, fa0, vv0);
-        load_q(0, qa0);
+        if constexpr (OUT) load_q(0, qa0);
         if (more) {
             fetch_v(j + 1);
             fetch(j + 1, 0, 5);
@@ -1369,7 +1368,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         split_state(sh, sl);
         __builtin_amdgcn_sched_barrier(0);
         load_r(1, fa1, vv1);
-        load_q(1, qa1);
+        if constexpr (OUT) load_q(1, qa1);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 ut[4], oq[4];
         step_rq(0, fa0, qa0, vv0, sh, sl, ut, oq);
@@ -1388,8 +1387,10 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         step_rq(1, fa1, qa1, vv1, sh, sl, ut, oq);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ah0[2][2], al0[2][2], ah1[2][2], al1[2][2];
-        load_a(0, ah0, al0);
-        load_a(1, ah1, al1);
+        if constexpr (OUT) {
+            load_a(0, ah0, al0);
+            load_a(1, ah1, al1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ub[2], ubl[2];
         step_t(th, tl, ut, ub, ubl);
@@ -1403,9 +1404,9 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         float4 gm1[4];
         load_k(1, ka1, gm1);
         if (more) fetch(j + 1, 15, RFULL + 1);
-        step_oa(0, buf, oq, ah0, al0, ub);
+        if constexpr (OUT) step_oa(0, buf, oq, ah0, al0, ub);
         step_k(0, ka0, gm0, ub, ubl);
-        step_oa(1, buf, oq, ah1, al1, ub);
+        if constexpr (OUT) step_oa(1, buf, oq, ah1, al1, ub);
         step_k(1, ka1, gm1, ub, ubl);
         __syncthreads();
         // every read of this chunk's record is done: the next one moves in
@@ -1530,7 +1531,7 @@ TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bo
     L.norm_off = static_cast<size_t>(slots) * H * kChunkRecordBytes;
     L.norm_off += packed ? (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256
                          : static_cast<size_t>(B) * H * DK * DV * sizeof(float);
-    const long long units = may_segment ? seg_units_a(kMaxSegments) : 1;
+    const long long units = may_segment ? seg_units_c(kMaxSegments) : 1;   // phase C writes o
     L.seg_off = L.norm_off + (norm ? norm_slot_words(chains * units) * sizeof(unsigned long long) : 0);
     L.seg_off = (L.seg_off + 255) / 256 * 256;
     L.total = L.seg_off + (may_segment ? static_cast<size_t>(chains) * seg_state_blocks(kMaxSegments) * DK * DV *
@@ -1554,7 +1555,7 @@ WindowLayout window_layout(int B, int H, int num_seqs, bool packed, bool norm, l
     WindowLayout L;
     L.carry_off = static_cast<size_t>(window) * chains * kChunkRecordBytes;
     L.norm_off = L.carry_off + static_cast<size_t>(chains) * DK * DV * sizeof(float);
-    const long long units = seg ? seg_units_a(kMaxSegments) : 1;
+    const long long units = seg ? seg_units_c(kMaxSegments) : 1;
     L.seg_off = L.norm_off + (norm ? norm_slot_words(chains * units) * sizeof(unsigned long long) : 0);
     L.seg_off = (L.seg_off + 255) / 256 * 256;
     L.total = L.seg_off + (seg ? static_cast<size_t>(chains) * seg_state_blocks(kMaxSegments) * DK * DV *
@@ -1660,6 +1661,13 @@ void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, un
     // ids: chain = 8 * (bid >> 4) + (bid & 7), slice = (bid >> 3) & 1
     const int groups = (chains + 7) / 8;
     const dim3 grid(groups * 8 * NSLICE);
+    if (a.seg_phase == 1) {   // summaries of the segmented order: no outputs
+        if (a.conv)
+            chunk_scan_kernel<uint16_t, true, false, true, false><<<grid, NT, 0, stream>>>(a, recs, slots, nullptr);
+        else
+            chunk_scan_kernel<uint16_t, false, false, true, false><<<grid, NT, 0, stream>>>(a, recs, slots, nullptr);
+        return;
+    }
     if (a.conv) {
         if (a.out_bf16)
             launch_scan<uint16_t, true>(a, recs, slots, norm_slots, grid, stream);
@@ -1674,10 +1682,11 @@ void scan(const ChunkArgs& a, const ChunkRecord* recs, int slots, int chains, un
 }
 
 // The segmented order over the chunk range b.chunk_lo .. + b.chunk_cnt of
-// every chain, whose records are in place: phase A (segment 0 from
-// b.init_state with outputs, the middle segments' summaries), phase B (the
-// initial states of segments 1 .. P-1), phase C (those segments with
-// outputs; the last one ends in b.final_state), all on `stream`.
+// every chain, whose records are in place: phase A, without outputs
+// (segment 0 from b.init_state to its end state, the middle segments'
+// summaries), phase B (the initial states of segments 1 .. P-1), phase C
+// (every segment from its initial state with outputs; the last one ends in
+// b.final_state), all on `stream`.
 void run_segments(ChunkArgs b, const ChunkRecord* recs, int slots, int chains, int nseg, float* seg_states,
                   unsigned long long* norm_slots, hipStream_t stream)
 {
@@ -1813,7 +1822,7 @@ hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_byt
     unsigned long long* norm_slots = nullptr;
     if (norm) {
         norm_slots = reinterpret_cast<unsigned long long*>(base + lay.norm_off);
-        const size_t words = norm_slot_words(static_cast<long long>(chains) * (seg ? seg_units_a(kMaxSegments) : 1));
+        const size_t words = norm_slot_words(static_cast<long long>(chains) * (seg ? seg_units_c(kMaxSegments) : 1));
         const size_t blocks = (words + 255) / 256;
         zero_words_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(norm_slots, words);
     }
@@ -1872,7 +1881,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
 
     // the segmented order for a dense batch with few chains
     const int nseg = packed ? 1 : segments_for(nck, chains, stream);
-    const long long units = nseg > 1 ? seg_units_a(nseg) : 1;
+    const long long units = nseg > 1 ? seg_units_c(nseg) : 1;
 
     // output norm: the row-sum words the two value slices of a chain (or of a
     // segment unit) exchange, zeroed by a kernel (no memset node) before any
@@ -1886,9 +1895,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
     }
 
     if (nseg > 1) {
-        // pass 1 over every chunk, then phase A (segment 0 and the middle
-        // segments' summaries), phase B (the initial states of segments
-        // 1 .. P-1), phase C (those segments with outputs), all on `stream`
+        // pass 1 over every chunk, then the three phases of run_segments
         ChunkArgs b = args;
         b.chunk_lo = 0;
         b.chunk_cnt = nck;

@@ -61,12 +61,12 @@ struct ChunkArgs {
     // n + cu_seqlens[n]/64 and pass 1 finds its sequence in the slot map
     int rec_stride, rec_base;
     // segmented sequential pass (plan_segments in kda_stage_plan.h): 0 = off;
-    // 1 = phase A, 2P - 3 units per chain: (chain, 0) = segment 0 with
-    // outputs, (chain, 2s - 1) / (chain, 2s) = segment s (1 .. P-2) from zero
-    // with the values / from the identity with zero values, no outputs; 2 =
-    // phase C, P - 1 units: (chain, s - 1) = segment s from its initial state
-    // with outputs.  seg_states holds per chain seg_state_blocks(seg_count)
-    // blocks of d_k x d_v fp32 (see there).
+    // 1 = phase A, no outputs, 2P - 3 units per chain: (chain, 0) = segment 0
+    // from the initial state, (chain, 2s - 1) / (chain, 2s) = segment s
+    // (1 .. P-2) from zero with the values / from the identity with zero
+    // values; 2 = phase C, P units: (chain, s) = segment s from its initial
+    // state with outputs.  seg_states holds per chain
+    // seg_state_blocks(seg_count) blocks of d_k x d_v fp32 (see there).
     int seg_phase, seg_count, seg_len;
     float* seg_states;
 };
@@ -79,7 +79,7 @@ constexpr int seg_block_b(int P, int s) { return s; }
 constexpr int seg_block_m(int P, int s) { return P - 2 + s; }
 constexpr int seg_block_in(int P, int s) { return 2 * P - 4 + s; }
 constexpr int seg_units_a(int P) { return 2 * P - 3; }
-constexpr int seg_units_c(int P) { return P - 1; }
+constexpr int seg_units_c(int P) { return P; }
 
 // Inputs of one decode step; z/A_log/dt_bias replace g when gated.
 struct DecodeArgs {

@@ -61,13 +61,14 @@ inline int plan_stages(int nck, int chains, int cus, int* bounds)
 // the map of a sequence is the composition of the affine maps of its
 // segments, S -> M S + B, so segments can be summarised apart and combined in
 // order).  For a dense batch with few chains the sequential pass occupies few
-// CUs; splitting every chain into P segments runs (A) segment 0 as usual and
-// every middle segment 1 .. P-2 twice in parallel -- from a zero state with
-// the values (its B) and from the identity with zero values (its M) -- then
-// (B) chains the segments' initial states S_{s+1} = M_s S_s + B_s, then (C)
-// reruns segments 1 .. P-1 from their initial states with outputs: about 2
-// segment lengths of sequential chunks instead of P.  Phase A needs
-// 2 * chains * (2P - 3) workgroups of one CU each, so
+// CUs; splitting every chain into P segments runs (A), without outputs,
+// segment 0 from the initial state and every middle segment 1 .. P-2 twice
+// in parallel -- from a zero state with the values (its B) and from the
+// identity with zero values (its M) -- then (B) chains the segments' initial
+// states S_{s+1} = M_s S_s + B_s, then (C) runs all P segments from their
+// initial states with outputs: about 2 segment lengths of sequential chunks
+// instead of P.  Phase A needs 2 * chains * (2P - 3) workgroups of one CU
+// each (phase C, 2 * chains * P, no more), so
 // P = floor((cus / (2 chains) + 3) / 2), capped by kMaxSegments and by
 // segments of at least kMinSegChunks.  Returns P, or 1 when fewer than 3
 // segments fit (2 segments take as long as the plain pass).

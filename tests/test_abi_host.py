@@ -298,8 +298,8 @@ def test_workspace_for_the_output_norm(lib):
     assert size(B=2, T=100, H=3, out_dtype=0, flags=on) == size(B=2, T=100, H=3) + 2 * 3 * words
     assert size(B=1, T=1000, H=2, num_seqs=5, flags=on) == size(B=1, T=1000, H=2, num_seqs=5) + 5 * 2 * words
     # a batch that may take the segmented pass: words for each of the up to
-    # 2 * 8 - 3 segment units of phase A per chain, then the segment states
-    assert size(B=1, T=96 * 64, H=2, flags=on) == 96 * 2 * RECORD + 2 * STATE + 2 * 13 * words + 2 * SEG_BLOCKS * STATE
+    # 8 segment units of the phase with outputs per chain, then the segment states
+    assert size(B=1, T=96 * 64, H=2, flags=on) == 96 * 2 * RECORD + 2 * STATE + 2 * 8 * words + 2 * SEG_BLOCKS * STATE
     # fp32 path: a bf16 o is staged in fp32 for the norm pass; an fp32 o is
     # normalised in place
     assert size(B=2, T=100, H=3, d_k=64, d_v=64, flags=on) == 2 * 100 * 3 * 64 * 4

@@ -111,7 +111,7 @@ def test_windowed_segments_against_oracle(kda, window):
     check("win_seg%d" % window, host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=True)
     y_ref = oracle.out_norm(o_ref, kda_inputs.bf16_to_f32(gate).astype(np.float64), None, EPS)
     o, s = kda.chunk_fwd(*_args(inp), out_gate=dev(gate), norm_eps=EPS, out_dtype=torch.float32,
-                         workspace_limit=_ws_seg(B, H, window) + 2 * 13 * 4096)
+                         workspace_limit=_ws_seg(B, H, window) + 2 * 8 * 4096)
     torch.cuda.synchronize()
     check("win_seg%d_norm" % window, host64(o), y_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
 
