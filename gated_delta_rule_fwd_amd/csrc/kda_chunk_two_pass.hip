@@ -1451,65 +1451,80 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
 // S_{s+1} = M_s S_s + B_s ("Kimi K3 の KDA ..." section 2.3.4.1: (A2, b2)
 // after (A1, b1) is (A2 A1, A2 b1 + b2)).  One workgroup per (chain,
 // 16-column strip of the state): the columns are independent affine systems
-// (section 2.3.2).  fp32 throughout; M_s is d_k x d_k, held like a state.
+// (section 2.3.2).  The products run on the fp32 matrix cores
+// (16x16x4, fp32 operands and accumulation): M_s (d_k x d_k, held like a
+// state) goes through LDS, loaded into registers one segment ahead; the
+// strip S_s stays in LDS; wave w computes rows 32w .. 32w + 31.
 __global__ void __launch_bounds__(256) seg_combine_kernel(float* __restrict__ seg_states, int P, int nchains)
 {
     static_assert(DK == DV, "M_s is stored in a state-shaped block");
     constexpr int SW = 16;                       // columns per workgroup
+    constexpr int MLD = DK + 4;                  // LDS row stride of M_s (floats)
     const int chain = blockIdx.x / (DV / SW), c0 = SW * (blockIdx.x % (DV / SW));
     if (chain >= nchains) return;
     float* blocks = seg_states + static_cast<size_t>(chain) * seg_state_blocks(P) * DK * DV;
     auto block = [&](int k) { return blocks + static_cast<size_t>(k) * DK * DV; };
     __shared__ float sx[DK][SW];
+    __shared__ __attribute__((aligned(16))) float sm[DK][MLD];
     const int t = threadIdx.x;
-    for (int e = t; e < DK * SW; e += 256) {
-        const int r = e / SW, c = e % SW;
-        const float x = block(0)[static_cast<size_t>(r) * DV + c0 + c];
-        sx[r][c] = x;
-        block(seg_block_in(P, 1))[static_cast<size_t>(r) * DV + c0 + c] = x;
+    const int w = t >> 6, l = t & 63, g = l >> 4, n = l & 15;
+    // thread t holds half a row of M_s (row t/2, columns 64 (t & 1) .. + 63)
+    // and its 8 accumulator values of B_s, both loaded one segment ahead
+    float4 mr[16];
+    f32x4 bq[2];
+    auto load_next = [&](int sg) __attribute__((always_inline)) {
+        const float4* src = reinterpret_cast<const float4*>(block(seg_block_m(P, sg)) +
+                                                            static_cast<size_t>(t >> 1) * DV + 64 * (t & 1));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mr[i] = src[i];
+        const float* Bs = block(seg_block_b(P, sg));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bq[tt][i] = Bs[static_cast<size_t>(32 * w + 16 * tt + 4 * g + i) * DV + c0 + n];
+    };
+    if (P > 2) load_next(1);
+    {
+        // S_1: this thread's 8 values of the strip, all loads before the stores
+        float x[DK * SW / 256];
+#pragma unroll
+        for (int u = 0; u < DK * SW / 256; ++u) {
+            const int e = t + 256 * u;
+            x[u] = block(0)[static_cast<size_t>(e / SW) * DV + c0 + e % SW];
+        }
+#pragma unroll
+        for (int u = 0; u < DK * SW / 256; ++u) {
+            const int e = t + 256 * u;
+            sx[e / SW][e % SW] = x[u];
+            block(seg_block_in(P, 1))[static_cast<size_t>(e / SW) * DV + c0 + e % SW] = x[u];
+        }
     }
-    // thread: row r of the strip, columns cb .. cb + 7; its row of M_s and
-    // its 8 values of B_s are loaded one segment ahead (two register sets)
-    const int r = t >> 1, cb = 8 * (t & 1);
-    float4 mA[DK / 4], mB[DK / 4], bA[2], bB[2];
-    auto load = [&](int sg, float4 (&m)[DK / 4], float4 (&b)[2]) __attribute__((always_inline)) {
-        const float4* M = reinterpret_cast<const float4*>(block(seg_block_m(P, sg)) + static_cast<size_t>(r) * DV);
+    for (int sg = 1; sg + 1 < P; ++sg) {
+        {
+            float* dst = &sm[t >> 1][64 * (t & 1)];
 #pragma unroll
-        for (int k4 = 0; k4 < DK / 4; ++k4) m[k4] = M[k4];
-        const float4* Bs =
-            reinterpret_cast<const float4*>(block(seg_block_b(P, sg)) + static_cast<size_t>(r) * DV + c0 + cb);
-        b[0] = Bs[0];
-        b[1] = Bs[1];
-    };
-    // S_{sg+1} = M_sg S_sg + B_sg for this thread's 8 values
-    auto step = [&](int sg, const float4 (&m)[DK / 4], const float4 (&b)[2]) __attribute__((always_inline)) {
-        float acc[8] = {b[0].x, b[0].y, b[0].z, b[0].w, b[1].x, b[1].y, b[1].z, b[1].w};
-#pragma unroll
+            for (int i = 0; i < 16; ++i) *reinterpret_cast<float4*>(dst + 4 * i) = mr[i];
+        }
+        f32x4 acc[2] = {bq[0], bq[1]};
+        __syncthreads();   // M_s and S_s in LDS
+        if (sg + 2 < P) load_next(sg + 1);
+#pragma unroll 8
         for (int k4 = 0; k4 < DK / 4; ++k4) {
-            const float mk[4] = {m[k4].x, m[k4].y, m[k4].z, m[k4].w};
+            const float b = sx[4 * k4 + g][n];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int tt = 0; tt < 2; ++tt) acc[tt] = mma32(sm[32 * w + 16 * tt + n][4 * k4 + g], b, acc[tt]);
+        }
+        __syncthreads();   // every wave has read S_s and M_s
+        float* out = block(seg_block_in(P, sg + 1));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += mk[u] * sx[4 * k4 + u][cb + e];
-        }
-        __syncthreads();
-        float* out = block(seg_block_in(P, sg + 1)) + static_cast<size_t>(r) * DV + c0 + cb;
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sx[r][cb + e] = acc[e];
-            out[e] = acc[e];
-        }
-        __syncthreads();
-    };
-    if (P > 2) load(1, mA, bA);
-    __syncthreads();
-    for (int sg = 1; sg + 1 < P; sg += 2) {
-        if (sg + 2 < P) load(sg + 1, mB, bB);
-        step(sg, mA, bA);
-        if (sg + 2 < P) {
-            if (sg + 3 < P) load(sg + 2, mA, bA);
-            step(sg + 1, mB, bB);
-        }
+            for (int i = 0; i < 4; ++i) {
+                const int r = 32 * w + 16 * tt + 4 * g + i;
+                sx[r][n] = acc[tt][i];
+                out[static_cast<size_t>(r) * DV + c0 + n] = acc[tt][i];
+            }
     }
 }
 
