@@ -62,6 +62,12 @@ def parse():
     p.add_argument("--oracle-table", action="store_true",
                    help="instead of the headline: time the fp64 oracle on bounded samples of the five workloads, "
                         "on all host cores and on one core; needs no GPU")
+    p.add_argument("--workspace-gib", type=float, default=None,
+                   help="with --workload: cap the prefill workspace at this many GiB (never below the least one; "
+                        "below the full size the windowed order runs)")
+    p.add_argument("--long-context", action="store_true",
+                   help="instead of the headline: prefill at 16 heads, T = 256K, 1M, 4M tokens, in a 1 GiB "
+                        "workspace (and the full one up to 1M), inputs drawn on the device; one JSON line")
     p.add_argument("--mfma-from", metavar="DIR",
                    help="summarise a rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and "
                         "GRBM_GUI_ACTIVE (MFMA-busy fraction per kernel) and exit; needs no GPU")
@@ -215,6 +221,51 @@ def context_sweep(kda, torch, kda_inputs, heads=16, lengths=(2048, 4096, 8192, 1
             "rows": rows}
 
 
+def long_context(kda, torch, heads=16, lengths=(262144, 1048576, 4194304), ws_gib=1.0, full_up_to=1048576,
+                 reps=3, seed=5):
+    """Prefill time per call at long contexts in a bounded workspace (the
+    windowed order: memory independent of T) and, up to full_up_to tokens,
+    with the full workspace.  Inputs are drawn on the device with torch's
+    seeded generator, from the distributions of the long-prefill workload
+    (q, k, v ~ N(0, 1) in bf16; g = -5 sigmoid(e^A_h z), A_h ~ U(-1, 1),
+    z ~ N(0, 1); beta = sigmoid(N(0, 1)); S0 ~ N(0, 0.02^2)); they serve
+    timing only."""
+    gen = torch.Generator(device="cuda")
+    rows = []
+    for T_ in lengths:
+        gen.manual_seed(seed + T_)
+        shape = (1, T_, heads, D)
+        x = {}
+        for name in ("q", "k", "v"):
+            x[name] = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        A = torch.rand((heads,), generator=gen, device="cuda") * 2 - 1
+        g = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+        g.mul_(torch.exp(A)[None, None, :, None]).sigmoid_().mul_(-5.0)
+        beta = torch.randn((1, T_, heads), generator=gen, device="cuda").sigmoid_()
+        s0 = torch.randn((1, heads, D, D), generator=gen, device="cuda") * 0.02
+        o = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+        sT = torch.empty((1, heads, D, D), dtype=torch.float32, device="cuda")
+        full = kda.workspace_bytes(1, T_, heads, D, D)
+        least = kda.min_workspace_bytes(1, T_, heads, D, D)
+        row = {"T": T_, "H": heads, "full_workspace_bytes": full, "least_workspace_bytes": least}
+        for label, nbytes in (("bounded", max(least, min(full, int(ws_gib * (1 << 30))))),
+                              ("full", full if T_ <= full_up_to else None)):
+            if nbytes is None:
+                continue
+            ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+            call = lambda: kda.chunk_fwd(x["q"], x["k"], x["v"], g, beta, s0, o=o, final_state=sT, workspace=ws)
+            ts = _time_calls(torch, call, reps, 1)
+            med = float(np.median(ts))
+            row[label] = {"workspace_bytes": nbytes, "ms_median": med, "tokens_per_s": T_ / (med * 1e-3)}
+            del ws
+            torch.cuda.empty_cache()
+        rows.append(row)
+        del x, g, beta, s0, o, sT
+        torch.cuda.empty_cache()
+    return {"long_context": "prefill B=1 H=%d d_k=d_v=128 bf16, inputs drawn on the device; median of %d calls; "
+                            "bounded workspace %.2f GiB" % (heads, reps, ws_gib), "rows": rows}
+
+
 def cpu_baseline(inp_full, heads, tokens):
     """The fp64 oracle on a bounded sample of the same workload, scaled to
     tokens/s of the full 96-head layer."""
@@ -360,10 +411,11 @@ def copy_bandwidth(torch):
     return {"bytes_moved": 2 * COPY_BYTES, "ms_median": ms, "gbs": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
 
 
-def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
+def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5, ws_gib=None):
     """Median call time of one prefill workload; with several input sets the
     calls rotate over them (a 200 MB working set would otherwise stay in the
-    256 MB Infinity Cache)."""
+    256 MB Infinity Cache).  ws_gib caps the workspace (not below the least
+    one the call accepts)."""
     to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
                     if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
     ins = []
@@ -378,9 +430,12 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
     f32 = inp.dtype == "f32"
     o = torch.empty((inp.B, inp.T, H, inp.dv), dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
     sT = torch.empty((n_seq, H, inp.dk, inp.dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, kda.workspace_bytes(inp.B, inp.T, H, inp.dk, inp.dv,
-                                                num_seqs=n_seq if d["cu"] is not None else 0, in_bf16=not f32,
-                                                out_bf16=not f32)), dtype=torch.uint8, device="cuda")
+    wkw = dict(num_seqs=n_seq if d["cu"] is not None else 0, in_bf16=not f32, out_bf16=not f32)
+    ws_bytes = kda.workspace_bytes(inp.B, inp.T, H, inp.dk, inp.dv, **wkw)
+    if ws_gib is not None:
+        ws_bytes = max(kda.min_workspace_bytes(inp.B, inp.T, H, inp.dk, inp.dv, **wkw),
+                       min(ws_bytes, int(ws_gib * (1 << 30))))
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
     call = lambda d: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d["cu"], o=o,
                                    final_state=sT, workspace=ws)
     for i in range(warm):
@@ -401,7 +456,8 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5):
         algo = BYTES_PER_TOKEN_HEAD * tokens * H + 2 * STATE_BYTES * n_seq * H
     del ins, o, sT, ws
     torch.cuda.empty_cache()
-    return {"tokens": tokens, "heads": H, "sequences": n_seq, "input_sets": sets, "ms_median": ms,
+    return {"tokens": tokens, "heads": H, "sequences": n_seq, "input_sets": sets, "workspace_bytes": ws_bytes,
+            "ms_median": ms,
             "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)), "tokens_per_s": tokens / (ms * 1e-3),
             "algorithmic_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -621,6 +677,9 @@ def main():
     if args.sweep:
         print(json.dumps(context_sweep(kda, torch, kda_inputs)))
         return
+    if args.long_context:
+        print(json.dumps(long_context(kda, torch)))
+        return
     if args.workload:
         name = WORKLOAD_LINES[args.workload]
         if name == "decode":
@@ -628,7 +687,7 @@ def main():
         else:
             sets = 2 if name == "mid_bf16" else 1
             line = dict(workload=name, **time_workload(kda, torch, kda_inputs, name, sets=sets, reps=args.steps,
-                                                       warm=args.warmup))
+                                                       warm=args.warmup, ws_gib=args.workspace_gib))
         print(json.dumps({"workload_line": args.workload, **line}), flush=True)
         return
 
@@ -664,6 +723,14 @@ def main():
         "launch_ms_mean": launch_ms, "launch_ms_median": float(np.median(launches)),
         "launch_ms_min": float(np.min(launches)), "launch_ms_max": float(np.max(launches)), "wall_s_timed": wall,
     }
+    if not args.no_extra:
+        # the same call in a 1 GiB workspace (the windowed order, overlapped on the context's stream)
+        ws1 = torch.empty(max(kda.min_workspace_bytes(B, T, H, D, D), 1 << 30), dtype=torch.uint8, device="cuda")
+        t1 = _time_calls(torch, lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], o=d["o"],
+                                                      final_state=d["sT"], workspace=ws1), 10, 2)
+        out["prefill_long_1gib_workspace"] = {"workspace_bytes": ws1.numel(), "ms_median": float(np.median(t1)),
+                                              "tokens_per_s": B * T / (float(np.median(t1)) * 1e-3)}
+        del ws1
     del d
     torch.cuda.empty_cache()
     if not args.no_decode:
