@@ -911,10 +911,11 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             if (sg > 0) sinit = block(seg_block_in(P, sg));
             if (sg + 1 < P) sfinal = nullptr;
         }
-        // segments of the launch's chunk range (the whole chain, or a window)
-        const int end = je;
-        jb = min(jb + sg * a.seg_len, end);
-        je = min(jb + a.seg_len, end);
+        // segments of this chain's chunk range in the launch (the whole
+        // chain, or a window): P pieces of ceil(range / P) chunks
+        const int end = je, len = (end - jb + P - 1) / P;
+        jb = min(jb + sg * len, end);
+        je = min(jb + len, end);
     }
     const ChunkRecord* __restrict__ rc = recs + static_cast<size_t>(h) * nslots + slot0;
     const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
@@ -1541,7 +1542,9 @@ TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bo
     const long long slots = chunk_record_slots(B, T, num_seqs, packed);
     const long long chains = static_cast<long long>(packed ? num_seqs : B) * H;
     const int nck = packed ? 0 : (T + C - 1) / C;
-    const bool may_segment = !packed && plan_segments(nck, static_cast<int>(chains), 1 << 20) > 1;
+    // packed sequences: ceil(T / 64) bounds the chunks of the longest one
+    const int nck_max = packed ? (T + C - 1) / C : nck;
+    const bool may_segment = plan_segments(nck_max, static_cast<int>(chains), 1 << 20) > 1;
     TwoPassLayout L;
     L.norm_off = static_cast<size_t>(slots) * H * kChunkRecordBytes;
     L.norm_off += packed ? (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256
@@ -1706,7 +1709,6 @@ void run_segments(ChunkArgs b, const ChunkRecord* recs, int slots, int chains, i
                   unsigned long long* norm_slots, hipStream_t stream)
 {
     b.seg_count = nseg;
-    b.seg_len = (b.chunk_cnt + nseg - 1) / nseg;
     b.seg_states = seg_states;
     b.seg_phase = 1;
     scan(b, recs, slots, chains * seg_units_a(nseg), norm_slots, stream);
@@ -1894,8 +1896,9 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
     char* after = static_cast<char*>(workspace) + static_cast<size_t>(slots) * args.H * kChunkRecordBytes;
     const int nck = packed ? 0 : (args.T + C - 1) / C;
 
-    // the segmented order for a dense batch with few chains
-    const int nseg = packed ? 1 : segments_for(nck, chains, stream);
+    // the segmented order for a batch with few chains (packed sequences:
+    // by the longest a sequence can be; each chain splits its own range)
+    const int nseg = segments_for(packed ? (args.T + C - 1) / C : nck, chains, stream);
     const long long units = nseg > 1 ? seg_units_c(nseg) : 1;
 
     // output norm: the row-sum words the two value slices of a chain (or of a
@@ -1912,11 +1915,19 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
     if (nseg > 1) {
         // pass 1 over every chunk, then the three phases of run_segments
         ChunkArgs b = args;
+        int* map = nullptr;
         b.chunk_lo = 0;
-        b.chunk_cnt = nck;
-        b.rec_stride = nck;
-        b.rec_base = 0;
-        prep(b, recs, nullptr, ns, static_cast<unsigned>(slots * args.H), stream);
+        if (packed) {
+            map = reinterpret_cast<int*>(after);
+            slot_map_kernel<<<static_cast<unsigned>((slots + 255) / 256), 256, 0, stream>>>(
+                b.cu_seqlens, b.num_seqs, b.T, ns, map);
+            b.chunk_cnt = ns;
+        } else {
+            b.chunk_cnt = nck;
+            b.rec_stride = nck;
+            b.rec_base = 0;
+        }
+        prep(b, recs, map, ns, static_cast<unsigned>(slots * args.H), stream);
         run_segments(b, recs, ns, chains, nseg,
                      reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.seg_off), norm_slots, stream);
         return hipGetLastError();

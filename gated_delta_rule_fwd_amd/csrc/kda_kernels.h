@@ -67,7 +67,7 @@ struct ChunkArgs {
     // values; 2 = phase C, P units: (chain, s) = segment s from its initial
     // state with outputs.  seg_states holds per chain
     // seg_state_blocks(seg_count) blocks of d_k x d_v fp32 (see there).
-    int seg_phase, seg_count, seg_len;
+    int seg_phase, seg_count;
     float* seg_states;
 };
 

@@ -183,8 +183,9 @@ def test_workspace_sizes(lib):
     slots = 7 + 1000 // 64
     assert size(B=1, T=1000, H=4, num_seqs=7) == max(slots * 4 * RECORD + 256, 16 * 4 * RECORD + 4 * STATE)
     assert size(B=1, T=64 * 40, H=2, num_seqs=3) == 40 * 2 * RECORD + 256 + 3 * 2 * RECORD
-    # here the dense reading (50 chunks of 2 chains) may take the segmented pass and needs more
-    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 50 * 2 * RECORD + 2 * STATE + 2 * SEG_BLOCKS * STATE
+    # both readings may take the segmented pass here (at least 48 chunks, few chains): the packed one
+    # (53 slots, 6 chains) needs more
+    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 53 * 2 * RECORD + 256 + 6 * SEG_BLOCKS * STATE
     # segment states: chains <= 42 and ceil(T / 64) >= 48 (dense only)
     assert size(B=1, T=96 * 64, H=42) == 96 * 42 * RECORD + 42 * STATE + 42 * SEG_BLOCKS * STATE
     assert size(B=1, T=96 * 64, H=43) == 96 * 43 * RECORD + 43 * STATE

@@ -102,6 +102,45 @@ def test_segments_conv_and_norm(kda):
               bf16_store=(odt == torch.bfloat16))
 
 
+def test_segments_packed(kda):
+    """Packed sequences of mixed lengths (one empty, one of a single token):
+    each chain cuts its own chunk range into the 4 segments (24 chains,
+    ceil(T/64) = 361); an empty sequence passes its initial state through
+    bit for bit."""
+    import torch
+    lens = [8000, 3000, 0, 64, 12000, 1]
+    inp = kda_inputs.make_prefill(56, 1, 0, 4, 128, 128, s0_std=0.02, lengths=lens)
+    d = [dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state), dev(inp.cu_seqlens)]
+    o_ref, s_ref = oracle.forward(inp)
+    for odt in (torch.bfloat16, torch.float32):
+        o, s = kda.chunk_fwd(*d, out_dtype=odt)
+        torch.cuda.synchronize()
+        check("seg_packed/%s" % str(odt).split(".")[-1], host64(o), o_ref, host64(s), s_ref, TOL_BF16,
+              bf16_store=(odt == torch.bfloat16))
+        np.testing.assert_array_equal(host64(s[2]), inp.init_state[2].astype(np.float64))
+
+
+def test_segments_packed_conv_norm(kda):
+    """Two long packed sequences, 3 heads (6 chains, 8 segments each) with
+    the short convolution and the output norm."""
+    import torch
+    lens = [5000, 7000]
+    H = 3
+    inp = kda_inputs.make_prefill(57, 1, 0, H, 128, 128, s0_std=0.02, lengths=lens)
+    ws = kda_inputs.conv_weights(57, H, 128, 128)
+    cs = kda_inputs.conv_states(57, len(lens), H, 128, 128)
+    gate = kda_inputs.make_out_gate(57, inp.v.shape)
+    w = kda_inputs.norm_weight(57, 128)
+    o_ref, s_ref, _ = oracle.forward_conv(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.g, inp.beta, ws,
+                                          tuple(_f(c) for c in cs), inp.init_state, inp.cu_seqlens)
+    y_ref = oracle.out_norm(o_ref, _f(gate).astype(np.float64), w, EPS)
+    o, s = kda.chunk_fwd(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(inp.init_state),
+                         dev(inp.cu_seqlens), out_dtype=torch.float32, conv_weights=tuple(dev(x) for x in ws),
+                         conv_init=tuple(dev(c) for c in cs), out_gate=dev(gate), norm_weight=dev(w), norm_eps=EPS)
+    torch.cuda.synchronize()
+    check("seg_packed_conv_norm", host64(o), y_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
+
+
 def test_segments_long_sampled_heads(kda):
     """64K tokens x 16 heads (5 segments of about 205 chunks), oracle on two
     sampled heads."""
