@@ -147,8 +147,9 @@ size_t two_pass_min_workspace_bytes(int B, int T, int H, int num_seqs, bool pack
 // With a context (nullable), a dense batch whose sequential pass leaves CUs
 // idle runs in stages: pass 1 of stage s+1 on the idle CUs while pass 2 of
 // stage s runs, pass 2 on the context's stream, joined to `stream` before
-// returning.  A dense batch of at most 42 chains with at least 48 chunks per
-// sequence takes the segmented order instead (plan_segments).  Otherwise (no
+// returning.  A batch of at most 42 chains with at least 48 chunks per
+// sequence (packed: ceil(T/64)) takes the segmented order instead
+// (plan_segments).  Otherwise (no
 // context, a context of another device or one whose stream belongs to
 // another graph capture, packed sequences, short chains, many chains) pass 1
 // then pass 2 on `stream`.  With ws_bytes below two_pass_workspace_bytes()

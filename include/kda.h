@@ -160,8 +160,9 @@ typedef struct kda_chunk_desc {
  * (64-token chunk, head) there, plus, for a dense batch, the fp32 state of
  * every (b, h) chain (64 KB each) carried between launches, or, for packed
  * sequences, one int32 per chunk slot (256-byte rounded); KDA_FLAG_OUT_NORM
- * adds 4 KB per chain of row-sum words; a dense batch of at most 42 chains
- * and at least 48 chunks per sequence, which may take the segmented order,
+ * adds 4 KB per chain of row-sum words; a batch of at most 42 chains and at
+ * least 48 chunks per sequence (packed: ceil(T/64)), which may take the
+ * segmented order,
  * adds 20 state-sized blocks (1.25 MiB) per chain and row-sum words for 8
  * segment units per chain.  The fp32 path needs none, except with
  * KDA_FLAG_OUT_NORM and a bf16 o: B*T*H*d_v fp32 values.  KDA_FLAG_VALIDATE
@@ -192,9 +193,10 @@ KDA_API size_t kda_chunk_fwd_min_workspace_bytes(const kda_chunk_desc* desc);
  * The matrix-core path runs a chunk-parallel kernel and then a sequential
  * one, in one of four orders, picked on the host from the shapes, the
  * workspace size and the context:
- *  - segmented: a dense batch of at most 42 (b, h) chains and at least 48
- *    chunks per sequence, with the full workspace.  Each chain is cut into
- *    P segments (3 <= P <= 8, as many as the device's CUs hold); the middle
+ *  - segmented: a batch of at most 42 chains and at least 48 chunks per
+ *    sequence (packed sequences: ceil(T/64) chunks), with the full
+ *    workspace.  Each chain is cut into P segments of its own chunk range
+ *    (3 <= P <= 8, as many as the device's CUs hold); the middle
  *    segments are summarised as affine maps S -> M S + B and combined
  *    ("Kimi K3 の KDA ..." sections 2.3.4.2-2.3.4.5), then the later
  *    segments run again from their true initial states.  All on `stream`;
