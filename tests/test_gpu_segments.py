@@ -143,24 +143,32 @@ def test_segments_packed_conv_norm(kda):
 
 def test_segments_long_sampled_heads(kda):
     """64K tokens x 16 heads (5 segments of about 205 chunks), oracle on two
-    sampled heads."""
+    sampled heads; with the default context the last segment's pass 1 runs
+    on the context's stream beside phase A, without one after it: the same
+    bits."""
     import torch
     inp = kda_inputs.workload("long_bf16", H=16)
     o, s = _run(kda, inp, torch.bfloat16)
+    o2, s2 = _run(kda, inp, torch.bfloat16, context=None)
+    assert torch.equal(o, o2) and torch.equal(s, s2)
+    del o2, s2
     for h in (0, 15):
         hs = slice(h, h + 1)
         o_ref, s_ref = oracle.forward(inp, hs)
         check("seg_long16/h%d" % h, host64(o[:, :, hs]), o_ref, host64(s[:, hs]), s_ref, TOL_BF16, bf16_store=True)
 
 
-def test_segments_in_a_graph(kda):
+@pytest.mark.parametrize("shape", [(1, 4096 + 33, 8), (1, 16384 + 50, 32)], ids=["serial", "tail_overlapped"])
+def test_segments_in_a_graph(kda, shape):
     """A segmented call (with the output norm, so the row-sum words are
     cleared by the fill kernel inside the graph) captured with its buffers;
     replays after the inputs are overwritten eagerly reproduce the eager
-    results bit for bit, and the eager results equal those of context=None
-    (the segmented order does not use the context)."""
+    results bit for bit, and the eager results equal those of context=None.
+    The second shape (257 chunks, 32 chains) runs the last segment's pass 1
+    on the context's stream beside phase A, so the capture records that fork
+    and its join."""
     import torch
-    B, T, H = 1, 4096 + 33, 8
+    B, T, H = shape
     inps = [kda_inputs.make_prefill(55 + i, B, T, H, 128, 128, s0_std=0.02) for i in range(2)]
     gate = dev(kda_inputs.make_out_gate(55, (B, T, H, 128)))
     bufs = {k: dev(getattr(inps[0], k)).clone() for k in ("q", "k", "v", "g", "beta", "init_state")}
