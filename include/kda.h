@@ -198,9 +198,12 @@ KDA_API size_t kda_chunk_fwd_min_workspace_bytes(const kda_chunk_desc* desc);
  *    workspace.  Each chain is cut into P segments of its own chunk range
  *    (3 <= P <= 8, as many as the device's CUs hold); the middle
  *    segments are summarised as affine maps S -> M S + B and combined
- *    ("Kimi K3 の KDA ..." sections 2.3.4.2-2.3.4.5), then the later
- *    segments run again from their true initial states.  All on `stream`;
- *    the results differ from the other orders by rounding only.
+ *    ("Kimi K3 の KDA ..." sections 2.3.4.2-2.3.4.5), then the segments run
+ *    again from their true initial states.  On `stream`; with a usable
+ *    context a long dense batch runs the chunk-parallel kernel of its last
+ *    segment on the context's stream beside the summaries (joined before the
+ *    last kernel, same bits).  The results differ from the other orders by
+ *    rounding only.
  *  - staged: when desc->context is given and usable (created on the device
  *    of `stream`, its stream not part of a graph capture other than the one
  *    `stream` belongs to), a dense batch of more chains, at least 256 chunks
