@@ -179,14 +179,26 @@ chunk_fp32_kernel(ChunkArgs a)
             while (r * (r + 1) / 2 > p) --r;
             while ((r + 1) * (r + 2) / 2 <= p) ++r;
             const int s = p - r * (r + 1) / 2;
-            float aq = 0.f, ak = 0.f;
-            for (int i = 0; i < DK; ++i) {
-                const float ks = sK[s][i] * __expf(sB[r][i] - sB[s][i]);
-                aq += sQ[r][i] * ks;
-                ak += sK[r][i] * ks;
+            // 8 channels per step, their LDS reads issued together, four
+            // partial sums each (the reads and the exp otherwise serialise)
+            float aq[4] = {0.f, 0.f, 0.f, 0.f}, ak[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+            for (int i0 = 0; i0 < DK; i0 += 8) {
+                float e[8], qv[8], kv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    e[u] = sK[s][i0 + u] * __expf(sB[r][i0 + u] - sB[s][i0 + u]);
+                    qv[u] = sQ[r][i0 + u];
+                    kv[u] = sK[r][i0 + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    aq[u & 3] += qv[u] * e[u];
+                    ak[u & 3] += kv[u] * e[u];
+                }
             }
-            sA[r][s] = aq;
-            if (s < r) sA[s][r] = sBeta[r] * ak;
+            sA[r][s] = (aq[0] + aq[1]) + (aq[2] + aq[3]);
+            if (s < r) sA[s][r] = sBeta[r] * ((ak[0] + ak[1]) + (ak[2] + ak[3]));
         }
         __syncthreads();
 
