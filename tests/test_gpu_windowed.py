@@ -263,3 +263,20 @@ def test_windowed_overlap_orders_and_graph(kda):
         torch.cuda.synchronize()
         assert torch.equal(o, refs[i][0]), "replay %d: o" % rep
         assert torch.equal(st, refs[i][1]), "replay %d: final state" % rep
+
+
+def test_windowed_million_tokens_against_oracle(kda):
+    """One sequence of 2^20 + 37 tokens, 2 heads, in a 64 MiB workspace
+    (windows of ~430 chunks, 8 segments inside each), against the fp64
+    oracle over every token and the final state: the constant-memory order
+    at a length whose full record area (2.3 GiB here) it never allocates."""
+    import torch
+    B, T, H = 1, (1 << 20) + 37, 2
+    inp = kda_inputs.make_prefill(72, B, T, H, 128, 128, s0_std=0.02)
+    assert kda.workspace_bytes(B, T, H, 128, 128) > 2 * (1 << 30)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    o, s = kda.chunk_fwd(*_args(inp), workspace=ws, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    print("million-token call done", flush=True)
+    o_ref, s_ref = oracle.forward(inp)
+    check("windowed_1M", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
