@@ -889,6 +889,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // (OUT = false: the summary launch of the segmented order, no outputs)
     constexpr bool with_out = OUT;
     bool identity = false, zero_v = false;
+    float* scopy = nullptr;   // where phase A keeps a copy of the chain's initial state
     if (a.seg_phase) {
         const int P = a.seg_count;
         float* blocks = a.seg_states + static_cast<size_t>(chain) * seg_state_blocks(P) * DK * DV;
@@ -898,6 +899,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             sg = (unit + 1) >> 1;
             if (unit == 0) {
                 sfinal = block(0);
+                scopy = block(seg_block_init(P));
             } else if (unit & 1) {
                 sinit = nullptr;
                 sfinal = block(seg_block_b(P, sg));
@@ -908,7 +910,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             }
         } else {
             sg = unit;
-            if (sg > 0) sinit = block(seg_block_in(P, sg));
+            sinit = block(sg > 0 ? seg_block_in(P, sg) : seg_block_init(P));
             if (sg + 1 < P) sfinal = nullptr;
         }
         // segments of this chain's chunk range in the launch (the whole
@@ -932,6 +934,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
                 const int ch = 16 * mt + 4 * g + i;
                 sacc[mt][i] = sinit ? sinit[sbase + static_cast<size_t>(ch) * DV]
                                     : ((identity && ch == static_cast<int>(sbase)) ? 1.f : 0.f);
+                if (scopy) scopy[sbase + static_cast<size_t>(ch) * DV] = sacc[mt][i];
             }
     }
 

@@ -73,11 +73,15 @@ struct ChunkArgs {
 
 // Blocks of a chain's segment states: 0 = state after segment 0, 1 .. P-2 =
 // B_s, P-1 .. 2P-4 = M_s (s = 1 .. P-2), 2P-3 .. 3P-5 = initial state of
-// segment s = 1 .. P-1.
-constexpr int seg_state_blocks(int P) { return 3 * P - 4; }
+// segment s = 1 .. P-1, 3P-4 = a copy of the chain's initial state, taken by
+// phase A, from which phase C starts segment 0: phase C's last segment writes
+// the final state in the same launch, and the caller's initial state may
+// alias its final state (a window's carried state always does).
+constexpr int seg_state_blocks(int P) { return 3 * P - 3; }
 constexpr int seg_block_b(int P, int s) { return s; }
 constexpr int seg_block_m(int P, int s) { return P - 2 + s; }
 constexpr int seg_block_in(int P, int s) { return 2 * P - 4 + s; }
+constexpr int seg_block_init(int P) { return 3 * P - 4; }
 constexpr int seg_units_a(int P) { return 2 * P - 3; }
 constexpr int seg_units_c(int P) { return P; }
 

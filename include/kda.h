@@ -163,7 +163,7 @@ typedef struct kda_chunk_desc {
  * adds 4 KB per chain of row-sum words; a batch of at most 42 chains and at
  * least 48 chunks per sequence (packed: ceil(T/64)), which may take the
  * segmented order,
- * adds 20 state-sized blocks (1.25 MiB) per chain and row-sum words for 8
+ * adds 21 state-sized blocks (1.31 MiB) per chain and row-sum words for 8
  * segment units per chain.  The fp32 path needs none, except with
  * KDA_FLAG_OUT_NORM and a bf16 o: B*T*H*d_v fp32 values.  KDA_FLAG_VALIDATE
  * adds 256 bytes in front.  When num_seqs > 0 and B == 1 the figure covers

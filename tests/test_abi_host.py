@@ -163,11 +163,12 @@ def test_size_limits(lib):
 
 RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
 STATE = 128 * 128 * 4   # fp32 state of one chain, carried between the stages of a dense batch
-# a dense batch of at most 42 chains and at least 48 chunks per sequence may
-# take the segmented sequential pass: 3 * 8 - 4 state-sized blocks per chain
+# a batch of at most 42 chains and at least 48 chunks per sequence may take
+# the segmented sequential pass: 3 * 8 - 3 state-sized blocks per chain
 # (segment 0's end state, B_s and M_s of the middle segments, the initial
-# states of segments 1 .. 7), 256-byte aligned after the rest
-SEG_BLOCKS = 3 * 8 - 4
+# states of segments 1 .. 7, a copy of the chain's initial state), 256-byte
+# aligned after the rest
+SEG_BLOCKS = 3 * 8 - 3
 
 
 def test_workspace_sizes(lib):

@@ -71,6 +71,22 @@ def test_segments_zero_initial_state_and_no_final_state(kda):
     assert torch.equal(o2, o)
 
 
+def test_segments_initial_state_aliasing_final_state(kda):
+    """init_state and final_state the same buffer (allowed by the ABI): phase C
+    starts segment 0 from phase A's copy of the initial state, so the last
+    segment's write of the final state in the same launch cannot reach it;
+    equal bit for bit to the call with separate buffers."""
+    import torch
+    inp = kda_inputs.make_prefill(58, 1, 8192 + 9, 4, 128, 128, s0_std=0.02)
+    a = [dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta)]
+    s0 = dev(inp.init_state)
+    o1, s1 = kda.chunk_fwd(*a, s0.clone(), out_dtype=torch.float32)
+    st = s0.clone()
+    o2, s2 = kda.chunk_fwd(*a, st, final_state=st, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, st)
+
+
 def test_segments_signed(kda):
     """Complex KDA: signed decays inside the segment maps."""
     import torch

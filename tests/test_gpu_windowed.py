@@ -40,9 +40,9 @@ def _ws(nseq, H, window, norm=False):
 
 def _ws_seg(nseq, H, window):
     """Workspace bytes of a window of `window` chunks with room for the
-    segmented order inside it (20 state-sized blocks per chain)."""
+    segmented order inside it (21 state-sized blocks per chain)."""
     chains = nseq * H
-    return chains * (window * RECORD + STATE + 20 * STATE)
+    return chains * (window * RECORD + STATE + 21 * STATE)
 
 
 def _args(inp):
