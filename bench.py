@@ -187,6 +187,57 @@ def time_decode(kda, torch, kda_inputs, norm=False):
     return line
 
 
+def time_decode_layer(kda, torch, kda_inputs):
+    """The decode step of the whole layer core: raw q, k, v through the short
+    convolution (caches advanced in place), the decay gate from bf16 z, beta
+    from logits, and the output norm; N=256 H=96 d=128, 128 steps."""
+    w = kda_inputs.DECODE_WORKLOAD
+    S0 = kda_inputs.decode_initial_state(w["seed"], DEC_N, DEC_H, D, w["s0_std"])
+    state = torch.from_numpy(S0).cuda()
+    del S0
+    A_log, dt_bias = kda_inputs.gate_params(w["seed"], DEC_H, D)
+    A_log, dt_bias = _dev(torch, A_log), _dev(torch, dt_bias)
+    cw = tuple(_dev(torch, x) for x in kda_inputs.conv_weights(w["seed"], DEC_H, D, D))
+    caches = tuple(_dev(torch, x) for x in kda_inputs.conv_states(w["seed"], DEC_N, DEC_H, D, D))
+    wt = _dev(torch, kda_inputs.norm_weight(w["seed"], D))
+    xs = []
+    for s in range(8):
+        x = kda_inputs.gated_decode_step(w["seed"], s, DEC_N, DEC_H, D)
+        gate = _dev(torch, kda_inputs.make_out_gate(w["seed"] + s, (DEC_N, DEC_H, D)))
+        xs.append((_dev(torch, x.q), _dev(torch, x.k), _dev(torch, x.v), _dev(torch, x.z),
+                   _dev(torch, x.beta_logits), gate))
+    o = torch.empty((DEC_N, DEC_H, D), dtype=torch.bfloat16, device="cuda")
+
+    def step(x):
+        kda.recurrent_step_gated(x[0], x[1], x[2], x[3], A_log, x[4], state, dt_bias=dt_bias, beta_logits=True,
+                                 out_gate=x[5], norm_weight=wt, conv_weights=cw, conv_state=caches, o=o)
+
+    for s in range(4):
+        step(xs[s % 8])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = []
+    for s in range(DEC_STEPS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(xs[s % 8])
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    med = float(np.median(us))
+    # state in and out (fp32), raw q, k, v, z and the gate (bf16), beta logit, o (bf16), the three conv
+    # caches read and written (3 rows of H*d bf16 each)
+    per_chain = 2 * 4 * D * D + 2 * (4 * D + D) + 4 + 2 * D + 2 * 3 * 3 * 2 * D
+    bytes_step = per_chain * DEC_N * DEC_H
+    gbs = bytes_step / (med * 1e-6) / 1e9
+    return {"workload": "decode step of the layer core: short convolution (caches in place) + gate prologue + "
+                        "output norm, N=256 H=96 d=128, 128 steps",
+            "us_per_step_median": med, "us_per_step_min": float(us.min()), "us_per_step_max": float(us.max()),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "bytes_per_launch": bytes_step}}
+
+
 def context_sweep(kda, torch, kda_inputs, heads=16, lengths=(2048, 4096, 8192, 16384, 32768, 65536), reps=10):
     """Prefill time per call over context lengths at 16 heads, d = 128 (the
     head count and dims of the throughput comparison on the Complex KDA
@@ -737,6 +788,7 @@ def main():
         out["decode"] = time_decode(kda, torch, kda_inputs)
         if not args.no_extra:
             out["decode_out_norm"] = time_decode(kda, torch, kda_inputs, norm=True)
+            out["decode_layer_core"] = time_decode_layer(kda, torch, kda_inputs)
     if not args.no_extra:
         out["prefill_tiny"] = dict(workload="B=1 H=2 T=256 d=64 fp32 (exact fp32 path), seed 0",
                                    **time_workload(kda, torch, kda_inputs, "tiny_f32", sets=1))
