@@ -780,15 +780,32 @@ constexpr int NSLICE = DV / DVS;
 // so that the 16 rows one wave instruction touches fall into distinct banks.
 constexpr int OSTRIDE_NORM = DVS + 4;
 
+// What the output-free summary launch of the segmented order reads of a
+// record: T', -K^ Gamma, (K^ gamma/Gamma)^T and gamma, without A_qk and
+// Q^ Gamma.  Each array keeps its place in whole 4 KB blocks of the record
+// (16-byte piece t + 256 i), so block i of this struct is block
+// summary_block(i) of the record.
+struct alignas(16) SummaryRecord {
+    bf16x8 tp[2][6][64];
+    f16x8 kgn[4][4][64];
+    f16x8 kp[8][2][64];
+    float gam[DK];
+};
+__host__ __device__ constexpr int summary_block(int i) { return i < 3 ? i : (i < 7 ? i + 3 : (i < 11 ? i + 7 : 18)); }
+static_assert(offsetof(ChunkRecord, kgn) == 6 * 4096 && offsetof(ChunkRecord, kp) == 14 * 4096 &&
+                  offsetof(ChunkRecord, gam) == 18 * 4096 && offsetof(SummaryRecord, kgn) == 3 * 4096 &&
+                  offsetof(SummaryRecord, kp) == 7 * 4096 && offsetof(SummaryRecord, gam) == 11 * 4096,
+              "summary blocks");
+
 // V staging: bf16 as loaded, or fp32 when it is the short convolution's output
-template <bool CONV, bool NORM>
+template <bool CONV, bool NORM, bool OUT>
 struct alignas(16) ScanSmem {
-    ChunkRecord r;                                               // this chunk's operands
+    typename std::conditional<OUT, ChunkRecord, SummaryRecord>::type r;   // this chunk's operands
     typename std::conditional<CONV, float, __bf16>::type vs[C][DVS];   // V slice [token][column]
     // output tile staging ([token][column], bf16 or fp32), two chunks; with
     // the output norm fp32 and three chunks (a tile waits one chunk for the
     // other slice's row sums before it is normalised and stored)
-    float obuf[NORM ? 3 : 2][C * (NORM ? OSTRIDE_NORM : DVS)];
+    float obuf[OUT ? (NORM ? 3 : 2) : 1][OUT ? C * (NORM ? OSTRIDE_NORM : DVS) : 4];
     float nw[NORM ? DVS : 4];        // output norm: gain of this slice's columns
 };
 
@@ -835,11 +852,15 @@ __device__ __forceinline__ void stage_out(float* base, int r, int c, float x, co
 // than one fp16 rounding: with the keys the model produces (SiLU'd, sharing a
 // common direction) the state stays small next to what each chunk writes,
 // and U~'s single fp16 rounding alone costs ~3e-2 of RMS(S).
+// The output-free instantiation (OUT = false) holds less in LDS and in
+// registers and runs two workgroups per CU (without the short convolution,
+// whose registers do not fit half a CU).
 template <typename Tout, bool CONV, bool NORM, bool SPLIT = true, bool OUT = true>
-__global__ void __launch_bounds__(NT, 1)
+__global__ void __launch_bounds__(NT, (OUT || CONV) ? 1 : 2)
 chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots, unsigned long long* norm_slots)
 {
-    __shared__ ScanSmem<CONV, NORM> s;
+    static_assert(OUT || !NORM, "the output norm needs the outputs");
+    __shared__ ScanSmem<CONV, NORM, OUT> s;
 
     const int t = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -941,9 +962,11 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     // The next chunk's record and V slice travel in registers while the
     // current chunk is computed (issued in pieces between the compute steps
     // so the loads overlap them), then go to LDS between two barriers.
-    constexpr int RV = static_cast<int>(sizeof(ChunkRecord) / 16);
+    constexpr int RV = static_cast<int>(sizeof(s.r) / 16);
     constexpr int RFULL = RV / NT;
     constexpr int RTAIL = RV - RFULL * NT;
+    // the four batches of pieces issued during a chunk: [0, F1) [F1, F2) [F2, F3) [F3, RFULL]
+    constexpr int F1 = OUT ? 5 : 3, F2 = OUT ? 10 : 6, F3 = OUT ? 15 : 9;
     constexpr int PPR = DVS / 8;                   // 16-byte pieces per V row
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     u32x4 P[RFULL + 1], PV[2];
@@ -960,14 +983,19 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         for (int e = 0; e < 8; ++e) WV[e] = *reinterpret_cast<const float4*>(a.conv_w[2] + 4 * (chv + e));
     }
     // record pieces i in [i0, i1) of chunk j; piece RFULL is the partial one
+    // (the summary launch: pieces of the summary's blocks)
+    // Pieces are read as raw buffer loads: the record's address in a
+    // workgroup-uniform descriptor (scalar registers), the block's offset as
+    // a scalar offset and this thread's fixed 16-byte offset, so issuing a
+    // piece needs no vector address arithmetic.
+    const int toff = 16 * t;
     auto fetch = [&](int j, int i0, int i1) __attribute__((always_inline)) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(rc + (j - rbase));
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<ChunkRecord*>(rc + (j - rbase)), 0, static_cast<int>(sizeof(ChunkRecord)), kBufferWord3);
 #pragma unroll
         for (int i = i0; i < i1; ++i) {
-            if (i < RFULL)
-                P[i] = src[t + NT * i];
-            else if (t < RTAIL)
-                P[i] = src[t + NT * i];
+            const int blk = OUT ? i : summary_block(i);
+            if (i < RFULL || t < RTAIL) P[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, toff, 4096 * blk, 0);
         }
     };
     auto fetch_v = [&](int j) __attribute__((always_inline)) {
@@ -1162,11 +1190,14 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         }
     };
     // Q^ Gamma fragments for token tiles 2mh, 2mh + 1
+    // (the summary launch's record has neither Q^ Gamma nor A_qk)
     auto load_q = [&](int mh, f16x8 (&qa)[2][4]) __attribute__((always_inline)) {
+        if constexpr (OUT) {
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2)
+            for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[2 * mh + m2][kb][l];
+                for (int kb = 0; kb < 4; ++kb) qa[m2][kb] = s.r.qg[2 * mh + m2][kb][l];
+        }
     };
     // R = V - (K^ Gamma) S and the first term of O, (Q^ Gamma) S, for token
     // tiles 2mh, 2mh + 1: four independent accumulation chains share the
@@ -1202,13 +1233,15 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     };
     // A_qk fragments for token tiles 2half, 2half + 1
     auto load_a = [&](int half, f16x8 (&ah)[2][2], f16x8 (&al)[2][2]) __attribute__((always_inline)) {
+        if constexpr (OUT) {
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-            const int mt = 2 * half + m2;
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const int mt = 2 * half + m2;
 #pragma unroll
-            for (int kb = 0; kb <= half; ++kb) {
-                ah[m2][kb] = s.r.aqk[0][tri_block(mt, kb)][l];
-                al[m2][kb] = s.r.aqk[1][tri_block(mt, kb)][l];
+                for (int kb = 0; kb <= half; ++kb) {
+                    ah[m2][kb] = s.r.aqk[0][tri_block(mt, kb)][l];
+                    al[m2][kb] = s.r.aqk[1][tri_block(mt, kb)][l];
+                }
             }
         }
     };
@@ -1363,7 +1396,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         if constexpr (OUT) load_q(0, qa0);
         if (more) {
             fetch_v(j + 1);
-            fetch(j + 1, 0, 5);
+            fetch(j + 1, 0, F1);
         }
         if constexpr (!NORM) {
             if (with_out && j > jb) store_tile(buf ^ 1, prev_c0, prev_L);
@@ -1379,7 +1412,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 th[6], tl[6];
         load_t(th, tl);
-        if (more) fetch(j + 1, 5, 10);
+        if (more) fetch(j + 1, F1, F2);
         if constexpr (NORM) {
             // the other slice published chunk j-1's sums at the start of its
             // iteration j; they and chunk j-1's gate rows are used at the start
@@ -1398,7 +1431,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ub[2], ubl[2];
         step_t(th, tl, ut, ub, ubl);
-        if (more) fetch(j + 1, 10, 15);
+        if (more) fetch(j + 1, F2, F3);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ka0[4][2];
         float4 gm0[4];
@@ -1406,10 +1439,13 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ka1[4][2];
         float4 gm1[4];
-        load_k(1, ka1, gm1);
-        if (more) fetch(j + 1, 15, RFULL + 1);
+        // (the summary launch, two workgroups per CU, keeps fewer
+        // fragments in flight)
+        if constexpr (OUT) load_k(1, ka1, gm1);
+        if (more) fetch(j + 1, F3, RFULL + 1);
         if constexpr (OUT) step_oa(0, buf, oq, ah0, al0, ub);
         step_k(0, ka0, gm0, ub, ubl);
+        if constexpr (!OUT) load_k(1, ka1, gm1);
         if constexpr (OUT) step_oa(1, buf, oq, ah1, al1, ub);
         step_k(1, ka1, gm1, ub, ubl);
         __syncthreads();
@@ -1547,7 +1583,7 @@ TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bo
     const int nck = packed ? 0 : (T + C - 1) / C;
     // packed sequences: ceil(T / 64) bounds the chunks of the longest one
     const int nck_max = packed ? (T + C - 1) / C : nck;
-    const bool may_segment = plan_segments(nck_max, static_cast<int>(chains), 1 << 20) > 1;
+    const bool may_segment = plan_segments(nck_max, static_cast<int>(chains), 1 << 20, true) > 1;
     TwoPassLayout L;
     L.norm_off = static_cast<size_t>(slots) * H * kChunkRecordBytes;
     L.norm_off += packed ? (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256
@@ -1726,15 +1762,16 @@ hipError_t run_segments(ChunkArgs b, const ChunkRecord* recs, int slots, int cha
     return hipGetLastError();
 }
 
-// Segments for a dense range of `nck` chunks per chain on the device of `stream`.
-int segments_for(int nck, int chains, hipStream_t stream)
+// Segments for a dense range of `nck` chunks per chain on the device of
+// `stream` (phase A paired on a CU unless the short convolution runs).
+int segments_for(int nck, int chains, bool conv, hipStream_t stream)
 {
-    if (plan_segments(nck, chains, 1 << 20) <= 1) return 1;
+    if (plan_segments(nck, chains, 1 << 20, true) <= 1) return 1;
     int dev = 0, cus = 0;
     if (hipStreamGetDevice(stream, &dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 1;
-    return plan_segments(nck, chains, cus);
+    return plan_segments(nck, chains, cus, !conv);
 }
 
 // The overlapped order over stages s = 0 .. n-1 (chunks lo(s) .. lo(s+1)-1
@@ -1835,7 +1872,7 @@ hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_byt
     bool seg = false;
     if (!packed) {
         w = window_chunks(args.B, args.H, args.num_seqs, packed, norm, nck, ws_bytes, true);
-        seg = w > 0 && segments_for(static_cast<int>(w), chains, stream) > 1;
+        seg = w > 0 && segments_for(static_cast<int>(w), chains, args.conv != 0, stream) > 1;
     }
     if (!seg) w = window_chunks(args.B, args.H, args.num_seqs, packed, norm, nck, ws_bytes);
     if (w < 1) return hipErrorInvalidValue;   // below two_pass_min_workspace_bytes
@@ -1877,7 +1914,7 @@ hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_byt
         b.init_state = lo == 0 ? args.init_state : carried;
         b.final_state = lo + b.chunk_cnt >= nck ? args.final_state : carried;
         prep(b, recs, nullptr, ring, static_cast<unsigned>(nseq * b.chunk_cnt * args.H), stream);
-        const int nseg = seg ? segments_for(b.chunk_cnt, chains, stream) : 1;
+        const int nseg = seg ? segments_for(b.chunk_cnt, chains, args.conv != 0, stream) : 1;
         if (nseg > 1)
             run_segments(b, recs, ring, chains, nseg, seg_states, norm_slots, stream);
         else
@@ -1907,7 +1944,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
 
     // the segmented order for a batch with few chains (packed sequences:
     // by the longest a sequence can be; each chain splits its own range)
-    const int nseg = segments_for(packed ? (args.T + C - 1) / C : nck, chains, stream);
+    const int nseg = segments_for(packed ? (args.T + C - 1) / C : nck, chains, args.conv != 0, stream);
     const long long units = nseg > 1 ? seg_units_c(nseg) : 1;
 
     // output norm: the row-sum words the two value slices of a chain (or of a
@@ -1949,7 +1986,7 @@ hipError_t launch_chunk_two_pass(const ChunkArgs& args, void* workspace, size_t 
         int cus = 0;
         bool capturing = false;
         if (!packed && lo_last < nck && stages_may_pay(nck, chains) && overlap_usable(ctx, stream, &cus, &capturing) &&
-            cus - 2 * chains * seg_units_a(nseg) >= 32) {
+            cus - (args.conv ? 2 : 1) * chains * seg_units_a(nseg) >= 32) {
             ChunkArgs head = b, tail = b;
             head.chunk_cnt = lo_last;
             tail.chunk_lo = lo_last;

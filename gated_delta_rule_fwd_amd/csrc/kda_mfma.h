@@ -92,6 +92,10 @@ __device__ __forceinline__ float quad_swap2(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
 }
 
+// Word 3 of a gfx9 buffer descriptor for untyped raw loads (32-bit data
+// format, no swizzle, no index stride).
+constexpr int kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

@@ -67,19 +67,23 @@ inline int plan_stages(int nck, int chains, int cus, int* bounds)
 // identity with zero values (its M) -- then (B) chains the segments' initial
 // states S_{s+1} = M_s S_s + B_s, then (C) runs all P segments from their
 // initial states with outputs: about 2 segment lengths of sequential chunks
-// instead of P.  Phase A needs 2 * chains * (2P - 3) workgroups of one CU
-// each (phase C, 2 * chains * P, no more), so
-// P = floor((cus / (2 chains) + 3) / 2), capped by kMaxSegments and by
-// segments of at least kMinSegChunks.  Returns P, or 1 when fewer than 3
-// segments fit (2 segments take as long as the plain pass).
+// instead of P.  Phase C needs 2 * chains * P workgroups of one CU each,
+// phase A 2 * chains * (2P - 3) output-free ones, which run two per CU
+// (`paired`; one per CU with the short convolution, whose registers do not
+// fit half a CU), so P = min(floor(cus / (2 chains)),
+// floor((w / (2 chains) + 3) / 2)) with w = 2 cus paired or cus, capped by
+// kMaxSegments and by segments of at least kMinSegChunks.  Returns P, or 1
+// when fewer than 3 segments fit (2 segments take as long as the plain pass).
 constexpr int kMaxSegments = 8;
 constexpr int kMinSegChunks = 16;
 constexpr int kMaxSegChains = 42;   // 3 segments of more chains never fit 256 CUs
 
-inline int plan_segments(int nck, int chains, int cus)
+inline int plan_segments(int nck, int chains, int cus, bool paired)
 {
     if (chains <= 0 || chains > kMaxSegChains || nck < 3 * kMinSegChunks) return 1;
-    int p = (cus / (2 * chains) + 3) / 2;
+    int p = cus / (2 * chains);
+    const int pa = ((paired ? 2 * cus : cus) / (2 * chains) + 3) / 2;
+    if (p > pa) p = pa;
     if (p > kMaxSegments) p = kMaxSegments;
     if (p > nck / kMinSegChunks) p = nck / kMinSegChunks;
     return p >= 3 ? p : 1;

@@ -120,7 +120,7 @@ def test_segments_conv_and_norm(kda):
 
 def test_segments_packed(kda):
     """Packed sequences of mixed lengths (one empty, one of a single token):
-    each chain cuts its own chunk range into the 4 segments (24 chains,
+    each chain cuts its own chunk range into the 5 segments (24 chains,
     ceil(T/64) = 361); an empty sequence passes its initial state through
     bit for bit."""
     import torch
@@ -158,7 +158,7 @@ def test_segments_packed_conv_norm(kda):
 
 
 def test_segments_long_sampled_heads(kda):
-    """64K tokens x 16 heads (5 segments of about 205 chunks), oracle on two
+    """64K tokens x 16 heads (8 segments of 128 chunks), oracle on two
     sampled heads; with the default context the last segment's pass 1 runs
     on the context's stream beside phase A, without one after it: the same
     bits."""

@@ -135,42 +135,45 @@ SEG_DRIVER = r"""
 int main()
 {
     std::printf("%d %d %d\n", kda::kMaxSegments, kda::kMinSegChunks, kda::kMaxSegChains);
-    int nck, chains, cus;
-    while (std::scanf("%d %d %d", &nck, &chains, &cus) == 3)
-        std::printf("%d\n", kda::plan_segments(nck, chains, cus));
+    int nck, chains, cus, paired;
+    while (std::scanf("%d %d %d %d", &nck, &chains, &cus, &paired) == 4)
+        std::printf("%d\n", kda::plan_segments(nck, chains, cus, paired != 0));
     return 0;
 }
 """
 
 
 def test_segment_plan(tmp_path):
-    """Segments of the sequential pass: phase A's 2 * chains * (2P - 3)
-    workgroups fit the CUs, every segment has at least the minimum number of
+    """Segments of the sequential pass: phase C's 2 * chains * P workgroups
+    fit the CUs one per CU and phase A's 2 * chains * (2P - 3) two per CU
+    (paired) or one per CU, every segment has at least the minimum number of
     chunks, P is the largest such count up to the cap, and 1 (no segments)
-    wherever fewer than 3 segments fit.  The 64K-token, 16-head prefill on 256
-    CUs takes 5 segments."""
+    wherever fewer than 3 segments fit.  On 256 CUs the 64K-token, 16-head
+    prefill takes 8 segments paired and 5 unpaired."""
     cxx = shutil.which("g++") or shutil.which("c++")
     if not cxx:
         pytest.skip("no host C++ compiler")
     src, exe = tmp_path / "seg.cpp", tmp_path / "seg"
     src.write_text(SEG_DRIVER)
     subprocess.run([cxx, "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
-    cases = [(nck, chains, cus) for nck in (1, 47, 48, 64, 95, 96, 100, 160, 200, 1024, 4096)
-             for chains in (1, 2, 8, 16, 24, 32, 42, 43, 96) for cus in (80, 256, 304)]
-    text = "".join("%d %d %d\n" % c for c in cases)
+    cases = [(nck, chains, cus, paired) for nck in (1, 47, 48, 64, 95, 96, 100, 160, 200, 1024, 4096)
+             for chains in (1, 2, 8, 16, 24, 32, 42, 43, 96) for cus in (80, 256, 304) for paired in (0, 1)]
+    text = "".join("%d %d %d %d\n" % c for c in cases)
     out = subprocess.run([str(exe)], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
     pmax, minc, maxch = (int(x) for x in out[0].split())
 
-    def fits(p, nck, chains, cus):
-        return p <= pmax and nck // p >= minc and 2 * chains * (2 * p - 3) <= cus
+    def fits(p, nck, chains, cus, paired):
+        return (p <= pmax and nck // p >= minc and 2 * chains * p <= cus and
+                2 * chains * (2 * p - 3) <= (2 * cus if paired else cus))
 
-    for (nck, chains, cus), line in zip(cases, out[1:]):
+    for (nck, chains, cus, paired), line in zip(cases, out[1:]):
         p = int(line)
         if p == 1:
-            assert chains > maxch or not fits(3, nck, chains, cus), (nck, chains, cus)
+            assert chains > maxch or not fits(3, nck, chains, cus, paired), (nck, chains, cus, paired)
         else:
-            assert p >= 3 and fits(p, nck, chains, cus), (nck, chains, cus, p)
-            assert not fits(p + 1, nck, chains, cus), (nck, chains, cus, p)
+            assert p >= 3 and fits(p, nck, chains, cus, paired), (nck, chains, cus, paired, p)
+            assert not fits(p + 1, nck, chains, cus, paired), (nck, chains, cus, paired, p)
     got = dict(zip(cases, (int(x) for x in out[1:])))
-    assert got[(1024, 16, 256)] == 5
-    assert got[(1024, 96, 256)] == 1 and got[(47, 1, 256)] == 1 and got[(64, 32, 256)] == 3
+    assert got[(1024, 16, 256, 1)] == 8 and got[(1024, 16, 256, 0)] == 5
+    assert got[(64, 32, 256, 1)] == 4 and got[(64, 32, 256, 0)] == 3
+    assert got[(1024, 96, 256, 1)] == 1 and got[(47, 1, 256, 1)] == 1 and got[(1024, 43, 256, 1)] == 1
