@@ -1491,40 +1491,46 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
 // S_{s+1} = M_s S_s + B_s ("Kimi K3 の KDA ..." section 2.3.4.1: (A2, b2)
 // after (A1, b1) is (A2 A1, A2 b1 + b2)).  One workgroup per (chain,
 // 16-column strip of the state): the columns are independent affine systems
-// (section 2.3.2).  The products run on the fp32 matrix cores
-// (16x16x4, fp32 operands and accumulation): M_s (d_k x d_k, held like a
-// state) goes through LDS, loaded into registers one segment ahead; the
-// strip S_s stays in LDS; wave w computes rows 32w .. 32w + 31.
+// (section 2.3.2).  The products run on the fp32 matrix cores (16x16x4, fp32
+// operands and accumulation); wave w computes rows 32w .. 32w + 31.  The
+// A operand (M_s) goes from memory straight into registers in the operand
+// layout, one segment ahead: product (kk, i) takes channel 16 kk + 4 g + i
+// for operand row g, so each lane's 8 values of a row tile are one 16-byte
+// load.  The strip S_s is the B operand, from LDS; four independent
+// accumulators per wave (row tile x halves of the channels) keep the chain
+// of dependent products short.
 __global__ void __launch_bounds__(256) seg_combine_kernel(float* __restrict__ seg_states, int P, int nchains)
 {
     static_assert(DK == DV, "M_s is stored in a state-shaped block");
     constexpr int SW = 16;                       // columns per workgroup
-    constexpr int MLD = DK + 4;                  // LDS row stride of M_s (floats)
+    constexpr int XLD = SW + 4;                  // LDS row stride of the strip (floats)
     const int chain = blockIdx.x / (DV / SW), c0 = SW * (blockIdx.x % (DV / SW));
     if (chain >= nchains) return;
     float* blocks = seg_states + static_cast<size_t>(chain) * seg_state_blocks(P) * DK * DV;
     auto block = [&](int k) { return blocks + static_cast<size_t>(k) * DK * DV; };
-    __shared__ float sx[DK][SW];
-    __shared__ __attribute__((aligned(16))) float sm[DK][MLD];
+    __shared__ float sx[DK][XLD];
     const int t = threadIdx.x;
     const int w = t >> 6, l = t & 63, g = l >> 4, n = l & 15;
-    // thread t holds half a row of M_s (row t/2, columns 64 (t & 1) .. + 63)
-    // and its 8 accumulator values of B_s, both loaded one segment ahead
-    float4 mr[16];
+    // this lane's operand values of M_s: row 32w + 16tt + n, channels
+    // 16kk + 4g .. + 3; and its accumulator values of B_s
+    float4 ma[2][8];
     f32x4 bq[2];
-    auto load_next = [&](int sg) __attribute__((always_inline)) {
-        const float4* src = reinterpret_cast<const float4*>(block(seg_block_m(P, sg)) +
-                                                            static_cast<size_t>(t >> 1) * DV + 64 * (t & 1));
+    auto load = [&](int sg, float4 (&m)[2][8], f32x4 (&b)[2]) __attribute__((always_inline)) {
+        const float* Ms = block(seg_block_m(P, sg));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mr[i] = src[i];
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+                m[tt][kk] = *reinterpret_cast<const float4*>(Ms + static_cast<size_t>(32 * w + 16 * tt + n) * DV +
+                                                             16 * kk + 4 * g);
         const float* Bs = block(seg_block_b(P, sg));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                bq[tt][i] = Bs[static_cast<size_t>(32 * w + 16 * tt + 4 * g + i) * DV + c0 + n];
+                b[tt][i] = Bs[static_cast<size_t>(32 * w + 16 * tt + 4 * g + i) * DV + c0 + n];
     };
-    if (P > 2) load_next(1);
+    if (P > 2) load(1, ma, bq);
     {
         // S_1: this thread's 8 values of the strip, all loads before the stores
         float x[DK * SW / 256];
@@ -1541,30 +1547,38 @@ __global__ void __launch_bounds__(256) seg_combine_kernel(float* __restrict__ se
         }
     }
     for (int sg = 1; sg + 1 < P; ++sg) {
-        {
-            float* dst = &sm[t >> 1][64 * (t & 1)];
+        __syncthreads();   // S_s in LDS
+        float4 mn[2][8];
+        f32x4 bn[2];
+        if (sg + 2 < P) load(sg + 1, mn, bn);
+        f32x4 acc[2][2] = {{bq[0], f32x4{0.f, 0.f, 0.f, 0.f}}, {bq[1], f32x4{0.f, 0.f, 0.f, 0.f}}};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) *reinterpret_cast<float4*>(dst + 4 * i) = mr[i];
-        }
-        f32x4 acc[2] = {bq[0], bq[1]};
-        __syncthreads();   // M_s and S_s in LDS
-        if (sg + 2 < P) load_next(sg + 1);
-#pragma unroll 8
-        for (int k4 = 0; k4 < DK / 4; ++k4) {
-            const float b = sx[4 * k4 + g][n];
+        for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) acc[tt] = mma32(sm[32 * w + 16 * tt + n][4 * k4 + g], b, acc[tt]);
-        }
-        __syncthreads();   // every wave has read S_s and M_s
+            for (int i = 0; i < 4; ++i) {
+                const float b = sx[16 * kk + 4 * g + i][n];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) acc[tt][kk & 1] = mma32(ma[tt][kk][i], b, acc[tt][kk & 1]);
+            }
+        __syncthreads();   // every wave has read S_s
         float* out = block(seg_block_in(P, sg + 1));
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 32 * w + 16 * tt + 4 * g + i;
-                sx[r][n] = acc[tt][i];
-                out[static_cast<size_t>(r) * DV + c0 + n] = acc[tt][i];
+                const float y = acc[tt][0][i] + acc[tt][1][i];
+                sx[r][n] = y;
+                out[static_cast<size_t>(r) * DV + c0 + n] = y;
             }
+        if (sg + 2 < P) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                bq[tt] = bn[tt];
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) ma[tt][kk] = mn[tt][kk];
+            }
+        }
     }
 }
 
