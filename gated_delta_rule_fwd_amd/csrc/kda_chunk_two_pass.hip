@@ -1137,10 +1137,25 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         gt[0] = *reinterpret_cast<const uint4*>(src);
         gt[1] = *reinterpret_cast<const uint4*>(src + 8);
     };
+    // w * sigmoid(gate) of the 16 values this thread finishes in a tile, from
+    // the tile's gate rows (independent of o: computed a chunk ahead, beside
+    // matrix products)
+    auto gate_scale = [&](const uint4 (&gt)[2], float (&sw)[16]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4 wt = *reinterpret_cast<const float4*>(&s.nw[16 * nq + 4 * e4]);
+            const uint4 g4 = gt[e4 >> 1];
+            const uint32_t w0 = (e4 & 1) ? g4.z : g4.x, w1 = (e4 & 1) ? g4.w : g4.y;
+            sw[4 * e4 + 0] = wt.x * sigmoid_fast(bf_lo(w0));
+            sw[4 * e4 + 1] = wt.y * sigmoid_fast(bf_hi(w0));
+            sw[4 * e4 + 2] = wt.z * sigmoid_fast(bf_lo(w1));
+            sw[4 * e4 + 3] = wt.w * sigmoid_fast(bf_hi(w1));
+        }
+    };
     // (live = false: nothing is waited for or stored; the loop calls these
     // unconditionally so that no branch around a load leaves the register
     // bookkeeping of later waits uncertain)
-    auto finish = [&](int m, int b, long cbase, int rows, float own, unsigned long long word, const uint4 (&gt)[2],
+    auto finish = [&](int m, int b, long cbase, int rows, float own, unsigned long long word, const float (&sw)[16],
                       bool live) __attribute__((always_inline)) {
         for (int it = 0;
              live && static_cast<unsigned>(word >> 32) != static_cast<unsigned>(m + 1) && it < kNormSpinLimit; ++it) {
@@ -1153,13 +1168,10 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
             const float4 x = *reinterpret_cast<const float4*>(src + 4 * e4);
-            const float4 wt = *reinterpret_cast<const float4*>(&s.nw[16 * nq + 4 * e4]);
-            const uint4 g4 = gt[e4 >> 1];
-            const uint32_t w0 = (e4 & 1) ? g4.z : g4.x, w1 = (e4 & 1) ? g4.w : g4.y;
-            y[4 * e4 + 0] = x.x * inv * wt.x * sigmoid_fast(bf_lo(w0));
-            y[4 * e4 + 1] = x.y * inv * wt.y * sigmoid_fast(bf_hi(w0));
-            y[4 * e4 + 2] = x.z * inv * wt.z * sigmoid_fast(bf_lo(w1));
-            y[4 * e4 + 3] = x.w * inv * wt.w * sigmoid_fast(bf_hi(w1));
+            y[4 * e4 + 0] = x.x * inv * sw[4 * e4 + 0];
+            y[4 * e4 + 1] = x.y * inv * sw[4 * e4 + 1];
+            y[4 * e4 + 2] = x.z * inv * sw[4 * e4 + 2];
+            y[4 * e4 + 3] = x.w * inv * sw[4 * e4 + 3];
         }
         if (live && nrow < rows) {
             Tout* dst = op + (static_cast<size_t>(cbase + nrow) * H + h) * DV + j0 + 16 * nq;
@@ -1372,11 +1384,14 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
     int prev_L = 0, prev2_L = 0;
     int cur = 0;                          // output norm: obuf buffer of chunk j, (j - jb) mod 3
     float own1 = 0.f, own2 = 0.f;         // output norm: this slice's row sums of chunks j-1, j-2
-    // output norm: the other slice's row sum and the gate rows of chunk j-2,
-    // requested during the previous iteration (with its record prefetch, so
-    // the wait at its commit covers them and nothing waits on them here)
+    // output norm: the other slice's row sum of chunk j-2, requested during
+    // the previous iteration (with its record prefetch, so the wait at its
+    // commit covers it and nothing waits on it here); the gate rows of chunk
+    // j-1, requested the same way; w * sigmoid(gate) of chunk j-2, computed
+    // from its rows during the previous iteration
     unsigned long long word2 = 0ull;
-    uint4 gate2[2] = {};
+    uint4 gcur[2] = {};
+    float sw[16] = {};
     for (int j = jb; j < je; ++j) {
         const long c0 = tok0 + static_cast<long>(j) * C;
         const int L = static_cast<int>(min(static_cast<long>(C), tok1 - c0));
@@ -1387,7 +1402,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             // first, before this iteration issues any load: chunk j-2 is
             // normalised and stored, chunk j-1's row sums go out (in this
             // order: the other slice reads a word before it can be reused)
-            finish(j - 2, cur == 2 ? 0 : cur + 1, prev2_c0, prev2_L, own2, word2, gate2, with_out && j >= jb + 2);
+            finish(j - 2, cur == 2 ? 0 : cur + 1, prev2_c0, prev2_L, own2, word2, sw, with_out && j >= jb + 2);
             own1 = publish(j - 1, cur == 0 ? 2 : cur - 1, with_out && j > jb);
         }
         f16x8 fa0[2][4], fa1[2][4], qa0[2][4], qa1[2][4];
@@ -1415,12 +1430,12 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         if (more) fetch(j + 1, F1, F2);
         if constexpr (NORM) {
             // the other slice published chunk j-1's sums at the start of its
-            // iteration j; they and chunk j-1's gate rows are used at the start
-            // of the next iteration
+            // iteration j; they are used at the start of the next iteration
             word2 = poll(j - 1);
-            load_gate(prev_c0, prev_L, gate2);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // (chunk j-1's gate factors, for the start of the next iteration)
+        if constexpr (NORM) gate_scale(gcur, sw);
         step_rq(1, fa1, qa1, vv1, sh, sl, ut, oq);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ah0[2][2], al0[2][2], ah1[2][2], al1[2][2];
@@ -1432,6 +1447,7 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         f16x8 ub[2], ubl[2];
         step_t(th, tl, ut, ub, ubl);
         if (more) fetch(j + 1, F2, F3);
+        if constexpr (NORM) load_gate(c0, L, gcur);
         __builtin_amdgcn_sched_barrier(0);
         f16x8 ka0[4][2];
         float4 gm0[4];
@@ -1464,13 +1480,13 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         // slice's were requested in the last iteration), then je - 1
         const int n_run = with_out ? je - jb : 0;
         if (n_run >= 2)
-            finish(je - 2, cur == 0 ? 1 : (cur == 1 ? 2 : 0), prev2_c0, prev2_L, own2, word2, gate2, true);
+            finish(je - 2, cur == 0 ? 1 : (cur == 1 ? 2 : 0), prev2_c0, prev2_L, own2, word2, sw, true);
         if (n_run >= 1) {
             const int b = cur == 0 ? 2 : cur - 1;
             const float own = publish(je - 1, b, true);
-            uint4 gt[2];
-            load_gate(prev_c0, prev_L, gt);
-            finish(je - 1, b, prev_c0, prev_L, own, poll(je - 1), gt, true);
+            float sl1[16];
+            gate_scale(gcur, sl1);
+            finish(je - 1, b, prev_c0, prev_L, own, poll(je - 1), sl1, true);
         }
     } else {
         if (with_out && je > jb) store_tile((je - 1) & 1, prev_c0, prev_L);
