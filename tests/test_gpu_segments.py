@@ -118,6 +118,24 @@ def test_segments_conv_and_norm(kda):
               bf16_store=(odt == torch.bfloat16))
 
 
+def test_segments_paired_and_unpaired_summaries(kda):
+    """16 chains of 129 chunks: without the short convolution the summary
+    units run two per CU and the chain takes 8 segments, with it one per CU
+    and 5 segments; both against the oracle."""
+    import torch
+    B, T, H = 1, 8192 + 70, 16
+    inp = kda_inputs.make_prefill(58, B, T, H, 128, 128, s0_std=0.02)
+    o_ref, s_ref = oracle.forward(inp)
+    o, s = _run(kda, inp, torch.bfloat16)
+    check("seg_paired", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=True)
+    ws = kda_inputs.conv_weights(58, H, 128, 128)
+    cs = kda_inputs.conv_states(58, B, H, 128, 128)
+    o_ref, s_ref, _ = oracle.forward_conv(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.g, inp.beta, ws,
+                                          tuple(_f(c) for c in cs), inp.init_state, inp.cu_seqlens)
+    o, s = _run(kda, inp, torch.float32, conv_weights=tuple(dev(x) for x in ws), conv_init=tuple(dev(c) for c in cs))
+    check("seg_unpaired_conv", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
+
+
 def test_segments_packed(kda):
     """Packed sequences of mixed lengths (one empty, one of a single token):
     each chain cuts its own chunk range into the 5 segments (24 chains,
