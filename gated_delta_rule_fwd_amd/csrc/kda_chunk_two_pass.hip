@@ -1012,6 +1012,23 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             }
             return;
         }
+        if constexpr (!CONV && OUT) {
+            // rows past the end read the last valid token (T' has zero
+            // columns for them, so only finiteness matters); raw buffer
+            // loads from the chunk's first row of this slice, a uniform base
+            // (the summary launch keeps the plain loads: under its register
+            // bound the offsets' registers would wait on loads in flight)
+            const int lim = static_cast<int>(min(static_cast<long>(C - 1), tok1 - 1 - cb));
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(vp + (static_cast<size_t>(cb) * H + h) * DV + j0), 0,
+                (lim * H * DV + DVS) * 2, kBufferWord3);
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int idx = t + NT * u, r = idx / PPR, part = idx % PPR;
+                PV[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (min(r, lim) * H * DV + 8 * part) * 2, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int idx = t + NT * u, r = idx / PPR, part = idx % PPR;
@@ -1081,16 +1098,21 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
 
     // Output tiles are staged in LDS (alternating buffers) and written out as
     // whole rows during the next chunk, or after the loop for the last one.
+    // (raw buffer stores from the tile's first row of this slice, a uniform base)
     auto store_tile = [&](int buf, long cbase, int rows) __attribute__((always_inline)) {
         constexpr int CH = 16 / sizeof(Tout);            // elements per 16-byte piece
         constexpr int PER_ROW = DVS / CH;
         const char* src = reinterpret_cast<const char*>(s.obuf[buf]);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            op + (static_cast<size_t>(cbase) * H + h) * DV + j0, 0,
+            static_cast<int>(((rows - 1) * H * DV + DVS) * sizeof(Tout)), kBufferWord3);
 #pragma unroll
         for (int pc = t; pc < C * PER_ROW; pc += NT) {
             const int r = pc / PER_ROW, part = pc % PER_ROW;
             if (r < rows) {
-                const uint4 val = *reinterpret_cast<const uint4*>(src + (r * DVS + part * CH) * sizeof(Tout));
-                *reinterpret_cast<uint4*>(op + (static_cast<size_t>(cbase + r) * H + h) * DV + j0 + part * CH) = val;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(src + (r * DVS + part * CH) * sizeof(Tout));
+                __builtin_amdgcn_raw_buffer_store_b128(val, rs, static_cast<int>((r * H * DV + part * CH) * sizeof(Tout)),
+                                                       0, 0);
             }
         }
     };
@@ -1131,11 +1153,18 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
         return __hip_atomic_load(other_words + (m & (kNormSlotsPerRow - 1)) * C, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
     };
+    // (raw buffer loads from the tile's first gate row of this slice, a
+    // uniform base; rows past the end read the last valid one)
     auto load_gate = [&](long cbase, int rows, uint4 (&gt)[2]) __attribute__((always_inline)) {
-        const long tk = cbase + min(nrow, max(rows - 1, 0));
-        const uint16_t* src = gp + (static_cast<size_t>(tk) * H + h) * DV + j0 + 16 * nq;
-        gt[0] = *reinterpret_cast<const uint4*>(src);
-        gt[1] = *reinterpret_cast<const uint4*>(src + 8);
+        const int last = max(rows - 1, 0);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(gp + (static_cast<size_t>(cbase) * H + h) * DV + j0), 0,
+            (last * H * DV + DVS) * 2, kBufferWord3);
+        const int off = (min(nrow, last) * H * DV + 16 * nq) * 2;
+        const u32x4 g0 = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const u32x4 g1 = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16, 0, 0);
+        gt[0] = make_uint4(g0[0], g0[1], g0[2], g0[3]);
+        gt[1] = make_uint4(g1[0], g1[1], g1[2], g1[3]);
     };
     // w * sigmoid(gate) of the 16 values this thread finishes in a tile, from
     // the tile's gate rows (independent of o: computed a chunk ahead, beside
@@ -1174,18 +1203,25 @@ chunk_scan_kernel(ChunkArgs a, const ChunkRecord* __restrict__ recs, int nslots,
             y[4 * e4 + 3] = x.w * inv * sw[4 * e4 + 3];
         }
         if (live && nrow < rows) {
-            Tout* dst = op + (static_cast<size_t>(cbase + nrow) * H + h) * DV + j0 + 16 * nq;
+            // raw buffer stores from the tile's first row of this slice
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                op + (static_cast<size_t>(cbase) * H + h) * DV + j0, 0,
+                static_cast<int>(((rows - 1) * H * DV + DVS) * sizeof(Tout)), kBufferWord3);
+            const int off = static_cast<int>((nrow * H * DV + 16 * nq) * sizeof(Tout));
             if constexpr (std::is_same<Tout, float>::value) {
 #pragma unroll
                 for (int e4 = 0; e4 < 4; ++e4)
-                    *reinterpret_cast<float4*>(dst + 4 * e4) =
-                        make_float4(y[4 * e4], y[4 * e4 + 1], y[4 * e4 + 2], y[4 * e4 + 3]);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4{__float_as_uint(y[4 * e4]), __float_as_uint(y[4 * e4 + 1]), __float_as_uint(y[4 * e4 + 2]),
+                              __float_as_uint(y[4 * e4 + 3])},
+                        rs, off + 16 * e4, 0, 0);
             } else {
 #pragma unroll
                 for (int h8 = 0; h8 < 2; ++h8)
-                    *reinterpret_cast<uint4*>(dst + 8 * h8) =
-                        make_uint4(pack_bf16x2(y[8 * h8], y[8 * h8 + 1]), pack_bf16x2(y[8 * h8 + 2], y[8 * h8 + 3]),
-                                   pack_bf16x2(y[8 * h8 + 4], y[8 * h8 + 5]), pack_bf16x2(y[8 * h8 + 6], y[8 * h8 + 7]));
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4{pack_bf16x2(y[8 * h8], y[8 * h8 + 1]), pack_bf16x2(y[8 * h8 + 2], y[8 * h8 + 3]),
+                              pack_bf16x2(y[8 * h8 + 4], y[8 * h8 + 5]), pack_bf16x2(y[8 * h8 + 6], y[8 * h8 + 7])},
+                        rs, off + 16 * h8, 0, 0);
             }
         }
     };
