@@ -1650,15 +1650,15 @@ TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bo
     // packed sequences: ceil(T / 64) bounds the chunks of the longest one
     const int nck_max = packed ? (T + C - 1) / C : nck;
     const bool may_segment = plan_segments(nck_max, static_cast<int>(chains), 1 << 20, true) > 1;
+    const int pcap = may_segment ? segment_cap(nck_max, static_cast<int>(chains)) : 1;
     TwoPassLayout L;
     L.norm_off = static_cast<size_t>(slots) * H * kChunkRecordBytes;
     L.norm_off += packed ? (static_cast<size_t>(slots) * sizeof(int) + 255) / 256 * 256
                          : static_cast<size_t>(B) * H * DK * DV * sizeof(float);
-    const long long units = may_segment ? seg_units_c(kMaxSegments) : 1;   // phase C writes o
+    const long long units = may_segment ? seg_units_c(pcap) : 1;   // phase C writes o
     L.seg_off = L.norm_off + (norm ? norm_slot_words(chains * units) * sizeof(unsigned long long) : 0);
     L.seg_off = (L.seg_off + 255) / 256 * 256;
-    L.total = L.seg_off + (may_segment ? static_cast<size_t>(chains) * seg_state_blocks(kMaxSegments) * DK * DV *
-                                             sizeof(float)
+    L.total = L.seg_off + (may_segment ? static_cast<size_t>(chains) * seg_state_blocks(pcap) * DK * DV * sizeof(float)
                                        : 0);
     return L;
 }
@@ -1666,33 +1666,34 @@ TwoPassLayout two_pass_layout(int B, int T, int H, int num_seqs, bool packed, bo
 // Workspace of the windowed order: a ring of records for `window` chunks of
 // every sequence, the state carried between windows, the output norm's
 // row-sum words.
-// With `seg`, room for the segmented order inside each window: row-sum words
-// for its segment units and the segment states.
+// With seg_p > 0, room for the segmented order inside each window, up to
+// seg_p segments: row-sum words for its segment units and the segment states.
 struct WindowLayout {
     size_t carry_off, norm_off, seg_off, total;
 };
 
-WindowLayout window_layout(int B, int H, int num_seqs, bool packed, bool norm, long long window, bool seg = false)
+WindowLayout window_layout(int B, int H, int num_seqs, bool packed, bool norm, long long window, int seg_p = 0)
 {
     const long long chains = static_cast<long long>(packed ? num_seqs : B) * H;
     WindowLayout L;
     L.carry_off = static_cast<size_t>(window) * chains * kChunkRecordBytes;
     L.norm_off = L.carry_off + static_cast<size_t>(chains) * DK * DV * sizeof(float);
-    const long long units = seg ? seg_units_c(kMaxSegments) : 1;
+    const long long units = seg_p > 0 ? seg_units_c(seg_p) : 1;
     L.seg_off = L.norm_off + (norm ? norm_slot_words(chains * units) * sizeof(unsigned long long) : 0);
     L.seg_off = (L.seg_off + 255) / 256 * 256;
-    L.total = L.seg_off + (seg ? static_cast<size_t>(chains) * seg_state_blocks(kMaxSegments) * DK * DV *
-                                     sizeof(float)
-                               : 0);
+    L.total = L.seg_off + (seg_p > 0 ? static_cast<size_t>(chains) * seg_state_blocks(seg_p) * DK * DV * sizeof(float)
+                                     : 0);
     return L;
 }
 
 // Largest window (chunks of every sequence per launch) that fits `bytes`,
 // at most `nck` and below 2^24 pass-1 workgroups per launch; 0: none fits.
+// With `seg`, room for the segmented order over windows of up to nck chunks.
 long long window_chunks(int B, int H, int num_seqs, bool packed, bool norm, int nck, size_t bytes, bool seg = false)
 {
     const long long chains = static_cast<long long>(packed ? num_seqs : B) * H;
-    const size_t fixed = window_layout(B, H, num_seqs, packed, norm, 0, seg).total;
+    const int seg_p = seg && chains <= kMaxSegChains ? segment_cap(nck, static_cast<int>(chains)) : 0;
+    const size_t fixed = window_layout(B, H, num_seqs, packed, norm, 0, seg_p).total;
     if (chains <= 0 || bytes < fixed) return 0;
     long long w = static_cast<long long>((bytes - fixed) / (static_cast<size_t>(chains) * kChunkRecordBytes));
     if (w > nck) w = nck;
@@ -1942,7 +1943,8 @@ hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_byt
     }
     if (!seg) w = window_chunks(args.B, args.H, args.num_seqs, packed, norm, nck, ws_bytes);
     if (w < 1) return hipErrorInvalidValue;   // below two_pass_min_workspace_bytes
-    const WindowLayout lay = window_layout(args.B, args.H, args.num_seqs, packed, norm, w, seg);
+    const int seg_p = seg ? segment_cap(nck, static_cast<int>(chains)) : 0;
+    const WindowLayout lay = window_layout(args.B, args.H, args.num_seqs, packed, norm, w, seg_p);
     char* base = static_cast<char*>(workspace);
     ChunkRecord* recs = reinterpret_cast<ChunkRecord*>(base);
     float* carried = reinterpret_cast<float*>(base + lay.carry_off);
@@ -1951,7 +1953,7 @@ hipError_t launch_windowed(const ChunkArgs& args, void* workspace, size_t ws_byt
     unsigned long long* norm_slots = nullptr;
     if (norm) {
         norm_slots = reinterpret_cast<unsigned long long*>(base + lay.norm_off);
-        const size_t words = norm_slot_words(static_cast<long long>(chains) * (seg ? seg_units_c(kMaxSegments) : 1));
+        const size_t words = norm_slot_words(static_cast<long long>(chains) * (seg_p > 0 ? seg_units_c(seg_p) : 1));
         const size_t blocks = (words + 255) / 256;
         zero_words_kernel<<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(norm_slots, words);
     }

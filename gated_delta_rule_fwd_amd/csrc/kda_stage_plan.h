@@ -72,11 +72,26 @@ inline int plan_stages(int nck, int chains, int cus, int* bounds)
 // (`paired`; one per CU with the short convolution, whose registers do not
 // fit half a CU), so P = min(floor(cus / (2 chains)),
 // floor((w / (2 chains) + 3) / 2)) with w = 2 cus paired or cus, capped by
-// kMaxSegments and by segments of at least kMinSegChunks.  Returns P, or 1
-// when fewer than 3 segments fit (2 segments take as long as the plain pass).
-constexpr int kMaxSegments = 8;
+// segment_cap.  Returns P, or 1 when fewer than 3 segments fit (2 segments
+// take as long as the plain pass).
+constexpr int kMaxSegments = 32;
 constexpr int kMinSegChunks = 16;
 constexpr int kMaxSegChains = 42;   // 3 segments of more chains never fit 256 CUs
+// segments x chains at most: the segment states a call reserves (3P - 3
+// state-sized blocks per chain) stay below 3 * kSegBudget blocks, ~24 MB
+constexpr int kSegBudget = 128;
+
+// The most segments `chains` chains of `nck` chunks may take on any device:
+// at most kMaxSegments, kSegBudget / chains and segments of at least
+// kMinSegChunks chunks.  The workspace reserves for this many.
+inline int segment_cap(int nck, int chains)
+{
+    if (chains <= 0) return 1;
+    int p = kMaxSegments;
+    if (p > kSegBudget / chains) p = kSegBudget / chains;
+    if (p > nck / kMinSegChunks) p = nck / kMinSegChunks;
+    return p < 1 ? 1 : p;
+}
 
 inline int plan_segments(int nck, int chains, int cus, bool paired)
 {
@@ -84,8 +99,8 @@ inline int plan_segments(int nck, int chains, int cus, bool paired)
     int p = cus / (2 * chains);
     const int pa = ((paired ? 2 * cus : cus) / (2 * chains) + 3) / 2;
     if (p > pa) p = pa;
-    if (p > kMaxSegments) p = kMaxSegments;
-    if (p > nck / kMinSegChunks) p = nck / kMinSegChunks;
+    const int cap = segment_cap(nck, chains);
+    if (p > cap) p = cap;
     return p >= 3 ? p : 1;
 }
 

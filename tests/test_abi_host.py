@@ -153,7 +153,7 @@ def test_size_limits(lib):
     # matrix-core path: 2^24 or more (chunk, head) records run in windows,
     # so such a call is not refused and its least workspace stays small
     d = _desc(B=1, T=2 ** 30, H=1)
-    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)) == 2 ** 24 * RECORD + STATE + SEG_BLOCKS * STATE
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d)) == 2 ** 24 * RECORD + STATE + seg_blocks(1, 2 ** 24) * STATE
     assert lib.kda_chunk_fwd_min_workspace_bytes(ctypes.byref(d)) == RECORD + STATE
     assert _call(lib, d, ws=FAKE, ws_bytes=RECORD + STATE - 16) == 3
     # decode: N*H <= 2^24 - 1 chains
@@ -164,11 +164,19 @@ def test_size_limits(lib):
 RECORD = 74240   # bytes of chunk-local operands per (64-token chunk, head)
 STATE = 128 * 128 * 4   # fp32 state of one chain, carried between the stages of a dense batch
 # a batch of at most 42 chains and at least 48 chunks per sequence may take
-# the segmented sequential pass: 3 * 8 - 3 state-sized blocks per chain
-# (segment 0's end state, B_s and M_s of the middle segments, the initial
-# states of segments 1 .. 7, a copy of the chain's initial state), 256-byte
-# aligned after the rest
-SEG_BLOCKS = 3 * 8 - 3
+# the segmented sequential pass: 3P - 3 state-sized blocks per chain for the
+# most segments P it may take on any device, min(32, 128 // chains,
+# chunks // 16) (segment 0's end state, B_s and M_s of the middle segments,
+# the initial states of segments 1 .. P-1, a copy of the chain's initial
+# state), 256-byte aligned after the rest
+
+
+def seg_cap(chains, nck):
+    return min(32, 128 // chains, nck // 16)
+
+
+def seg_blocks(chains, nck):
+    return 3 * seg_cap(chains, nck) - 3
 
 
 def test_workspace_sizes(lib):
@@ -186,13 +194,17 @@ def test_workspace_sizes(lib):
     assert size(B=1, T=64 * 40, H=2, num_seqs=3) == 40 * 2 * RECORD + 256 + 3 * 2 * RECORD
     # both readings may take the segmented pass here (at least 48 chunks, few chains): the packed one
     # (53 slots, 6 chains) needs more
-    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 53 * 2 * RECORD + 256 + 6 * SEG_BLOCKS * STATE
+    assert size(B=1, T=64 * 50, H=2, num_seqs=3) == 53 * 2 * RECORD + 256 + 6 * seg_blocks(6, 50) * STATE
     # segment states: chains <= 42 and ceil(T / 64) >= 48 (dense only)
-    assert size(B=1, T=96 * 64, H=42) == 96 * 42 * RECORD + 42 * STATE + 42 * SEG_BLOCKS * STATE
+    assert size(B=1, T=96 * 64, H=42) == 96 * 42 * RECORD + 42 * STATE + 42 * seg_blocks(42, 96) * STATE
     assert size(B=1, T=96 * 64, H=43) == 96 * 43 * RECORD + 43 * STATE
     assert size(B=1, T=47 * 64, H=2) == 47 * 2 * RECORD + 2 * STATE
-    assert size(B=1, T=47 * 64 + 1, H=2) == 48 * 2 * RECORD + 2 * STATE + 2 * SEG_BLOCKS * STATE
-    assert size(B=2, T=6100, H=3) == 2 * 96 * 3 * RECORD + 6 * STATE + 6 * SEG_BLOCKS * STATE
+    assert size(B=1, T=47 * 64 + 1, H=2) == 48 * 2 * RECORD + 2 * STATE + 2 * seg_blocks(2, 48) * STATE
+    assert size(B=2, T=6100, H=3) == 2 * 96 * 3 * RECORD + 6 * STATE + 6 * seg_blocks(6, 96) * STATE
+    # few chains of a long sequence: up to 32 segments, 93 blocks per chain
+    assert size(B=1, T=64 * 4096, H=1) == 4096 * RECORD + STATE + 93 * STATE
+    assert size(B=1, T=64 * 4096, H=4) == 4 * 4096 * RECORD + 4 * STATE + 4 * 93 * STATE
+    assert size(B=1, T=64 * 4096, H=16) == 16 * 4096 * RECORD + 16 * STATE + 16 * 21 * STATE
     # validation counters come first
     assert size(B=2, T=64, H=1, flags=kda.FLAG_QK_L2NORM | kda.FLAG_VALIDATE) == 256 + 2 * RECORD + 2 * STATE
     # a misaligned workspace is refused before anything runs
@@ -300,8 +312,9 @@ def test_workspace_for_the_output_norm(lib):
     assert size(B=2, T=100, H=3, out_dtype=0, flags=on) == size(B=2, T=100, H=3) + 2 * 3 * words
     assert size(B=1, T=1000, H=2, num_seqs=5, flags=on) == size(B=1, T=1000, H=2, num_seqs=5) + 5 * 2 * words
     # a batch that may take the segmented pass: words for each of the up to
-    # 8 segment units of the phase with outputs per chain, then the segment states
-    assert size(B=1, T=96 * 64, H=2, flags=on) == 96 * 2 * RECORD + 2 * STATE + 2 * 8 * words + 2 * SEG_BLOCKS * STATE
+    # P segment units of the phase with outputs per chain, then the segment states
+    assert size(B=1, T=96 * 64, H=2, flags=on) == (96 * 2 * RECORD + 2 * STATE + 2 * seg_cap(2, 96) * words +
+                                                   2 * seg_blocks(2, 96) * STATE)
     # fp32 path: a bf16 o is staged in fp32 for the norm pass; an fp32 o is
     # normalised in place
     assert size(B=2, T=100, H=3, d_k=64, d_v=64, flags=on) == 2 * 100 * 3 * 64 * 4

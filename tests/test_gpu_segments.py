@@ -3,7 +3,7 @@ and many chunks splits every chain into P segments, summarises the middle
 segments as affine maps S -> M S + B, chains the segments' initial states and
 reruns the segments with outputs ("Kimi K3 の KDA ..." sections 2.3.4.2-
 2.3.4.5).  The shapes here make the library take that order on a 256-CU
-MI355X (3 to 8 segments; the plan itself is checked on the CPU in
+MI355X (3 to 32 segments; the plan itself is checked on the CPU in
 test_stage_plan.py); o and the final state are compared with the fp64 oracle
 at the same tolerances as the plain order.  Marked ``gpu``."""
 import numpy as np
@@ -134,6 +134,38 @@ def test_segments_paired_and_unpaired_summaries(kda):
                                           tuple(_f(c) for c in cs), inp.init_state, inp.cu_seqlens)
     o, s = _run(kda, inp, torch.float32, conv_weights=tuple(dev(x) for x in ws), conv_init=tuple(dev(c) for c in cs))
     check("seg_unpaired_conv", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
+
+
+@pytest.mark.parametrize("shape", [(1, 64 * 600 + 17, 1), (2, 64 * 520, 2)], ids=["P32_one_chain", "P32_four_chains"])
+def test_segments_many(kda, shape):
+    """Few chains of many chunks take up to 32 segments (at most 128
+    segment-chains in all): 32 segments of 19 chunks for one chain, of 17
+    for four; against the oracle, with the output norm too (its row-sum
+    words indexed per segment unit)."""
+    import torch
+    B, T, H = shape
+    inp = kda_inputs.make_prefill(59, B, T, H, 128, 128, s0_std=0.02)
+    o_ref, s_ref = oracle.forward(inp)
+    o, s = _run(kda, inp, torch.bfloat16)
+    check("seg_many_%dx%d" % (B, H), host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=True)
+    gate = kda_inputs.make_out_gate(59, inp.v.shape)
+    y_ref = oracle.out_norm(o_ref, _f(gate).astype(np.float64), None, EPS)
+    o, s = _run(kda, inp, torch.float32, out_gate=dev(gate), norm_eps=EPS)
+    check("seg_many_norm_%dx%d" % (B, H), host64(o), y_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
+
+
+def test_segments_many_with_the_short_convolution(kda):
+    """Four chains of 520 chunks with the short convolution: the summaries
+    run one per CU, so 17 segments; against the oracle."""
+    import torch
+    B, T, H = 2, 64 * 520, 2
+    inp = kda_inputs.make_prefill(60, B, T, H, 128, 128, s0_std=0.02)
+    ws = kda_inputs.conv_weights(60, H, 128, 128)
+    cs = kda_inputs.conv_states(60, B, H, 128, 128)
+    o_ref, s_ref, _ = oracle.forward_conv(inp.f32("q"), inp.f32("k"), inp.f32("v"), inp.g, inp.beta, ws,
+                                          tuple(_f(c) for c in cs), inp.init_state, inp.cu_seqlens)
+    o, s = _run(kda, inp, torch.float32, conv_weights=tuple(dev(x) for x in ws), conv_init=tuple(dev(c) for c in cs))
+    check("seg_many_conv", host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
 
 
 def test_segments_packed(kda):

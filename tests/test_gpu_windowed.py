@@ -38,11 +38,17 @@ def _ws(nseq, H, window, norm=False):
     return chains * (window * RECORD + STATE + (4096 if norm else 0))
 
 
-def _ws_seg(nseq, H, window):
+def _ws_seg(nseq, H, window, nck):
     """Workspace bytes of a window of `window` chunks with room for the
-    segmented order inside it (21 state-sized blocks per chain)."""
+    segmented order inside it: 3P - 3 state-sized blocks per chain for the
+    most segments P a sequence of nck chunks may take, min(32, 128 // chains,
+    nck // 16)."""
     chains = nseq * H
-    return chains * (window * RECORD + STATE + 21 * STATE)
+    return chains * (window * RECORD + STATE + (3 * _seg_cap(chains, nck) - 3) * STATE)
+
+
+def _seg_cap(chains, nck):
+    return min(32, 128 // chains, nck // 16)
 
 
 def _args(inp):
@@ -106,12 +112,13 @@ def test_windowed_segments_against_oracle(kda, window):
     inp = kda_inputs.make_prefill(69, B, T, H, 128, 128, s0_std=0.02)
     gate = kda_inputs.make_out_gate(69, inp.v.shape)
     o_ref, s_ref = oracle.forward(inp)
-    o, s = kda.chunk_fwd(*_args(inp), workspace_limit=_ws_seg(B, H, window))
+    nck = (T + 63) // 64
+    o, s = kda.chunk_fwd(*_args(inp), workspace_limit=_ws_seg(B, H, window, nck))
     torch.cuda.synchronize()
     check("win_seg%d" % window, host64(o), o_ref, host64(s), s_ref, TOL_BF16, bf16_store=True)
     y_ref = oracle.out_norm(o_ref, kda_inputs.bf16_to_f32(gate).astype(np.float64), None, EPS)
     o, s = kda.chunk_fwd(*_args(inp), out_gate=dev(gate), norm_eps=EPS, out_dtype=torch.float32,
-                         workspace_limit=_ws_seg(B, H, window) + 2 * 8 * 4096)
+                         workspace_limit=_ws_seg(B, H, window, nck) + B * H * _seg_cap(B * H, nck) * 4096)
     torch.cuda.synchronize()
     check("win_seg%d_norm" % window, host64(o), y_ref, host64(s), s_ref, TOL_BF16, bf16_store=False)
 

@@ -134,7 +134,7 @@ SEG_DRIVER = r"""
 #include <cstdio>
 int main()
 {
-    std::printf("%d %d %d\n", kda::kMaxSegments, kda::kMinSegChunks, kda::kMaxSegChains);
+    std::printf("%d %d %d %d\n", kda::kMaxSegments, kda::kMinSegChunks, kda::kMaxSegChains, kda::kSegBudget);
     int nck, chains, cus, paired;
     while (std::scanf("%d %d %d %d", &nck, &chains, &cus, &paired) == 4)
         std::printf("%d\n", kda::plan_segments(nck, chains, cus, paired != 0));
@@ -147,23 +147,26 @@ def test_segment_plan(tmp_path):
     """Segments of the sequential pass: phase C's 2 * chains * P workgroups
     fit the CUs one per CU and phase A's 2 * chains * (2P - 3) two per CU
     (paired) or one per CU, every segment has at least the minimum number of
-    chunks, P is the largest such count up to the cap, and 1 (no segments)
-    wherever fewer than 3 segments fit.  On 256 CUs the 64K-token, 16-head
-    prefill takes 8 segments paired and 5 unpaired."""
+    chunks, P * chains stays within the budget the workspace reserves for,
+    P is the largest such count up to the cap, and 1 (no segments) wherever
+    fewer than 3 segments fit.  On 256 CUs the 64K-token, 16-head prefill
+    takes 8 segments paired and 5 unpaired; one or four chains of 4096 chunks
+    take 32."""
     cxx = shutil.which("g++") or shutil.which("c++")
     if not cxx:
         pytest.skip("no host C++ compiler")
     src, exe = tmp_path / "seg.cpp", tmp_path / "seg"
     src.write_text(SEG_DRIVER)
     subprocess.run([cxx, "-std=c++17", "-O1", "-I", CSRC, str(src), "-o", str(exe)], check=True)
-    cases = [(nck, chains, cus, paired) for nck in (1, 47, 48, 64, 95, 96, 100, 160, 200, 1024, 4096)
-             for chains in (1, 2, 8, 16, 24, 32, 42, 43, 96) for cus in (80, 256, 304) for paired in (0, 1)]
+    cases = [(nck, chains, cus, paired) for nck in (1, 47, 48, 64, 95, 96, 100, 160, 200, 512, 1024, 4096)
+             for chains in (1, 2, 3, 4, 8, 12, 16, 24, 32, 42, 43, 96) for cus in (80, 256, 304, 1024)
+             for paired in (0, 1)]
     text = "".join("%d %d %d %d\n" % c for c in cases)
     out = subprocess.run([str(exe)], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
-    pmax, minc, maxch = (int(x) for x in out[0].split())
+    pmax, minc, maxch, budget = (int(x) for x in out[0].split())
 
     def fits(p, nck, chains, cus, paired):
-        return (p <= pmax and nck // p >= minc and 2 * chains * p <= cus and
+        return (p <= pmax and p * chains <= budget and nck // p >= minc and 2 * chains * p <= cus and
                 2 * chains * (2 * p - 3) <= (2 * cus if paired else cus))
 
     for (nck, chains, cus, paired), line in zip(cases, out[1:]):
@@ -177,3 +180,5 @@ def test_segment_plan(tmp_path):
     assert got[(1024, 16, 256, 1)] == 8 and got[(1024, 16, 256, 0)] == 5
     assert got[(64, 32, 256, 1)] == 4 and got[(64, 32, 256, 0)] == 3
     assert got[(1024, 96, 256, 1)] == 1 and got[(47, 1, 256, 1)] == 1 and got[(1024, 43, 256, 1)] == 1
+    assert got[(4096, 1, 256, 1)] == 32 and got[(4096, 4, 256, 1)] == 32 and got[(1024, 8, 256, 1)] == 16
+    assert got[(1024, 12, 256, 1)] == 10 and got[(4096, 1, 1024, 1)] == 32 and got[(4096, 8, 1024, 1)] == 16
