@@ -163,8 +163,10 @@ typedef struct kda_chunk_desc {
  * adds 4 KB per chain of row-sum words; a batch of at most 42 chains and at
  * least 48 chunks per sequence (packed: ceil(T/64)), which may take the
  * segmented order,
- * adds 21 state-sized blocks (1.31 MiB) per chain and row-sum words for 8
- * segment units per chain.  The fp32 path needs none, except with
+ * adds 3P - 3 state-sized blocks (64 KB each) per chain and, with
+ * KDA_FLAG_OUT_NORM, row-sum words for P segment units per chain, where
+ * P = min(32, 128 / chains, chunks / 16) is the most segments the call may
+ * take (at most ~23 MB in all).  The fp32 path needs none, except with
  * KDA_FLAG_OUT_NORM and a bf16 o: B*T*H*d_v fp32 values.  KDA_FLAG_VALIDATE
  * adds 256 bytes in front.  When num_seqs > 0 and B == 1 the figure covers
  * both the dense and the packed (cu_seqlens) layout.  Returns 0 for a
@@ -196,7 +198,8 @@ KDA_API size_t kda_chunk_fwd_min_workspace_bytes(const kda_chunk_desc* desc);
  *  - segmented: a batch of at most 42 chains and at least 48 chunks per
  *    sequence (packed sequences: ceil(T/64) chunks), with the full
  *    workspace.  Each chain is cut into P segments of its own chunk range
- *    (3 <= P <= 8, as many as the device's CUs hold); the middle
+ *    (3 <= P <= 32, as many as the device's CUs hold and at most 128
+ *    segment-chains in all); the middle
  *    segments are summarised as affine maps S -> M S + B and combined
  *    ("Kimi K3 の KDA ..." sections 2.3.4.2-2.3.4.5), then the segments run
  *    again from their true initial states.  On `stream`; with a usable
