@@ -331,10 +331,18 @@ typedef struct kda_decay_gate {
  *           (ones), 16-byte aligned
  *   eps     >= 0, added to the mean square (the pages give no value)
  *
- * The decode step applies it in the kernel that computes o.  The prefill
- * paths split each row of o over workgroups, so there it runs as a second
- * kernel over fp32 o: in place for an fp32 o, from the workspace (sized by
- * KDA_FLAG_OUT_NORM) for a bf16 o.
+ * The decode step applies it in the kernel that computes o.  The matrix-core
+ * prefill applies it in the sequential kernel that computes o: each row of o
+ * is split over the two value-slice workgroups of a chain, which exchange
+ * per-row sums of o^2 (taken before rounding) through words in the
+ * workspace and normalise their own columns as they store them.  A slice
+ * waits for its partner's word with a bounded number of retries; should the
+ * partner not get a compute unit while it waits (the pair's workgroup ids
+ * are 8 apart, so a device that holds fewer than 9 of them at once), the
+ * rows it did not deliver come out NaN rather than wrongly scaled.  The
+ * exact fp32 path runs the norm as a second kernel over fp32 o: in place
+ * for an fp32 o, from the workspace (sized by KDA_FLAG_OUT_NORM) for a
+ * bf16 o.
  */
 typedef struct kda_out_norm {
     const void* gate;
