@@ -133,13 +133,6 @@ __device__ __forceinline__ float flip_sign(float x, uint32_t mask, int i)
 // into q^ and k^ of row r, which gives every pair factor its sigma_r sigma_s,
 // and the chunk-end sign sigma_L into gamma and K^ gamma/Gamma.  All the
 // exponential factors stay those of b = sum log|alpha|.
-// Pass 1 writes each record with non-temporal stores: pass 2 reads it back
-// hundreds of MB of traffic later, so keeping it in the caches gains nothing
-// (the 64K-token, 96-head prefill runs ~0.3 % faster).  The input loads stay
-// ordinary: as non-temporal loads they made that call 5 % slower (each
-// 128-byte line of q, k and g is read by two load instructions, which
-// probably then fetch it twice).
-typedef unsigned int u32x4nt __attribute__((ext_vector_type(4)));
 constexpr int XS_LD = DK + 8;   // row stride (bf16) of the short convolution's staging
 
 template <bool SIGNED, bool CONV>
@@ -456,7 +449,7 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             s.fac[3][1][c] = __expf(t3);
             s.fac[3][2][c] = __expf(r3);
             s.fac[3][3][c] = 1.f;
-            __builtin_nontemporal_store(__expf(r4), &rg->gam[c]);
+            rg->gam[c] = __expf(r4);
         }
         if constexpr (SIGNED) {
             // sign of the decay product over the whole chunk, channel c
@@ -470,7 +463,7 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             } else {
                 s.fac[2][3][c] *= sL;
                 s.fac[3][3][c] = sL;
-                __builtin_nontemporal_store(rg->gam[c] * sL, &rg->gam[c]);
+                rg->gam[c] *= sL;
             }
         }
     }
@@ -560,10 +553,10 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
                 k0[e] = static_cast<_Float16>(kgv[e]);
                 k1[e] = static_cast<_Float16>(kgv[4 + e]);
             }
-            __builtin_nontemporal_store(q0, reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->qg[w][kb][l0]) + eo));
-            __builtin_nontemporal_store(q1, reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->qg[w][kb][l1]) + eo));
-            __builtin_nontemporal_store(k0, reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->kgn[w][kb][l0]) + eo));
-            __builtin_nontemporal_store(k1, reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->kgn[w][kb][l1]) + eo));
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->qg[w][kb][l0]) + eo) = q0;
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->qg[w][kb][l1]) + eo) = q1;
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->kgn[w][kb][l0]) + eo) = k0;
+            *reinterpret_cast<f16x4*>(reinterpret_cast<_Float16*>(&rg->kgn[w][kb][l1]) + eo) = k1;
         }
     }
     // diagonal tile (w, w): lane holds rows 16w + 4g + i, column 16w + n.
@@ -757,8 +750,8 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
             tl[e] = lo;
         }
         const int p = tri_block(w, kb);
-        __builtin_nontemporal_store(th, &rg->tp[0][p][l]);
-        __builtin_nontemporal_store(tl, &rg->tp[1][p][l]);
+        rg->tp[0][p][l] = th;
+        rg->tp[1][p][l] = tl;
     }
 
     // A_qk and K'^T fragments: LDS -> record, whole 16-byte pieces
@@ -767,18 +760,12 @@ chunk_prep_kernel(ChunkArgs a, ChunkRecord* __restrict__ recs, const int* __rest
         uint4* dst = reinterpret_cast<uint4*>(&rg->aqk[0][0][0]);
         constexpr int NA = static_cast<int>(sizeof(s.aqk) / 16);
 #pragma unroll
-        for (int i = t; i < NA; i += NT) {
-            const uint4 x = src[(i & ~63) | swz(i & 63)];
-            __builtin_nontemporal_store(u32x4nt{x.x, x.y, x.z, x.w}, reinterpret_cast<u32x4nt*>(dst + i));
-        }
+        for (int i = t; i < NA; i += NT) dst[i] = src[(i & ~63) | swz(i & 63)];
         const uint4* src2 = reinterpret_cast<const uint4*>(&s.u.kp[0][0][0]);
         uint4* dst2 = reinterpret_cast<uint4*>(&rg->kp[0][0][0]);
         constexpr int NK = static_cast<int>(sizeof(s.u.kp) / 16);
 #pragma unroll
-        for (int i = t; i < NK; i += NT) {
-            const uint4 x = src2[(i & ~63) | swz(i & 63)];
-            __builtin_nontemporal_store(u32x4nt{x.x, x.y, x.z, x.w}, reinterpret_cast<u32x4nt*>(dst2 + i));
-        }
+        for (int i = t; i < NK; i += NT) dst2[i] = src2[(i & ~63) | swz(i & 63)];
     }
 }
 
