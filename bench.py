@@ -462,11 +462,14 @@ def copy_bandwidth(torch):
     return {"bytes_moved": 2 * COPY_BYTES, "ms_median": ms, "gbs": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
 
 
-def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5, ws_gib=None):
+def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5, ws_gib=None, graphs=False):
     """Median call time of one prefill workload; with several input sets the
     calls rotate over them (a 200 MB working set would otherwise stay in the
     256 MB Infinity Cache).  ws_gib caps the workspace (not below the least
-    one the call accepts)."""
+    one the call accepts).  With graphs, the same calls are also captured
+    into HIP graphs (one per input set, each checked bit for bit against its
+    eager call) and timed as replays: the host's launch work then leaves the
+    timed region, which matters for calls of a few hundred microseconds."""
     to = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
                     if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).cuda())
     ins = []
@@ -501,14 +504,48 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5, ws_gib=No
         e1.synchronize()
         ts.append(e0.elapsed_time(e1))
     ms = float(np.median(ts))
+    graph_ms = None
+    if graphs:
+        refs = []
+        for i in range(sets):
+            call(ins[i])
+            torch.cuda.synchronize()
+            refs.append(o.clone())
+        gs = []
+        for i in range(sets):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                call(ins[i])
+            gs.append(gr)
+        torch.cuda.synchronize()
+        for i in range(sets):
+            o.zero_()
+            gs[i].replay()
+            torch.cuda.synchronize()
+            if not torch.equal(o, refs[i]):
+                raise SystemExit("%s: the graph replay differs from the eager call" % name)
+        for i in range(warm):
+            gs[i % sets].replay()
+        torch.cuda.synchronize()
+        tg = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gs[i % sets].replay()
+            e1.record()
+            e1.synchronize()
+            tg.append(e0.elapsed_time(e1))
+        graph_ms = float(np.median(tg))
+        del gs, refs
     if f32:   # fp32 q, k, v, o (4 bytes each per channel), fp32 g, beta; d_k, d_v of the workload
         algo = (4 * (2 * inp.dk + 2 * inp.dv) + 4 * inp.dk + 4) * tokens * H + 2 * 4 * inp.dk * inp.dv * n_seq * H
     else:
         algo = BYTES_PER_TOKEN_HEAD * tokens * H + 2 * STATE_BYTES * n_seq * H
     del ins, o, sT, ws
     torch.cuda.empty_cache()
+    extra = {} if graph_ms is None else {"graph_replay_ms_median": graph_ms}
     return {"tokens": tokens, "heads": H, "sequences": n_seq, "input_sets": sets, "workspace_bytes": ws_bytes,
-            "ms_median": ms,
+            "ms_median": ms, **extra,
             "ms_min": float(np.min(ts)), "ms_max": float(np.max(ts)), "tokens_per_s": tokens / (ms * 1e-3),
             "algorithmic_gbs": algo / (ms * 1e-3) / 1e9, "hbm_frac": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -791,11 +828,11 @@ def main():
             out["decode_layer_core"] = time_decode_layer(kda, torch, kda_inputs)
     if not args.no_extra:
         out["prefill_tiny"] = dict(workload="B=1 H=2 T=256 d=64 fp32 (exact fp32 path), seed 0",
-                                   **time_workload(kda, torch, kda_inputs, "tiny_f32", sets=1))
+                                   **time_workload(kda, torch, kda_inputs, "tiny_f32", sets=1, graphs=True))
         out["prefill_mid"] = dict(workload="B=1 H=32 T=4096 d=128 bf16, seed 1; two input sets rotated",
-                                  **time_workload(kda, torch, kda_inputs, "mid_bf16", sets=2))
+                                  **time_workload(kda, torch, kda_inputs, "mid_bf16", sets=2, graphs=True))
         out["prefill_varlen"] = dict(workload="16 packed sequences, lengths U[512,16384] from seed 3, H=32 d=128 bf16",
-                                     **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1))
+                                     **time_workload(kda, torch, kda_inputs, "varlen_bf16", sets=1, graphs=True))
         out["prefill_gated"] = time_gated(kda, torch, kda_inputs)
         out["prefill_gated_out_norm"] = time_gated(kda, torch, kda_inputs, norm=True)
         out["prefill_layer_core"] = time_gated(kda, torch, kda_inputs, norm=True, conv=True)
