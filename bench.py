@@ -462,6 +462,41 @@ def copy_bandwidth(torch):
     return {"bytes_moved": 2 * COPY_BYTES, "ms_median": ms, "gbs": 2 * COPY_BYTES / (ms * 1e-3) / 1e9}
 
 
+def _graph_replay_ms(torch, call, ins, o, sets, reps, warm):
+    """Median time of `call` replayed from HIP graphs, one per input set, each
+    first checked bit for bit (o) against its eager call."""
+    refs = []
+    for i in range(sets):
+        call(ins[i])
+        torch.cuda.synchronize()
+        refs.append(o.clone())
+    gs = []
+    for i in range(sets):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            call(ins[i])
+        gs.append(gr)
+    torch.cuda.synchronize()
+    for i in range(sets):
+        o.zero_()
+        gs[i].replay()
+        torch.cuda.synchronize()
+        if not torch.equal(o, refs[i]):
+            raise RuntimeError("the graph replay differs from the eager call")
+    for i in range(warm):
+        gs[i % sets].replay()
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gs[i % sets].replay()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
 def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5, ws_gib=None, graphs=False):
     """Median call time of one prefill workload; with several input sets the
     calls rotate over them (a 200 MB working set would otherwise stay in the
@@ -506,37 +541,10 @@ def time_workload(kda, torch, kda_inputs, name, sets, reps=20, warm=5, ws_gib=No
     ms = float(np.median(ts))
     graph_ms = None
     if graphs:
-        refs = []
-        for i in range(sets):
-            call(ins[i])
-            torch.cuda.synchronize()
-            refs.append(o.clone())
-        gs = []
-        for i in range(sets):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                call(ins[i])
-            gs.append(gr)
-        torch.cuda.synchronize()
-        for i in range(sets):
-            o.zero_()
-            gs[i].replay()
-            torch.cuda.synchronize()
-            if not torch.equal(o, refs[i]):
-                raise SystemExit("%s: the graph replay differs from the eager call" % name)
-        for i in range(warm):
-            gs[i % sets].replay()
-        torch.cuda.synchronize()
-        tg = []
-        for i in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            gs[i % sets].replay()
-            e1.record()
-            e1.synchronize()
-            tg.append(e0.elapsed_time(e1))
-        graph_ms = float(np.median(tg))
-        del gs, refs
+        try:
+            graph_ms = _graph_replay_ms(torch, call, ins, o, sets, reps, warm)
+        except Exception as exc:   # an extra figure: never lose the bench line over it
+            graph_ms = "not measured: %s" % exc
     if f32:   # fp32 q, k, v, o (4 bytes each per channel), fp32 g, beta; d_k, d_v of the workload
         algo = (4 * (2 * inp.dk + 2 * inp.dv) + 4 * inp.dk + 4) * tokens * H + 2 * 4 * inp.dk * inp.dv * n_seq * H
     else:
