@@ -96,10 +96,12 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def load_traffic(kernel: str, path: str = TRAFFIC_JSON):
     """HBM bytes per launch from committed rocprofv3 --pmc counters, valid only
     for the kernel sources they were taken on."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f).get(kernel)
@@ -400,7 +402,7 @@ def _counter_rows(d):
     return rows
 
 
-def write_traffic(fetch_dir, write_dir):
+def write_traffic(fetch_dir, write_dir, path: str = TRAFFIC_JSON):
     """HBM bytes per call of each path from rocprofv3 FETCH_SIZE / WRITE_SIZE
     (KiB per dispatch).  Each counter is scaled by what it reads for the bench's
     own device-to-device copy of COPY_BYTES, whose true traffic is COPY_BYTES
@@ -433,10 +435,10 @@ def write_traffic(fetch_dir, write_dir):
             wr = v["WRITE_SIZE"] * scale["WRITE_SIZE"]
             out[key] = {"source_hash": kernel_source_hash(key), "hbm_bytes_per_launch": rd + wr, "read_bytes": rd,
                         "write_bytes": wr, "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
     print(json.dumps(out, indent=1, sort_keys=True))
+    return out
 
 
 COPY_BYTES = 1 << 30
@@ -744,6 +746,7 @@ def mfma_summary(d):
                      "mfma_busy_frac": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * 256 * 4),
                      "sq_busy_cycles": c.get("SQ_BUSY_CYCLES"), "gpu_cycles_per_xcd": cycles}
     print(json.dumps(out, indent=1, sort_keys=True))
+    return out
 
 
 def main():
