@@ -79,7 +79,8 @@ WORKLOAD_LINES = {"tiny": "tiny_f32", "mid": "mid_bf16", "long": "long_bf16", "v
                   "decode": "decode"}
 
 
-# the sources each measured path is built from (kernels, their headers, the launch code)
+# the sources each measured path is built from (kernels, their headers, the launch code; the build
+# script is hashed with them)
 KERNEL_SOURCES = {
     "chunk_fwd": ("kda_chunk_two_pass.hip", "kda_stage_plan.h", "kda_mfma.h", "kda_kernels.h", "kda_device.h",
                   "kda_abi.hip"),
@@ -88,11 +89,15 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the sources a path is built from and of the build script (its
+    compiler options change the kernels too)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "gated_delta_rule_fwd_amd", "csrc")
+    pkg = os.path.join(ROOT, "gated_delta_rule_fwd_amd")
     for name in sorted(KERNEL_SOURCES[kernel]):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(pkg, "csrc", name), "rb") as f:
             h.update(name.encode() + f.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(b"build.py" + f.read())
     return h.hexdigest()[:16]
 
 
